@@ -112,7 +112,7 @@ def core_out_f64(core_codes, core_scale, w_codes, w_scales, g_w):
 
 
 def delta_linear(core_out64, row_to_cube, d_codes, d_scales, g_d, w_codes, w_scales, g_w,
-                 D_bits, lora_up_bits, rows=None):
+                 D, lora_up_bits, rows=None):
     """Y64 = core_out[cube(m)] + delta_deq @ W_deqᵀ + D @ L2, and its bf16 bits.
 
     `rows` (optional) restricts the output to those rows (the inputs are then the full tensors).
@@ -121,5 +121,5 @@ def delta_linear(core_out64, row_to_cube, d_codes, d_scales, g_d, w_codes, w_sca
         rows = np.arange(d_codes.shape[0])
     Ad = nvfp4_dequantize(d_codes[rows], d_scales[rows], g_d)
     Wd = nvfp4_dequantize(w_codes, w_scales, g_w)
-    y64 = core_out64[row_to_cube[rows]] + Ad @ Wd.T + lowrank_up(D_bits[rows], lora_up_bits)
+    y64 = core_out64[row_to_cube[rows]] + Ad @ Wd.T + lowrank_up(np.asarray(D)[rows], lora_up_bits)
     return y64, bf16_rne(y64)

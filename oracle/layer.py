@@ -4,7 +4,7 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 
     calibrate (ax, aw, λ, act_amax)  ->  weight prep (R32 = W' − L1L2, quantised with its own
     dynamic tensor amax max|R32|)  ->  activation prep (X̂ = X/λ quantised with the static
-    act_amax for NVFP4, or per 64-group for int4; D = bf16(bf16(X̂)·L1))  ->  GEMM.
+    act_amax for NVFP4, or per 64-group for int4; D = bf16(X̂)·L1 unrounded)  ->  GEMM.
 """
 import numpy as np
 
@@ -25,7 +25,7 @@ def prepare_weight(W_bits, lam, lora_down_bits, lora_up_bits, fmt):
 
 
 def prepare_activation(X_bits, lam, act_amax, lora_down_bits, fmt):
-    """Quantised activation: dict(codes, scales, g (NVFP4), n_sat (NVFP4), D bits, xhat)."""
+    """Quantised activation: dict(codes, scales, g (NVFP4), n_sat (NVFP4), D float64, xhat)."""
     xhat = calib.smooth(X_bits, lam)
     D = gemm.lowrank_down(xhat, lora_down_bits)
     if fmt == "int4":
