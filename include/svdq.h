@@ -1,0 +1,225 @@
+/*
+ * svdq.h — C ABI of the MI355X (gfx950) SVDQuant W4A4 linear layer.
+ *
+ * The layer of a packed [text | video | audio] video DiT:
+ *
+ *     Y = X̂·L1·L2 + Q(X̂)·Q(R),    X̂ = X·diag(λ)⁻¹,   W' = diag(λ)·W = L1·L2 + R
+ *
+ * ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph: outliers absorbed by a
+ * 16-bit low-rank branch, 4-bit residual weight, activations quantised at run time;
+ * "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", sections "Why" and
+ * "Calibration": NVFP4 blocks of 16 channels with an FP8 scale, the kernel sees X / λ, λ fed by
+ * activation statistics accumulated under a modality mask.)
+ *
+ * Conventions common to every entry point
+ * ---------------------------------------
+ *  - Tensors are DEVICE pointers owned by the caller; the library never keeps them and never
+ *    allocates memory.  Host pointers are marked "host".
+ *  - bf16 tensors are passed as uint16_t bit patterns.
+ *  - Matrices are row-major with the reduction dimension K contiguous.  X is [M, K] with
+ *    leading dimension ldx (elements), W is [N, K] (out, in) with leading dimension ldw.
+ *    Channels are in NATURAL order everywhere; any interleaving used by a kernel is private.
+ *  - Packed 4-bit codes: two per byte, element 2j in the low nibble of byte j.
+ *      NVFP4: sign-magnitude E2M1 codes; scales one E4M3 byte per 16 elements, [rows, K/16];
+ *             plus one fp32 tensor scale g (device float[1]).
+ *      INT4_G64: two's-complement int4 codes; scales one fp16 per 64 elements, [rows, K/64].
+ *  - Shapes: K must be a multiple of 256; N a multiple of 256 for the GEMMs; M >= 1 any value
+ *    (ragged tails are masked).  Rank r in [0, 128].  Leading dimensions must keep every row
+ *    16-byte aligned, and every device pointer must be 16-byte aligned.
+ *  - Streams: every call enqueues on `stream` (a hipStream_t; NULL = the default stream) and
+ *    returns without synchronising.  Arguments are validated on the host before anything is
+ *    enqueued; an invalid call enqueues nothing.
+ *  - Errors: every entry point returns an svdq_status.  svdq_last_error() returns a
+ *    thread-local message describing the last failure of the calling thread.  Inputs must be
+ *    finite; NaN / Inf inputs give unspecified codes.  Calls that overlap on one stream are
+ *    ordered; the library has no global mutable state (it is reentrant).
+ */
+#ifndef SVDQ_H
+#define SVDQ_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef struct ihipStream_t* svdq_stream_t; /* same type as hipStream_t */
+
+typedef enum svdq_status {
+  SVDQ_OK = 0,
+  SVDQ_INVALID_ARG = 1,       /* bad enum, flag or value */
+  SVDQ_UNSUPPORTED_SHAPE = 2, /* sizes, leading dimensions or alignment not supported */
+  SVDQ_NULL_POINTER = 3,      /* a required pointer is NULL */
+  SVDQ_HIP_ERROR = 4,         /* a HIP launch or runtime call failed */
+  SVDQ_NOT_IMPLEMENTED = 5
+} svdq_status;
+
+typedef enum svdq_format {
+  SVDQ_NVFP4 = 0,    /* E2M1 codes, E4M3 scale per 16 along K, fp32 tensor scale */
+  SVDQ_INT4_G64 = 1  /* symmetric int4 codes, fp16 scale per 64 along K */
+} svdq_format;
+
+/* Modality bits of a calibration mask (rows are packed text | video | audio). */
+#define SVDQ_MOD_TEXT 1u
+#define SVDQ_MOD_VIDEO 2u
+#define SVDQ_MOD_AUDIO 4u
+
+/* Human-readable name of a status code (static storage). */
+const char* svdq_status_string(int status);
+/* Message of the calling thread's last failed call ("" if none). */
+const char* svdq_last_error(void);
+/* ABI version: 1. */
+int svdq_abi_version(void);
+
+/*
+ * λ calibration reduction ("MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated
+ * on", section "Calibration": activation statistics accumulated under a modality mask feed λ;
+ * opening section: one λ per input channel shared by all modalities).
+ *
+ *   ax[μ, k] = max over rows m of modality μ of |X[m, k]|        μ = 0 text, 1 video, 2 audio
+ *   aw[k]    = max_n |W[n, k]|                                   (1 when W is NULL)
+ *   sel[k]   = max over the modalities set in modality_mask of ax[μ, k]
+ *   λ[k]     = sqrt(sel/aw) in fp32 for alpha == 0.5 (sel^α / aw^(1-α) in fp64 otherwise),
+ *              1 when sel == 0, aw == 0 or modality_mask == 0
+ *   act_amax = max_k fp32(max_μ ax[μ, k] · fp32(1/λ[k]))   (= max |X̂| over ALL rows)
+ *
+ * seg (host int64[4]) = {0, n_text, n_text + n_video, M}, non-decreasing.
+ * accumulate != 0 folds this batch into the running maxima already held in ax / aw
+ * (calibration over several batches); accumulate == 0 overwrites them.  λ and act_amax are
+ * always recomputed from the (accumulated) ax and aw.
+ * Outputs (device, fp32): ax [3, K], aw [K], lambda [K], act_amax [1].  Bit-exact.
+ */
+svdq_status svdq_calibrate_lambda(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                  const int64_t* seg, const uint16_t* W, int64_t N, int64_t ldw,
+                                  uint32_t modality_mask, float alpha, int accumulate, float* ax,
+                                  float* aw, float* lambda, float* act_amax,
+                                  svdq_stream_t stream);
+
+/*
+ * Weight preparation ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph:
+ * low-rank branch plus a 4-bit residual; here rounded to nearest).
+ *
+ *   R[n, k] = λ_k·W[n, k] − Σ_{i=0..r-1} lora_up[n, i]·lora_down[i, k]   (fp64, i ascending)
+ *   R32 = fp32(R), then quantised:
+ *     NVFP4: tensor amax = max |R32|; g = amax/2688; per 16-block s = E4M3(max|x| / (6g)),
+ *            codes = E2M1(x · 1/(s·g)), round to nearest even, satfinite.
+ *     INT4_G64: s = fp16(max|x| / 7); codes = clamp(rint(x · 1/s), −8, 7).
+ * lambda may be NULL (λ = 1).  lora_down [r, K] and lora_up [N, r] are bf16 (ignored when
+ * r == 0).  Outputs: codes [N, K/2]; scales ([N, K/16] E4M3 bytes or [N, K/64] fp16);
+ * tensor_scale (device float[1], g; required for NVFP4, ignored for INT4_G64).  Bit-exact.
+ */
+svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                 const float* lambda, const uint16_t* lora_down,
+                                 const uint16_t* lora_up, int64_t r, uint8_t* codes,
+                                 void* scales, float* tensor_scale, svdq_stream_t stream);
+
+/*
+ * Activation quantisation fused with the low-rank down-projection (the kernel sees X / λ:
+ * "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", section "Why").
+ *
+ *   X̂ = fp32(X) · fp32(1/λ)          (lambda may be NULL: λ = 1)
+ *   NVFP4: g_a = act_amax / 2688, blocks of 16 as in svdq_quantize_weight.  act_amax is the
+ *          static amax from svdq_calibrate_lambda; NULL selects a dynamic pre-pass computing
+ *          max |X̂| over all M rows.  tensor_scale (device float[1]) receives g_a.
+ *   INT4_G64: per 64-group scales; tensor_scale and act_amax are ignored.
+ *   D = bf16(X̂) · lora_downᵀ         [M, r] fp32: products of bf16 operands accumulated in
+ *                                     fp32 and NOT rounded to bf16 (D may be NULL iff r == 0)
+ * sat_count (nullable, device uint32[1]): the number of NVFP4 blocks whose absmax exceeds the
+ * tensor amax is ADDED to it (the caller zeroes it).
+ * Outputs: codes [M, K/2], scales, tensor_scale, D.  Codes and scales bit-exact.
+ */
+svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, int64_t K,
+                                        int64_t ldx, const float* lambda, const float* act_amax,
+                                        const uint16_t* lora_down, int64_t r, uint8_t* codes,
+                                        void* scales, float* tensor_scale, float* D,
+                                        uint32_t* sat_count, svdq_stream_t stream);
+
+/*
+ * W4A4 GEMM with the low-rank up-projection, bf16 output.
+ *
+ *   NVFP4:    Y = bf16( g_a·g_w · Σ_k (c_a·s_a)(c_w·s_w) + D·lora_upᵀ [+ core_out[cube(m)]] )
+ *   INT4_G64: Y = bf16( Σ_groups s_a·s_w · Σ_k c_a·c_w + D·lora_upᵀ )
+ * a_codes/a_scales [M, ...] from svdq_quant_act_lowrank_down, w_codes/w_scales [N, ...] from
+ * svdq_quantize_weight; g_a / g_w device float[1] (NVFP4 only).  D [M, r] fp32 (from the
+ * activation kernel), lora_up [N, r] bf16.
+ * core_out (nullable, fp32 [n_cubes, N]) and row_to_cube (int32 [M]) add the DeltaQuant core
+ * term ("DeltaQuant on MiniMax-H3"; NVFP4 only; both or neither).  Y [M, N] bf16, leading
+ * dimension ldy.  fp32 accumulation; results within the layer tolerance of the float64 value.
+ */
+svdq_status svdq_w4a4_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                           const void* a_scales, const float* g_a, const uint8_t* w_codes,
+                           const void* w_scales, const float* g_w, const float* D,
+                           const uint16_t* lora_up, int64_t r, const float* core_out,
+                           const int32_t* row_to_cube, uint16_t* Y, int64_t ldy,
+                           svdq_stream_t stream);
+
+/*
+ * DeltaQuant cube geometry, HOST function ("DeltaQuant on MiniMax-H3", sections "The audio win
+ * has a mechanism" (1-D cubes of consecutive rows for non-video rows) and "Standing
+ * configuration" (geometry derived per request, identical across steps)).
+ *
+ * Rows are [n_text | T·H·W video in raster (t, h, w) order | n_audio].  A video row belongs to
+ * cube (t/ct, h/ch, w/cw) (ragged at the grid edges); text and audio rows form cubes of cube1d
+ * consecutive rows of their segment.  Cubes are numbered in order of their first row; members
+ * are listed ascending.  All pointers are HOST pointers: row_to_cube int32 [M],
+ * cube_ptr int32 [n_cubes + 1], cube_rows int32 [M], n_cubes int64 [1].  Pass row_to_cube ==
+ * NULL to only count: n_cubes is written and nothing else.
+ */
+svdq_status svdq_cube_geometry(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch,
+                               int64_t cw, int64_t n_text, int64_t n_audio, int64_t cube1d,
+                               int32_t* row_to_cube, int32_t* cube_ptr, int32_t* cube_rows,
+                               int64_t* n_cubes);
+
+/*
+ * DeltaQuant activations ("DeltaQuant on MiniMax-H3", sections "Why DeltaQuant does not beat
+ * SVDQuant here", "The activation scale bound held", "Deviations from the paper").
+ *
+ *   X̂ = fp32(X)·fp32(1/λ)
+ *   core[c, k] = fp32(ascending fp32 sum of X̂ over the cube's rows) / |c|
+ *   core codes: E4M3(core · 1/s_c) per core row, s_c = max_k|core[c, k]| / 448 (fp32)
+ *   delta = X̂ − core[cube(m)] (fp32, unquantised core), NVFP4 with tensor amax 2·act_amax
+ *   D = bf16(X̂)·lora_downᵀ  (fp32, as in svdq_quant_act_lowrank_down)
+ * cube_ptr / cube_rows: device int32 CSR from svdq_cube_geometry.  Outputs: core_codes
+ * [n_cubes, K] E4M3 bytes, core_scale fp32 [n_cubes], delta_codes [M, K/2], delta_scales
+ * [M, K/16], g_delta float[1], D [M, r] fp32; sat_count (nullable) as in
+ * svdq_quant_act_lowrank_down.  Codes and scales bit-exact.
+ */
+svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                 const float* lambda, const float* act_amax,
+                                 const int32_t* cube_ptr, const int32_t* cube_rows,
+                                 int64_t n_cubes, const uint16_t* lora_down, int64_t r,
+                                 uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
+                                 uint8_t* delta_scales, float* g_delta, float* D,
+                                 uint32_t* sat_count, svdq_stream_t stream);
+
+/*
+ * DeltaQuant core GEMM on a 16-bit path ("DeltaQuant on MiniMax-H3", section "Deviations from
+ * the paper": the core branch does not take the FP4 scaled dot):
+ *   core_out[c, n] = s_c · g_w · Σ_k e4m3(core_codes[c, k]) · (c_w·s_w)[n, k]     fp32 [n_cubes, N]
+ * w_* are NVFP4 weights from svdq_quantize_weight.
+ */
+svdq_status svdq_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,
+                           const float* core_scale, const uint8_t* w_codes,
+                           const uint8_t* w_scales, const float* g_w, float* core_out,
+                           svdq_stream_t stream);
+
+/*
+ * Per-modality relative-L2 sums ("MiniMax-H3 NVFP4 — what the smoothing scale should be
+ * calibrated on", section "The metric that picks the winner also hides the cost").
+ * For each of the n_rows sampled rows m = rows[i] with group μ = row_group[i] in 0..3
+ * (text, video, audio, uniform):
+ *   Y_ref[m, :] = bf16(X[m, :] · Wᵀ)   (unsmoothed bf16 X [M, K] and W [N, K], fp32 accumulation)
+ *   sums[μ][0] += Σ_n (Y[m, n] − Y_ref[m, n])²,   sums[μ][1] += Σ_n Y_ref[m, n]²   (fp64)
+ * sums (device double[8]) is ADDED to (the caller zeroes it).  rows int32, row_group int8.
+ */
+svdq_status svdq_score_modal_rel_l2(const uint16_t* Y, int64_t ldy, const uint16_t* X,
+                                    int64_t ldx, const uint16_t* W, int64_t ldw, int64_t M,
+                                    int64_t N, int64_t K, const int32_t* rows,
+                                    const int8_t* row_group, int64_t n_rows, double* sums,
+                                    svdq_stream_t stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* SVDQ_H */

@@ -1,0 +1,108 @@
+"""CPU tests of the C ABI: the library loads without a GPU, exports every entry point declared in
+include/svdq.h, validates arguments before enqueuing anything, and computes the host-side cube
+geometry exactly like the oracle."""
+import ctypes
+
+import numpy as np
+import pytest
+
+from w4a4_quantized_dit_amd import _lib
+from oracle import delta as DQ
+
+OK, INVALID, SHAPE, NULLP, HIPERR, NOTIMPL = 0, 1, 2, 3, 4, 5
+P = 1 << 20          # a fake, 16-byte aligned, non-NULL "device pointer" (never dereferenced)
+MIS = P + 4          # misaligned
+
+
+@pytest.fixture(scope="module")
+def lib():
+    return _lib.load()
+
+
+def test_every_declared_entry_point_is_exported(lib):
+    names = _lib.header_entry_points()
+    assert len(names) >= 11
+    for n in names:
+        assert hasattr(lib, n), n
+    assert lib.svdq_abi_version() == 1
+    for s in range(6):
+        assert lib.svdq_status_string(s).decode().startswith("SVDQ_")
+
+
+def _seg(*v):
+    return ctypes.cast((ctypes.c_int64 * 4)(*v), ctypes.c_void_p)
+
+
+def _err(lib):
+    return lib.svdq_last_error().decode()
+
+
+def test_calibrate_validation(lib):
+    f = lib.svdq_calibrate_lambda
+    good = dict(X=P, M=64, K=256, ldx=256, seg=_seg(0, 1, 60, 64), W=P, N=32, ldw=256, mask=7,
+                alpha=0.5, acc=0, ax=P, aw=P, lam=P, amax=P, s=None)
+
+    def call(**kw):
+        a = dict(good, **kw)
+        return f(a["X"], a["M"], a["K"], a["ldx"], a["seg"], a["W"], a["N"], a["ldw"], a["mask"],
+                 a["alpha"], a["acc"], a["ax"], a["aw"], a["lam"], a["amax"], a["s"])
+    assert call(X=None) == NULLP and "X" in _err(lib)
+    assert call(K=100) == SHAPE and "K=100" in _err(lib)
+    assert call(ldx=200) == SHAPE
+    assert call(X=MIS) == SHAPE
+    assert call(seg=_seg(0, 10, 5, 64)) == INVALID
+    assert call(seg=_seg(0, 1, 60, 63)) == INVALID
+    assert call(mask=8) == INVALID
+    assert call(alpha=1.0) == INVALID
+    assert call(M=0, seg=_seg(0, 0, 0, 0)) == SHAPE
+    assert call(lam=None) == NULLP
+
+
+def test_quantize_weight_validation(lib):
+    f = lib.svdq_quantize_weight
+    assert f(7, P, 64, 256, 256, None, P, P, 32, P, P, P, None) == INVALID
+    assert f(0, P, 64, 256, 256, None, P, P, 32, P, P, None, None) == NULLP   # NVFP4 needs g
+    assert f(0, P, 64, 256, 256, None, P, P, 12, P, P, P, None) == SHAPE      # r % 8
+    assert f(0, P, 64, 256, 256, None, P, P, 136, P, P, P, None) == SHAPE     # r > 128
+    assert f(0, P, 64, 256, 256, None, None, P, 32, P, P, P, None) == NULLP
+    assert f(0, P, 64, 320, 320, None, P, P, 32, P, P, P, None) == SHAPE
+
+
+def test_quant_act_and_gemm_validation(lib):
+    qa = lib.svdq_quant_act_lowrank_down
+    assert qa(0, P, 64, 256, 256, None, None, P, 32, P, P, None, P, None, None) == NULLP
+    assert qa(0, P, 64, 256, 128, None, None, P, 32, P, P, P, P, None, None) == SHAPE
+    assert qa(1, P, 64, 256, 256, None, None, P, 32, P, P, None, None, None, None) == NULLP
+    g = lib.svdq_w4a4_gemm
+    assert g(0, 64, 128, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
+    assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
+    assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, P, None, P, 256, None) == INVALID
+    assert g(1, 64, 256, 256, P, P, None, P, P, None, P, P, 32, P, P, P, 256, None) == INVALID
+    assert g(0, 64, 256, 256, P, P, None, P, P, P, P, P, 32, None, None, P, 256, None) == NULLP
+
+
+def test_other_validation(lib):
+    assert lib.svdq_gemm_core(0, 256, 256, P, P, P, P, P, P, None) == SHAPE
+    assert lib.svdq_score_modal_rel_l2(P, 256, P, 256, P, 256, 10, 256, 256, P, P, 4, None,
+                                       None) == NULLP
+    assert lib.svdq_delta_quant_act(P, 10, 256, 256, None, P, P, P, 11, P, 8, P, P, P, P, P, P,
+                                    None, None) == INVALID
+    assert lib.svdq_cube_geometry(2, 2, 2, 4, 4, 4, 0, 0, 4, None, None, None, None) == NULLP
+
+
+def test_cube_geometry_matches_oracle():
+    for args in ((31, 24, 42, 2, 2, 2, 312, 128, 4), (3, 2, 3, 2, 2, 2, 5, 2, 2),
+                 (5, 7, 3, 2, 2, 2, 0, 9, 4), (1, 1, 1, 1, 1, 1, 3, 0, 2)):
+        got = _lib.svdq_cube_geometry(*args)
+        want = DQ.cube_geometry(*args)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w), args
+
+
+def test_cube_geometry_rejects_bad_sizes(lib):
+    n = ctypes.c_int64(0)
+    pn = ctypes.cast(ctypes.pointer(n), ctypes.c_void_p)
+    assert lib.svdq_cube_geometry(2, 2, 2, 0, 2, 2, 0, 0, 4, None, None, None, pn) == INVALID
+    assert lib.svdq_cube_geometry(2, 2, 2, 4, 4, 2, 0, 0, 4, None, None, None, pn) == SHAPE
+    assert lib.svdq_cube_geometry(31, 24, 42, 2, 2, 2, 312, 128, 4, None, None, None, pn) == OK
+    assert n.value == 4142

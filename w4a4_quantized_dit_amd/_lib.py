@@ -1,0 +1,258 @@
+"""ctypes binding of libsvdq.so: argument marshalling only.
+
+Every function below has the name of the C entry point it calls and takes torch tensors (device
+memory owned by the caller) plus sizes; it checks dtypes / devices / shapes, passes raw pointers
+and the current torch stream, and raises SvdqError on a non-zero status.  No step of the layer
+runs in Python: when the library is missing, loading fails loudly.
+"""
+import ctypes
+import os
+import re
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(HERE, "libsvdq.so")
+HEADER = os.path.join(os.path.dirname(HERE), "include", "svdq.h")
+
+NVFP4, INT4_G64 = 0, 1
+
+_c_p = ctypes.c_void_p
+_i64 = ctypes.c_int64
+_SIGS = {
+    "svdq_status_string": (ctypes.c_char_p, [ctypes.c_int]),
+    "svdq_last_error": (ctypes.c_char_p, []),
+    "svdq_abi_version": (ctypes.c_int, []),
+    "svdq_calibrate_lambda": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _i64, _i64,
+                                             ctypes.c_uint32, ctypes.c_float, ctypes.c_int,
+                                             _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "svdq_quantize_weight": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p, _c_p,
+                                            _c_p, _i64, _c_p, _c_p, _c_p, _c_p]),
+    "svdq_quant_act_lowrank_down": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p,
+                                                   _c_p, _c_p, _i64, _c_p, _c_p, _c_p, _c_p,
+                                                   _c_p, _c_p]),
+    "svdq_w4a4_gemm": (ctypes.c_int, [ctypes.c_int, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p,
+                                      _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p, _i64,
+                                      _c_p]),
+    "svdq_cube_geometry": (ctypes.c_int, [_i64] * 9 + [_c_p, _c_p, _c_p, _c_p]),
+    "svdq_delta_quant_act": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p,
+                                            _i64, _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                            _c_p, _c_p, _c_p]),
+    "svdq_gemm_core": (ctypes.c_int, [_i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
+                                      _c_p]),
+    "svdq_score_modal_rel_l2": (ctypes.c_int, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _i64, _i64,
+                                               _i64, _c_p, _c_p, _i64, _c_p, _c_p]),
+}
+
+_lib = None
+
+
+class SvdqError(RuntimeError):
+    def __init__(self, status, message):
+        super().__init__(f"{message} ({status_string(status)})")
+        self.status = status
+
+
+def load():
+    """Load libsvdq.so (built in-tree by w4a4_quantized_dit_amd.build)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise ImportError(f"{LIB_PATH} is missing: build it with "
+                              "`python -m w4a4_quantized_dit_amd.build`")
+        lib = ctypes.CDLL(LIB_PATH)
+        for name, (res, args) in _SIGS.items():
+            fn = getattr(lib, name)
+            fn.restype = res
+            fn.argtypes = args
+        _lib = lib
+    return _lib
+
+
+def header_entry_points():
+    """Names of the functions declared in include/svdq.h."""
+    with open(HEADER) as f:
+        text = f.read()
+    return sorted(set(re.findall(r"^\s*(?:const\s+)?\w+\*?\s+\*?(svdq_\w+)\s*\(", text, re.M)))
+
+
+def status_string(status):
+    return load().svdq_status_string(status).decode()
+
+
+def last_error():
+    return load().svdq_last_error().decode()
+
+
+def _check(status):
+    if status != 0:
+        raise SvdqError(status, last_error())
+
+
+# ------------------------------------------------------------------------------------------
+# tensor marshalling
+# ------------------------------------------------------------------------------------------
+
+def _torch():
+    import torch
+    return torch
+
+
+def _ptr(t, dtype=None, name="tensor", numel=None):
+    """Device pointer of a contiguous cuda tensor (None -> NULL)."""
+    if t is None:
+        return None
+    torch = _torch()
+    if not isinstance(t, torch.Tensor):
+        raise TypeError(f"{name} must be a torch.Tensor")
+    if not t.is_cuda:
+        raise ValueError(f"{name} must be a device tensor")
+    if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
+        raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if numel is not None and t.numel() < numel:
+        raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
+    return t.data_ptr()
+
+
+def _stream(stream=None):
+    torch = _torch()
+    s = torch.cuda.current_stream() if stream is None else stream
+    return s.cuda_stream
+
+
+def _bf16():
+    torch = _torch()
+    return (torch.bfloat16, torch.int16)
+
+
+def _scale_dtype(fmt):
+    torch = _torch()
+    return torch.uint8 if fmt == NVFP4 else torch.float16
+
+
+# ------------------------------------------------------------------------------------------
+# entry points
+# ------------------------------------------------------------------------------------------
+
+def svdq_calibrate_lambda(X, seg, W, modality_mask, alpha, accumulate, ax, aw, lam, act_amax,
+                          stream=None):
+    """λ calibration reduction; X [M, K] bf16, seg 4 ints, W [N, K] bf16 or None; outputs fp32."""
+    torch = _torch()
+    M, K = X.shape
+    N = W.shape[0] if W is not None else 0
+    seg_arr = (ctypes.c_int64 * 4)(*[int(v) for v in seg])
+    f32 = torch.float32
+    _check(load().svdq_calibrate_lambda(
+        _ptr(X, _bf16(), "X"), M, K, X.stride(0), ctypes.cast(seg_arr, _c_p),
+        _ptr(W, _bf16(), "W"), N, W.stride(0) if W is not None else K,
+        int(modality_mask), float(alpha), int(accumulate),
+        _ptr(ax, f32, "ax", 3 * K), _ptr(aw, f32, "aw", K), _ptr(lam, f32, "lambda", K),
+        _ptr(act_amax, f32, "act_amax", 1), _stream(stream)))
+
+
+def svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, tensor_scale,
+                         stream=None):
+    """Residual weight quantisation; W [N, K] bf16; outputs codes [N, K/2] u8, scales, g_w."""
+    torch = _torch()
+    N, K = W.shape
+    blk = 16 if fmt == NVFP4 else 64
+    _check(load().svdq_quantize_weight(
+        int(fmt), _ptr(W, _bf16(), "W"), N, K, W.stride(0), _ptr(lam, torch.float32, "lambda", K),
+        _ptr(lora_down if r else None, _bf16(), "lora_down", r * K),
+        _ptr(lora_up if r else None, _bf16(), "lora_up", N * r), int(r),
+        _ptr(codes, torch.uint8, "codes", N * K // 2),
+        _ptr(scales, _scale_dtype(fmt), "scales", N * K // blk),
+        _ptr(tensor_scale, torch.float32, "tensor_scale", 1), _stream(stream)))
+
+
+def svdq_quant_act_lowrank_down(fmt, X, lam, act_amax, lora_down, r, codes, scales,
+                                tensor_scale, D, sat_count=None, stream=None):
+    """Activation quantisation + D = bf16(X̂)·L1 (fp32 [M, r]); X [M, K] bf16."""
+    torch = _torch()
+    M, K = X.shape
+    blk = 16 if fmt == NVFP4 else 64
+    _check(load().svdq_quant_act_lowrank_down(
+        int(fmt), _ptr(X, _bf16(), "X"), M, K, X.stride(0),
+        _ptr(lam, torch.float32, "lambda", K), _ptr(act_amax, torch.float32, "act_amax", 1),
+        _ptr(lora_down if r else None, _bf16(), "lora_down", r * K), int(r),
+        _ptr(codes, torch.uint8, "codes", M * K // 2),
+        _ptr(scales, _scale_dtype(fmt), "scales", M * K // blk),
+        _ptr(tensor_scale, torch.float32, "tensor_scale", 1),
+        _ptr(D if r else None, torch.float32, "D", M * r),
+        _ptr(sat_count, (torch.int32,), "sat_count", 1), _stream(stream)))
+
+
+def svdq_w4a4_gemm(fmt, M, N, K, a_codes, a_scales, g_a, w_codes, w_scales, g_w, D, lora_up, r,
+                   Y, core_out=None, row_to_cube=None, stream=None):
+    """Y [M, N] bf16 = W4A4 GEMM + D·L2 (+ core term)."""
+    torch = _torch()
+    blk = 16 if fmt == NVFP4 else 64
+    _check(load().svdq_w4a4_gemm(
+        int(fmt), M, N, K, _ptr(a_codes, torch.uint8, "a_codes", M * K // 2),
+        _ptr(a_scales, _scale_dtype(fmt), "a_scales", M * K // blk),
+        _ptr(g_a, torch.float32, "g_a", 1), _ptr(w_codes, torch.uint8, "w_codes", N * K // 2),
+        _ptr(w_scales, _scale_dtype(fmt), "w_scales", N * K // blk),
+        _ptr(g_w, torch.float32, "g_w", 1), _ptr(D if r else None, torch.float32, "D", M * r),
+        _ptr(lora_up if r else None, _bf16(), "lora_up", N * r), int(r),
+        _ptr(core_out, torch.float32, "core_out"), _ptr(row_to_cube, torch.int32, "row_to_cube", M),
+        _ptr(Y, _bf16(), "Y", M * N), Y.stride(0), _stream(stream)))
+
+
+def svdq_cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d):
+    """Host geometry: returns numpy (row_to_cube, cube_ptr, cube_rows)."""
+    import numpy as np
+    lib = load()
+    n = ctypes.c_int64(0)
+    _check(lib.svdq_cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d, None, None, None,
+                                  ctypes.cast(ctypes.pointer(n), _c_p)))
+    M = n_text + T * H * W + n_audio
+    r2c = np.zeros(M, np.int32)
+    ptr = np.zeros(n.value + 1, np.int32)
+    rows = np.zeros(M, np.int32)
+    _check(lib.svdq_cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d,
+                                  r2c.ctypes.data, ptr.ctypes.data, rows.ctypes.data,
+                                  ctypes.cast(ctypes.pointer(n), _c_p)))
+    return r2c, ptr, rows
+
+
+def svdq_delta_quant_act(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, lora_down, r,
+                         core_codes, core_scale, delta_codes, delta_scales, g_delta, D,
+                         sat_count=None, stream=None):
+    """DeltaQuant activations: FP8 cube-mean core + NVFP4 delta + D."""
+    torch = _torch()
+    M, K = X.shape
+    _check(load().svdq_delta_quant_act(
+        _ptr(X, _bf16(), "X"), M, K, X.stride(0), _ptr(lam, torch.float32, "lambda", K),
+        _ptr(act_amax, torch.float32, "act_amax", 1), _ptr(cube_ptr, torch.int32, "cube_ptr"),
+        _ptr(cube_rows, torch.int32, "cube_rows", M), int(n_cubes),
+        _ptr(lora_down if r else None, _bf16(), "lora_down", r * K), int(r),
+        _ptr(core_codes, torch.uint8, "core_codes", n_cubes * K),
+        _ptr(core_scale, torch.float32, "core_scale", n_cubes),
+        _ptr(delta_codes, torch.uint8, "delta_codes", M * K // 2),
+        _ptr(delta_scales, torch.uint8, "delta_scales", M * K // 16),
+        _ptr(g_delta, torch.float32, "g_delta", 1), _ptr(D if r else None, torch.float32, "D", M * r),
+        _ptr(sat_count, (torch.int32,), "sat_count", 1), _stream(stream)))
+
+
+def svdq_gemm_core(n_cubes, N, K, core_codes, core_scale, w_codes, w_scales, g_w, core_out,
+                   stream=None):
+    """core_out [n_cubes, N] fp32."""
+    torch = _torch()
+    _check(load().svdq_gemm_core(
+        int(n_cubes), N, K, _ptr(core_codes, torch.uint8, "core_codes", n_cubes * K),
+        _ptr(core_scale, torch.float32, "core_scale", n_cubes),
+        _ptr(w_codes, torch.uint8, "w_codes", N * K // 2),
+        _ptr(w_scales, torch.uint8, "w_scales", N * K // 16), _ptr(g_w, torch.float32, "g_w", 1),
+        _ptr(core_out, torch.float32, "core_out", n_cubes * N), _stream(stream)))
+
+
+def svdq_score_modal_rel_l2(Y, X, W, rows, row_group, sums, stream=None):
+    """Adds per-group (Σ(Y−Y_ref)², ΣY_ref²) into sums (fp64 [4, 2])."""
+    torch = _torch()
+    M, K = X.shape
+    N = W.shape[0]
+    _check(load().svdq_score_modal_rel_l2(
+        _ptr(Y, _bf16(), "Y", M * N), Y.stride(0), _ptr(X, _bf16(), "X"), X.stride(0),
+        _ptr(W, _bf16(), "W"), W.stride(0), M, N, K, _ptr(rows, torch.int32, "rows"),
+        _ptr(row_group, torch.int8, "row_group"), rows.numel(),
+        _ptr(sums, torch.float64, "sums", 8), _stream(stream)))

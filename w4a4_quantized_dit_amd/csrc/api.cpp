@@ -1,0 +1,303 @@
+// C ABI: argument validation on the host (nothing is enqueued for an invalid call), dispatch to
+// the gfx950 kernels, status codes and a thread-local error message.
+#include <hip/hip_runtime.h>
+#include <stdarg.h>
+#include <stdint.h>
+#include <stdio.h>
+
+#include "../../include/svdq.h"
+#include "launch.h"
+
+namespace svdq {
+int64_t cube_count(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch, int64_t cw,
+                   int64_t n_text, int64_t n_audio, int64_t c1);
+void cube_geometry_fill(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch, int64_t cw,
+                        int64_t n_text, int64_t n_audio, int64_t c1, int32_t* row_to_cube,
+                        int32_t* cube_ptr, int32_t* cube_rows);
+}  // namespace svdq
+
+namespace {
+
+thread_local char g_err[512] = "";
+
+svdq_status fail(svdq_status st, const char* fmt, ...) {
+  va_list ap;
+  va_start(ap, fmt);
+  vsnprintf(g_err, sizeof g_err, fmt, ap);
+  va_end(ap);
+  return st;
+}
+
+svdq_status ok() {
+  g_err[0] = '\0';
+  return SVDQ_OK;
+}
+
+svdq_status hip_result(hipError_t e, const char* what) {
+  if (e != hipSuccess) return fail(SVDQ_HIP_ERROR, "%s: %s", what, hipGetErrorString(e));
+  return ok();
+}
+
+bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
+
+#define REQUIRE_PTR(p)                                                                \
+  do {                                                                                \
+    if (!(p)) return fail(SVDQ_NULL_POINTER, "%s: '%s' must not be NULL", fn, #p);    \
+  } while (0)
+#define REQUIRE_ALIGNED(p)                                                                \
+  do {                                                                                    \
+    if ((p) && !aligned16(p))                                                             \
+      return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: '%s' must be 16-byte aligned", fn, #p);    \
+  } while (0)
+
+svdq_status check_k(const char* fn, int64_t K) {
+  if (K <= 0 || K % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: K=%lld must be a positive multiple of 256", fn,
+                (long long)K);
+  return SVDQ_OK;
+}
+
+svdq_status check_ld(const char* fn, const char* name, int64_t ld, int64_t K) {
+  if (ld < K || ld % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE,
+                "%s: %s=%lld must be >= K=%lld and a multiple of 8 (16-byte rows)", fn, name,
+                (long long)ld, (long long)K);
+  return SVDQ_OK;
+}
+
+svdq_status check_rank(const char* fn, int64_t r) {
+  if (r < 0 || r > 128 || r % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: rank r=%lld must be a multiple of 8 in [0, 128]", fn,
+                (long long)r);
+  return SVDQ_OK;
+}
+
+svdq_status check_fmt(const char* fn, int fmt) {
+  if (fmt != SVDQ_NVFP4 && fmt != SVDQ_INT4_G64)
+    return fail(SVDQ_INVALID_ARG, "%s: unknown format %d", fn, fmt);
+  return SVDQ_OK;
+}
+
+#define TRY(x)                      \
+  do {                              \
+    svdq_status _s = (x);           \
+    if (_s != SVDQ_OK) return _s;   \
+  } while (0)
+
+}  // namespace
+
+extern "C" {
+
+const char* svdq_status_string(int status) {
+  switch (status) {
+    case SVDQ_OK: return "SVDQ_OK";
+    case SVDQ_INVALID_ARG: return "SVDQ_INVALID_ARG";
+    case SVDQ_UNSUPPORTED_SHAPE: return "SVDQ_UNSUPPORTED_SHAPE";
+    case SVDQ_NULL_POINTER: return "SVDQ_NULL_POINTER";
+    case SVDQ_HIP_ERROR: return "SVDQ_HIP_ERROR";
+    case SVDQ_NOT_IMPLEMENTED: return "SVDQ_NOT_IMPLEMENTED";
+    default: return "SVDQ_UNKNOWN_STATUS";
+  }
+}
+
+const char* svdq_last_error(void) { return g_err; }
+
+int svdq_abi_version(void) { return 1; }
+
+svdq_status svdq_calibrate_lambda(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                  const int64_t* seg, const uint16_t* W, int64_t N, int64_t ldw,
+                                  uint32_t modality_mask, float alpha, int accumulate, float* ax,
+                                  float* aw, float* lambda, float* act_amax,
+                                  svdq_stream_t stream) {
+  const char* fn = "svdq_calibrate_lambda";
+  REQUIRE_PTR(X); REQUIRE_PTR(seg); REQUIRE_PTR(ax); REQUIRE_PTR(aw); REQUIRE_PTR(lambda);
+  REQUIRE_PTR(act_amax);
+  REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(W);
+  if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldx", ldx, K));
+  if (seg[0] != 0 || seg[3] != M || seg[1] < seg[0] || seg[2] < seg[1] || seg[3] < seg[2])
+    return fail(SVDQ_INVALID_ARG, "%s: seg must be non-decreasing {0, n_text, n_text+n_video, M}",
+                fn);
+  if (modality_mask > 7u) return fail(SVDQ_INVALID_ARG, "%s: modality_mask=%u > 7", fn, modality_mask);
+  if (!(alpha > 0.0f && alpha < 1.0f))
+    return fail(SVDQ_INVALID_ARG, "%s: alpha must lie in (0, 1)", fn);
+  if (W) {
+    if (N < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be >= 1", fn, (long long)N);
+    TRY(check_ld(fn, "ldw", ldw, K));
+  }
+  return hip_result(svdq::launch_calibrate(X, M, K, ldx, seg, W, N, ldw, modality_mask, alpha,
+                                           accumulate, ax, aw, lambda, act_amax,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                 const float* lambda, const uint16_t* lora_down,
+                                 const uint16_t* lora_up, int64_t r, uint8_t* codes,
+                                 void* scales, float* tensor_scale, svdq_stream_t stream) {
+  const char* fn = "svdq_quantize_weight";
+  TRY(check_fmt(fn, fmt));
+  REQUIRE_PTR(W); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
+  if (fmt == SVDQ_NVFP4) REQUIRE_PTR(tensor_scale);
+  REQUIRE_ALIGNED(W); REQUIRE_ALIGNED(codes); REQUIRE_ALIGNED(lora_down); REQUIRE_ALIGNED(lora_up);
+  if (N < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be >= 1", fn, (long long)N);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldw", ldw, K));
+  TRY(check_rank(fn, r));
+  if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(lora_up); }
+  return hip_result(svdq::launch_quantize_weight(fmt, W, N, K, ldw, lambda, lora_down, lora_up, r,
+                                                 codes, scales, tensor_scale,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, int64_t K,
+                                        int64_t ldx, const float* lambda, const float* act_amax,
+                                        const uint16_t* lora_down, int64_t r, uint8_t* codes,
+                                        void* scales, float* tensor_scale, float* D,
+                                        uint32_t* sat_count, svdq_stream_t stream) {
+  const char* fn = "svdq_quant_act_lowrank_down";
+  TRY(check_fmt(fn, fmt));
+  REQUIRE_PTR(X); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
+  if (fmt == SVDQ_NVFP4) REQUIRE_PTR(tensor_scale);
+  REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(codes); REQUIRE_ALIGNED(scales); REQUIRE_ALIGNED(lora_down);
+  REQUIRE_ALIGNED(D);
+  if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldx", ldx, K));
+  TRY(check_rank(fn, r));
+  if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
+  if ((size_t)K * sizeof(float) > 64 * 1024)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: K=%lld exceeds 16384", fn, (long long)K);
+  return hip_result(svdq::launch_quant_act(fmt, X, M, K, ldx, lambda, act_amax, lora_down, r,
+                                           codes, scales, tensor_scale, D, sat_count,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_w4a4_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                           const void* a_scales, const float* g_a, const uint8_t* w_codes,
+                           const void* w_scales, const float* g_w, const float* D,
+                           const uint16_t* lora_up, int64_t r, const float* core_out,
+                           const int32_t* row_to_cube, uint16_t* Y, int64_t ldy,
+                           svdq_stream_t stream) {
+  const char* fn = "svdq_w4a4_gemm";
+  TRY(check_fmt(fn, fmt));
+  REQUIRE_PTR(a_codes); REQUIRE_PTR(a_scales); REQUIRE_PTR(w_codes); REQUIRE_PTR(w_scales);
+  REQUIRE_PTR(Y);
+  if (fmt == SVDQ_NVFP4) { REQUIRE_PTR(g_a); REQUIRE_PTR(g_w); }
+  REQUIRE_ALIGNED(a_codes); REQUIRE_ALIGNED(w_codes); REQUIRE_ALIGNED(D); REQUIRE_ALIGNED(lora_up);
+  if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
+  if (N < 1 || N % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn,
+                (long long)N);
+  TRY(check_k(fn, K));
+  TRY(check_rank(fn, r));
+  if (ldy < N) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldy=%lld < N", fn, (long long)ldy);
+  if (r > 0) { REQUIRE_PTR(D); REQUIRE_PTR(lora_up); }
+  if ((core_out == nullptr) != (row_to_cube == nullptr))
+    return fail(SVDQ_INVALID_ARG, "%s: core_out and row_to_cube must be given together", fn);
+  if (core_out && fmt != SVDQ_NVFP4)
+    return fail(SVDQ_INVALID_ARG, "%s: the core term is defined for NVFP4 only", fn);
+  return hip_result(svdq::launch_gemm(fmt, M, N, K, a_codes, a_scales, g_a, w_codes, w_scales, g_w,
+                                      D, lora_up, r, core_out, row_to_cube, Y, ldy,
+                                      reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_cube_geometry(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch,
+                               int64_t cw, int64_t n_text, int64_t n_audio, int64_t cube1d,
+                               int32_t* row_to_cube, int32_t* cube_ptr, int32_t* cube_rows,
+                               int64_t* n_cubes) {
+  const char* fn = "svdq_cube_geometry";
+  REQUIRE_PTR(n_cubes);
+  if (T < 0 || H < 0 || W < 0 || n_text < 0 || n_audio < 0)
+    return fail(SVDQ_INVALID_ARG, "%s: sizes must be non-negative", fn);
+  if (ct < 1 || ch < 1 || cw < 1 || cube1d < 1)
+    return fail(SVDQ_INVALID_ARG, "%s: cube sizes must be >= 1", fn);
+  if (ct * ch * cw > 16 || cube1d > 16)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: cubes of more than 16 rows are not supported", fn);
+  const int64_t M = n_text + T * H * W + n_audio;
+  if (M < 1 || M > INT32_MAX) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: bad row count", fn);
+  *n_cubes = svdq::cube_count(T, H, W, ct, ch, cw, n_text, n_audio, cube1d);
+  if (!row_to_cube) return ok();
+  REQUIRE_PTR(cube_ptr); REQUIRE_PTR(cube_rows);
+  svdq::cube_geometry_fill(T, H, W, ct, ch, cw, n_text, n_audio, cube1d, row_to_cube, cube_ptr,
+                           cube_rows);
+  return ok();
+}
+
+svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                 const float* lambda, const float* act_amax,
+                                 const int32_t* cube_ptr, const int32_t* cube_rows,
+                                 int64_t n_cubes, const uint16_t* lora_down, int64_t r,
+                                 uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
+                                 uint8_t* delta_scales, float* g_delta, float* D,
+                                 uint32_t* sat_count, svdq_stream_t stream) {
+  const char* fn = "svdq_delta_quant_act";
+  REQUIRE_PTR(X); REQUIRE_PTR(act_amax); REQUIRE_PTR(cube_ptr); REQUIRE_PTR(cube_rows);
+  REQUIRE_PTR(core_codes); REQUIRE_PTR(core_scale); REQUIRE_PTR(delta_codes);
+  REQUIRE_PTR(delta_scales); REQUIRE_PTR(g_delta);
+  REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(core_codes); REQUIRE_ALIGNED(delta_codes);
+  REQUIRE_ALIGNED(lora_down); REQUIRE_ALIGNED(D);
+  if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
+  if (n_cubes < 1 || n_cubes > M) return fail(SVDQ_INVALID_ARG, "%s: bad n_cubes", fn);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldx", ldx, K));
+  TRY(check_rank(fn, r));
+  if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
+  if ((size_t)K * sizeof(float) > 64 * 1024)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: K=%lld exceeds 16384", fn, (long long)K);
+  return hip_result(svdq::launch_delta_quant_act(X, M, K, ldx, lambda, act_amax, cube_ptr,
+                                                 cube_rows, n_cubes, lora_down, r, core_codes,
+                                                 core_scale, delta_codes, delta_scales, g_delta,
+                                                 D, sat_count,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,
+                           const float* core_scale, const uint8_t* w_codes,
+                           const uint8_t* w_scales, const float* g_w, float* core_out,
+                           svdq_stream_t stream) {
+  const char* fn = "svdq_gemm_core";
+  REQUIRE_PTR(core_codes); REQUIRE_PTR(core_scale); REQUIRE_PTR(w_codes); REQUIRE_PTR(w_scales);
+  REQUIRE_PTR(g_w); REQUIRE_PTR(core_out);
+  REQUIRE_ALIGNED(core_codes); REQUIRE_ALIGNED(w_codes);
+  if (n_cubes < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: n_cubes must be >= 1", fn);
+  if (N < 1 || N % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn,
+                (long long)N);
+  TRY(check_k(fn, K));
+  return hip_result(svdq::launch_gemm_core(n_cubes, N, K, core_codes, core_scale, w_codes,
+                                           w_scales, g_w, core_out,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_score_modal_rel_l2(const uint16_t* Y, int64_t ldy, const uint16_t* X,
+                                    int64_t ldx, const uint16_t* W, int64_t ldw, int64_t M,
+                                    int64_t N, int64_t K, const int32_t* rows,
+                                    const int8_t* row_group, int64_t n_rows, double* sums,
+                                    svdq_stream_t stream) {
+  const char* fn = "svdq_score_modal_rel_l2";
+  REQUIRE_PTR(Y); REQUIRE_PTR(X); REQUIRE_PTR(W); REQUIRE_PTR(rows); REQUIRE_PTR(row_group);
+  REQUIRE_PTR(sums);
+  REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(W); REQUIRE_ALIGNED(Y);
+  if (M < 1 || n_rows < 0) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: bad M or n_rows", fn);
+  if (N < 1 || N % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn,
+                (long long)N);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldx", ldx, K));
+  TRY(check_ld(fn, "ldw", ldw, K));
+  if (ldy < N || ldy % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldy must be >= N and a multiple of 8", fn);
+  if (n_rows == 0) return ok();
+  return hip_result(svdq::launch_score(Y, ldy, X, ldx, W, ldw, M, N, K, rows, row_group, n_rows,
+                                       sums, reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+}  // extern "C"

@@ -1,0 +1,138 @@
+// λ calibration reduction ("MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated
+// on", section "Calibration": per-channel activation absmax accumulated under a modality mask
+// feeds λ).  HBM-bound: one streaming read of X (and of W), order-free max reductions.
+#include "device.h"
+#include "launch.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kAbsmaxThreads = 64;   // one wave; 8 channels per lane -> 512 channels per block
+constexpr int kAbsmaxRows = 64;      // rows per block (never straddling a modality segment)
+
+struct SegChunks {
+  int64_t seg[4];     // {0, n_text, n_text + n_video, M}
+  int64_t cstart[4];  // first chunk of each segment (cumulative), cstart[3] = total
+};
+
+__global__ void k_fill(float* __restrict__ p, int64_t n, float v) {
+  int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i < n) p[i] = v;
+}
+
+// out[mu*K + k] = max(out, max over the chunk's rows of |X[row, k]|); bf16 magnitudes compare as
+// unsigned 15-bit patterns, so the max is taken on integers and converted once.
+__global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint16_t* __restrict__ X,
+                                                           int64_t ld, int64_t K, SegChunks sc,
+                                                           float* __restrict__ out,
+                                                           int per_modality) {
+  const int64_t chunk = blockIdx.y;
+  const int mu = (chunk >= sc.cstart[1]) + (chunk >= sc.cstart[2]);
+  const int64_t r0 = sc.seg[mu] + (chunk - sc.cstart[mu]) * kAbsmaxRows;
+  const int64_t r1 = min(r0 + (int64_t)kAbsmaxRows, sc.seg[mu + 1]);
+  const int64_t col = ((int64_t)blockIdx.x * kAbsmaxThreads + threadIdx.x) * 8;
+  if (col >= K) return;
+  typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+  const u16x8 mask = (u16x8)(0x7FFF);
+  u16x8 m = (u16x8)(0);
+  const uint16_t* p = X + r0 * ld + col;
+  int64_t r = r0;
+  for (; r + 4 <= r1; r += 4, p += 4 * ld) {
+    u16x8 v0 = *(const u16x8*)(p);
+    u16x8 v1 = *(const u16x8*)(p + ld);
+    u16x8 v2 = *(const u16x8*)(p + 2 * ld);
+    u16x8 v3 = *(const u16x8*)(p + 3 * ld);
+    m = __builtin_elementwise_max(m, __builtin_elementwise_max(v0 & mask, v1 & mask));
+    m = __builtin_elementwise_max(m, __builtin_elementwise_max(v2 & mask, v3 & mask));
+  }
+  for (; r < r1; ++r, p += ld) m = __builtin_elementwise_max(m, *(const u16x8*)(p)&mask);
+  float* o = out + (per_modality ? (int64_t)mu * K : 0) + col;
+#pragma unroll
+  for (int j = 0; j < 8; ++j)
+    if (m[j]) atomic_max_pos(o + j, bf16_to_f32(m[j]));
+}
+
+// λ from the (accumulated) maxima, and the static activation amax max_k ax_all[k]·(1/λ[k]).
+__global__ __launch_bounds__(1024) void k_lambda(const float* __restrict__ ax,
+                                                 const float* __restrict__ aw, int64_t K,
+                                                 uint32_t mask, float alpha,
+                                                 float* __restrict__ lam,
+                                                 float* __restrict__ act_amax) {
+  __shared__ float red[16];
+  float local = 0.0f;
+  for (int64_t k = threadIdx.x; k < K; k += blockDim.x) {
+    const float a0 = ax[k], a1 = ax[K + k], a2 = ax[2 * K + k];
+    float sel = 0.0f;
+    if (mask & 1u) sel = fmaxf(sel, a0);
+    if (mask & 2u) sel = fmaxf(sel, a1);
+    if (mask & 4u) sel = fmaxf(sel, a2);
+    const float w = aw[k];
+    float l = 1.0f;
+    if (mask != 0u && sel != 0.0f && w != 0.0f) {
+      if (alpha == 0.5f) {
+        l = __builtin_sqrtf(sel / w);
+      } else {
+        l = (float)(pow((double)sel, (double)alpha) / pow((double)w, 1.0 - (double)alpha));
+      }
+    }
+    lam[k] = l;
+    const float inv = 1.0f / l;
+    local = fmaxf(local, fmaxf(fmaxf(a0, a1), a2) * inv);
+  }
+  for (int off = 32; off > 0; off >>= 1) local = fmaxf(local, __shfl_xor(local, off));
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = local;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    float m = 0.0f;
+    for (int i = 0; i < (int)(blockDim.x >> 6); ++i) m = fmaxf(m, red[i]);
+    act_amax[0] = m;
+  }
+}
+
+SegChunks make_chunks(const int64_t seg[4]) {
+  SegChunks sc;
+  for (int i = 0; i < 4; ++i) sc.seg[i] = seg[i];
+  sc.cstart[0] = 0;
+  for (int i = 0; i < 3; ++i)
+    sc.cstart[i + 1] = sc.cstart[i] + (seg[i + 1] - seg[i] + kAbsmaxRows - 1) / kAbsmaxRows;
+  return sc;
+}
+
+hipError_t fill(float* p, int64_t n, float v, hipStream_t s) {
+  if (n <= 0) return hipSuccess;
+  k_fill<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p, n, v);
+  return hipGetLastError();
+}
+
+hipError_t absmax(const uint16_t* X, int64_t ld, int64_t K, const int64_t seg[4], float* out,
+                  int per_modality, hipStream_t s) {
+  SegChunks sc = make_chunks(seg);
+  if (sc.cstart[3] == 0) return hipSuccess;
+  dim3 grid((unsigned)((K / 8 + kAbsmaxThreads - 1) / kAbsmaxThreads), (unsigned)sc.cstart[3]);
+  k_absmax<<<grid, dim3(kAbsmaxThreads), 0, s>>>(X, ld, K, sc, out, per_modality);
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                            const int64_t seg[4], const uint16_t* W, int64_t N, int64_t ldw,
+                            uint32_t mask, float alpha, int accumulate, float* ax, float* aw,
+                            float* lambda, float* act_amax, hipStream_t s) {
+  hipError_t e;
+  if (!accumulate) {
+    if ((e = fill(ax, 3 * K, 0.0f, s)) != hipSuccess) return e;
+    if (W && (e = fill(aw, K, 0.0f, s)) != hipSuccess) return e;
+  }
+  if (!W && (e = fill(aw, K, 1.0f, s)) != hipSuccess) return e;
+  if ((e = absmax(X, ldx, K, seg, ax, 1, s)) != hipSuccess) return e;
+  if (W) {
+    const int64_t wseg[4] = {0, N, N, N};
+    if ((e = absmax(W, ldw, K, wseg, aw, 0, s)) != hipSuccess) return e;
+  }
+  k_lambda<<<dim3(1), dim3(1024), 0, s>>>(ax, aw, K, mask, alpha, lambda, act_amax);
+  return hipGetLastError();
+}
+
+}  // namespace svdq

@@ -1,0 +1,124 @@
+// Device-side helpers shared by the gfx950 kernels: vector types, bf16 / E4M3 / E2M1 / fp16
+// conversions with the exact rounding the layer's codes are defined by.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <hip/hip_fp16.h>
+#include <stdint.h>
+
+namespace svdq {
+
+typedef __attribute__((ext_vector_type(2))) __bf16 bf16x2_t;
+typedef __attribute__((ext_vector_type(8))) __bf16 bf16x8_t;
+typedef __attribute__((ext_vector_type(2))) _Float16 f16x2_t;
+typedef __attribute__((ext_vector_type(8))) _Float16 f16x8_t;
+typedef __attribute__((ext_vector_type(4))) float f32x4_t;
+typedef __attribute__((ext_vector_type(16))) float f32x16_t;
+typedef __attribute__((ext_vector_type(4))) uint32_t u32x4_t;
+typedef __attribute__((ext_vector_type(8))) int32_t i32x8_t;
+typedef __attribute__((ext_vector_type(4))) int32_t i32x4_t;
+typedef __attribute__((ext_vector_type(16))) int32_t i32x16_t;
+typedef __attribute__((ext_vector_type(2))) uint16_t u16x2_t;
+
+constexpr int NVFP4_BLOCK = 16;
+constexpr int INT4_GROUP = 64;
+
+__device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
+__device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
+__device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }
+
+// Two fp32 -> packed bf16 pair, round to nearest even (v_cvt_pk_bf16_f32).
+__device__ __forceinline__ uint32_t pack_bf16x2(float lo, float hi) {
+  bf16x2_t v;
+  v[0] = (__bf16)lo;
+  v[1] = (__bf16)hi;
+  return __builtin_bit_cast(uint32_t, v);
+}
+__device__ __forceinline__ uint16_t f32_to_bf16(float x) {
+  __bf16 b = (__bf16)x;
+  return __builtin_bit_cast(uint16_t, b);
+}
+
+// Non-negative fp32 magnitude -> E4M3 code, nearest even, satfinite at 448; *val receives the
+// code's value.  Normal range: keep 3 mantissa bits of the fp32 pattern with RNE on the bits
+// (a carry moves into the exponent); subnormal range (below 2^-6): quantum 2^-9.
+__device__ __forceinline__ uint32_t e4m3_encode_pos(float q, float* val) {
+  if (q >= 448.0f) {
+    *val = 448.0f;
+    return 0x7Eu;
+  }
+  if (q < 0.015625f) {
+    float t = __builtin_rintf(q * 512.0f);  // exact scaling; rint rounds half to even
+    *val = t * 0.001953125f;
+    return (uint32_t)t;  // t == 8 is the smallest normal, code 0x08
+  }
+  uint32_t b = __float_as_uint(q);
+  b = (b + 0x7FFFFu + ((b >> 20) & 1u)) & 0xFFF00000u;
+  *val = __uint_as_float(b);
+  return (b >> 20) - (120u << 3);
+}
+
+// NVFP4 block scale: q = a / d6, s = E4M3(q), S = s·g, inv = 1/S (0 when S == 0).
+__device__ __forceinline__ uint32_t nvfp4_block_scale(float a, float g, float d6, float* inv) {
+  float sval;
+  uint32_t code = e4m3_encode_pos(a / d6, &sval);
+  float S = sval * g;
+  *inv = (S != 0.0f) ? 1.0f / S : 0.0f;
+  return code;
+}
+
+// Two fp32 values (already multiplied by the block's inverse scale) -> two E2M1 nibbles written
+// into byte `sel` of `old` (low nibble = first value).  The hardware conversion with scale 1.0
+// rounds to nearest even, saturates at ±6 and keeps the sign of zero.
+template <int SEL>
+__device__ __forceinline__ uint32_t e2m1_pack2(uint32_t old, float y0, float y1) {
+  return __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(old, y0, y1, 1.0f, SEL);
+}
+
+// Eight fp32 values -> one dword of eight E2M1 nibbles (element i in nibble i).
+__device__ __forceinline__ uint32_t e2m1_pack8(const float* y) {
+  uint32_t w = 0;
+  w = e2m1_pack2<0>(w, y[0], y[1]);
+  w = e2m1_pack2<1>(w, y[2], y[3]);
+  w = e2m1_pack2<2>(w, y[4], y[5]);
+  w = e2m1_pack2<3>(w, y[6], y[7]);
+  return w;
+}
+
+// int4 code from fp32 value times inverse scale: clamp(rint(v), -8, 7) as a nibble.
+__device__ __forceinline__ uint32_t int4_code(float v) {
+  int c = (int)__builtin_rintf(v);
+  c = c < -8 ? -8 : (c > 7 ? 7 : c);
+  return (uint32_t)c & 0xFu;
+}
+
+// Eight fp32 low-rank activations D[k0 .. k0+8) as an exact-to-2^-16 pair of bf16 MFMA operands:
+// hi = bf16(d), lo = bf16(d - hi) (d - hi is exact in fp32), so hi·u + lo·u carries d to 16
+// significant bits through a bf16 MFMA.  `valid` false gives zeros (rank padding).
+__device__ __forceinline__ void lowrank_operand(const float* p, bool valid, bf16x8_t& hi,
+                                                bf16x8_t& lo) {
+  u32x4_t a = u32x4_t{0u, 0u, 0u, 0u}, b = u32x4_t{0u, 0u, 0u, 0u};
+  if (valid) {
+    a = reinterpret_cast<const u32x4_t*>(p)[0];
+    b = reinterpret_cast<const u32x4_t*>(p)[1];
+  }
+  const float d[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
+                      __uint_as_float(a[3]), __uint_as_float(b[0]), __uint_as_float(b[1]),
+                      __uint_as_float(b[2]), __uint_as_float(b[3])};
+  u32x4_t vh, vl;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const uint32_t ph = pack_bf16x2(d[2 * j], d[2 * j + 1]);
+    vh[j] = ph;
+    vl[j] = pack_bf16x2(d[2 * j] - bf16_lo(ph), d[2 * j + 1] - bf16_hi(ph));
+  }
+  hi = __builtin_bit_cast(bf16x8_t, vh);
+  lo = __builtin_bit_cast(bf16x8_t, vl);
+}
+
+// Running maximum of non-negative floats stored as their bit patterns (monotone for >= 0).
+__device__ __forceinline__ void atomic_max_pos(float* addr, float v) {
+  atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));
+}
+
+}  // namespace svdq

@@ -1,0 +1,49 @@
+// Internal host-side launchers (called by api.cpp after validation).  Each returns the HIP
+// error of its launches.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace svdq {
+
+hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                            const int64_t seg[4], const uint16_t* W, int64_t N, int64_t ldw,
+                            uint32_t mask, float alpha, int accumulate, float* ax, float* aw,
+                            float* lambda, float* act_amax, hipStream_t s);
+
+hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                  const float* lambda, const uint16_t* down, const uint16_t* up,
+                                  int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
+                                  hipStream_t s);
+
+hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                            const float* lambda, const float* act_amax, const uint16_t* down,
+                            int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
+                            float* D, uint32_t* sat, hipStream_t s);
+
+hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                       const void* a_scales, const float* g_a, const uint8_t* w_codes,
+                       const void* w_scales, const float* g_w, const float* D,
+                       const uint16_t* up, int64_t r, const float* core_out,
+                       const int32_t* row_to_cube, uint16_t* Y, int64_t ldy, hipStream_t s);
+
+hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                  const float* lambda, const float* act_amax,
+                                  const int32_t* cube_ptr, const int32_t* cube_rows,
+                                  int64_t n_cubes, const uint16_t* down, int64_t r,
+                                  uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
+                                  uint8_t* delta_scales, float* g_delta, float* D,
+                                  uint32_t* sat, hipStream_t s);
+
+hipError_t launch_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,
+                            const float* core_scale, const uint8_t* w_codes,
+                            const uint8_t* w_scales, const float* g_w, float* core_out,
+                            hipStream_t s);
+
+hipError_t launch_score(const uint16_t* Y, int64_t ldy, const uint16_t* X, int64_t ldx,
+                        const uint16_t* W, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                        const int32_t* rows, const int8_t* grp, int64_t n_rows, double* sums,
+                        hipStream_t s);
+
+}  // namespace svdq

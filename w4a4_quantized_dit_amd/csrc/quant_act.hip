@@ -1,0 +1,258 @@
+// Fused activation kernel: smoothing (X̂ = X · 1/λ), per-block absmax, NVFP4 (E2M1 + E4M3 block
+// scale) or int4-g64 rounding with nibble packing, and the low-rank down-projection
+// D = bf16(X̂)·L1 (fp32) on MFMA — one streaming read of X ("MiniMax-H3 NVFP4 — what the smoothing
+// scale should be calibrated on", section "Why": the kernel sees X / λ, 16 channels per FP8
+// scale; "MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)": activations quantised at run time).
+//
+// Work split: one wave owns 16 rows.  Lane (row = lane % 16, q = lane / 16) holds 64 contiguous
+// channels [k0 + 64q, k0 + 64q + 64) of a 256-channel chunk, i.e. four whole NVFP4 blocks or one
+// whole int4 group, so every block absmax is lane-local (no cross-lane reduction).  The same
+// registers feed v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry
+// channels k0 + 64q + 8t .. +8, and the L1 operand is loaded with the same channel mapping.
+#include "device.h"
+#include "launch.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kWaves = 4;
+constexpr int kThreads = 64 * kWaves;
+constexpr int kRowsPerWave = 16;
+constexpr int kChunk = 256;
+
+template <int FMT, int NT>
+__global__ __launch_bounds__(kThreads) void k_quant_act(
+    const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
+    const float* __restrict__ lambda, const float* __restrict__ amax_p,
+    const uint16_t* __restrict__ down, int r, uint8_t* __restrict__ codes,
+    void* __restrict__ scales, float* __restrict__ tensor_scale, int write_g,
+    float* __restrict__ D, uint32_t* __restrict__ sat) {
+  extern __shared__ float s_inv[];  // 1/λ for all K channels
+  for (int64_t k = threadIdx.x; k < K; k += kThreads) s_inv[k] = lambda ? 1.0f / lambda[k] : 1.0f;
+  __syncthreads();
+
+  float amax = 0.0f, g = 1.0f, d6 = 6.0f;
+  if (FMT == 0) {
+    amax = amax_p[0];
+    g = amax == 0.0f ? 1.0f : amax / 2688.0f;
+    d6 = 6.0f * g;
+    if (write_g && blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = g;
+  }
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRowsPerWave;
+  if (row0 >= M) return;
+  const int rl = lane & 15, q = lane >> 4;
+  const int64_t row = row0 + rl;
+  const bool valid = row < M;
+  const uint16_t* xp = X + (valid ? row : row0) * ldx + 64 * q;
+
+  f32x4_t acc[NT > 0 ? NT : 1];
+#pragma unroll
+  for (int j = 0; j < (NT > 0 ? NT : 1); ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  uint32_t nsat = 0;
+
+  u32x4_t nxt[8];
+#pragma unroll
+  for (int i = 0; i < 8; ++i) nxt[i] = reinterpret_cast<const u32x4_t*>(xp)[i];
+
+  for (int64_t k0 = 0; k0 < K; k0 += kChunk) {
+    u32x4_t v[8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) v[i] = nxt[i];
+    if (k0 + kChunk < K) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) nxt[i] = reinterpret_cast<const u32x4_t*>(xp + k0 + kChunk)[i];
+    }
+    const int64_t kb = k0 + 64 * q;  // first channel of this lane
+    float x[64];
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        const uint32_t w = valid ? v[i][c] : 0u;
+        x[8 * i + 2 * c] = bf16_lo(w) * s_inv[kb + 8 * i + 2 * c];
+        x[8 * i + 2 * c + 1] = bf16_hi(w) * s_inv[kb + 8 * i + 2 * c + 1];
+      }
+    }
+
+    if (FMT == 0) {
+      uint32_t cw[8];
+      uint32_t sbytes = 0;
+#pragma unroll
+      for (int b = 0; b < 4; ++b) {
+        float a = 0.0f;
+#pragma unroll
+        for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(x[16 * b + j]));
+        nsat += (a > amax) ? 1u : 0u;
+        float inv;
+        const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
+        float y[16];
+#pragma unroll
+        for (int j = 0; j < 16; ++j) y[j] = x[16 * b + j] * inv;
+        cw[2 * b] = e2m1_pack8(y);
+        cw[2 * b + 1] = e2m1_pack8(y + 8);
+        sbytes |= sc << (8 * b);
+      }
+      if (valid) {
+        u32x4_t* cp = reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + kb / 2);
+        cp[0] = u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+        cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
+        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(scales) + row * (K / 16) + kb / 16) = sbytes;
+      }
+    } else {
+      float a = 0.0f;
+#pragma unroll
+      for (int j = 0; j < 64; ++j) a = fmaxf(a, fabsf(x[j]));
+      const __half s = __float2half_rn(a / 7.0f);
+      const float sf = __half2float(s);
+      const float inv = sf != 0.0f ? 1.0f / sf : 0.0f;
+      uint32_t cw[8];
+#pragma unroll
+      for (int d = 0; d < 8; ++d) {
+        uint32_t w = 0;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) w |= int4_code(x[8 * d + j] * inv) << (4 * j);
+        cw[d] = w;
+      }
+      if (valid) {
+        u32x4_t* cp = reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + kb / 2);
+        cp[0] = u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+        cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
+        reinterpret_cast<__half*>(scales)[row * (K / 64) + kb / 64] = s;
+      }
+    }
+
+    if (NT > 0) {
+#pragma unroll
+      for (int t = 0; t < 8; ++t) {
+        u32x4_t av;
+        av[0] = pack_bf16x2(x[8 * t + 0], x[8 * t + 1]);
+        av[1] = pack_bf16x2(x[8 * t + 2], x[8 * t + 3]);
+        av[2] = pack_bf16x2(x[8 * t + 4], x[8 * t + 5]);
+        av[3] = pack_bf16x2(x[8 * t + 6], x[8 * t + 7]);
+        const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+        for (int j = 0; j < NT; ++j) {
+          const int n = 16 * j + rl;
+          u32x4_t bv = u32x4_t{0u, 0u, 0u, 0u};
+          if (n < r) bv = *reinterpret_cast<const u32x4_t*>(down + (int64_t)n * K + kb + 8 * t);
+          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, __builtin_bit_cast(bf16x8_t, bv),
+                                                           acc[j], 0, 0, 0);
+        }
+      }
+    }
+  }
+
+  if (NT > 0) {
+    // 16x16 output: lane holds rank column 16j + rl and rows 4q .. 4q+3 of the wave's 16 rows.
+#pragma unroll
+    for (int j = 0; j < NT; ++j) {
+      const int n = 16 * j + rl;
+      if (n < r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int64_t m = row0 + 4 * q + i;
+          if (m < M) D[m * r + n] = acc[j][i];
+        }
+      }
+    }
+  }
+  if (FMT == 0 && sat) {
+    for (int off = 32; off > 0; off >>= 1) nsat += __shfl_xor(nsat, off);
+    if (lane == 0 && nsat) atomicAdd(sat, nsat);
+  }
+}
+
+// Dynamic tensor amax: max over all elements of |X · 1/λ| (used when no static amax is given).
+__global__ __launch_bounds__(256) void k_xhat_amax(const uint16_t* __restrict__ X, int64_t M,
+                                                   int64_t K, int64_t ldx,
+                                                   const float* __restrict__ lambda,
+                                                   float* __restrict__ out) {
+  const int64_t col = ((int64_t)blockIdx.x * 256 + threadIdx.x) * 8;
+  float m = 0.0f;
+  if (col < K) {
+    float inv[8];
+#pragma unroll
+    for (int j = 0; j < 8; ++j) inv[j] = lambda ? 1.0f / lambda[col + j] : 1.0f;
+    for (int64_t row = blockIdx.y; row < M; row += gridDim.y) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + row * ldx + col);
+#pragma unroll
+      for (int c = 0; c < 4; ++c) {
+        m = fmaxf(m, fabsf(bf16_lo(v[c]) * inv[2 * c]));
+        m = fmaxf(m, fabsf(bf16_hi(v[c]) * inv[2 * c + 1]));
+      }
+    }
+  }
+  for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+  if ((threadIdx.x & 63) == 0 && m > 0.0f) atomic_max_pos(out, m);
+}
+
+__global__ void k_set(float* t, float v) { t[0] = v; }
+__global__ void k_amax_to_g(float* t) {
+  const float a = t[0];
+  t[0] = a == 0.0f ? 1.0f : a / 2688.0f;
+}
+
+template <int FMT>
+hipError_t dispatch(int nt, dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int64_t M,
+                    int64_t K, int64_t ldx, const float* lambda, const float* amax_p,
+                    const uint16_t* down, int r, uint8_t* codes, void* scales, float* ts,
+                    int write_g, float* D, uint32_t* sat) {
+#define SVDQ_QA_CASE(NTV)                                                                  \
+  case NTV:                                                                                \
+    k_quant_act<FMT, NTV><<<grid, dim3(kThreads), lds, s>>>(X, M, K, ldx, lambda, amax_p, \
+                                                             down, r, codes, scales, ts,   \
+                                                             write_g, D, sat);             \
+    break;
+  switch (nt) {
+    SVDQ_QA_CASE(0)
+    SVDQ_QA_CASE(1)
+    SVDQ_QA_CASE(2)
+    SVDQ_QA_CASE(3)
+    SVDQ_QA_CASE(4)
+    SVDQ_QA_CASE(5)
+    SVDQ_QA_CASE(6)
+    SVDQ_QA_CASE(7)
+    SVDQ_QA_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef SVDQ_QA_CASE
+  return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                            const float* lambda, const float* act_amax, const uint16_t* down,
+                            int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
+                            float* D, uint32_t* sat, hipStream_t s) {
+  const int nt = (int)((r + 15) / 16);
+  const int64_t rows_per_block = (int64_t)kWaves * kRowsPerWave;
+  const dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block));
+  const size_t lds = (size_t)K * sizeof(float);
+  if (fmt == 1)
+    return dispatch<1>(nt, grid, lds, s, X, M, K, ldx, lambda, nullptr, down, (int)r, codes,
+                       scales, nullptr, 0, D, nullptr);
+  const float* amax_p = act_amax;
+  int write_g = 1;
+  if (!act_amax) {
+    // Dynamic pre-pass: tensor_scale holds max|X̂| until the final conversion to g.
+    k_set<<<1, 1, 0, s>>>(tensor_scale, 0.0f);
+    const dim3 g2((unsigned)((K / 8 + 255) / 256), (unsigned)(M < 1024 ? M : 1024));
+    k_xhat_amax<<<g2, dim3(256), 0, s>>>(X, M, K, ldx, lambda, tensor_scale);
+    amax_p = tensor_scale;
+    write_g = 0;
+  }
+  hipError_t e = dispatch<0>(nt, grid, lds, s, X, M, K, ldx, lambda, amax_p, down, (int)r, codes,
+                             scales, tensor_scale, write_g, D, sat);
+  if (e != hipSuccess) return e;
+  if (!act_amax) {
+    k_amax_to_g<<<1, 1, 0, s>>>(tensor_scale);
+    return hipGetLastError();
+  }
+  return hipSuccess;
+}
+
+}  // namespace svdq

@@ -1,0 +1,97 @@
+"""Allocating helpers over the C ABI for the W4A4 layer (torch provides memory and streams).
+
+Every numeric step runs in libsvdq.so; these functions only allocate outputs and call the
+entry points in order: calibration -> weight preparation -> activation quantisation with the
+low-rank down-projection -> W4A4 GEMM.
+"""
+from dataclasses import dataclass
+
+from . import _lib
+from ._lib import NVFP4, INT4_G64  # noqa: F401
+
+
+def _torch():
+    import torch
+    return torch
+
+
+@dataclass
+class PreparedWeight:
+    fmt: int
+    N: int
+    K: int
+    r: int
+    codes: object        # uint8 [N, K/2]
+    scales: object       # uint8 [N, K/16] (E4M3) or float16 [N, K/64]
+    g: object            # float32 [1] (NVFP4) or None
+    lora_up: object      # bf16 [N, r] or None
+
+
+def calibrate(X, seg, W=None, mask=7, alpha=0.5, state=None):
+    """λ calibration on X [M, K]; pass the previous result as `state` to accumulate batches."""
+    torch = _torch()
+    K = X.shape[1]
+    dev = X.device
+    if state is None:
+        state = dict(ax=torch.empty(3, K, device=dev), aw=torch.empty(K, device=dev),
+                     **{"lambda": torch.empty(K, device=dev)},
+                     act_amax=torch.empty(1, device=dev))
+        acc = 0
+    else:
+        acc = 1
+    _lib.svdq_calibrate_lambda(X, seg, W, mask, alpha, acc, state["ax"], state["aw"],
+                               state["lambda"], state["act_amax"])
+    return state
+
+
+def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
+    """Quantised residual of diag(λ)·W − L1·L2 (W [N, K] bf16)."""
+    torch = _torch()
+    N, K = W.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    dev = W.device
+    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
+    if fmt == NVFP4:
+        scales = torch.empty(N, K // 16, dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        scales = torch.empty(N, K // 64, dtype=torch.float16, device=dev)
+        g = None
+    _lib.svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, g)
+    return PreparedWeight(fmt, N, K, r, codes, scales, g, lora_up)
+
+
+def quantize_activation(X, lam, act_amax, lora_down, fmt=NVFP4, sat_count=None):
+    """(codes, scales, g_a, D) of X [M, K]."""
+    torch = _torch()
+    M, K = X.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    dev = X.device
+    codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
+    if fmt == NVFP4:
+        scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    else:
+        scales = torch.empty(M, K // 64, dtype=torch.float16, device=dev)
+        g = None
+    D = torch.empty(M, r, dtype=torch.float32, device=dev) if r else None
+    _lib.svdq_quant_act_lowrank_down(fmt, X, lam, act_amax, lora_down, r, codes, scales, g, D,
+                                     sat_count)
+    return codes, scales, g, D
+
+
+def gemm(codes, scales, g_a, D, pw, M, out=None, core_out=None, row_to_cube=None):
+    torch = _torch()
+    Y = out if out is not None else torch.empty(M, pw.N, dtype=torch.bfloat16, device=codes.device)
+    _lib.svdq_w4a4_gemm(pw.fmt, M, pw.N, pw.K, codes, scales, g_a, pw.codes, pw.scales, pw.g, D,
+                        pw.lora_up, pw.r, Y, core_out, row_to_cube)
+    return Y
+
+
+def forward(X, pw, act_amax, lam, lora_down, out=None):
+    """Y = X̂·L1·L2 + Q(X̂)·Q(R) for X [..., K]; leading dimensions are flattened exactly once."""
+    lead = X.shape[:-1]
+    X2 = X.reshape(-1, X.shape[-1])
+    codes, scales, g, D = quantize_activation(X2, lam, act_amax, lora_down, pw.fmt)
+    Y = gemm(codes, scales, g, D, pw, X2.shape[0], out=out)
+    return Y.reshape(*lead, pw.N)
