@@ -92,19 +92,21 @@ __device__ __forceinline__ uint32_t int4_code(float v) {
   return (uint32_t)c & 0xFu;
 }
 
-// Eight fp32 low-rank activations D[k0 .. k0+8) as an exact-to-2^-16 pair of bf16 MFMA operands:
-// hi = bf16(d), lo = bf16(d - hi) (d - hi is exact in fp32), so hi·u + lo·u carries d to 16
-// significant bits through a bf16 MFMA.  `valid` false gives zeros (rank padding).
-__device__ __forceinline__ void lowrank_operand(const float* p, bool valid, bf16x8_t& hi,
-                                                bf16x8_t& lo) {
+// Eight fp32 low-rank activations D[k0 .. k0+8), times `mul`, as an exact-to-2^-16 pair of bf16
+// MFMA operands: hi = bf16(d), lo = bf16(d - hi) (d - hi is exact in fp32), so hi·u + lo·u
+// carries d to 16 significant bits through a bf16 MFMA.  `valid` false gives zeros (rank
+// padding).
+__device__ __forceinline__ void lowrank_operand(const float* p, bool valid, float mul,
+                                                bf16x8_t& hi, bf16x8_t& lo) {
   u32x4_t a = u32x4_t{0u, 0u, 0u, 0u}, b = u32x4_t{0u, 0u, 0u, 0u};
   if (valid) {
     a = reinterpret_cast<const u32x4_t*>(p)[0];
     b = reinterpret_cast<const u32x4_t*>(p)[1];
   }
-  const float d[8] = {__uint_as_float(a[0]), __uint_as_float(a[1]), __uint_as_float(a[2]),
-                      __uint_as_float(a[3]), __uint_as_float(b[0]), __uint_as_float(b[1]),
-                      __uint_as_float(b[2]), __uint_as_float(b[3])};
+  const float d[8] = {__uint_as_float(a[0]) * mul, __uint_as_float(a[1]) * mul,
+                      __uint_as_float(a[2]) * mul, __uint_as_float(a[3]) * mul,
+                      __uint_as_float(b[0]) * mul, __uint_as_float(b[1]) * mul,
+                      __uint_as_float(b[2]) * mul, __uint_as_float(b[3]) * mul};
   u32x4_t vh, vl;
 #pragma unroll
   for (int j = 0; j < 4; ++j) {

@@ -129,7 +129,7 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_int4(
     const int k0 = 16 * t + 8 * h;
     bf16x8_t d_hi[FM], d_lo[FM], u_op[FN];
 #pragma unroll
-    for (int i = 0; i < FM; ++i) lowrank_operand(D + arow[i] * r + k0, k0 < r, d_hi[i], d_lo[i]);
+    for (int i = 0; i < FM; ++i) lowrank_operand(D + arow[i] * r + k0, k0 < r, 1.0f, d_hi[i], d_lo[i]);
 #pragma unroll
     for (int j = 0; j < FN; ++j) {
       u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};

@@ -11,8 +11,8 @@
 // block-scaled FP4 MFMA takes power-of-two (E8M0) scales per 32 elements, which cannot carry an
 // E4M3 scale per 16 exactly, so it is not used for this format.
 //
-// K mapping: within a 64-element chunk, lane (row = lane % 32, h = lane / 32) holds elements
-// [32h, 32h + 32) of its row (16 contiguous bytes of codes).  MFMA step t (0..3) takes the lane's
+// K mapping: within each 64-element half of a stage, lane (row = lane % 32, h = lane / 32) holds
+// elements [32h, 32h + 32) of its row (16 contiguous bytes of codes).  MFMA step t (0..3) takes the lane's
 // elements [8t, 8t + 8) as its k-slots; the weight operand uses the identical mapping, so every
 // product pairs equal K indices.
 #include "device.h"
@@ -46,7 +46,118 @@ __device__ __forceinline__ f16x8_t dequant8(uint32_t codes, f16x2_t s2) {
   return r;
 }
 
+// Epilogue: low-rank up-projection, tensor scales, DeltaQuant core term, bf16 store.
+// The accumulators hold Σ A'·W' without the tensor scales gsc = g_a·g_w; the low-rank term is
+// folded in before the scaling as (D/gsc)·L2 so the accumulators stay with the MFMA unit, and
+// y = gsc·acc (+ core_out[cube(m)]) is formed element by element at the store.  fp32 D/gsc is
+// split into an exact-to-2^-16 bf16 pair for the bf16 MFMA.
+// 32x32 accumulator layout: lane holds column r32 and rows (e/4)*8 + 4h + e%4.
 template <int FM, int FN>
+__device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[FM][FN], float gsc, int64_t M,
+                                              int64_t N, int64_t m_base, int64_t n_base, int r32,
+                                              int h, const float* __restrict__ D,
+                                              const uint16_t* __restrict__ up, int r,
+                                              const float* __restrict__ core_out,
+                                              const int32_t* __restrict__ row_to_cube,
+                                              uint16_t* __restrict__ Y, int64_t ldy) {
+  const float inv_gsc = 1.0f / gsc;
+  for (int t = 0; 16 * t < r; ++t) {
+    const int k0 = 16 * t + 8 * h;
+    bf16x8_t u_op[FN];
+#pragma unroll
+    for (int j = 0; j < FN; ++j) {
+      const int64_t col = n_base + 32 * j + r32;
+      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
+      if (k0 < r) v = *reinterpret_cast<const u32x4_t*>(up + col * r + k0);
+      u_op[j] = __builtin_bit_cast(bf16x8_t, v);
+    }
+#pragma unroll
+    for (int i = 0; i < FM; ++i) {
+      int64_t row = m_base + 32 * i + r32;
+      row = row < M ? row : M - 1;
+      bf16x8_t d_hi, d_lo;
+      lowrank_operand(D + row * r + k0, k0 < r, inv_gsc, d_hi, d_lo);
+#pragma unroll
+      for (int j = 0; j < FN; ++j) {
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d_hi, u_op[j], acc[i][j], 0, 0, 0);
+        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d_lo, u_op[j], acc[i][j], 0, 0, 0);
+      }
+    }
+  }
+
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t row = m_base + 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
+      if (row < M) {
+        const float* co = core_out ? core_out + (int64_t)row_to_cube[row] * N : nullptr;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const int64_t col = n_base + 32 * j + r32;
+          float v = acc[i][j][e] * gsc;
+          if (co) v += co[col];
+          Y[row * ldy + col] = f32_to_bf16(v);
+        }
+      }
+    }
+  }
+}
+
+// Workgroup tile 256 x 256, 4 waves in 2 x 2, each wave 128 x 128 (4 x 4 MFMA tiles of 32x32).
+// K advances 128 elements per stage.  Raw codes and scales are staged global -> registers ->
+// LDS through three LDS buffers (the loads for stage s+3 are in flight while stage s is
+// computed); each wave dequantises its own fragments from LDS.
+constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kRowBytes = kBK / 2;          // 64 bytes of codes per row per stage
+constexpr int kRowPitch = kRowBytes + 16;   // padded pitch: conflict-free 16-byte reads
+constexpr int kStages = 3;
+constexpr int kCodeBuf = kBM * kRowPitch;   // per operand per stage
+constexpr int kScaleBuf = kBM * (kBK / 16); // 8 scale bytes per row per stage
+constexpr int kStageBytes = 2 * kCodeBuf + 2 * kScaleBuf;
+
+struct StageRegs {
+  u32x4_t a[4], b[4];  // 4 x 16 B of codes per operand per thread
+  uint2 sa, sb;        // threads 0..255: 8 scale bytes of one row (A and W)
+};
+
+__device__ __forceinline__ void stage_load(StageRegs& g, const uint8_t* __restrict__ A,
+                                           const uint8_t* __restrict__ As,
+                                           const uint8_t* __restrict__ B,
+                                           const uint8_t* __restrict__ Bs, int64_t M,
+                                           int64_t m0, int64_t n0, int64_t kb, int64_t ks,
+                                           int64_t stage, int tid) {
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j;            // chunk id: row = c / 4, part = c % 4
+    const int row = c >> 2, part = c & 3;
+    int64_t ar = m0 + row;
+    ar = ar < M ? ar : M - 1;
+    g.a[j] = *reinterpret_cast<const u32x4_t*>(A + ar * kb + stage * kRowBytes + part * 16);
+    g.b[j] = *reinterpret_cast<const u32x4_t*>(B + (n0 + row) * kb + stage * kRowBytes + part * 16);
+  }
+  int64_t ar = m0 + tid;
+  ar = ar < M ? ar : M - 1;
+  g.sa = *reinterpret_cast<const uint2*>(As + ar * ks + stage * (kBK / 16));
+  g.sb = *reinterpret_cast<const uint2*>(Bs + (n0 + tid) * ks + stage * (kBK / 16));
+}
+
+__device__ __forceinline__ void stage_store(const StageRegs& g, uint8_t* lds, int tid) {
+  uint8_t* la = lds;
+  uint8_t* lb = lds + kCodeBuf;
+  uint8_t* lsa = lds + 2 * kCodeBuf;
+  uint8_t* lsb = lsa + kScaleBuf;
+#pragma unroll
+  for (int j = 0; j < 4; ++j) {
+    const int c = tid + 256 * j;
+    const int row = c >> 2, part = c & 3;
+    *reinterpret_cast<u32x4_t*>(la + row * kRowPitch + part * 16) = g.a[j];
+    *reinterpret_cast<u32x4_t*>(lb + row * kRowPitch + part * 16) = g.b[j];
+  }
+  *reinterpret_cast<uint2*>(lsa + tid * 8) = g.sa;
+  *reinterpret_cast<uint2*>(lsb + tid * 8) = g.sb;
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
     const uint8_t* __restrict__ As, const float* __restrict__ g_a,
@@ -54,31 +165,16 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     const float* __restrict__ g_w, const float* __restrict__ D,
     const uint16_t* __restrict__ up, int r, const float* __restrict__ core_out,
     const int32_t* __restrict__ row_to_cube, uint16_t* __restrict__ Y, int64_t ldy) {
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  constexpr int FM = 4, FN = 4;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStageBytes];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m_base = (int64_t)blockIdx.y * (64 * FM) + wm * (32 * FM);
-  const int64_t n_base = (int64_t)blockIdx.x * (64 * FN) + wn * (32 * FN);
-  if (m_base >= M) return;
+  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  const int64_t m_base = m0 + wm * 128, n_base = n0 + wn * 128;
   const int r32 = lane & 31, h = lane >> 5;
   const int64_t kb = K / 2, ks = K / 16;
-
-  const uint8_t* pa[FM];
-  const uint8_t* psa[FM];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    int64_t row = m_base + 32 * i + r32;
-    row = row < M ? row : M - 1;  // rows past M load valid data whose outputs are discarded
-    pa[i] = A + row * kb + 16 * h;
-    psa[i] = As + row * ks;
-  }
-  const uint8_t* pb[FN];
-  const uint8_t* psb[FN];
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t col = n_base + 32 * j + r32;
-    pb[j] = B + col * kb + 16 * h;
-    psb[j] = Bs + col * ks;
-  }
+  const int64_t nstage = K / kBK;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -88,133 +184,64 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  const int64_t nchunk = K / 64;
-  u32x4_t ca[FM], cb[FN];
-  uint32_t sa[FM], sb[FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    ca[i] = *reinterpret_cast<const u32x4_t*>(pa[i]);
-    sa[i] = *reinterpret_cast<const uint32_t*>(psa[i]);
+  StageRegs g;
+  // prologue: stages 0 and 1 into LDS, stage 2 in registers
+  stage_load(g, A, As, B, Bs, M, m0, n0, kb, ks, 0, tid);
+  stage_store(g, lds, tid);
+  if (nstage > 1) {
+    stage_load(g, A, As, B, Bs, M, m0, n0, kb, ks, 1, tid);
+    stage_store(g, lds + kStageBytes, tid);
   }
-#pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    cb[j] = *reinterpret_cast<const u32x4_t*>(pb[j]);
-    sb[j] = *reinterpret_cast<const uint32_t*>(psb[j]);
-  }
+  if (nstage > 2) stage_load(g, A, As, B, Bs, M, m0, n0, kb, ks, 2, tid);
+  __syncthreads();
 
-  for (int64_t c = 0; c < nchunk; ++c) {
-    u32x4_t ca_cur[FM], cb_cur[FN];
-    uint32_t sa_cur[FM], sb_cur[FN];
+  for (int64_t s = 0; s < nstage; ++s) {
+    const uint8_t* buf = lds + (s % kStages) * kStageBytes;
+    const uint8_t* la = buf + (wm * 128 + r32) * kRowPitch + 16 * h;
+    const uint8_t* lb = buf + kCodeBuf + (wn * 128 + r32) * kRowPitch + 16 * h;
+    const uint8_t* lsa = buf + 2 * kCodeBuf + (wm * 128 + r32) * 8 + 2 * h;
+    const uint8_t* lsb = buf + 2 * kCodeBuf + kScaleBuf + (wn * 128 + r32) * 8 + 2 * h;
 #pragma unroll
-    for (int i = 0; i < FM; ++i) { ca_cur[i] = ca[i]; sa_cur[i] = sa[i]; }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) { cb_cur[j] = cb[j]; sb_cur[j] = sb[j]; }
-    if (c + 1 < nchunk) {
+    for (int sub = 0; sub < 2; ++sub) {
+      u32x4_t ca[FM], cb[FN];
+      f16x2_t sA[FM][2], sB[FN][2];
 #pragma unroll
       for (int i = 0; i < FM; ++i) {
-        ca[i] = *reinterpret_cast<const u32x4_t*>(pa[i] + (c + 1) * 32);
-        sa[i] = *reinterpret_cast<const uint32_t*>(psa[i] + (c + 1) * 4);
+        ca[i] = *reinterpret_cast<const u32x4_t*>(la + i * 32 * kRowPitch + 32 * sub);
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(lsa + i * 32 * 8 + 4 * sub);
+        const _Float16 v0 = e4m3_to_f16(sc & 0xFFu), v1 = e4m3_to_f16(sc >> 8);
+        sA[i][0] = f16x2_t{v0, v0};
+        sA[i][1] = f16x2_t{v1, v1};
       }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
-        cb[j] = *reinterpret_cast<const u32x4_t*>(pb[j] + (c + 1) * 32);
-        sb[j] = *reinterpret_cast<const uint32_t*>(psb[j] + (c + 1) * 4);
+        cb[j] = *reinterpret_cast<const u32x4_t*>(lb + j * 32 * kRowPitch + 32 * sub);
+        const uint32_t sc = *reinterpret_cast<const uint16_t*>(lsb + j * 32 * 8 + 4 * sub);
+        const _Float16 v0 = e4m3_to_f16(sc & 0xFFu), v1 = e4m3_to_f16(sc >> 8);
+        sB[j][0] = f16x2_t{v0, v0};
+        sB[j][1] = f16x2_t{v1, v1};
+      }
+#pragma unroll
+      for (int t = 0; t < 4; ++t) {
+        f16x8_t a_op[FM], b_op[FN];
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a_op[i] = dequant8(ca[i][t], sA[i][t >> 1]);
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b_op[j] = dequant8(cb[j][t], sB[j][t >> 1]);
+#pragma unroll
+        for (int i = 0; i < FM; ++i)
+#pragma unroll
+          for (int j = 0; j < FN; ++j)
+            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[i], b_op[j], acc[i][j], 0, 0, 0);
       }
     }
-    // block scales of this lane: elements 0..15 -> block 2h, 16..31 -> block 2h + 1
-    f16x2_t sA[FM][2], sB[FN][2];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const _Float16 v = e4m3_to_f16((sa_cur[i] >> (8 * (2 * h + u))) & 0xFFu);
-        sA[i][u] = f16x2_t{v, v};
-      }
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-#pragma unroll
-      for (int u = 0; u < 2; ++u) {
-        const _Float16 v = e4m3_to_f16((sb_cur[j] >> (8 * (2 * h + u))) & 0xFFu);
-        sB[j][u] = f16x2_t{v, v};
-      }
-    }
-#pragma unroll
-    for (int t = 0; t < 4; ++t) {
-      f16x8_t a_op[FM], b_op[FN];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) a_op[i] = dequant8(ca_cur[i][t], sA[i][t >> 1]);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) b_op[j] = dequant8(cb_cur[j][t], sB[j][t >> 1]);
-#pragma unroll
-      for (int i = 0; i < FM; ++i)
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[i], b_op[j], acc[i][j], 0, 0, 0);
-    }
+    if (s + 2 < nstage) stage_store(g, lds + ((s + 2) % kStages) * kStageBytes, tid);
+    if (s + 3 < nstage) stage_load(g, A, As, B, Bs, M, m0, n0, kb, ks, s + 3, tid);
+    __syncthreads();
   }
 
-  // ---- epilogue: tensor scales, DeltaQuant core, low-rank up-projection, bf16 store ----
-  const float gsc = g_a[0] * g_w[0];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] *= gsc;
-
-  if (core_out) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-#pragma unroll
-      for (int e = 0; e < 16; ++e) {
-        int64_t row = m_base + 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
-        row = row < M ? row : M - 1;
-        const float* co = core_out + (int64_t)row_to_cube[row] * N;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) acc[i][j][e] += co[n_base + 32 * j + r32];
-      }
-    }
-  }
-
-  for (int t = 0; 16 * t < r; ++t) {
-    const int k0 = 16 * t + 8 * h;
-    bf16x8_t d_hi[FM], d_lo[FM], u_op[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      int64_t row = m_base + 32 * i + r32;
-      row = row < M ? row : M - 1;
-      lowrank_operand(D + row * r + k0, k0 < r, d_hi[i], d_lo[i]);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n_base + 32 * j + r32;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (k0 < r) v = *reinterpret_cast<const u32x4_t*>(up + col * r + k0);
-      u_op[j] = __builtin_bit_cast(bf16x8_t, v);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i)
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d_hi[i], u_op[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d_lo[i], u_op[j], acc[i][j], 0, 0, 0);
-      }
-  }
-
-  // 32x32 accumulator layout: lane holds column r32 and rows (e/4)*8 + 4h + e%4.
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t row = m_base + 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
-      if (row < M) {
-#pragma unroll
-        for (int j = 0; j < FN; ++j)
-          Y[row * ldy + n_base + 32 * j + r32] = f32_to_bf16(acc[i][j][e]);
-      }
-    }
-  }
+  gemm_epilogue<FM, FN>(acc, g_a[0] * g_w[0], M, N, m_base, n_base, r32, h, D, up, r, core_out,
+                        row_to_cube, Y, ldy);
 }
 
 }  // namespace
@@ -231,9 +258,8 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
                        const int32_t* row_to_cube, uint16_t* Y, int64_t ldy, hipStream_t s) {
   if (fmt == 1)
     return launch_gemm_int4(M, N, K, a_codes, a_scales, w_codes, w_scales, D, up, r, Y, ldy, s);
-  constexpr int FM = 4, FN = 2;
-  const dim3 grid((unsigned)(N / (64 * FN)), (unsigned)((M + 64 * FM - 1) / (64 * FM)));
-  k_gemm_nvfp4<FM, FN><<<grid, dim3(kThreads), 0, s>>>(
+  const dim3 grid((unsigned)(N / kBN), (unsigned)((M + kBM - 1) / kBM));
+  k_gemm_nvfp4<<<grid, dim3(kThreads), 0, s>>>(
       M, N, K, a_codes, reinterpret_cast<const uint8_t*>(a_scales), g_a, w_codes,
       reinterpret_cast<const uint8_t*>(w_scales), g_w, D, up, (int)r, core_out, row_to_cube, Y,
       ldy);
