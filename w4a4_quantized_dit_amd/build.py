@@ -27,11 +27,13 @@ FLAGS = [
 ]
 
 
-def build(verbose=False):
-    """Compile every source into libsvdq.so (always recompiles)."""
+def build(verbose=False, out=None, defines=()):
+    """Compile every source into libsvdq.so (always recompiles).  `out` / `defines` build a
+    differently named library with extra -D tuning definitions."""
     srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    tmp = LIB + ".tmp"
-    cmd = [HIPCC] + FLAGS + srcs + ["-o", tmp]
+    target = out or LIB
+    tmp = target + ".tmp"
+    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + srcs + ["-o", tmp]
     t0 = time.time()
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
@@ -39,10 +41,10 @@ def build(verbose=False):
         raise RuntimeError("hipcc failed:\n" + out)
     if verbose and out.strip():
         print(out)
-    os.replace(tmp, LIB)
+    os.replace(tmp, target)
     if verbose:
-        print(f"built {LIB} in {time.time() - t0:.1f}s")
-    return LIB
+        print(f"built {target} in {time.time() - t0:.1f}s")
+    return target
 
 
 if __name__ == "__main__":

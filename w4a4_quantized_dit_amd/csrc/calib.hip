@@ -8,49 +8,63 @@ namespace svdq {
 
 namespace {
 
-constexpr int kAbsmaxThreads = 64;   // one wave; 8 channels per lane -> 512 channels per block
-constexpr int kAbsmaxRows = 64;      // rows per block (never straddling a modality segment)
+constexpr int kAbsmaxWaves = 4;
+constexpr int kAbsmaxThreads = 64 * kAbsmaxWaves;  // a block covers 512 channels (8 per lane)
+constexpr int kAbsmaxRows = 256;                    // rows per block (never straddling a segment)
+constexpr int kUnroll = 8;                          // loads in flight per lane
 
 struct SegChunks {
   int64_t seg[4];     // {0, n_text, n_text + n_video, M}
   int64_t cstart[4];  // first chunk of each segment (cumulative), cstart[3] = total
 };
 
-__global__ void k_fill(float* __restrict__ p, int64_t n, float v) {
+__global__ void k_fill2(float* __restrict__ p, int64_t n, float v, float* __restrict__ q,
+                        int64_t nq, float vq) {
   int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i < n) p[i] = v;
+  if (q && i < nq) q[i] = vq;
 }
 
-// out[mu*K + k] = max(out, max over the chunk's rows of |X[row, k]|); bf16 magnitudes compare as
-// unsigned 15-bit patterns, so the max is taken on integers and converted once.
+typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+
+// out[mu*K + k] = max(out, max over the chunk's rows of |X[row, k]|).  bf16 magnitudes compare as
+// unsigned 15-bit patterns, so the max is taken on integers; the four waves of a block take
+// interleaved rows and combine through LDS before one atomic per channel.
 __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint16_t* __restrict__ X,
                                                            int64_t ld, int64_t K, SegChunks sc,
                                                            float* __restrict__ out,
                                                            int per_modality) {
+  __shared__ u16x8 red[kAbsmaxWaves][64];
   const int64_t chunk = blockIdx.y;
   const int mu = (chunk >= sc.cstart[1]) + (chunk >= sc.cstart[2]);
   const int64_t r0 = sc.seg[mu] + (chunk - sc.cstart[mu]) * kAbsmaxRows;
   const int64_t r1 = min(r0 + (int64_t)kAbsmaxRows, sc.seg[mu + 1]);
-  const int64_t col = ((int64_t)blockIdx.x * kAbsmaxThreads + threadIdx.x) * 8;
-  if (col >= K) return;
-  typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int64_t col = ((int64_t)blockIdx.x * 64 + lane) * 8;
   const u16x8 mask = (u16x8)(0x7FFF);
   u16x8 m = (u16x8)(0);
-  const uint16_t* p = X + r0 * ld + col;
-  int64_t r = r0;
-  for (; r + 4 <= r1; r += 4, p += 4 * ld) {
-    u16x8 v0 = *(const u16x8*)(p);
-    u16x8 v1 = *(const u16x8*)(p + ld);
-    u16x8 v2 = *(const u16x8*)(p + 2 * ld);
-    u16x8 v3 = *(const u16x8*)(p + 3 * ld);
-    m = __builtin_elementwise_max(m, __builtin_elementwise_max(v0 & mask, v1 & mask));
-    m = __builtin_elementwise_max(m, __builtin_elementwise_max(v2 & mask, v3 & mask));
-  }
-  for (; r < r1; ++r, p += ld) m = __builtin_elementwise_max(m, *(const u16x8*)(p)&mask);
-  float* o = out + (per_modality ? (int64_t)mu * K : 0) + col;
+  if (col < K) {
+    const uint16_t* p = X + col;
+    int64_t r = r0 + wave;
+    for (; r + (kUnroll - 1) * kAbsmaxWaves < r1; r += kUnroll * kAbsmaxWaves) {
+      u16x8 v[kUnroll];
 #pragma unroll
-  for (int j = 0; j < 8; ++j)
-    if (m[j]) atomic_max_pos(o + j, bf16_to_f32(m[j]));
+      for (int u = 0; u < kUnroll; ++u) v[u] = *(const u16x8*)(p + (r + u * kAbsmaxWaves) * ld);
+#pragma unroll
+      for (int u = 0; u < kUnroll; ++u) m = __builtin_elementwise_max(m, v[u] & mask);
+    }
+    for (; r < r1; r += kAbsmaxWaves) m = __builtin_elementwise_max(m, *(const u16x8*)(p + r * ld) & mask);
+  }
+  red[wave][lane] = m;
+  __syncthreads();
+  if (wave == 0 && col < K) {
+#pragma unroll
+    for (int w = 1; w < kAbsmaxWaves; ++w) m = __builtin_elementwise_max(m, red[w][lane]);
+    float* o = out + (per_modality ? (int64_t)mu * K : 0) + col;
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      if (m[j]) atomic_max_pos(o + j, bf16_to_f32(m[j]));
+  }
 }
 
 // λ from the (accumulated) maxima, and the static activation amax max_k ax_all[k]·(1/λ[k]).
@@ -99,17 +113,11 @@ SegChunks make_chunks(const int64_t seg[4]) {
   return sc;
 }
 
-hipError_t fill(float* p, int64_t n, float v, hipStream_t s) {
-  if (n <= 0) return hipSuccess;
-  k_fill<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(p, n, v);
-  return hipGetLastError();
-}
-
 hipError_t absmax(const uint16_t* X, int64_t ld, int64_t K, const int64_t seg[4], float* out,
                   int per_modality, hipStream_t s) {
   SegChunks sc = make_chunks(seg);
   if (sc.cstart[3] == 0) return hipSuccess;
-  dim3 grid((unsigned)((K / 8 + kAbsmaxThreads - 1) / kAbsmaxThreads), (unsigned)sc.cstart[3]);
+  dim3 grid((unsigned)((K / 8 + 63) / 64), (unsigned)sc.cstart[3]);
   k_absmax<<<grid, dim3(kAbsmaxThreads), 0, s>>>(X, ld, K, sc, out, per_modality);
   return hipGetLastError();
 }
@@ -121,11 +129,16 @@ hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx
                             uint32_t mask, float alpha, int accumulate, float* ax, float* aw,
                             float* lambda, float* act_amax, hipStream_t s) {
   hipError_t e;
-  if (!accumulate) {
-    if ((e = fill(ax, 3 * K, 0.0f, s)) != hipSuccess) return e;
-    if (W && (e = fill(aw, K, 0.0f, s)) != hipSuccess) return e;
+  // one fill launch: clears ax (unless accumulating) and sets aw (0 before a max over W, or 1
+  // without W)
+  if (!accumulate || !W) {
+    float* p = accumulate ? nullptr : ax;
+    float* q = (!accumulate || !W) ? aw : nullptr;
+    const int64_t n = 3 * K;
+    k_fill2<<<dim3((unsigned)((n + 255) / 256)), dim3(256), 0, s>>>(
+        p ? p : aw, p ? n : 0, 0.0f, q, q ? K : 0, W ? 0.0f : 1.0f);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if (!W && (e = fill(aw, K, 1.0f, s)) != hipSuccess) return e;
   if ((e = absmax(X, ldx, K, seg, ax, 1, s)) != hipSuccess) return e;
   if (W) {
     const int64_t wseg[4] = {0, N, N, N};

@@ -4,11 +4,15 @@
 // scale should be calibrated on", section "Why": the kernel sees X / λ, 16 channels per FP8
 // scale; "MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)": activations quantised at run time).
 //
-// Work split: one wave owns 16 rows.  Lane (row = lane % 16, q = lane / 16) holds 64 contiguous
-// channels [k0 + 64q, k0 + 64q + 64) of a 256-channel chunk, i.e. four whole NVFP4 blocks or one
-// whole int4 group, so every block absmax is lane-local (no cross-lane reduction).  The same
-// registers feed v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry
-// channels k0 + 64q + 8t .. +8, and the L1 operand is loaded with the same channel mapping.
+// Work split: a block of four waves owns 64 rows (16 per wave) and walks K in 256-channel
+// chunks.  X is read with coalesced 16-byte loads (one load instruction covers two whole rows of
+// the chunk) and re-laid through LDS so that lane (row = lane % 16, q = lane / 16) holds 64
+// contiguous channels [k0 + 64q, k0 + 64q + 64): four whole NVFP4 blocks or one whole int4
+// group, so every block absmax is lane-local (no cross-lane reduction).  The same registers feed
+// v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry channels
+// k0 + 64q + 8t .. +8, and the block stages the matching slice of L1 (lora_down[:, k0:k0+256])
+// in LDS once for its four waves.  The next chunk's global loads are issued before the current
+// chunk is processed.
 #include "device.h"
 #include "launch.h"
 
@@ -18,8 +22,9 @@ namespace {
 
 constexpr int kWaves = 4;
 constexpr int kThreads = 64 * kWaves;
-constexpr int kRowsPerWave = 16;
+constexpr int kRowsPerBlock = 16 * kWaves;
 constexpr int kChunk = 256;
+constexpr int kPitch = kChunk + 8;   // bf16 elements per LDS row: 528 B, conflict-free reads
 
 template <int FMT, int NT>
 __global__ __launch_bounds__(kThreads) void k_quant_act(
@@ -28,9 +33,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
     const uint16_t* __restrict__ down, int r, uint8_t* __restrict__ codes,
     void* __restrict__ scales, float* __restrict__ tensor_scale, int write_g,
     float* __restrict__ D, uint32_t* __restrict__ sat) {
+  constexpr int NTc = NT > 0 ? NT : 1;
+  constexpr int kLPieces = NT * 16 * (kChunk / 8) / kThreads;  // 16-B pieces of L1 per thread
   extern __shared__ float s_inv[];  // 1/λ for all K channels
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kWaves][16 * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_l[NTc * 16 * kPitch];
   for (int64_t k = threadIdx.x; k < K; k += kThreads) s_inv[k] = lambda ? 1.0f / lambda[k] : 1.0f;
-  __syncthreads();
 
   float amax = 0.0f, g = 1.0f, d6 = 6.0f;
   if (FMT == 0) {
@@ -40,37 +48,69 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
     if (write_g && blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = g;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row0 = ((int64_t)blockIdx.x * kWaves + wave) * kRowsPerWave;
-  if (row0 >= M) return;
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock + 16 * wave;
   const int rl = lane & 15, q = lane >> 4;
   const int64_t row = row0 + rl;
   const bool valid = row < M;
-  const uint16_t* xp = X + (valid ? row : row0) * ldx + 64 * q;
 
-  f32x4_t acc[NT > 0 ? NT : 1];
+  // coalesced X loads: instruction i covers rows 2i, 2i+1 of the wave, lane piece = lane % 32
+  // (rows past M read row M-1; their results are never stored)
+  const uint16_t* xg[8];
 #pragma unroll
-  for (int j = 0; j < (NT > 0 ? NT : 1); ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  for (int i = 0; i < 8; ++i) {
+    int64_t xrow = row0 + 2 * i + (lane >> 5);
+    xrow = xrow < M ? xrow : M - 1;
+    xg[i] = X + xrow * ldx + 8 * (lane & 31);
+  }
+  // L1 staging: piece p of the block = rank p / 32, channels 8 * (p % 32) .. +8 (ranks past r
+  // read rank r-1 and are zeroed)
+  const uint16_t* lg[kLPieces > 0 ? kLPieces : 1];
+#pragma unroll
+  for (int u = 0; u < kLPieces; ++u) {
+    const int p = threadIdx.x + kThreads * u;
+    const int n = p >> 5;
+    lg[u] = down + (int64_t)(n < r ? n : r - 1) * K + 8 * (p & 31);
+  }
+
+  f32x4_t acc[NTc];
+#pragma unroll
+  for (int j = 0; j < NTc; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint32_t nsat = 0;
 
-  u32x4_t nxt[8];
+  u32x4_t xr[8], lr[kLPieces > 0 ? kLPieces : 1];
 #pragma unroll
-  for (int i = 0; i < 8; ++i) nxt[i] = reinterpret_cast<const u32x4_t*>(xp)[i];
+  for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i]);
+#pragma unroll
+  for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u]);
+  __syncthreads();  // s_inv complete
 
   for (int64_t k0 = 0; k0 < K; k0 += kChunk) {
-    u32x4_t v[8];
+    // registers -> LDS (the previous chunk's readers finished at the loop-end barrier)
 #pragma unroll
-    for (int i = 0; i < 8; ++i) v[i] = nxt[i];
+    for (int i = 0; i < 8; ++i)
+      *reinterpret_cast<u32x4_t*>(&s_x[wave][(2 * i + (lane >> 5)) * kPitch + 8 * (lane & 31)]) = xr[i];
+#pragma unroll
+    for (int u = 0; u < kLPieces; ++u) {
+      const int p = threadIdx.x + kThreads * u;
+      const int n = p >> 5;
+      const u32x4_t v = n < r ? lr[u] : u32x4_t{0u, 0u, 0u, 0u};
+      *reinterpret_cast<u32x4_t*>(&s_l[n * kPitch + 8 * (p & 31)]) = v;
+    }
+    __syncthreads();
     if (k0 + kChunk < K) {
 #pragma unroll
-      for (int i = 0; i < 8; ++i) nxt[i] = reinterpret_cast<const u32x4_t*>(xp + k0 + kChunk)[i];
+      for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + k0 + kChunk);
+#pragma unroll
+      for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + k0 + kChunk);
     }
     const int64_t kb = k0 + 64 * q;  // first channel of this lane
     float x[64];
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
+      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&s_x[wave][rl * kPitch + 64 * q + 8 * i]);
 #pragma unroll
       for (int c = 0; c < 4; ++c) {
-        const uint32_t w = valid ? v[i][c] : 0u;
+        const uint32_t w = valid ? v[c] : 0u;
         x[8 * i + 2 * c] = bf16_lo(w) * s_inv[kb + 8 * i + 2 * c];
         x[8 * i + 2 * c + 1] = bf16_hi(w) * s_inv[kb + 8 * i + 2 * c + 1];
       }
@@ -134,14 +174,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
         const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
         for (int j = 0; j < NT; ++j) {
-          const int n = 16 * j + rl;
-          u32x4_t bv = u32x4_t{0u, 0u, 0u, 0u};
-          if (n < r) bv = *reinterpret_cast<const u32x4_t*>(down + (int64_t)n * K + kb + 8 * t);
+          const u32x4_t bv =
+              *reinterpret_cast<const u32x4_t*>(&s_l[(16 * j + rl) * kPitch + 64 * q + 8 * t]);
           acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, __builtin_bit_cast(bf16x8_t, bv),
                                                            acc[j], 0, 0, 0);
         }
       }
     }
+    __syncthreads();  // the LDS chunk buffers are rewritten next iteration
   }
 
   if (NT > 0) {
@@ -201,6 +241,11 @@ hipError_t dispatch(int nt, dim3 grid, size_t lds, hipStream_t s, const uint16_t
                     int write_g, float* D, uint32_t* sat) {
 #define SVDQ_QA_CASE(NTV)                                                                  \
   case NTV:                                                                                \
+    if (lds > 48 * 1024) {                                                                 \
+      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_quant_act<FMT, NTV>), \
+                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
+      if (e != hipSuccess) return e;                                                       \
+    }                                                                                      \
     k_quant_act<FMT, NTV><<<grid, dim3(kThreads), lds, s>>>(X, M, K, ldx, lambda, amax_p, \
                                                              down, r, codes, scales, ts,   \
                                                              write_g, D, sat);             \
@@ -229,8 +274,7 @@ hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, in
                             int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
                             float* D, uint32_t* sat, hipStream_t s) {
   const int nt = (int)((r + 15) / 16);
-  const int64_t rows_per_block = (int64_t)kWaves * kRowsPerWave;
-  const dim3 grid((unsigned)((M + rows_per_block - 1) / rows_per_block));
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
   const size_t lds = (size_t)K * sizeof(float);
   if (fmt == 1)
     return dispatch<1>(nt, grid, lds, s, X, M, K, ldx, lambda, nullptr, down, (int)r, codes,
