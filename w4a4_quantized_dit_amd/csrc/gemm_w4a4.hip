@@ -23,16 +23,9 @@ namespace svdq {
 namespace {
 
 constexpr int kThreads = 256;  // 4 waves, 2 x 2 over the workgroup tile
-
-__device__ __forceinline__ _Float16 e4m3_to_f16(uint32_t b) {
-  const uint32_t e = (b >> 3) & 15u, m = b & 7u;
-  float v;
-  if (e == 0u)
-    v = (float)m * 0.001953125f;
-  else
-    v = __uint_as_float(((e + 120u) << 23) | (m << 20));
-  return (_Float16)v;  // exact: every E4M3 value is an fp16 value
-}
+#ifndef SVDQ_GEMM_VALU_PER_MFMA
+#define SVDQ_GEMM_VALU_PER_MFMA 4   // scheduling hint: dequantisation VALU ops between MFMAs
+#endif
 
 // 8 E2M1 codes (one dword, element i in nibble i) times a block scale -> 8 exact fp16 values.
 __device__ __forceinline__ f16x8_t dequant8(uint32_t codes, f16x2_t s2) {
@@ -158,6 +151,35 @@ __device__ __forceinline__ void stage_store(const StageRegs& g, uint8_t* lds, in
   *reinterpret_cast<uint2*>(lsb + tid * 8) = g.sb;
 }
 
+// Raw operand fragments of one 64-element sub-stage: per MFMA tile row / column, 16 B of codes
+// (32 elements of the lane's row) and the two E4M3 block scales as broadcast fp16 pairs.
+template <int F>
+struct Frags {
+  u32x4_t c[F];
+  f16x2_t s[F][2];
+};
+
+// Two E4M3 scale bytes (low byte first) -> fp16 pair, exactly: the E4M3 pattern without its
+// sign, shifted into an fp16 exponent/mantissa, is the value times 2^-8 (subnormals included),
+// and the multiply by 256 is exact.
+__device__ __forceinline__ f16x2_t e4m3x2_to_f16x2(uint32_t x) {
+  const uint32_t bits = ((x & 0x7Fu) << 7) | ((x & 0x7F00u) << 15);
+  return __builtin_bit_cast(f16x2_t, bits) * f16x2_t{(_Float16)256.0f, (_Float16)256.0f};
+}
+
+template <int F>
+__device__ __forceinline__ void read_frags(Frags<F>& f, const uint8_t* codes,
+                                           const uint8_t* scales, int sub) {
+#pragma unroll
+  for (int i = 0; i < F; ++i) {
+    f.c[i] = *reinterpret_cast<const u32x4_t*>(codes + i * 32 * kRowPitch + 32 * sub);
+    const uint32_t sc = *reinterpret_cast<const uint16_t*>(scales + i * 32 * 8 + 4 * sub);
+    const f16x2_t p = e4m3x2_to_f16x2(sc);
+    f.s[i][0] = f16x2_t{p[0], p[0]};
+    f.s[i][1] = f16x2_t{p[1], p[1]};
+  }
+}
+
 __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
     const uint8_t* __restrict__ As, const float* __restrict__ g_a,
@@ -175,6 +197,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   const int r32 = lane & 31, h = lane >> 5;
   const int64_t kb = K / 2, ks = K / 16;
   const int64_t nstage = K / kBK;
+  // this lane's fragment rows within a stage buffer
+  const int a_off = (wm * 128 + r32) * kRowPitch + 16 * h;
+  const int b_off = kCodeBuf + (wn * 128 + r32) * kRowPitch + 16 * h;
+  const int sa_off = 2 * kCodeBuf + (wm * 128 + r32) * 8 + 2 * h;
+  const int sb_off = 2 * kCodeBuf + kScaleBuf + (wn * 128 + r32) * 8 + 2 * h;
 
   f32x16_t acc[FM][FN];
 #pragma unroll
@@ -195,45 +222,65 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   if (nstage > 2) stage_load(g, A, As, B, Bs, M, m0, n0, kb, ks, 2, tid);
   __syncthreads();
 
+  // Software pipeline over K16 steps: while the 16 MFMAs of one step run, the operands of the
+  // next step are dequantised (VALU) and, at the last step of a sub-stage, the next sub-stage's
+  // raw fragments are read from LDS.  Stage s+1 is already complete in its LDS buffer while
+  // stage s is computed (three buffers), so the look-ahead never waits on a barrier.
+  Frags<FM> fa;
+  Frags<FN> fb;
+  read_frags(fa, lds + a_off, lds + sa_off, 0);
+  read_frags(fb, lds + b_off, lds + sb_off, 0);
+  f16x8_t a_op[FM], b_op[FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) a_op[i] = dequant8(fa.c[i][0], fa.s[i][0]);
+#pragma unroll
+  for (int j = 0; j < FN; ++j) b_op[j] = dequant8(fb.c[j][0], fb.s[j][0]);
+
   for (int64_t s = 0; s < nstage; ++s) {
-    const uint8_t* buf = lds + (s % kStages) * kStageBytes;
-    const uint8_t* la = buf + (wm * 128 + r32) * kRowPitch + 16 * h;
-    const uint8_t* lb = buf + kCodeBuf + (wn * 128 + r32) * kRowPitch + 16 * h;
-    const uint8_t* lsa = buf + 2 * kCodeBuf + (wm * 128 + r32) * 8 + 2 * h;
-    const uint8_t* lsb = buf + 2 * kCodeBuf + kScaleBuf + (wn * 128 + r32) * 8 + 2 * h;
 #pragma unroll
     for (int sub = 0; sub < 2; ++sub) {
-      u32x4_t ca[FM], cb[FN];
-      f16x2_t sA[FM][2], sB[FN][2];
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        ca[i] = *reinterpret_cast<const u32x4_t*>(la + i * 32 * kRowPitch + 32 * sub);
-        const uint32_t sc = *reinterpret_cast<const uint16_t*>(lsa + i * 32 * 8 + 4 * sub);
-        const _Float16 v0 = e4m3_to_f16(sc & 0xFFu), v1 = e4m3_to_f16(sc >> 8);
-        sA[i][0] = f16x2_t{v0, v0};
-        sA[i][1] = f16x2_t{v1, v1};
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        cb[j] = *reinterpret_cast<const u32x4_t*>(lb + j * 32 * kRowPitch + 32 * sub);
-        const uint32_t sc = *reinterpret_cast<const uint16_t*>(lsb + j * 32 * 8 + 4 * sub);
-        const _Float16 v0 = e4m3_to_f16(sc & 0xFFu), v1 = e4m3_to_f16(sc >> 8);
-        sB[j][0] = f16x2_t{v0, v0};
-        sB[j][1] = f16x2_t{v1, v1};
+      Frags<FM> na;
+      Frags<FN> nb;
+      const bool more = sub == 0 || s + 1 < nstage;
+      if (more) {
+        const uint8_t* nbuf = lds + ((sub == 0 ? s : s + 1) % kStages) * kStageBytes;
+        read_frags(na, nbuf + a_off, nbuf + sa_off, sub ^ 1);
+        read_frags(nb, nbuf + b_off, nbuf + sb_off, sub ^ 1);
       }
 #pragma unroll
       for (int t = 0; t < 4; ++t) {
-        f16x8_t a_op[FM], b_op[FN];
+        f16x8_t a_nx[FM], b_nx[FN];
+        if (t < 3) {
 #pragma unroll
-        for (int i = 0; i < FM; ++i) a_op[i] = dequant8(ca[i][t], sA[i][t >> 1]);
+          for (int i = 0; i < FM; ++i) a_nx[i] = dequant8(fa.c[i][t + 1], fa.s[i][(t + 1) >> 1]);
 #pragma unroll
-        for (int j = 0; j < FN; ++j) b_op[j] = dequant8(cb[j][t], sB[j][t >> 1]);
+          for (int j = 0; j < FN; ++j) b_nx[j] = dequant8(fb.c[j][t + 1], fb.s[j][(t + 1) >> 1]);
+        } else if (more) {
+#pragma unroll
+          for (int i = 0; i < FM; ++i) a_nx[i] = dequant8(na.c[i][0], na.s[i][0]);
+#pragma unroll
+          for (int j = 0; j < FN; ++j) b_nx[j] = dequant8(nb.c[j][0], nb.s[j][0]);
+        }
 #pragma unroll
         for (int i = 0; i < FM; ++i)
 #pragma unroll
           for (int j = 0; j < FN; ++j)
             acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[i], b_op[j], acc[i][j], 0, 0, 0);
+        // interleave: one MFMA, then a few VALU instructions of the next step's dequantisation
+#if SVDQ_GEMM_VALU_PER_MFMA > 0
+#pragma unroll
+        for (int k = 0; k < FM * FN; ++k) {
+          __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
+          __builtin_amdgcn_sched_group_barrier(0x002, SVDQ_GEMM_VALU_PER_MFMA, 0);
+        }
+#endif
+#pragma unroll
+        for (int i = 0; i < FM; ++i) a_op[i] = a_nx[i];
+#pragma unroll
+        for (int j = 0; j < FN; ++j) b_op[j] = b_nx[j];
       }
+      fa = na;
+      fb = nb;
     }
     if (s + 2 < nstage) stage_store(g, lds + ((s + 2) % kStages) * kStageBytes, tid);
     if (s + 3 < nstage) stage_load(g, A, As, B, Bs, M, m0, n0, kb, ks, s + 3, tid);

@@ -4,14 +4,14 @@
 // scale should be calibrated on", section "Why": the kernel sees X / λ, 16 channels per FP8
 // scale; "MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)": activations quantised at run time).
 //
-// Work split: a block of four waves owns 64 rows (16 per wave) and walks K in 256-channel
+// Work split: a block of kWaves waves owns 16 rows per wave and walks K in 256-channel
 // chunks.  X is read with coalesced 16-byte loads (one load instruction covers two whole rows of
 // the chunk) and re-laid through LDS so that lane (row = lane % 16, q = lane / 16) holds 64
 // contiguous channels [k0 + 64q, k0 + 64q + 64): four whole NVFP4 blocks or one whole int4
 // group, so every block absmax is lane-local (no cross-lane reduction).  The same registers feed
 // v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry channels
 // k0 + 64q + 8t .. +8, and the block stages the matching slice of L1 (lora_down[:, k0:k0+256])
-// in LDS once for its four waves.  The next chunk's global loads are issued before the current
+// in LDS once for its waves.  The next chunk's global loads are issued before the current
 // chunk is processed.
 #include "device.h"
 #include "launch.h"
@@ -20,7 +20,13 @@ namespace svdq {
 
 namespace {
 
-constexpr int kWaves = 4;
+#ifndef SVDQ_QA_WAVES
+#define SVDQ_QA_WAVES 4    // waves (16 rows each) per block
+#endif
+#ifndef SVDQ_QA_DEPTH
+#define SVDQ_QA_DEPTH 1    // chunks of X / L1 loads in flight ahead of the chunk in LDS (1 or 2)
+#endif
+constexpr int kWaves = SVDQ_QA_WAVES;
 constexpr int kThreads = 64 * kWaves;
 constexpr int kRowsPerBlock = 16 * kWaves;
 constexpr int kChunk = 256;
@@ -78,10 +84,17 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
   uint32_t nsat = 0;
 
   u32x4_t xr[8], lr[kLPieces > 0 ? kLPieces : 1];
+  u32x4_t xr2[SVDQ_QA_DEPTH == 2 ? 8 : 1], lr2[SVDQ_QA_DEPTH == 2 && kLPieces > 0 ? kLPieces : 1];
 #pragma unroll
   for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i]);
 #pragma unroll
   for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u]);
+  if (SVDQ_QA_DEPTH == 2 && kChunk < K) {
+#pragma unroll
+    for (int i = 0; i < 8; ++i) xr2[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + kChunk);
+#pragma unroll
+    for (int u = 0; u < kLPieces; ++u) lr2[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + kChunk);
+  }
   __syncthreads();  // s_inv complete
 
   for (int64_t k0 = 0; k0 < K; k0 += kChunk) {
@@ -97,7 +110,19 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
       *reinterpret_cast<u32x4_t*>(&s_l[n * kPitch + 8 * (p & 31)]) = v;
     }
     __syncthreads();
-    if (k0 + kChunk < K) {
+    if (SVDQ_QA_DEPTH == 2) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) xr[i] = xr2[i];
+#pragma unroll
+      for (int u = 0; u < kLPieces; ++u) lr[u] = lr2[u];
+      if (k0 + 2 * kChunk < K) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) xr2[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + k0 + 2 * kChunk);
+#pragma unroll
+        for (int u = 0; u < kLPieces; ++u)
+          lr2[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + k0 + 2 * kChunk);
+      }
+    } else if (k0 + kChunk < K) {
 #pragma unroll
       for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + k0 + kChunk);
 #pragma unroll
