@@ -118,6 +118,26 @@ __device__ __forceinline__ void lowrank_operand(const float* p, bool valid, floa
   lo = __builtin_bit_cast(bf16x8_t, vl);
 }
 
+// 8 E2M1 codes (one dword, element i in nibble i) times a block scale -> 8 exact fp16 values.
+__device__ __forceinline__ f16x8_t dequant8(uint32_t codes, f16x2_t s2) {
+  f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 0) * s2;
+  f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 1) * s2;
+  f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 2) * s2;
+  f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp4(codes, 1.0f, 3) * s2;
+  f16x8_t r;
+  r[0] = p0[0]; r[1] = p0[1]; r[2] = p1[0]; r[3] = p1[1];
+  r[4] = p2[0]; r[5] = p2[1]; r[6] = p3[0]; r[7] = p3[1];
+  return r;
+}
+
+// Two E4M3 scale bytes (low byte first) -> fp16 pair, exactly: the E4M3 pattern without its
+// sign, shifted into an fp16 exponent/mantissa, is the value times 2^-8 (subnormals included),
+// and the multiply by 256 is exact.
+__device__ __forceinline__ f16x2_t e4m3x2_to_f16x2(uint32_t x) {
+  const uint32_t bits = ((x & 0x7Fu) << 7) | ((x & 0x7F00u) << 15);
+  return __builtin_bit_cast(f16x2_t, bits) * f16x2_t{(_Float16)256.0f, (_Float16)256.0f};
+}
+
 // Running maximum of non-negative floats stored as their bit patterns (monotone for >= 0).
 __device__ __forceinline__ void atomic_max_pos(float* addr, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));

@@ -1,0 +1,132 @@
+// Per-modality relative-L2 scoring against the unquantised bf16 layer ("MiniMax-H3 NVFP4 — what
+// the smoothing scale should be calibrated on", section "The metric that picks the winner also
+// hides the cost": relative L2 on rows drawn uniformly and on rows sampled per modality).
+//
+// For the sampled rows, Y_ref = bf16(X·Wᵀ) is recomputed on bf16 MFMA (fp32 accumulation) with
+// the X rows gathered by index; the epilogue forms (Y − Y_ref)² and Y_ref² per element and
+// accumulates them per row group in fp64, then adds each wave's eight sums to `sums`.
+// Workgroup tile 128 sampled rows x 128 columns, 4 waves of 64 x 64 (2 x 2 MFMA 32x32 tiles).
+// K mapping: in a 64-element chunk, lane (row = lane % 32, h = lane / 32) holds elements
+// [32h, 32h + 32) of its row; MFMA step t takes [8t, 8t + 8) of them, for X and W alike.
+#include "device.h"
+#include "launch.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kThreads = 256;
+
+__global__ __launch_bounds__(kThreads) void k_score(const uint16_t* __restrict__ Y, int64_t ldy,
+                                                    const uint16_t* __restrict__ X, int64_t ldx,
+                                                    const uint16_t* __restrict__ W, int64_t ldw,
+                                                    int64_t M, int64_t N, int64_t K,
+                                                    const int32_t* __restrict__ rows,
+                                                    const int8_t* __restrict__ grp,
+                                                    int64_t n_rows, double* __restrict__ sums) {
+  constexpr int FM = 2, FN = 2;
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  const int wm = wave >> 1, wn = wave & 1;
+  const int64_t i_base = (int64_t)blockIdx.y * 128 + wm * 64;   // sampled-row index
+  const int64_t n_base = (int64_t)blockIdx.x * 128 + wn * 64;
+  const int r32 = lane & 31, h = lane >> 5;
+
+  const uint16_t* pa[FM];
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    int64_t idx = i_base + 32 * i + r32;
+    idx = idx < n_rows ? idx : n_rows - 1;
+    int64_t m = rows[idx];
+    m = m < 0 ? 0 : (m < M ? m : M - 1);  // an out-of-range index reads a valid row
+    pa[i] = X + m * ldx + 32 * h;
+  }
+  const uint16_t* pb[FN];
+#pragma unroll
+  for (int j = 0; j < FN; ++j) pb[j] = W + (n_base + 32 * j + r32) * ldw + 32 * h;
+
+  f32x16_t acc[FM][FN];
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
+
+  for (int64_t k0 = 0; k0 < K; k0 += 64) {
+    u32x4_t a[FM][4], b[FN][4];
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) a[i][t] = reinterpret_cast<const u32x4_t*>(pa[i] + k0)[t];
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int t = 0; t < 4; ++t) b[j][t] = reinterpret_cast<const u32x4_t*>(pb[j] + k0)[t];
+#pragma unroll
+    for (int t = 0; t < 4; ++t)
+#pragma unroll
+      for (int i = 0; i < FM; ++i)
+#pragma unroll
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+              __builtin_bit_cast(bf16x8_t, a[i][t]), __builtin_bit_cast(bf16x8_t, b[j][t]),
+              acc[i][j], 0, 0, 0);
+  }
+
+  // 32x32 accumulator layout: lane holds column r32 and rows (e/4)*8 + 4h + e%4
+  double sd[4] = {0.0, 0.0, 0.0, 0.0}, sr[4] = {0.0, 0.0, 0.0, 0.0};
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+#pragma unroll
+    for (int e = 0; e < 16; ++e) {
+      const int64_t idx = i_base + 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
+      if (idx < n_rows) {
+        int64_t m = rows[idx];
+        m = m < 0 ? 0 : (m < M ? m : M - 1);
+        const int gsel = grp[idx];
+        double d2 = 0.0, r2 = 0.0;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) {
+          const float yref = bf16_to_f32(f32_to_bf16(acc[i][j][e]));
+          const float y = bf16_to_f32(Y[m * ldy + n_base + 32 * j + r32]);
+          const double d = (double)y - (double)yref;
+          d2 += d * d;
+          r2 += (double)yref * (double)yref;
+        }
+#pragma unroll
+        for (int g = 0; g < 4; ++g) {
+          sd[g] += gsel == g ? d2 : 0.0;
+          sr[g] += gsel == g ? r2 : 0.0;
+        }
+      }
+    }
+  }
+#pragma unroll
+  for (int g = 0; g < 4; ++g) {
+    for (int off = 32; off > 0; off >>= 1) {
+      sd[g] += __shfl_xor(sd[g], off);
+      sr[g] += __shfl_xor(sr[g], off);
+    }
+  }
+  if (lane == 0) {
+#pragma unroll
+    for (int g = 0; g < 4; ++g) {
+      if (sd[g] != 0.0) atomicAdd(sums + 2 * g, sd[g]);
+      if (sr[g] != 0.0) atomicAdd(sums + 2 * g + 1, sr[g]);
+    }
+  }
+}
+
+}  // namespace
+
+hipError_t launch_score(const uint16_t* Y, int64_t ldy, const uint16_t* X, int64_t ldx,
+                        const uint16_t* W, int64_t ldw, int64_t M, int64_t N, int64_t K,
+                        const int32_t* rows, const int8_t* grp, int64_t n_rows, double* sums,
+                        hipStream_t s) {
+  const dim3 grid((unsigned)(N / 128), (unsigned)((n_rows + 127) / 128));
+  k_score<<<grid, dim3(kThreads), 0, s>>>(Y, ldy, X, ldx, W, ldw, M, N, K, rows, grp, n_rows,
+                                           sums);
+  return hipGetLastError();
+}
+
+}  // namespace svdq
