@@ -1,19 +1,28 @@
 #!/usr/bin/env python3
 """Benchmark of the SVDQuant W4A4 layer on one MI355X.
 
-One step = the whole per-batch path of the attention-projection-sized workload (M = 16384 packed
-rows: 164 text / 16154 video / 66 audio, K = N = 5120, rank 32, NVFP4):
+Default workload (the JSON line's `value`): the attention-projection-sized layer, M = 16384
+packed rows (164 text / 16154 video / 66 audio), K = N = 5120, rank 32, NVFP4.  One step is the
+whole per-batch path:
     λ calibration over the batch -> residual-weight quantisation -> activation quantisation
     with the low-rank down-projection -> W4A4 GEMM with the up-projection (bf16 out).
-Inputs are seeded synthetic tensors resident in HBM before the timed region; four copies of X
-are rotated so the 256 MB last-level cache cannot serve the activation reads.
+Inputs are seeded synthetic tensors resident in HBM before the timed region; copies of X are
+rotated so the 256 MB last-level cache cannot serve the activation reads.
 
-Prints ONE JSON line (rank 0): metric, value (TFLOP/s of the layer per step), per-kernel
-timings, the roofline of the dominant kernel, and the CPU-oracle baseline.
+`--workload` also times the int4-g64 MLP up-projection (M = 32768, K = 5120, N = 13824) and
+the DeltaQuant cube-field layer (31x24x42 grid, K = N = 5120, rank 128) for profiling; the
+`--copy-probe` mode runs a plain 1 GiB device copy whose hardware byte counters calibrate the
+per-kernel traffic figures.
+
+Prints ONE JSON line: metric, value (TFLOP/s of the layer per step), per-kernel timings from
+HIP events on the launch stream, the roofline of the dominant kernel, and the CPU-oracle
+baseline.
 """
 import argparse
+import hashlib
 import json
 import os
+import re
 import sys
 import time
 
@@ -24,7 +33,37 @@ sys.path.insert(0, ROOT)
 
 METRIC = "W4A4 SVDQuant linear TFLOP/s + % MFMA peak; quant kernel GB/s, 5120² M=16k"
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA
+PEAK_I8_TOPS = 5000.0         # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+WORKLOADS = {"attn": 1, "mlp-up-int4": 2, "delta": 4}
+# Sources of each GEMM kernel: the PMC traffic figure is valid only for the source it was taken on.
+GEMM_SOURCES = {"attn": ("gemm_w4a4.hip", "device.h"), "mlp-up-int4": ("gemm_int4.hip", "device.h"),
+                "delta": ("gemm_w4a4.hip", "device.h")}
+
+
+def source_digest(files):
+    h = hashlib.sha256()
+    for f in files:
+        with open(os.path.join(ROOT, "w4a4_quantized_dit_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def measured_traffic(workload):
+    """HBM bytes per GEMM launch from the committed hardware-counter summary, if it was taken on
+    the current kernel source; otherwise None."""
+    import synth
+    kern = "k_gemm_int4" if workload == "mlp-up-int4" else "k_gemm_nvfp4"
+    name = synth.config(WORKLOADS[workload])["name"]
+    path = os.path.join(ROOT, "profiles", f"{kern}_{name}_traffic.md")
+    if not os.path.exists(path):
+        return None
+    text = open(path).read()
+    dig = re.search(r"kernel source digest:\s*`?([0-9a-f]+)", text)
+    val = re.search(r"traffic bytes per launch:\s*`?([0-9.eE+]+)", text)
+    if not dig or not val or dig.group(1) != source_digest(GEMM_SOURCES[workload]):
+        return None
+    return float(val.group(1))
 
 
 def lowrank_factors_rangefinder(W_bits, lam, r, seed=0):
@@ -44,16 +83,19 @@ def lowrank_factors_rangefinder(W_bits, lam, r, seed=0):
     return to_bf16_bits(L1.T), to_bf16_bits(L2.T)
 
 
-def cpu_baseline(cfg, X, W, lam_np, down, up, rows=512):
+def cpu_baseline(cfg, X, W, down, up, rows):
     """The oracle, as it stands, on the first `rows` rows of the workload (whole weight)."""
     from oracle import calib as OC, layer as OL
-    seg = (0, min(cfg["seg"][1], rows), rows, rows)
+    rows = min(rows, cfg["M"])
+    s = cfg["seg"]
+    seg = (0, min(s[1], rows), min(s[2], rows), rows)
     Xs = X[:rows]
+    fmt = "int4" if cfg["fmt"] == "int4" else "nvfp4"
     t0 = time.perf_counter()
     ax, aw, lam, amax = OC.calibrate(Xs, seg, W, 7)
-    wt = OL.prepare_weight(W, lam, down, up, "nvfp4")
-    act = OL.prepare_activation(Xs, lam, amax, down, "nvfp4")
-    OL.forward(act, wt, up, "nvfp4")
+    wt = OL.prepare_weight(W, lam, down, up, fmt)
+    act = OL.prepare_activation(Xs, lam, amax, down, fmt)
+    OL.forward(act, wt, up, fmt)
     dt = time.perf_counter() - t0
     K, N, r = cfg["K"], cfg["N"], cfg["r"]
     flops = 2.0 * rows * N * K + 2.0 * rows * K * r + 2.0 * rows * r * N
@@ -62,9 +104,127 @@ def cpu_baseline(cfg, X, W, lam_np, down, up, rows=512):
     except AttributeError:
         cores = os.cpu_count()
     return {"value": flops / dt / 1e12, "unit": "TFLOP/s", "cores": cores, "kind": "oracle",
-            "sample": f"{rows} of {cfg['M']} rows of the same workload, whole 5120x5120 weight "
+            "sample": f"{rows} of {cfg['M']} rows of the same workload, whole {N}x{K} weight "
                       f"(calibration, fp64 residual + quantisation, activation quantisation, "
                       f"float64 GEMM); {dt:.2f} s"}
+
+
+def copy_probe(torch, nbytes=1 << 30, reps=3):
+    """A plain elementwise device kernel that reads `nbytes` and writes `nbytes` per launch."""
+    src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        torch.bitwise_not(src, out=dst)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_probe_bytes_per_launch": nbytes, "launches": reps}), flush=True)
+
+
+def to_dev(torch, bits):
+    return torch.from_numpy(bits.view(np.int16)).to("cuda").view(torch.bfloat16)
+
+
+def setup(torch, workload, n_rot):
+    """Inputs, outputs and the per-step launch list of one workload."""
+    import synth
+    from w4a4_quantized_dit_amd import _lib
+    cfg = synth.config(WORKLOADS[workload])
+    M, K, N, r = cfg["M"], cfg["K"], cfg["N"], cfg["r"]
+    seg = cfg["seg"]
+    dev = "cuda"
+    print(f"[bench] generating {cfg['name']} inputs", file=sys.stderr, flush=True)
+    X = synth.x_bits(cfg)
+    W = synth.weight_bits(N, K)
+    Xd0, Wd = to_dev(torch, X), to_dev(torch, W)
+    Xs = [Xd0] + [Xd0.clone() for _ in range(n_rot - 1)]
+    ax = torch.empty(3, K, device=dev); aw = torch.empty(K, device=dev)
+    lam = torch.empty(K, device=dev); amax = torch.empty(1, device=dev)
+    _lib.svdq_calibrate_lambda(Xd0, seg, Wd, 7, 0.5, 0, ax, aw, lam, amax)
+    down, up = lowrank_factors_rangefinder(W, lam.cpu().numpy(), r)
+    downd, upd = to_dev(torch, down), to_dev(torch, up)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
+    u8 = torch.uint8
+    st = dict(cfg=cfg, X=X, W=W, down=down, up=up, Y=Y)
+
+    def cal(Xi):
+        _lib.svdq_calibrate_lambda(Xi, seg, Wd, 7, 0.5, 0, ax, aw, lam, amax)
+
+    if workload in ("attn", "delta"):
+        w_codes = torch.empty(N, K // 2, dtype=u8, device=dev)
+        w_scales = torch.empty(N, K // 16, dtype=u8, device=dev)
+        g_w = torch.empty(1, device=dev)
+
+        def wq(Xi):
+            _lib.svdq_quantize_weight(0, Wd, lam, downd, upd, r, w_codes, w_scales, g_w)
+    if workload == "attn":
+        a_codes = torch.empty(M, K // 2, dtype=u8, device=dev)
+        a_scales = torch.empty(M, K // 16, dtype=u8, device=dev)
+        g_a = torch.empty(1, device=dev)
+        D = torch.empty(M, r, device=dev)
+
+        def qa(Xi):
+            _lib.svdq_quant_act_lowrank_down(0, Xi, lam, amax, downd, r, a_codes, a_scales, g_a, D)
+
+        def gemm(Xi):
+            _lib.svdq_w4a4_gemm(0, M, N, K, a_codes, a_scales, g_a, w_codes, w_scales, g_w, D,
+                                upd, r, Y)
+        st["steps"] = [("cal", cal), ("wq", wq), ("qa", qa), ("gemm", gemm)]
+        st["qa_bytes"] = M * K * 2 + M * K // 2 + M * K // 16 + M * r * 4 + r * K * 2 + K * 4
+        st["gemm_flops"] = 2.0 * M * N * K + 2.0 * M * r * N
+        st["gemm_peak"] = PEAK_F16_TFLOPS
+    elif workload == "mlp-up-int4":
+        w_codes = torch.empty(N, K // 2, dtype=u8, device=dev)
+        w_scales = torch.empty(N, K // 64, dtype=torch.float16, device=dev)
+        a_codes = torch.empty(M, K // 2, dtype=u8, device=dev)
+        a_scales = torch.empty(M, K // 64, dtype=torch.float16, device=dev)
+        D = torch.empty(M, r, device=dev)
+
+        def wq(Xi):
+            _lib.svdq_quantize_weight(1, Wd, lam, downd, upd, r, w_codes, w_scales, None)
+
+        def qa(Xi):
+            _lib.svdq_quant_act_lowrank_down(1, Xi, lam, None, downd, r, a_codes, a_scales, None,
+                                             D)
+
+        def gemm(Xi):
+            _lib.svdq_w4a4_gemm(1, M, N, K, a_codes, a_scales, None, w_codes, w_scales, None, D,
+                                upd, r, Y)
+        st["steps"] = [("cal", cal), ("wq", wq), ("qa", qa), ("gemm", gemm)]
+        st["qa_bytes"] = M * K * 2 + M * K // 2 + M * K // 32 + M * r * 4 + r * K * 2 + K * 4
+        st["gemm_flops"] = 2.0 * M * N * K + 2.0 * M * r * N
+        st["gemm_peak"] = PEAK_I8_TOPS
+    else:  # delta
+        T, H, Wg = cfg["grid"]
+        r2c, ptr, crow = _lib.svdq_cube_geometry(T, H, Wg, *cfg["cube"], cfg["n_text"],
+                                                 cfg["n_audio"], cfg["cube1d"])
+        nc = len(ptr) - 1
+        r2c_d = torch.from_numpy(r2c).to(dev)
+        ptr_d, crow_d = torch.from_numpy(ptr).to(dev), torch.from_numpy(crow).to(dev)
+        cc = torch.empty(nc, K, dtype=u8, device=dev)
+        cs = torch.empty(nc, device=dev)
+        dc = torch.empty(M, K // 2, dtype=u8, device=dev)
+        dsc = torch.empty(M, K // 16, dtype=u8, device=dev)
+        gd = torch.empty(1, device=dev)
+        D = torch.empty(M, r, device=dev)
+        core_out = torch.empty(nc, N, device=dev)
+
+        def qa(Xi):
+            _lib.svdq_delta_quant_act(Xi, lam, amax, ptr_d, crow_d, nc, downd, r, cc, cs, dc, dsc,
+                                      gd, D)
+
+        def core(Xi):
+            _lib.svdq_gemm_core(nc, N, K, cc, cs, w_codes, w_scales, g_w, core_out)
+
+        def gemm(Xi):
+            _lib.svdq_w4a4_gemm(0, M, N, K, dc, dsc, gd, w_codes, w_scales, g_w, D, upd, r, Y,
+                                core_out=core_out, row_to_cube=r2c_d)
+        st["steps"] = [("cal", cal), ("wq", wq), ("qa", qa), ("core", core), ("gemm", gemm)]
+        st["qa_bytes"] = (M * K * 2 + nc * K + nc * 4 + M * K // 2 + M * K // 16 + M * r * 4
+                          + r * K * 2 + K * 4)
+        st["gemm_flops"] = 2.0 * M * N * K + 2.0 * M * r * N
+        st["core_flops"] = 2.0 * nc * N * K
+        st["gemm_peak"] = PEAK_F16_TFLOPS
+    st["Xs"] = Xs
+    return st
 
 
 def main():
@@ -72,8 +232,10 @@ def main():
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", choices=sorted(WORKLOADS), default="attn")
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-rows", type=int, default=512)
+    ap.add_argument("--cpu-rows", type=int, default=16384)
+    ap.add_argument("--copy-probe", action="store_true")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer is "
@@ -81,58 +243,32 @@ def main():
         sys.exit(2)
 
     import torch
-    import synth
-    from w4a4_quantized_dit_amd import layer, _lib
+    from w4a4_quantized_dit_amd import _lib
 
     _lib.load()
-    cfg = synth.config(1)
+    if args.copy_probe:
+        copy_probe(torch)
+        return
+    n_rot = 4
+    st = setup(torch, args.workload, n_rot)
+    cfg = st["cfg"]
     M, K, N, r = cfg["M"], cfg["K"], cfg["N"], cfg["r"]
     seg = cfg["seg"]
-    print(f"[bench] generating {cfg['name']} inputs", file=sys.stderr, flush=True)
-    X = synth.x_bits(cfg)
-    W = synth.weight_bits(N, K)
-    dev = torch.device("cuda:0")
-    Xd0 = torch.from_numpy(X.view(np.int16)).to(dev).view(torch.bfloat16)
-    Wd = torch.from_numpy(W.view(np.int16)).to(dev).view(torch.bfloat16)
-    n_rot = 4
-    Xs = [Xd0] + [Xd0.clone() for _ in range(n_rot - 1)]
-
-    cal = layer.calibrate(Xd0, seg, Wd, 7)
-    lam_np = cal["lambda"].cpu().numpy()
-    down, up = lowrank_factors_rangefinder(W, lam_np, r)
-    downd = torch.from_numpy(down.view(np.int16)).to(dev).view(torch.bfloat16)
-    upd = torch.from_numpy(up.view(np.int16)).to(dev).view(torch.bfloat16)
-
-    # outputs preallocated once
-    ax = torch.empty(3, K, device=dev); aw = torch.empty(K, device=dev)
-    lam = torch.empty(K, device=dev); amax = torch.empty(1, device=dev)
-    w_codes = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
-    w_scales = torch.empty(N, K // 16, dtype=torch.uint8, device=dev)
-    g_w = torch.empty(1, device=dev)
-    a_codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
-    a_scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
-    g_a = torch.empty(1, device=dev)
-    D = torch.empty(M, r, dtype=torch.float32, device=dev)
-    Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
-
-    ev = {k: [] for k in ("cal", "wq", "qa", "gemm")}
+    names = [n for n, _ in st["steps"]]
+    ev = {k: [] for k in names}
 
     def step(i, record):
-        Xi = Xs[i % n_rot]
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(5)] if record else None
-        if record: e[0].record()
-        _lib.svdq_calibrate_lambda(Xi, seg, Wd, 7, 0.5, 0, ax, aw, lam, amax)
-        if record: e[1].record()
-        _lib.svdq_quantize_weight(0, Wd, lam, downd, upd, r, w_codes, w_scales, g_w)
-        if record: e[2].record()
-        _lib.svdq_quant_act_lowrank_down(0, Xi, lam, amax, downd, r, a_codes, a_scales, g_a, D)
-        if record: e[3].record()
-        _lib.svdq_w4a4_gemm(0, M, N, K, a_codes, a_scales, g_a, w_codes, w_scales, g_w, D, upd,
-                            r, Y)
-        if record:
-            e[4].record()
-            for k, (a, b) in zip(("cal", "wq", "qa", "gemm"), zip(e[:-1], e[1:])):
-                ev[k].append((a, b))
+        Xi = st["Xs"][i % n_rot]
+        if not record:
+            for _, fn in st["steps"]:
+                fn(Xi)
+            return
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        e[0].record()
+        for j, (name, fn) in enumerate(st["steps"]):
+            fn(Xi)
+            e[j + 1].record()
+            ev[name].append((e[j], e[j + 1]))
 
     print("[bench] warmup", file=sys.stderr, flush=True)
     for i in range(args.warmup):
@@ -147,10 +283,13 @@ def main():
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
     ms_step = wall * 1e3 / args.steps
 
-    gemm_flops = 2.0 * M * N * K + 2.0 * M * r * N
-    layer_flops = gemm_flops + 2.0 * M * K * r
-    qa_bytes = M * K * 2 + M * K // 2 + M * K // 16 + M * r * 4 + r * K * 2 + K * 4
+    gemm_flops = st["gemm_flops"]
+    layer_flops = gemm_flops + 2.0 * M * K * r + st.get("core_flops", 0.0)
+    fwd_ms = ms["qa"] + ms["gemm"] + ms.get("core", 0.0)
     gemm_tflops = gemm_flops / (ms["gemm"] * 1e-3) / 1e12
+    peak = st["gemm_peak"]
+    qa_gbs = st["qa_bytes"] / (ms["qa"] * 1e-3) / 1e9
+    dtype = {"attn": "f16", "mlp-up-int4": "i8", "delta": "f16"}[args.workload]
     out = {
         "metric": METRIC,
         "value": round(layer_flops / (ms_step * 1e-3) / 1e12, 2),
@@ -158,27 +297,35 @@ def main():
         "n_gpus": 1, "steps": args.steps, "warmup": args.warmup,
         "ms_per_step": round(ms_step, 4),
         "higher_is_better": True, "scaling": "weak", "vs_baseline": None,
-        "dtype": "f16",
-        "data": "synthetic (seeded outlier-channel activations, N(0,1/K) weights)",
+        "dtype": dtype,
+        "data": "synthetic (seeded outlier-channel activations, N(0,1/K) weights)"
+                if cfg["gen"] == "outlier" else
+                "synthetic (seeded cube-mean field plus noise, N(0,1/K) weights)",
         "config": {"workload": cfg["name"], "M": M, "K": K, "N": N, "rank": r,
-                   "format": "nvfp4", "rows_text_video_audio": [seg[1], seg[2] - seg[1],
+                   "format": cfg["fmt"], "rows_text_video_audio": [seg[1], seg[2] - seg[1],
                                                                  seg[3] - seg[2]],
                    "lambda": "all rows, alpha 0.5",
-                   "step": "calibrate + weight quant + act quant/low-rank down + W4A4 GEMM"},
+                   "step": " + ".join(names)},
         "kernels_ms": {k: round(v, 4) for k, v in ms.items()},
-        "forward_tflops": round(layer_flops / ((ms["qa"] + ms["gemm"]) * 1e-3) / 1e12, 2),
+        "forward_tflops": round(layer_flops / (fwd_ms * 1e-3) / 1e12, 2),
         "gemm_tflops": round(gemm_tflops, 2),
-        "gemm_frac_of_f16_peak": round(gemm_tflops / PEAK_F16_TFLOPS, 4),
+        "gemm_frac_of_mfma_peak": round(gemm_tflops / peak, 4),
         "gemm_frac_of_fp4_peak": round(gemm_tflops / 10100.0, 4),
-        "quant_act_gbs": round(qa_bytes / (ms["qa"] * 1e-3) / 1e9, 1),
-        "quant_act_frac_of_hbm": round(qa_bytes / (ms["qa"] * 1e-3) / 1e9 / PEAK_HBM_GBS, 4),
-        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2),
-                     "peak": PEAK_F16_TFLOPS, "unit": "TFLOP/s",
-                     "frac": round(gemm_tflops / PEAK_F16_TFLOPS, 4), "traffic": None},
+        "quant_act_gbs": round(qa_gbs, 1),
+        "quant_act_frac_of_hbm": round(qa_gbs / PEAK_HBM_GBS, 4),
+        "roofline": {"bound": "mfma", "achieved": round(gemm_tflops, 2), "peak": peak,
+                     "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
+                     "traffic": measured_traffic(args.workload)},
     }
+    if "core" in ms:
+        out["core_gemm_tflops"] = round(st["core_flops"] / (ms["core"] * 1e-3) / 1e12, 2)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
-        out["cpu_baseline"] = cpu_baseline(cfg, X, W, lam_np, down, up, rows=args.cpu_rows)
+        if cfg["fmt"] == "nvfp4-delta":
+            out["cpu_baseline"] = None
+        else:
+            out["cpu_baseline"] = cpu_baseline(cfg, st["X"], st["W"], st["down"], st["up"],
+                                               rows=args.cpu_rows)
     print(json.dumps(out), flush=True)
 
 
