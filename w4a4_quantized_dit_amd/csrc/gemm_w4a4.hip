@@ -16,6 +16,7 @@
 // elements [8t, 8t + 8) as its k-slots; the weight operand uses the identical mapping, so every
 // product pairs equal K indices.
 #include "device.h"
+#include "gemm_common.h"
 #include "launch.h"
 
 namespace svdq {
@@ -27,66 +28,8 @@ constexpr int kThreads = 256;  // 4 waves, 2 x 2 over the workgroup tile
 #define SVDQ_GEMM_VALU_PER_MFMA 4   // scheduling hint: dequantisation VALU ops between MFMAs
 #endif
 
-// Epilogue: low-rank up-projection, tensor scales, DeltaQuant core term, bf16 store.
-// The accumulators hold Σ A'·W' without the tensor scales gsc = g_a·g_w; the low-rank term is
-// folded in before the scaling as (D/gsc)·L2 so the accumulators stay with the MFMA unit, and
-// y = gsc·acc (+ core_out[cube(m)]) is formed element by element at the store.  fp32 D/gsc is
-// split into an exact-to-2^-16 bf16 pair for the bf16 MFMA.
-// 32x32 accumulator layout: lane holds column r32 and rows (e/4)*8 + 4h + e%4.
-template <int FM, int FN>
-__device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[FM][FN], float gsc, int64_t M,
-                                              int64_t N, int64_t m_base, int64_t n_base, int r32,
-                                              int h, const float* __restrict__ D,
-                                              const uint16_t* __restrict__ up, int r,
-                                              const float* __restrict__ core_out,
-                                              const int32_t* __restrict__ row_to_cube,
-                                              uint16_t* __restrict__ Y, int64_t ldy) {
-  const float inv_gsc = 1.0f / gsc;
-  for (int t = 0; 16 * t < r; ++t) {
-    const int k0 = 16 * t + 8 * h;
-    bf16x8_t u_op[FN];
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int64_t col = n_base + 32 * j + r32;
-      u32x4_t v = u32x4_t{0u, 0u, 0u, 0u};
-      if (k0 < r) v = *reinterpret_cast<const u32x4_t*>(up + col * r + k0);
-      u_op[j] = __builtin_bit_cast(bf16x8_t, v);
-    }
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      int64_t row = m_base + 32 * i + r32;
-      row = row < M ? row : M - 1;
-      bf16x8_t d_hi, d_lo;
-      lowrank_operand(D + row * r + k0, k0 < r, inv_gsc, d_hi, d_lo);
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d_hi, u_op[j], acc[i][j], 0, 0, 0);
-        acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(d_lo, u_op[j], acc[i][j], 0, 0, 0);
-      }
-    }
-  }
-
-#pragma unroll
-  for (int i = 0; i < FM; ++i) {
-#pragma unroll
-    for (int e = 0; e < 16; ++e) {
-      const int64_t row = m_base + 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
-      if (row < M) {
-        const float* co = core_out ? core_out + (int64_t)row_to_cube[row] * N : nullptr;
-#pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t col = n_base + 32 * j + r32;
-          float v = acc[i][j][e] * gsc;
-          if (co) v += co[col];
-          Y[row * ldy + col] = f32_to_bf16(v);
-        }
-      }
-    }
-  }
-}
-
-// Workgroup tile 256 x 256, 4 waves in 2 x 2, each wave 128 x 128 (4 x 4 MFMA tiles of 32x32).
-// K advances 128 elements per stage.  Raw codes and scales are staged global -> registers ->
+// Workgroup tile 256 x 256, 4 waves in 2 x 2, each wave 128 x 128 (4 x 4 MFMA tiles of 32x32),
+// tiles assigned in XCD-grouped order.  K advances 128 elements per stage.  Raw codes and scales are staged global -> registers ->
 // LDS through three LDS buffers (the loads for stage s+3 are in flight while stage s is
 // computed); each wave dequantises its own fragments from LDS.
 constexpr int kBM = 256, kBN = 256, kBK = 128;
@@ -172,7 +115,9 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_nvfp4(
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
-  const int64_t m0 = (int64_t)blockIdx.y * kBM, n0 = (int64_t)blockIdx.x * kBN;
+  int64_t tm, tn;
+  if (!tile_of_block((M + kBM - 1) / kBM, N / kBN, tm, tn)) return;
+  const int64_t m0 = tm * kBM, n0 = tn * kBN;
   const int64_t m_base = m0 + wm * 128, n_base = n0 + wn * 128;
   const int r32 = lane & 31, h = lane >> 5;
   const int64_t kb = K / 2, ks = K / 16;
@@ -285,7 +230,7 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
                        const int32_t* row_to_cube, uint16_t* Y, int64_t ldy, hipStream_t s) {
   if (fmt == 1)
     return launch_gemm_int4(M, N, K, a_codes, a_scales, w_codes, w_scales, D, up, r, Y, ldy, s);
-  const dim3 grid((unsigned)(N / kBN), (unsigned)((M + kBM - 1) / kBM));
+  const dim3 grid(grid_of_tiles((M + kBM - 1) / kBM, N / kBN));
   k_gemm_nvfp4<<<grid, dim3(kThreads), 0, s>>>(
       M, N, K, a_codes, reinterpret_cast<const uint8_t*>(a_scales), g_a, w_codes,
       reinterpret_cast<const uint8_t*>(w_scales), g_w, D, up, (int)r, core_out, row_to_cube, Y,
