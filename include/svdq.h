@@ -179,7 +179,9 @@ svdq_status svdq_cube_geometry(int64_t T, int64_t H, int64_t W, int64_t ct, int6
  *   core codes: E4M3(core · 1/s_c) per core row, s_c = max_k|core[c, k]| / 448 (fp32)
  *   delta = X̂ − core[cube(m)] (fp32, unquantised core), NVFP4 with tensor amax 2·act_amax
  *   D = bf16(X̂)·lora_downᵀ  (fp32, as in svdq_quant_act_lowrank_down)
- * cube_ptr / cube_rows: device int32 CSR from svdq_cube_geometry.  Outputs: core_codes
+ * cube_ptr / cube_rows: device int32 CSR from svdq_cube_geometry (every cube has at most 16
+ * rows; members beyond the 16th of a larger cube are not processed).  K <= 16384.  Outputs:
+ * core_codes
  * [n_cubes, K] E4M3 bytes, core_scale fp32 [n_cubes], delta_codes [M, K/2], delta_scales
  * [M, K/16], g_delta float[1], D [M, r] fp32; sat_count (nullable) as in
  * svdq_quant_act_lowrank_down.  Codes and scales bit-exact.

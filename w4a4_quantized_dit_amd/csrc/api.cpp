@@ -247,7 +247,7 @@ svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_
   TRY(check_ld(fn, "ldx", ldx, K));
   TRY(check_rank(fn, r));
   if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
-  if ((size_t)K * sizeof(float) > 64 * 1024)
+  if ((size_t)K * sizeof(float) > 64 * 1024 || svdq::delta_act_lds_bytes(K) > 160 * 1024)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: K=%lld exceeds 16384", fn, (long long)K);
   return hip_result(svdq::launch_delta_quant_act(X, M, K, ldx, lambda, act_amax, cube_ptr,
                                                  cube_rows, n_cubes, lora_down, r, core_codes,

@@ -3,13 +3,16 @@
 // |x − core| ≤ 2·max|x| ("The activation scale bound held"); the core branch stays on a 16-bit
 // path ("Deviations from the paper")).
 //
-// k_delta_act: one workgroup per cube (persistent over cubes).  The cube's rows are smoothed
-// (X̂ = X · 1/λ), summed in ascending row order in fp32 and divided by the member count; the
-// core row is kept in LDS, quantised to E4M3 with a per-row scale amax/448, and every member's
-// delta X̂ − core (unquantised core) is quantised to NVFP4 with tensor amax 2·act_amax.  Finally
-// the members' low-rank activations D = bf16(X̂)·L1 are formed on MFMA with the member rows as
-// the 16 row slots of v_mfma_f32_16x16x32_bf16.
-//
+// k_delta_act: one workgroup per cube (at most 16 member rows), walking K in chunks of 256
+// channels.  Per chunk the members' smoothed rows X̂ = X · 1/λ are staged in LDS (fp32, read from
+// HBM once, coalesced, the next chunk's loads in flight while this one is processed); a thread
+// per channel sums the members in ascending row order in fp32 and divides by the member count
+// (the core row stays in LDS); a thread per member row and 16-channel block quantises the delta
+// X̂ − core (unquantised core) to NVFP4 with tensor amax 2·act_amax.  After the last chunk the
+// core row's amax gives its E4M3 scale amax/448 and the core codes are written from LDS.  The
+// workgroup needs about 4·K + 18 KB of LDS, so several cubes are resident per CU.
+// The members' low-rank activations D = bf16(X̂)·L1 come from the activation kernel's D-only
+// mode, whose 64-row tiles share each slice of L1 across many rows.
 // k_gemm_core: core_out[c, n] = s_c · g_w · Σ_k e4m3(core[c, k]) · (c_w·s_w)[n, k] on fp16 MFMA:
 // E4M3 values and the NVFP4 weight products are exact in fp16.
 #include "device.h"
@@ -19,150 +22,149 @@ namespace svdq {
 
 namespace {
 
-constexpr int kThreads = 256;
-constexpr int kMaxCube = 16;
+constexpr int kThreads = 256;       // k_gemm_core and k_delta_act: 4 waves
+constexpr int kMaxCube = 16;        // rows per cube (svdq_cube_geometry guarantees it)
+constexpr int kChunk = 256;         // channels per chunk
+constexpr int kStashPitch = kChunk + 4;  // floats per staged row (padded)
 
 __global__ __launch_bounds__(kThreads) void k_delta_act(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ lambda, const float* __restrict__ act_amax,
-    const int32_t* __restrict__ cube_ptr, const int32_t* __restrict__ cube_rows, int64_t n_cubes,
-    const uint16_t* __restrict__ down, int r, uint8_t* __restrict__ core_codes,
-    float* __restrict__ core_scale, uint8_t* __restrict__ dcodes, uint8_t* __restrict__ dscales,
-    float* __restrict__ g_delta, float* __restrict__ D, uint32_t* __restrict__ sat) {
-  extern __shared__ float s_dyn[];
-  float* s_inv = s_dyn;       // [K]
-  float* s_core = s_dyn + K;  // [K]
-  __shared__ float s_red[kThreads / 64];
+    const int32_t* __restrict__ cube_ptr, const int32_t* __restrict__ cube_rows,
+    uint8_t* __restrict__ core_codes, float* __restrict__ core_scale,
+    uint8_t* __restrict__ dcodes, uint8_t* __restrict__ dscales, float* __restrict__ g_delta,
+    uint32_t* __restrict__ sat) {
+  extern __shared__ __attribute__((aligned(16))) float s_dyn[];
+  float* s_core = s_dyn;                          // [K] fp32 core row
+  float* s_x = s_dyn + K;                         // [kMaxCube][kStashPitch] staged X̂ chunk
+  float* s_inv = s_x + kMaxCube * kStashPitch;    // [2][kChunk] 1/λ of this and the next chunk
   __shared__ int s_rows[kMaxCube];
+  __shared__ float s_red[kThreads / 64];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  for (int64_t k = tid; k < K; k += kThreads) s_inv[k] = lambda ? 1.0f / lambda[k] : 1.0f;
+  const int64_t c = blockIdx.x;
+  const int p0 = cube_ptr[c];
+  int n = cube_ptr[c + 1] - p0;
+  n = n < 0 ? 0 : (n > kMaxCube ? kMaxCube : n);
+  if (n == 0) return;  // uniform: nothing to do for an empty cube
+  if (tid < n) {
+    const int m = cube_rows[p0 + tid];
+    s_rows[tid] = m < 0 ? 0 : (m < M ? m : (int)M - 1);
+  }
+  s_inv[tid] = lambda ? 1.0f / lambda[tid] : 1.0f;
   const float amax_t = 2.0f * act_amax[0];
   const float g = amax_t == 0.0f ? 1.0f : amax_t / 2688.0f;
   const float d6 = 6.0f * g;
-  if (blockIdx.x == 0 && tid == 0) g_delta[0] = g;
+  if (c == 0 && tid == 0) g_delta[0] = g;
+  __syncthreads();
+
+  // staging: rows tid/32 and tid/32 + 8, channels 8·(tid%32) .. +8 (rows past n repeat row n-1
+  // and are not stored)
+  const int g8 = tid & 31;
+  const uint16_t* xg[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) {
+    const int row = (tid >> 5) + 8 * t;
+    xg[t] = X + (int64_t)s_rows[row < n ? row : n - 1] * ldx + 8 * g8;
+  }
+  u32x4_t xr[2];
+#pragma unroll
+  for (int t = 0; t < 2; ++t) xr[t] = *reinterpret_cast<const u32x4_t*>(xg[t]);
+  const int dl_row = tid >> 4, dl_blk = tid & 15;  // delta: one 16-channel block of one row
+  float core_amax = 0.0f;
   uint32_t nsat = 0;
 
-  for (int64_t c = blockIdx.x; c < n_cubes; c += gridDim.x) {
-    const int p0 = cube_ptr[c];
-    int n = cube_ptr[c + 1] - p0;
-    n = n < 0 ? 0 : (n > kMaxCube ? kMaxCube : n);
-    __syncthreads();  // the previous cube's LDS readers are done (and s_inv is complete)
-    if (n == 0) continue;  // uniform across the block
-    if (tid < n) {
-      int m = cube_rows[p0 + tid];
-      s_rows[tid] = m < 0 ? 0 : (m < M ? m : (int)M - 1);
+  for (int64_t k0 = 0; k0 < K; k0 += kChunk) {
+    const int buf = (int)((k0 / kChunk) & 1);
+    const float* inv = s_inv + buf * kChunk;
+    // 1. stage X̂ (fp32) and issue the next chunk's loads
+#pragma unroll
+    for (int t = 0; t < 2; ++t) {
+      const int row = (tid >> 5) + 8 * t;
+      if (row < n) {
+        const f32x4_t i0 = *reinterpret_cast<const f32x4_t*>(inv + 8 * g8);
+        const f32x4_t i1 = *reinterpret_cast<const f32x4_t*>(inv + 8 * g8 + 4);
+        const u32x4_t v = xr[t];
+        f32x4_t x0, x1;
+        x0[0] = bf16_lo(v[0]) * i0[0]; x0[1] = bf16_hi(v[0]) * i0[1];
+        x0[2] = bf16_lo(v[1]) * i0[2]; x0[3] = bf16_hi(v[1]) * i0[3];
+        x1[0] = bf16_lo(v[2]) * i1[0]; x1[1] = bf16_hi(v[2]) * i1[1];
+        x1[2] = bf16_lo(v[3]) * i1[2]; x1[3] = bf16_hi(v[3]) * i1[3];
+        float* dst = s_x + row * kStashPitch + 8 * g8;
+        *reinterpret_cast<f32x4_t*>(dst) = x0;
+        *reinterpret_cast<f32x4_t*>(dst + 4) = x1;
+      }
+    }
+    if (k0 + kChunk < K) {
+#pragma unroll
+      for (int t = 0; t < 2; ++t)
+        xr[t] = *reinterpret_cast<const u32x4_t*>(xg[t] + k0 + kChunk);
+      s_inv[(buf ^ 1) * kChunk + tid] = lambda ? 1.0f / lambda[k0 + kChunk + tid] : 1.0f;
     }
     __syncthreads();
 
-    // core: ascending fp32 sum of the members' X̂, divided by the count; row amax
-    float amax = 0.0f;
-    for (int64_t k = 8 * tid; k < K; k += 8 * kThreads) {
-      float acc[8] = {0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f, 0.f};
-      for (int j = 0; j < n; ++j) {
-        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(X + (int64_t)s_rows[j] * ldx + k);
-#pragma unroll
-        for (int c2 = 0; c2 < 4; ++c2) {
-          acc[2 * c2] += bf16_lo(v[c2]) * s_inv[k + 2 * c2];
-          acc[2 * c2 + 1] += bf16_hi(v[c2]) * s_inv[k + 2 * c2 + 1];
-        }
-      }
-      const float fn = (float)n;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float cv = acc[e] / fn;
-        s_core[k + e] = cv;
-        amax = fmaxf(amax, fabsf(cv));
-      }
+    // 2. core channel: ascending fp32 sum over the members, divided by the count
+    {
+      float acc = 0.0f;
+      for (int j = 0; j < n; ++j) acc += s_x[j * kStashPitch + tid];
+      const float cv = acc / (float)n;
+      s_core[k0 + tid] = cv;
+      core_amax = fmaxf(core_amax, fabsf(cv));
     }
-    for (int off = 32; off > 0; off >>= 1) amax = fmaxf(amax, __shfl_xor(amax, off));
-    if (lane == 0) s_red[wave] = amax;
     __syncthreads();
-    amax = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    const float sc = amax / 448.0f;
-    const float inv_c = sc != 0.0f ? 1.0f / sc : 0.0f;
-    if (tid == 0) core_scale[c] = sc;
 
-    // FP8 core codes: sign | E4M3(|core| · 1/s_c)
-    for (int64_t k = 8 * tid; k < K; k += 8 * kThreads) {
-      uint32_t lo = 0, hi = 0;
-#pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        const float v = s_core[k + e];
-        float val;
-        const uint32_t code = e4m3_encode_pos(fabsf(v) * inv_c, &val) | (__builtin_signbit(v) ? 0x80u : 0u);
-        if (e < 4)
-          lo |= code << (8 * e);
-        else
-          hi |= code << (8 * (e - 4));
-      }
-      *reinterpret_cast<uint2*>(core_codes + c * K + k) = uint2{lo, hi};
-    }
-
-    // deltas: one NVFP4 block (16 channels of one member) per task
-    const int64_t nblk = K / NVFP4_BLOCK;
-    for (int64_t task = tid; task < (int64_t)n * nblk; task += kThreads) {
-      const int j = (int)(task / nblk);
-      const int64_t b = task % nblk, k0 = b * NVFP4_BLOCK;
-      const int64_t m = s_rows[j];
-      const u32x4_t* xp = reinterpret_cast<const u32x4_t*>(X + m * ldx + k0);
-      const u32x4_t v0 = xp[0], v1 = xp[1];
-      const uint32_t w[8] = {v0[0], v0[1], v0[2], v0[3], v1[0], v1[1], v1[2], v1[3]};
+    // 3. delta block: X̂ − core, NVFP4 with the static tensor amax
+    if (dl_row < n) {
+      const float* xrow = s_x + dl_row * kStashPitch + 16 * dl_blk;
+      const float* crow = s_core + k0 + 16 * dl_blk;
       float d[16];
       float a = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        d[2 * e] = bf16_lo(w[e]) * s_inv[k0 + 2 * e] - s_core[k0 + 2 * e];
-        d[2 * e + 1] = bf16_hi(w[e]) * s_inv[k0 + 2 * e + 1] - s_core[k0 + 2 * e + 1];
-        a = fmaxf(a, fmaxf(fabsf(d[2 * e]), fabsf(d[2 * e + 1])));
+      for (int e4 = 0; e4 < 4; ++e4) {
+        const f32x4_t xq = *reinterpret_cast<const f32x4_t*>(xrow + 4 * e4);
+        const f32x4_t cq = *reinterpret_cast<const f32x4_t*>(crow + 4 * e4);
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          d[4 * e4 + e] = xq[e] - cq[e];
+          a = fmaxf(a, fabsf(d[4 * e4 + e]));
+        }
       }
       nsat += a > amax_t ? 1u : 0u;
-      float inv;
-      const uint32_t scode = nvfp4_block_scale(a, g, d6, &inv);
+      float sinv;
+      const uint32_t scode = nvfp4_block_scale(a, g, d6, &sinv);
       float y[16];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) y[e] = d[e] * inv;
-      *reinterpret_cast<uint2*>(dcodes + m * (K / 2) + k0 / 2) = uint2{e2m1_pack8(y), e2m1_pack8(y + 8)};
-      dscales[m * nblk + b] = (uint8_t)scode;
+      for (int e = 0; e < 16; ++e) y[e] = d[e] * sinv;
+      const int64_t m = s_rows[dl_row];
+      const int64_t kq = k0 + 16 * dl_blk;
+      *reinterpret_cast<uint2*>(dcodes + m * (K / 2) + kq / 2) =
+          uint2{e2m1_pack8(y), e2m1_pack8(y + 8)};
+      dscales[m * (K / 16) + kq / 16] = (uint8_t)scode;
     }
+    __syncthreads();  // the staged rows are rewritten by the next chunk
+  }
 
-    // low-rank activations of the members: D = bf16(X̂)·L1, rank tiles split over the waves
-    if (r > 0) {
-      const int slot = lane & 15, q = lane >> 4;
-      const bool live = slot < n;
-      const int64_t xm = s_rows[live ? slot : 0];
-      const int ntile = (r + 15) / 16;
-      for (int j = wave; j < ntile; j += kThreads / 64) {
-        const int rank = 16 * j + slot;
-        const uint16_t* dp = down + (int64_t)(rank < r ? rank : r - 1) * K;
-        f32x4_t acc = f32x4_t{0.f, 0.f, 0.f, 0.f};
-        const int nk = (int)(K / 32);  // a multiple of 8
-
-        for (int it = 0; it < nk; ++it) {
-          const int64_t kk = (int64_t)it * 32 + 8 * q;
-          const u32x4_t xv = *reinterpret_cast<const u32x4_t*>(X + xm * ldx + kk);
-          u32x4_t av;
+  // core scale and FP8 codes: sign | E4M3(|core| · 1/s_c), 8 channels per thread per step
+  for (int off = 32; off > 0; off >>= 1) core_amax = fmaxf(core_amax, __shfl_xor(core_amax, off));
+  if (lane == 0) s_red[wave] = core_amax;
+  __syncthreads();
+  const float am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
+  const float sc = am / 448.0f;
+  const float inv_c = sc != 0.0f ? 1.0f / sc : 0.0f;
+  if (tid == 0) core_scale[c] = sc;
+  for (int64_t k = 8 * tid; k < K; k += 8 * kThreads) {
+    uint32_t lo = 0, hi = 0;
 #pragma unroll
-          for (int c2 = 0; c2 < 4; ++c2) {
-            const float x0 = live ? bf16_lo(xv[c2]) * s_inv[kk + 2 * c2] : 0.0f;
-            const float x1 = live ? bf16_hi(xv[c2]) * s_inv[kk + 2 * c2 + 1] : 0.0f;
-            av[c2] = pack_bf16x2(x0, x1);
-          }
-          u32x4_t bv = *reinterpret_cast<const u32x4_t*>(dp + kk);
-          bv = rank < r ? bv : u32x4_t{0u, 0u, 0u, 0u};
-          acc = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8_t, av),
-                                                        __builtin_bit_cast(bf16x8_t, bv), acc, 0,
-                                                        0, 0);
-        }
-        // 16x16 output: lane holds rank column 16j + slot and member slots 4q .. 4q+3
-        if (rank < r) {
-#pragma unroll
-          for (int i = 0; i < 4; ++i) {
-            const int ms = 4 * q + i;
-            if (ms < n) D[(int64_t)s_rows[ms] * r + rank] = acc[i];
-          }
-        }
-      }
+    for (int e = 0; e < 8; ++e) {
+      const float v = s_core[k + e];
+      float val;
+      const uint32_t code =
+          e4m3_encode_pos(fabsf(v) * inv_c, &val) | (__builtin_signbit(v) ? 0x80u : 0u);
+      if (e < 4)
+        lo |= code << (8 * e);
+      else
+        hi |= code << (8 * (e - 4));
     }
+    *reinterpret_cast<uint2*>(core_codes + c * K + k) = uint2{lo, hi};
   }
   if (sat) {
     for (int off = 32; off > 0; off >>= 1) nsat += __shfl_xor(nsat, off);
@@ -263,6 +265,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_core(
 
 }  // namespace
 
+size_t delta_act_lds_bytes(int64_t K) {
+  return ((size_t)K + kMaxCube * kStashPitch + 2 * kChunk) * sizeof(float);
+}
+
 hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* lambda, const float* act_amax,
                                   const int32_t* cube_ptr, const int32_t* cube_rows,
@@ -270,15 +276,16 @@ hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64
                                   uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
                                   uint8_t* delta_scales, float* g_delta, float* D, uint32_t* sat,
                                   hipStream_t s) {
-  const size_t lds = (size_t)2 * K * sizeof(float);
+  const size_t lds = delta_act_lds_bytes(K);
   hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_delta_act),
                                      hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
   if (e != hipSuccess) return e;
-  const int64_t blocks = n_cubes < 2048 ? n_cubes : 2048;
-  k_delta_act<<<dim3((unsigned)blocks), dim3(kThreads), lds, s>>>(
-      X, M, K, ldx, lambda, act_amax, cube_ptr, cube_rows, n_cubes, down, (int)r, core_codes,
-      core_scale, delta_codes, delta_scales, g_delta, D, sat);
-  return hipGetLastError();
+  k_delta_act<<<dim3((unsigned)n_cubes), dim3(kThreads), lds, s>>>(
+      X, M, K, ldx, lambda, act_amax, cube_ptr, cube_rows, core_codes, core_scale, delta_codes,
+      delta_scales, g_delta, sat);
+  e = hipGetLastError();
+  if (e != hipSuccess || r == 0) return e;
+  return launch_lowrank_down(X, M, K, ldx, lambda, down, r, D, s);
 }
 
 hipError_t launch_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,

@@ -22,6 +22,11 @@ hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, in
                             int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
                             float* D, uint32_t* sat, hipStream_t s);
 
+// D = bf16(X·1/λ)·lora_downᵀ alone (fp32 [M, r], r >= 1), with the activation kernel's tiling.
+hipError_t launch_lowrank_down(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                               const float* lambda, const uint16_t* down, int64_t r, float* D,
+                               hipStream_t s);
+
 hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const void* a_scales, const float* g_a, const uint8_t* w_codes,
                        const void* w_scales, const float* g_w, const float* D,
@@ -35,6 +40,9 @@ hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64
                                   uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
                                   uint8_t* delta_scales, float* g_delta, float* D,
                                   uint32_t* sat, hipStream_t s);
+
+// Dynamic LDS bytes of the DeltaQuant activation kernel for K channels.
+size_t delta_act_lds_bytes(int64_t K);
 
 hipError_t launch_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,
                             const float* core_scale, const uint8_t* w_codes,

@@ -12,7 +12,8 @@
 // v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry channels
 // k0 + 64q + 8t .. +8, and the block stages the matching slice of L1 (lora_down[:, k0:k0+256])
 // in LDS once for its waves.  The next chunk's global loads are issued before the current
-// chunk is processed.
+// chunk is processed.  FMT 2 computes D alone (the DeltaQuant path quantises its deltas in its
+// own kernel and takes D from here).
 #include "device.h"
 #include "launch.h"
 
@@ -165,7 +166,7 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
         cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
         *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(scales) + row * (K / 16) + kb / 16) = sbytes;
       }
-    } else {
+    } else if (FMT == 1) {
       float a = 0.0f;
 #pragma unroll
       for (int j = 0; j < 64; ++j) a = fmaxf(a, fabsf(x[j]));
@@ -293,6 +294,15 @@ hipError_t dispatch(int nt, dim3 grid, size_t lds, hipStream_t s, const uint16_t
 }
 
 }  // namespace
+
+hipError_t launch_lowrank_down(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                               const float* lambda, const uint16_t* down, int64_t r, float* D,
+                               hipStream_t s) {
+  const int nt = (int)((r + 15) / 16);
+  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
+  return dispatch<2>(nt, grid, (size_t)K * sizeof(float), s, X, M, K, ldx, lambda, nullptr, down,
+                     (int)r, nullptr, nullptr, nullptr, 0, D, nullptr);
+}
 
 hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                             const float* lambda, const float* act_amax, const uint16_t* down,
