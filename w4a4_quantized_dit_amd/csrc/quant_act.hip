@@ -12,7 +12,7 @@
 // v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry channels
 // k0 + 64q + 8t .. +8, and the block stages the matching slice of L1 (lora_down[:, k0:k0+256])
 // in LDS once for its waves.  The next chunk's global loads are issued before the current
-// chunk is processed.  FMT 2 computes D alone (the DeltaQuant path quantises its deltas in its
+// chunk is processed, and two K groups of waves walk alternate chunks of the same rows.  FMT 2 computes D alone (the DeltaQuant path quantises its deltas in its
 // own kernel and takes D from here).
 #include "device.h"
 #include "launch.h"
@@ -22,29 +22,31 @@ namespace svdq {
 namespace {
 
 #ifndef SVDQ_QA_WAVES
-#define SVDQ_QA_WAVES 4    // waves (16 rows each) per block
-#endif
-#ifndef SVDQ_QA_DEPTH
-#define SVDQ_QA_DEPTH 1    // chunks of X / L1 loads in flight ahead of the chunk in LDS (1 or 2)
+#define SVDQ_QA_WAVES 4    // row waves (16 rows each) per block
 #endif
 constexpr int kWaves = SVDQ_QA_WAVES;
-constexpr int kThreads = 64 * kWaves;
+constexpr int kGroupThreads = 64 * kWaves;      // threads of one K group
 constexpr int kRowsPerBlock = 16 * kWaves;
 constexpr int kChunk = 256;
 constexpr int kPitch = kChunk + 8;   // bf16 elements per LDS row: 528 B, conflict-free reads
 
-template <int FMT, int NT>
-__global__ __launch_bounds__(kThreads) void k_quant_act(
+// K group ks of a block processes chunks ks, ks + SPLIT, ks + 2 SPLIT, ... of its rows, so a CU
+// streams SPLIT chunks of X at once; the groups' partial D are added in group order at the end
+// (the quantisation blocks never straddle chunks).
+template <int FMT, int NT, int SPLIT>
+__global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ lambda, const float* __restrict__ amax_p,
     const uint16_t* __restrict__ down, int r, uint8_t* __restrict__ codes,
     void* __restrict__ scales, float* __restrict__ tensor_scale, int write_g,
     float* __restrict__ D, uint32_t* __restrict__ sat) {
   constexpr int NTc = NT > 0 ? NT : 1;
-  constexpr int kLPieces = NT * 16 * (kChunk / 8) / kThreads;  // 16-B pieces of L1 per thread
+  constexpr int kSplit = SPLIT;
+  constexpr int kThreads = kGroupThreads * SPLIT;
+  constexpr int kLPieces = NT * 16 * (kChunk / 8) / kGroupThreads;  // 16-B L1 pieces per thread
   extern __shared__ float s_inv[];  // 1/λ for all K channels
-  __shared__ __attribute__((aligned(16))) uint16_t s_x[kWaves][16 * kPitch];
-  __shared__ __attribute__((aligned(16))) uint16_t s_l[NTc * 16 * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kWaves * kSplit][16 * kPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_l[kSplit][NTc * 16 * kPitch];
   for (int64_t k = threadIdx.x; k < K; k += kThreads) s_inv[k] = lambda ? 1.0f / lambda[k] : 1.0f;
 
   float amax = 0.0f, g = 1.0f, d6 = 6.0f;
@@ -55,10 +57,14 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
     if (write_g && blockIdx.x == 0 && threadIdx.x == 0) tensor_scale[0] = g;
   }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
-  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock + 16 * wave;
+  const int rw = wave % kWaves, ks = wave / kWaves;   // row wave, K group
+  const int gtid = threadIdx.x % kGroupThreads;       // thread index within the K group
+  const int64_t row0 = (int64_t)blockIdx.x * kRowsPerBlock + 16 * rw;
   const int rl = lane & 15, q = lane >> 4;
   const int64_t row = row0 + rl;
   const bool valid = row < M;
+  const int64_t nchunk = K / kChunk;
+  const int64_t nloop = (nchunk + kSplit - 1) / kSplit;
 
   // coalesced X loads: instruction i covers rows 2i, 2i+1 of the wave, lane piece = lane % 32
   // (rows past M read row M-1; their results are never stored)
@@ -69,12 +75,12 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
     xrow = xrow < M ? xrow : M - 1;
     xg[i] = X + xrow * ldx + 8 * (lane & 31);
   }
-  // L1 staging: piece p of the block = rank p / 32, channels 8 * (p % 32) .. +8 (ranks past r
-  // read rank r-1 and are zeroed)
+  // L1 staging within the K group: piece p = rank p / 32, channels 8 * (p % 32) .. +8 (ranks
+  // past r read rank r-1 and are zeroed)
   const uint16_t* lg[kLPieces > 0 ? kLPieces : 1];
 #pragma unroll
   for (int u = 0; u < kLPieces; ++u) {
-    const int p = threadIdx.x + kThreads * u;
+    const int p = gtid + kGroupThreads * u;
     const int n = p >> 5;
     lg[u] = down + (int64_t)(n < r ? n : r - 1) * K + 8 * (p & 31);
   }
@@ -85,125 +91,116 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
   uint32_t nsat = 0;
 
   u32x4_t xr[8], lr[kLPieces > 0 ? kLPieces : 1];
-  u32x4_t xr2[SVDQ_QA_DEPTH == 2 ? 8 : 1], lr2[SVDQ_QA_DEPTH == 2 && kLPieces > 0 ? kLPieces : 1];
+  if (ks < nchunk) {
+    const int64_t k0 = (int64_t)ks * kChunk;
 #pragma unroll
-  for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i]);
+    for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + k0);
 #pragma unroll
-  for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u]);
-  if (SVDQ_QA_DEPTH == 2 && kChunk < K) {
-#pragma unroll
-    for (int i = 0; i < 8; ++i) xr2[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + kChunk);
-#pragma unroll
-    for (int u = 0; u < kLPieces; ++u) lr2[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + kChunk);
+    for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + k0);
   }
   __syncthreads();  // s_inv complete
 
-  for (int64_t k0 = 0; k0 < K; k0 += kChunk) {
+  for (int64_t it = 0; it < nloop; ++it) {
+    const int64_t kc = it * kSplit + ks;  // this group's chunk
+    const bool has = kc < nchunk;
     // registers -> LDS (the previous chunk's readers finished at the loop-end barrier)
+    if (has) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      *reinterpret_cast<u32x4_t*>(&s_x[wave][(2 * i + (lane >> 5)) * kPitch + 8 * (lane & 31)]) = xr[i];
+      for (int i = 0; i < 8; ++i)
+        *reinterpret_cast<u32x4_t*>(&s_x[wave][(2 * i + (lane >> 5)) * kPitch + 8 * (lane & 31)]) = xr[i];
 #pragma unroll
-    for (int u = 0; u < kLPieces; ++u) {
-      const int p = threadIdx.x + kThreads * u;
-      const int n = p >> 5;
-      const u32x4_t v = n < r ? lr[u] : u32x4_t{0u, 0u, 0u, 0u};
-      *reinterpret_cast<u32x4_t*>(&s_l[n * kPitch + 8 * (p & 31)]) = v;
+      for (int u = 0; u < kLPieces; ++u) {
+        const int p = gtid + kGroupThreads * u;
+        const int n = p >> 5;
+        const u32x4_t v = n < r ? lr[u] : u32x4_t{0u, 0u, 0u, 0u};
+        *reinterpret_cast<u32x4_t*>(&s_l[ks][n * kPitch + 8 * (p & 31)]) = v;
+      }
     }
     __syncthreads();
-    if (SVDQ_QA_DEPTH == 2) {
+    if (kc + kSplit < nchunk) {
+      const int64_t kn = (kc + kSplit) * kChunk;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xr[i] = xr2[i];
+      for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + kn);
 #pragma unroll
-      for (int u = 0; u < kLPieces; ++u) lr[u] = lr2[u];
-      if (k0 + 2 * kChunk < K) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) xr2[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + k0 + 2 * kChunk);
-#pragma unroll
-        for (int u = 0; u < kLPieces; ++u)
-          lr2[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + k0 + 2 * kChunk);
-      }
-    } else if (k0 + kChunk < K) {
-#pragma unroll
-      for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + k0 + kChunk);
-#pragma unroll
-      for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + k0 + kChunk);
+      for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + kn);
     }
-    const int64_t kb = k0 + 64 * q;  // first channel of this lane
-    float x[64];
+    if (has) {
+      const int64_t kb = kc * kChunk + 64 * q;  // first channel of this lane
+      float x[64];
 #pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&s_x[wave][rl * kPitch + 64 * q + 8 * i]);
+      for (int i = 0; i < 8; ++i) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&s_x[wave][rl * kPitch + 64 * q + 8 * i]);
 #pragma unroll
-      for (int c = 0; c < 4; ++c) {
-        const uint32_t w = valid ? v[c] : 0u;
-        x[8 * i + 2 * c] = bf16_lo(w) * s_inv[kb + 8 * i + 2 * c];
-        x[8 * i + 2 * c + 1] = bf16_hi(w) * s_inv[kb + 8 * i + 2 * c + 1];
+        for (int c = 0; c < 4; ++c) {
+          const uint32_t w = valid ? v[c] : 0u;
+          x[8 * i + 2 * c] = bf16_lo(w) * s_inv[kb + 8 * i + 2 * c];
+          x[8 * i + 2 * c + 1] = bf16_hi(w) * s_inv[kb + 8 * i + 2 * c + 1];
+        }
       }
-    }
 
-    if (FMT == 0) {
-      uint32_t cw[8];
-      uint32_t sbytes = 0;
+      if (FMT == 0) {
+        uint32_t cw[8];
+        uint32_t sbytes = 0;
 #pragma unroll
-      for (int b = 0; b < 4; ++b) {
+        for (int b = 0; b < 4; ++b) {
+          float a = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(x[16 * b + j]));
+          nsat += (a > amax) ? 1u : 0u;
+          float inv;
+          const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
+          float y[16];
+#pragma unroll
+          for (int j = 0; j < 16; ++j) y[j] = x[16 * b + j] * inv;
+          cw[2 * b] = e2m1_pack8(y);
+          cw[2 * b + 1] = e2m1_pack8(y + 8);
+          sbytes |= sc << (8 * b);
+        }
+        if (valid) {
+          u32x4_t* cp = reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + kb / 2);
+          cp[0] = u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+          cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
+          *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(scales) + row * (K / 16) + kb / 16) = sbytes;
+        }
+      } else if (FMT == 1) {
         float a = 0.0f;
 #pragma unroll
-        for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(x[16 * b + j]));
-        nsat += (a > amax) ? 1u : 0u;
-        float inv;
-        const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
-        float y[16];
+        for (int j = 0; j < 64; ++j) a = fmaxf(a, fabsf(x[j]));
+        const __half s = __float2half_rn(a / 7.0f);
+        const float sf = __half2float(s);
+        const float inv = sf != 0.0f ? 1.0f / sf : 0.0f;
+        uint32_t cw[8];
 #pragma unroll
-        for (int j = 0; j < 16; ++j) y[j] = x[16 * b + j] * inv;
-        cw[2 * b] = e2m1_pack8(y);
-        cw[2 * b + 1] = e2m1_pack8(y + 8);
-        sbytes |= sc << (8 * b);
-      }
-      if (valid) {
-        u32x4_t* cp = reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + kb / 2);
-        cp[0] = u32x4_t{cw[0], cw[1], cw[2], cw[3]};
-        cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
-        *reinterpret_cast<uint32_t*>(reinterpret_cast<uint8_t*>(scales) + row * (K / 16) + kb / 16) = sbytes;
-      }
-    } else if (FMT == 1) {
-      float a = 0.0f;
+        for (int d = 0; d < 8; ++d) {
+          uint32_t w = 0;
 #pragma unroll
-      for (int j = 0; j < 64; ++j) a = fmaxf(a, fabsf(x[j]));
-      const __half s = __float2half_rn(a / 7.0f);
-      const float sf = __half2float(s);
-      const float inv = sf != 0.0f ? 1.0f / sf : 0.0f;
-      uint32_t cw[8];
-#pragma unroll
-      for (int d = 0; d < 8; ++d) {
-        uint32_t w = 0;
-#pragma unroll
-        for (int j = 0; j < 8; ++j) w |= int4_code(x[8 * d + j] * inv) << (4 * j);
-        cw[d] = w;
+          for (int j = 0; j < 8; ++j) w |= int4_code(x[8 * d + j] * inv) << (4 * j);
+          cw[d] = w;
+        }
+        if (valid) {
+          u32x4_t* cp = reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + kb / 2);
+          cp[0] = u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+          cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
+          reinterpret_cast<__half*>(scales)[row * (K / 64) + kb / 64] = s;
+        }
       }
-      if (valid) {
-        u32x4_t* cp = reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + kb / 2);
-        cp[0] = u32x4_t{cw[0], cw[1], cw[2], cw[3]};
-        cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
-        reinterpret_cast<__half*>(scales)[row * (K / 64) + kb / 64] = s;
-      }
-    }
 
-    if (NT > 0) {
+      if (NT > 0) {
 #pragma unroll
-      for (int t = 0; t < 8; ++t) {
-        u32x4_t av;
-        av[0] = pack_bf16x2(x[8 * t + 0], x[8 * t + 1]);
-        av[1] = pack_bf16x2(x[8 * t + 2], x[8 * t + 3]);
-        av[2] = pack_bf16x2(x[8 * t + 4], x[8 * t + 5]);
-        av[3] = pack_bf16x2(x[8 * t + 6], x[8 * t + 7]);
-        const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, av);
+        for (int t = 0; t < 8; ++t) {
+          u32x4_t av;
+          av[0] = pack_bf16x2(x[8 * t + 0], x[8 * t + 1]);
+          av[1] = pack_bf16x2(x[8 * t + 2], x[8 * t + 3]);
+          av[2] = pack_bf16x2(x[8 * t + 4], x[8 * t + 5]);
+          av[3] = pack_bf16x2(x[8 * t + 6], x[8 * t + 7]);
+          const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, av);
 #pragma unroll
-        for (int j = 0; j < NT; ++j) {
-          const u32x4_t bv =
-              *reinterpret_cast<const u32x4_t*>(&s_l[(16 * j + rl) * kPitch + 64 * q + 8 * t]);
-          acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, __builtin_bit_cast(bf16x8_t, bv),
-                                                           acc[j], 0, 0, 0);
+          for (int j = 0; j < NT; ++j) {
+            const u32x4_t bv =
+                *reinterpret_cast<const u32x4_t*>(&s_l[ks][(16 * j + rl) * kPitch + 64 * q + 8 * t]);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(a_op, __builtin_bit_cast(bf16x8_t, bv),
+                                                             acc[j], 0, 0, 0);
+          }
         }
       }
     }
@@ -211,15 +208,37 @@ __global__ __launch_bounds__(kThreads) void k_quant_act(
   }
 
   if (NT > 0) {
+    // add the other K groups' partial sums (in group order) through LDS; the X staging buffers
+    // are free now
+    if (kSplit > 1) {
+      f32x4_t* part = reinterpret_cast<f32x4_t*>(&s_x[0][0]);  // [kSplit-1][kWaves][NT][64]
+      if (ks > 0) {
+#pragma unroll
+        for (int j = 0; j < NT; ++j) part[(((ks - 1) * kWaves + rw) * NT + j) * 64 + lane] = acc[j];
+      }
+      __syncthreads();
+      if (ks == 0) {
+#pragma unroll
+        for (int o = 1; o < kSplit; ++o)
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            const f32x4_t v = part[(((o - 1) * kWaves + rw) * NT + j) * 64 + lane];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) acc[j][i] += v[i];
+          }
+      }
+    }
     // 16x16 output: lane holds rank column 16j + rl and rows 4q .. 4q+3 of the wave's 16 rows.
+    if (ks == 0) {
 #pragma unroll
-    for (int j = 0; j < NT; ++j) {
-      const int n = 16 * j + rl;
-      if (n < r) {
+      for (int j = 0; j < NT; ++j) {
+        const int n = 16 * j + rl;
+        if (n < r) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-          const int64_t m = row0 + 4 * q + i;
-          if (m < M) D[m * r + n] = acc[j][i];
+          for (int i = 0; i < 4; ++i) {
+            const int64_t m = row0 + 4 * q + i;
+            if (m < M) D[m * r + n] = acc[j][i];
+          }
         }
       }
     }
@@ -260,22 +279,42 @@ __global__ void k_amax_to_g(float* t) {
   t[0] = a == 0.0f ? 1.0f : a / 2688.0f;
 }
 
+// Static LDS of an instantiation (the X staging and L1 slices of every K group).
+constexpr size_t static_lds(int nt, int split) {
+  return (size_t)kWaves * split * 16 * kPitch * 2 + (size_t)split * (nt > 0 ? nt : 1) * 16 * kPitch * 2;
+}
+
+template <int FMT, int NT, int SPLIT>
+hipError_t launch_one(dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int64_t M, int64_t K,
+                      int64_t ldx, const float* lambda, const float* amax_p, const uint16_t* down,
+                      int r, uint8_t* codes, void* scales, float* ts, int write_g, float* D,
+                      uint32_t* sat) {
+  if (lds > 48 * 1024) {
+    hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_quant_act<FMT, NT, SPLIT>),
+                                       hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
+    if (e != hipSuccess) return e;
+  }
+  k_quant_act<FMT, NT, SPLIT><<<grid, dim3(kGroupThreads * SPLIT), lds, s>>>(
+      X, M, K, ldx, lambda, amax_p, down, r, codes, scales, ts, write_g, D, sat);
+  return hipGetLastError();
+}
+
 template <int FMT>
 hipError_t dispatch(int nt, dim3 grid, size_t lds, hipStream_t s, const uint16_t* X, int64_t M,
                     int64_t K, int64_t ldx, const float* lambda, const float* amax_p,
                     const uint16_t* down, int r, uint8_t* codes, void* scales, float* ts,
                     int write_g, float* D, uint32_t* sat) {
+  // two K groups when both fit in LDS (160 KB per workgroup), otherwise one
+  const bool split = nt <= 2 && static_lds(nt, 2) + lds <= 160 * 1024;
 #define SVDQ_QA_CASE(NTV)                                                                  \
   case NTV:                                                                                \
-    if (lds > 48 * 1024) {                                                                 \
-      hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_quant_act<FMT, NTV>), \
-                                         hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds); \
-      if (e != hipSuccess) return e;                                                       \
+    if constexpr (NTV <= 2) {                                                              \
+      if (split)                                                                           \
+        return launch_one<FMT, NTV, 2>(grid, lds, s, X, M, K, ldx, lambda, amax_p, down, r, \
+                                       codes, scales, ts, write_g, D, sat);                \
     }                                                                                      \
-    k_quant_act<FMT, NTV><<<grid, dim3(kThreads), lds, s>>>(X, M, K, ldx, lambda, amax_p, \
-                                                             down, r, codes, scales, ts,   \
-                                                             write_g, D, sat);             \
-    break;
+    return launch_one<FMT, NTV, 1>(grid, lds, s, X, M, K, ldx, lambda, amax_p, down, r,    \
+                                   codes, scales, ts, write_g, D, sat);
   switch (nt) {
     SVDQ_QA_CASE(0)
     SVDQ_QA_CASE(1)
@@ -290,7 +329,6 @@ hipError_t dispatch(int nt, dim3 grid, size_t lds, hipStream_t s, const uint16_t
       return hipErrorInvalidValue;
   }
 #undef SVDQ_QA_CASE
-  return hipGetLastError();
 }
 
 }  // namespace
