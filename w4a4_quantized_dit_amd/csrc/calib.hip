@@ -10,12 +10,13 @@ namespace {
 
 constexpr int kAbsmaxWaves = 4;
 constexpr int kAbsmaxThreads = 64 * kAbsmaxWaves;  // a block covers 512 channels (8 per lane)
-constexpr int kAbsmaxRows = 256;                    // rows per block (never straddling a segment)
+constexpr int kAbsmaxRows = 128;                    // rows per block (never straddling a segment)
 constexpr int kUnroll = 8;                          // loads in flight per lane
 
+// Row chunks of one launch: X's three modality segments, then (optionally) W as a fourth.
 struct SegChunks {
-  int64_t seg[4];     // {0, n_text, n_text + n_video, M}
-  int64_t cstart[4];  // first chunk of each segment (cumulative), cstart[3] = total
+  int64_t seg[5];     // {0, n_text, n_text + n_video, M, M + N}: X rows, then W rows
+  int64_t cstart[5];  // first chunk of each segment (cumulative), cstart[4] = total
 };
 
 __global__ void k_fill2(float* __restrict__ p, int64_t n, float v, float* __restrict__ q,
@@ -27,24 +28,35 @@ __global__ void k_fill2(float* __restrict__ p, int64_t n, float v, float* __rest
 
 typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
 
-// out[mu*K + k] = max(out, max over the chunk's rows of |X[row, k]|).  bf16 magnitudes compare as
-// unsigned 15-bit patterns, so the max is taken on integers; the four waves of a block take
-// interleaved rows and combine through LDS before one atomic per channel.
+// ax[mu*K + k] = max(ax, max over the chunk's rows of |X[row, k]|) for the three modality
+// segments, and aw[k] = max(aw, max |W[row, k]|) for the fourth (W's rows).  bf16 magnitudes
+// compare as unsigned 15-bit patterns, so the max is taken on integers; the four waves of a
+// block take interleaved rows and combine through LDS before one atomic per channel.
 __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint16_t* __restrict__ X,
-                                                           int64_t ld, int64_t K, SegChunks sc,
-                                                           float* __restrict__ out,
-                                                           int per_modality) {
+                                                           int64_t ldx,
+                                                           const uint16_t* __restrict__ W,
+                                                           int64_t ldw, int64_t K, SegChunks sc,
+                                                           float* __restrict__ ax,
+                                                           float* __restrict__ aw) {
   __shared__ u16x8 red[kAbsmaxWaves][64];
   const int64_t chunk = blockIdx.y;
-  const int mu = (chunk >= sc.cstart[1]) + (chunk >= sc.cstart[2]);
-  const int64_t r0 = sc.seg[mu] + (chunk - sc.cstart[mu]) * kAbsmaxRows;
-  const int64_t r1 = min(r0 + (int64_t)kAbsmaxRows, sc.seg[mu + 1]);
+  const int mu = (chunk >= sc.cstart[1]) + (chunk >= sc.cstart[2]) + (chunk >= sc.cstart[3]);
+  int64_t r0 = sc.seg[mu] + (chunk - sc.cstart[mu]) * kAbsmaxRows;
+  int64_t r1 = min(r0 + (int64_t)kAbsmaxRows, sc.seg[mu + 1]);
+  const uint16_t* base = X;
+  int64_t ld = ldx;
+  if (mu == 3) {  // W rows
+    base = W;
+    ld = ldw;
+    r0 -= sc.seg[3];
+    r1 -= sc.seg[3];
+  }
   const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
   const int64_t col = ((int64_t)blockIdx.x * 64 + lane) * 8;
   const u16x8 mask = (u16x8)(0x7FFF);
   u16x8 m = (u16x8)(0);
   if (col < K) {
-    const uint16_t* p = X + col;
+    const uint16_t* p = base + col;
     int64_t r = r0 + wave;
     for (; r + (kUnroll - 1) * kAbsmaxWaves < r1; r += kUnroll * kAbsmaxWaves) {
       u16x8 v[kUnroll];
@@ -60,7 +72,7 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint16_t* __res
   if (wave == 0 && col < K) {
 #pragma unroll
     for (int w = 1; w < kAbsmaxWaves; ++w) m = __builtin_elementwise_max(m, red[w][lane]);
-    float* o = out + (per_modality ? (int64_t)mu * K : 0) + col;
+    float* o = (mu == 3 ? aw : ax + (int64_t)mu * K) + col;
 #pragma unroll
     for (int j = 0; j < 8; ++j)
       if (m[j]) atomic_max_pos(o + j, bf16_to_f32(m[j]));
@@ -104,22 +116,14 @@ __global__ __launch_bounds__(1024) void k_lambda(const float* __restrict__ ax,
   }
 }
 
-SegChunks make_chunks(const int64_t seg[4]) {
+SegChunks make_chunks(const int64_t seg[4], int64_t n_w) {
   SegChunks sc;
   for (int i = 0; i < 4; ++i) sc.seg[i] = seg[i];
+  sc.seg[4] = seg[3] + n_w;
   sc.cstart[0] = 0;
-  for (int i = 0; i < 3; ++i)
-    sc.cstart[i + 1] = sc.cstart[i] + (seg[i + 1] - seg[i] + kAbsmaxRows - 1) / kAbsmaxRows;
+  for (int i = 0; i < 4; ++i)
+    sc.cstart[i + 1] = sc.cstart[i] + (sc.seg[i + 1] - sc.seg[i] + kAbsmaxRows - 1) / kAbsmaxRows;
   return sc;
-}
-
-hipError_t absmax(const uint16_t* X, int64_t ld, int64_t K, const int64_t seg[4], float* out,
-                  int per_modality, hipStream_t s) {
-  SegChunks sc = make_chunks(seg);
-  if (sc.cstart[3] == 0) return hipSuccess;
-  dim3 grid((unsigned)((K / 8 + 63) / 64), (unsigned)sc.cstart[3]);
-  k_absmax<<<grid, dim3(kAbsmaxThreads), 0, s>>>(X, ld, K, sc, out, per_modality);
-  return hipGetLastError();
 }
 
 }  // namespace
@@ -139,10 +143,12 @@ hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx
         p ? p : aw, p ? n : 0, 0.0f, q, q ? K : 0, W ? 0.0f : 1.0f);
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
-  if ((e = absmax(X, ldx, K, seg, ax, 1, s)) != hipSuccess) return e;
-  if (W) {
-    const int64_t wseg[4] = {0, N, N, N};
-    if ((e = absmax(W, ldw, K, wseg, aw, 0, s)) != hipSuccess) return e;
+  // one launch over X's modality segments and W's rows
+  const SegChunks sc = make_chunks(seg, W ? N : 0);
+  if (sc.cstart[4] > 0) {
+    const dim3 grid((unsigned)((K / 8 + 63) / 64), (unsigned)sc.cstart[4]);
+    k_absmax<<<grid, dim3(kAbsmaxThreads), 0, s>>>(X, ldx, W, ldw, K, sc, ax, aw);
+    if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   k_lambda<<<dim3(1), dim3(1024), 0, s>>>(ax, aw, K, mask, alpha, lambda, act_amax);
   return hipGetLastError();
