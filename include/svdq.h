@@ -144,7 +144,9 @@ svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, i
  * activation kernel), lora_up [N, r] bf16.
  * core_out (nullable, fp32 [n_cubes, N]) and row_to_cube (int32 [M]) add the DeltaQuant core
  * term ("DeltaQuant on MiniMax-H3"; NVFP4 only; both or neither).  Y [M, N] bf16, leading
- * dimension ldy.  fp32 accumulation; results within the layer tolerance of the float64 value.
+ * dimension ldy (a multiple of 8, >= N).  Codes, scales, D, lora_up and Y must be 16-byte
+ * aligned; violations return SVDQ_UNSUPPORTED_SHAPE.  fp32 accumulation; results within the
+ * layer tolerance of the float64 value.
  */
 svdq_status svdq_w4a4_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                            const void* a_scales, const float* g_a, const uint8_t* w_codes,

@@ -79,6 +79,10 @@ def test_quant_act_and_gemm_validation(lib):
     assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, P, None, P, 256, None) == INVALID
     assert g(1, 64, 256, 256, P, P, None, P, P, None, P, P, 32, P, P, P, 256, None) == INVALID
     assert g(0, 64, 256, 256, P, P, None, P, P, P, P, P, 32, None, None, P, 256, None) == NULLP
+    assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 260, None) == SHAPE
+    assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, None, None, MIS, 256, None) == SHAPE
+    assert g(0, 64, 256, 256, P, MIS, P, P, P, P, P, P, 32, None, None, P, 256, None) == SHAPE
+    assert g(0, 64, 256, 256, P, P, P, P, MIS, P, P, P, 32, None, None, P, 256, None) == SHAPE
 
 
 def test_other_validation(lib):

@@ -188,13 +188,16 @@ svdq_status svdq_w4a4_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8
   REQUIRE_PTR(Y);
   if (fmt == SVDQ_NVFP4) { REQUIRE_PTR(g_a); REQUIRE_PTR(g_w); }
   REQUIRE_ALIGNED(a_codes); REQUIRE_ALIGNED(w_codes); REQUIRE_ALIGNED(D); REQUIRE_ALIGNED(lora_up);
+  REQUIRE_ALIGNED(a_scales); REQUIRE_ALIGNED(w_scales); REQUIRE_ALIGNED(Y);
   if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
   if (N < 1 || N % 256 != 0)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn,
                 (long long)N);
   TRY(check_k(fn, K));
   TRY(check_rank(fn, r));
-  if (ldy < N) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldy=%lld < N", fn, (long long)ldy);
+  if (ldy < N || ldy % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldy=%lld must be >= N and a multiple of 8", fn,
+                (long long)ldy);
   if (r > 0) { REQUIRE_PTR(D); REQUIRE_PTR(lora_up); }
   if ((core_out == nullptr) != (row_to_cube == nullptr))
     return fail(SVDQ_INVALID_ARG, "%s: core_out and row_to_cube must be given together", fn);

@@ -1,5 +1,6 @@
-// Pieces shared by the W4A4 GEMM kernels: the epilogue (low-rank up-projection, tensor scales,
-// DeltaQuant core term, bf16 store) and the XCD-grouped workgroup-to-tile mapping.
+// Pieces shared by the W4A4 GEMM kernels: the low-rank up-projection (the accumulators' starting
+// value), the store (tensor scales, DeltaQuant core term, bf16 through LDS) and the XCD-grouped
+// workgroup-to-tile mapping.
 #pragma once
 
 #include "device.h"
@@ -32,21 +33,23 @@ inline unsigned grid_of_tiles(int64_t tiles_m, int64_t tiles_n) {
   return (unsigned)(((tiles_m * tiles_n + 7) / 8) * 8);
 }
 
-// Epilogue: low-rank up-projection, tensor scales, DeltaQuant core term, bf16 store.
-// The accumulators hold Σ A'·W' without the tensor scales gsc = g_a·g_w; the low-rank term is
-// folded in before the scaling as (D/gsc)·L2 so the accumulators stay with the MFMA unit, and
-// y = gsc·acc (+ core_out[cube(m)]) is formed element by element at the store.  fp32 D/gsc is
-// split into an exact-to-2^-16 bf16 pair for the bf16 MFMA.
+// Low-rank term as the accumulators' starting value.  The accumulators hold Σ A'·W' without the
+// tensor scales gsc = g_a·g_w, so the term enters as (D/gsc)·L2 and y = gsc·acc at the store.
+// It is computed before the main loop, where its D and L2 loads overlap the first stage loads
+// instead of standing alone after the loop.  fp32 D/gsc is split into an exact-to-2^-16 bf16
+// pair for the bf16 MFMA.
 // 32x32 accumulator layout: lane holds column r32 and rows (e/4)*8 + 4h + e%4.
 template <int FM, int FN>
-__device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[FM][FN], float gsc, int64_t M,
-                                              int64_t N, int64_t m_base, int64_t n_base, int r32,
-                                              int h, const float* __restrict__ D,
-                                              const uint16_t* __restrict__ up, int r,
-                                              const float* __restrict__ core_out,
-                                              const int32_t* __restrict__ row_to_cube,
-                                              uint16_t* __restrict__ Y, int64_t ldy) {
-  const float inv_gsc = 1.0f / gsc;
+__device__ __forceinline__ void gemm_lowrank_init(f32x16_t (&acc)[FM][FN], float inv_gsc,
+                                                  int64_t M, int64_t m_base, int64_t n_base,
+                                                  int r32, int h, const float* __restrict__ D,
+                                                  const uint16_t* __restrict__ up, int r) {
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
   for (int t = 0; 16 * t < r; ++t) {
     const int k0 = 16 * t + 8 * h;
     bf16x8_t u_op[FN];
@@ -70,23 +73,63 @@ __device__ __forceinline__ void gemm_epilogue(f32x16_t (&acc)[FM][FN], float gsc
       }
     }
   }
+}
 
+// Bytes of LDS a wave needs to stage its (32 FM) x (32 FN) bf16 output tile.
+template <int FM, int FN>
+constexpr int gemm_store_bytes() {
+  return FM * 32 * FN * 64;
+}
+
+// Store y = bf16(gsc·acc (+ core_out[cube(m)][n])) of the wave's tile at (m_base, n_base).  The
+// elements go one by one, in the accumulator layout, into the wave's own LDS region (row-major,
+// 64 FN bytes per row), and come back as 16-byte row pieces that are written to Y with
+// full-width stores, eight lanes per 128-byte row segment.  Piece c of staged row R sits at
+// c ^ (4 ((R >> 2) & 1)), so the two half-waves of one element write (rows 4 apart) use
+// different banks.  Rows past M are not stored.  Y rows must be 16-byte aligned (ldy % 8 == 0).
+template <int FM, int FN>
+__device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[FM][FN], float gsc,
+                                           uint8_t* region, int lane, int64_t M, int64_t N,
+                                           int64_t m_base, int64_t n_base,
+                                           const float* __restrict__ core_out,
+                                           const int32_t* __restrict__ row_to_cube,
+                                           uint16_t* __restrict__ Y, int64_t ldy) {
+  static_assert(FN == 2, "row pieces assume 64-column wave tiles");
+  constexpr int kRowB = FN * 64;
+  const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
-      const int64_t row = m_base + 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
-      if (row < M) {
-        const float* co = core_out ? core_out + (int64_t)row_to_cube[row] * N : nullptr;
+      const int row = 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
+      const float* co = nullptr;
+      if (core_out) {
+        int64_t grow = m_base + row;
+        grow = grow < M ? grow : M - 1;
+        co = core_out + (int64_t)row_to_cube[grow] * N + n_base;
+      }
 #pragma unroll
-        for (int j = 0; j < FN; ++j) {
-          const int64_t col = n_base + 32 * j + r32;
-          float v = acc[i][j][e] * gsc;
-          if (co) v += co[col];
-          Y[row * ldy + col] = f32_to_bf16(v);
-        }
+      for (int j = 0; j < FN; ++j) {
+        const int col = 32 * j + r32;
+        float v = acc[i][j][e] * gsc;
+        if (co) v += co[col];
+        const int piece = (col >> 3) ^ (((row >> 2) & 1) << 2);
+        *reinterpret_cast<uint16_t*>(region + row * kRowB + piece * 16 + (col & 7) * 2) =
+            f32_to_bf16(v);
       }
     }
+  }
+  // the pieces are read back by other lanes of this wave
+  asm volatile("s_waitcnt lgkmcnt(0)" ::: "memory");
+  constexpr int kPieces = FM * 32 * (kRowB / 16);
+#pragma unroll
+  for (int it = 0; it < kPieces / 64; ++it) {
+    const int c = it * 64 + lane;
+    const int row = c / (kRowB / 16), piece = c % (kRowB / 16);
+    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(
+        region + row * kRowB + (piece ^ (((row >> 2) & 1) << 2)) * 16);
+    const int64_t grow = m_base + row;
+    if (grow < M) *reinterpret_cast<u32x4_t*>(Y + grow * ldy + n_base + piece * 8) = v;
   }
 }
 

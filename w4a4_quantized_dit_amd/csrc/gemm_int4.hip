@@ -129,16 +129,10 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_int4(
   const int sa_off = wm * 128 + 4 * h;                      // float index in the A scale block
   const int sw_off = kGroupsPerStage * kBM + wn * 64 + r32;  // float index of the W scales
 
-  f32x16_t acc[FM][FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i)
-#pragma unroll
-    for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
   StageRegs g;
   stage_load(g, A, As, B, Bs, M, m0, n0, kb, ng, 0, tid);
+  f32x16_t acc[FM][FN];
+  gemm_lowrank_init<FM, FN>(acc, 1.0f, M, m_base, n_base, r32, h, D, up, r);
   stage_store(g, lds, tid);
   if (nstage > 1) {
     stage_load(g, A, As, B, Bs, M, m0, n0, kb, ng, 1, tid);
@@ -189,8 +183,11 @@ __global__ __launch_bounds__(kThreads, 1) void k_gemm_int4(
     __syncthreads();
   }
 
-  gemm_epilogue<FM, FN>(acc, 1.0f, M, N, m_base, n_base, r32, h, D, up, r, nullptr, nullptr, Y,
-                        ldy);
+  // the loop ended with a barrier after the last LDS reads: the stage buffers are free for the
+  // output staging (each wave its own 16 KB)
+  static_assert(8 * gemm_store_bytes<FM, FN>() <= kStages * kStageBytes, "output staging fits");
+  gemm_store<FM, FN>(acc, 1.0f, lds + wave * gemm_store_bytes<FM, FN>(), lane, M, N, m_base,
+                     n_base, nullptr, nullptr, Y, ldy);
 }
 
 }  // namespace

@@ -26,66 +26,41 @@ namespace {
 constexpr int kThreads = 512;  // 8 waves, 2 x 4 over the workgroup tile (two per SIMD)
 
 // Workgroup tile 256 x 256, 8 waves in 2 x 4 (two per SIMD), each wave 128 x 64 (4 x 2 MFMA
-// tiles of 32x32), tiles assigned in XCD-grouped order.  The second wave on a SIMD issues its
-// MFMAs while the other one waits on its conversion chain, which is what keeps the matrix unit
-// busy: each wave's fp4 -> fp16 conversions (v_cvt_scalef32_pk_f16_fp4, then the block-scale
-// multiply) depend on each other, and a single wave cannot hide that latency.
+// tiles of 32x32), tiles assigned in XCD-grouped order.
 //
-// K advances 128 elements per stage.  Raw codes and scales go from global memory straight into
-// a ring of four LDS stage buffers (global_load_lds: no registers, no LDS store instructions),
-// three stages ahead.  Code rows are 64 bytes without padding; the 16-byte chunk p of row R
-// sits at chunk p ^ ((R >> 2) & 3), so the fragment reads (consecutive rows) spread over the
-// banks.  A lane reads its 16 code bytes of a fragment once per 64-element sub-stage (four
-// steps), one sub-stage ahead.
-constexpr int kBM = 256, kBN = 256, kBK = 128;
-constexpr int kRowBytes = kBK / 2;          // 64 bytes of codes per row per stage
-constexpr int kStages = 4;
-constexpr int kCodeBuf = kBM * kRowBytes;   // per operand per stage
-constexpr int kScaleBuf = kBM * (kBK / 16); // 8 scale bytes per row per stage
-constexpr int kStageBytes = 2 * kCodeBuf + 2 * kScaleBuf;
-constexpr int kLoadsPerStage = 6;           // direct-load instructions per wave per stage
+// Dequantisation is shared by the workgroup: K advances 64 elements per stage, and every
+// thread converts one row of one operand (thread t: operand t % 2, row t / 2) of the stage to
+// fp16 and stores it in LDS; the waves then read ready fp16 fragments.  Each code is converted
+// once per workgroup instead of once per wave that uses it (four waves share an A row, two a W
+// row).  The conversion of stage s+1 is spread over the four MFMA steps of stage s, and two fp16
+// LDS buffers alternate with one barrier per stage.
+//
+// Global traffic is shaped for the vector L1, which cannot hold a stage's 512 rows from one
+// stage to the next: a row is fetched as 64 code bytes (two stages, four 16-byte loads into
+// registers, two rounds in flight) and its E4M3 scales as 16 bytes covering four stages
+// (straight into LDS with global_load_lds, up to two chunks ahead), so a line is requested
+// about once per two stages instead of twice per stage.
+//
+// LDS: [A fp16 buf 0][A buf 1][W buf 0][W buf 1] (256 rows x 64 fp16 = 128 bytes each), then
+// two scale chunks [operand][row][16 bytes].  The 16-byte chunk c (elements [8c, 8c + 8)) of
+// row R sits at chunk c ^ ((R >> 1) & 7), and at c ^ ((R >> 1) & 7) ^ 4 in W: the fragment
+// reads (32 consecutive rows, one chunk) and the conversion stores (A and W rows interleaved
+// in a wave, one chunk each) are free of bank conflicts.
+constexpr int kBM = 256, kBN = 256, kBK = 64;
+constexpr int kRowBytes = kBK * 2;          // fp16 row of one stage
+constexpr int kOpBytes = kBM * kRowBytes;   // one operand, one buffer: 32 KB
+constexpr int kWOffset = 2 * kOpBytes;      // W buffers follow the two A buffers
+constexpr int kScaleOffset = 4 * kOpBytes;  // scale chunks follow the fp16 buffers
+constexpr int kScaleChunk = 2 * kBM * 16;   // both operands, four stages: 8 KB
+constexpr int kLdsBytes = kScaleOffset + 2 * kScaleChunk;
 
 typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
 
-__device__ __forceinline__ int swz(int row, int part) { return part ^ ((row >> 2) & 3); }
-
-// This wave's share of one stage: codes as 16-byte chunks (chunk c of an operand: row c / 4,
-// stored part c % 4, loaded part swz(row, c % 4)), scales as 4-byte pieces (piece c: row c / 2,
-// half c % 2).  Rows of A past M read row M-1 (never stored).
-__device__ __forceinline__ void stage_issue(uint8_t* buf, const uint8_t* __restrict__ A,
-                                            const uint8_t* __restrict__ As,
-                                            const uint8_t* __restrict__ B,
-                                            const uint8_t* __restrict__ Bs, int64_t M,
-                                            int64_t m0, int64_t n0, int64_t kb, int64_t ks,
-                                            int64_t stage, int wave, int lane) {
-#pragma unroll
-  for (int q = 0; q < 2; ++q) {
-    const int c = (wave * 2 + q) * 64 + lane;
-    const int row = c >> 2, part = swz(row, c & 3);
-    int64_t ar = m0 + row;
-    ar = ar < M ? ar : M - 1;
-    __builtin_amdgcn_global_load_lds((gvoid_t*)(A + ar * kb + stage * kRowBytes + part * 16),
-                                     (lvoid_t*)(buf + (wave * 2 + q) * 1024), 16, 0, 0);
-    __builtin_amdgcn_global_load_lds(
-        (gvoid_t*)(B + (n0 + row) * kb + stage * kRowBytes + part * 16),
-        (lvoid_t*)(buf + kCodeBuf + (wave * 2 + q) * 1024), 16, 0, 0);
-  }
-  const int c = wave * 64 + lane;
-  const int row = c >> 1, half = c & 1;
-  int64_t ar = m0 + row;
-  ar = ar < M ? ar : M - 1;
-  __builtin_amdgcn_global_load_lds((gvoid_t*)(As + ar * ks + stage * (kBK / 16) + 4 * half),
-                                   (lvoid_t*)(buf + 2 * kCodeBuf + wave * 256), 4, 0, 0);
-  __builtin_amdgcn_global_load_lds((gvoid_t*)(Bs + (n0 + row) * ks + stage * (kBK / 16) + 4 * half),
-                                   (lvoid_t*)(buf + 2 * kCodeBuf + kScaleBuf + wave * 256), 4, 0,
-                                   0);
-}
-
-// Workgroup barrier ordering LDS accesses only.  The stage loads are completed explicitly with
-// wait_vmcnt before it, so the barrier must not wait for the stages still in flight, which a full
-// __syncthreads() fence would do.  (The memory clobber keeps the compiler from moving memory
-// accesses across it.)
+// Workgroup barrier ordering LDS accesses only.  Loads in flight are waited for explicitly (scale
+// chunks) or where their registers are used (codes), so the barrier must not wait for them,
+// which a full __syncthreads() fence would do.  (The memory clobber keeps the compiler from
+// moving memory accesses across it.)
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -105,7 +80,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
     const uint16_t* __restrict__ up, int r, const float* __restrict__ core_out,
     const int32_t* __restrict__ row_to_cube, uint16_t* __restrict__ Y, int64_t ldy) {
   constexpr int FM = 4, FN = 2;
-  __shared__ __attribute__((aligned(16))) uint8_t lds[kStages * kStageBytes];
+  __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   int64_t tm, tn;
   if (!tile_of_block((M + kBM - 1) / kBM, N / kBN, tm, tn)) return;
   const int64_t m0 = tm * kBM, n0 = tn * kBN;
@@ -115,132 +90,157 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
   const int64_t m_base = m0 + wm * 128, n_base = n0 + wn * 64;
   const int r32 = lane & 31, h = lane >> 5;
   const int64_t kb = K / 2, ks = K / 16;
-  const int64_t nstage = K / kBK;
+  const int64_t nstage = K / kBK;    // a multiple of 4 (K % 256 == 0)
+  const int64_t nround = nstage / 2;  // code rounds of two stages
+  const int64_t nchunk = nstage / 4;  // scale chunks of four stages
 
-  // Per-fragment offsets inside a stage buffer: the lane's 16 code bytes of sub-stage `sub`
-  // (logical chunk 2 sub + h, swizzled) and its two scale bytes.
-  int a_code[2][FM], b_code[2][FN], a_sc[FM], b_sc[FN];
+  // Conversion share: operand co (0 A, 1 W), row crow.  Rows of A past M read row M-1 (never
+  // stored).
+  const int co = tid & 1, crow = tid >> 1;
+  int64_t ar = m0 + crow;
+  ar = ar < M ? ar : M - 1;
+  const uint8_t* pcode = co ? B + (n0 + crow) * kb : A + ar * kb;
+  const int w_base = co * kWOffset + crow * kRowBytes;
+  const int w_swz = ((crow >> 1) & 7) ^ (co << 2);
+  const int s_rd = kScaleOffset + co * (kBM * 16) + crow * 16;
+
+  // Scale chunk loads: wave w fetches 64 rows (16 bytes each) of operand w / 4.
+  const int srow = (wave & 3) * 64 + lane;
+  int64_t sr = (wave < 4 ? m0 : n0) + srow;
+  if (wave < 4) sr = sr < M ? sr : M - 1;
+  const uint8_t* pscale = (wave < 4 ? As : Bs) + sr * ks;
+  auto load_scales = [&](int buf, int64_t c) {
+    __builtin_amdgcn_global_load_lds((gvoid_t*)(pscale + c * 16),
+                                     (lvoid_t*)(lds + kScaleOffset + buf * kScaleChunk +
+                                                wave * 1024),
+                                     16, 0, 0);
+  };
+
+  // Fragment reads: step t (elements [16t, 16t + 16) of a stage) of the lane's row is chunk
+  // 2t + h; fragments i (j) of the wave are 32 rows apart.
+  const int x = (r32 >> 1) & 7;
+  int ra[4], rb[4];
 #pragma unroll
-  for (int sub = 0; sub < 2; ++sub) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      const int row = wm * 128 + 32 * i + r32;
-      a_code[sub][i] = row * kRowBytes + 16 * swz(row, 2 * sub + h);
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      const int row = wn * 64 + 32 * j + r32;
-      b_code[sub][j] = kCodeBuf + row * kRowBytes + 16 * swz(row, 2 * sub + h);
-    }
+  for (int t = 0; t < 4; ++t) {
+    ra[t] = (wm * 128 + r32) * kRowBytes + 16 * ((2 * t + h) ^ x);
+    rb[t] = kWOffset + (wn * 64 + r32) * kRowBytes + 16 * ((2 * t + h) ^ x ^ 4);
   }
-#pragma unroll
-  for (int i = 0; i < FM; ++i) a_sc[i] = 2 * kCodeBuf + (wm * 128 + 32 * i + r32) * 8 + 2 * h;
-#pragma unroll
-  for (int j = 0; j < FN; ++j)
-    b_sc[j] = 2 * kCodeBuf + kScaleBuf + (wn * 64 + 32 * j + r32) * 8 + 2 * h;
 
-  f32x16_t acc[FM][FN];
+  // a round: the row's 64 code bytes of stages 2q, 2q + 1
+  auto load_round = [&](u32x4_t (&g)[4], int64_t q) {
 #pragma unroll
-  for (int i = 0; i < FM; ++i)
+    for (int v = 0; v < 4; ++v) g[v] = *reinterpret_cast<const u32x4_t*>(pcode + q * 64 + v * 16);
+  };
+  // code dword d (elements [8d, 8d + 8), block d / 2) of the stage held in words w[0..7] -> LDS
+  auto convert = [&](const uint32_t* w, f16x2_t s01, f16x2_t s23, int buf, int d) {
+    const _Float16 sc = d < 2 ? s01[0] : d < 4 ? s01[1] : d < 6 ? s23[0] : s23[1];
+    *reinterpret_cast<f16x8_t*>(lds + buf * kOpBytes + w_base + 16 * (d ^ w_swz)) =
+        dequant8(w[d], f16x2_t{sc, sc});
+  };
+  auto stage_scales = [&](int64_t st, f16x2_t& s01, f16x2_t& s23) {
+    const uint32_t v = *reinterpret_cast<const uint32_t*>(
+        lds + s_rd + ((st >> 2) & 1) * kScaleChunk + (st & 3) * 4);
+    s01 = e4m3x2_to_f16x2(v & 0xFFFFu);
+    s23 = e4m3x2_to_f16x2(v >> 16);
+  };
+  auto read_frags = [&](int buf, int t, f16x8_t (&fa)[FM], f16x8_t (&fb)[FN]) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+      fa[i] = *reinterpret_cast<const f16x8_t*>(lds + buf * kOpBytes + ra[t] + i * 32 * kRowBytes);
 #pragma unroll
     for (int j = 0; j < FN; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
-
-  // prologue: stages 0, 1, 2 in flight; stages 0 and 1 must land (iteration s reads ahead into
-  // stage s+1)
-#pragma unroll
-  for (int p = 0; p < kStages - 1; ++p)
-    if (p < nstage) stage_issue(lds + p * kStageBytes, A, As, B, Bs, M, m0, n0, kb, ks, p, wave, lane);
-  if (nstage >= 3)
-    wait_vmcnt<kLoadsPerStage>();
-  else
-    wait_vmcnt<0>();
-  barrier_lds();
-
-  // Raw fragments of one 64-element sub-stage: 16 code bytes (four steps) and the packed pair
-  // of block scales per fragment.
-  u32x4_t ca[FM], cb[FN];
-  f16x2_t sa[FM], sb[FN];
-  auto read_sub = [&](const uint8_t* buf, int sub, u32x4_t (&xa)[FM], u32x4_t (&xb)[FN],
-                      f16x2_t (&ya)[FM], f16x2_t (&yb)[FN]) {
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      xa[i] = *reinterpret_cast<const u32x4_t*>(buf + a_code[sub][i]);
-      ya[i] = e4m3x2_to_f16x2(*reinterpret_cast<const uint16_t*>(buf + a_sc[i] + 4 * sub));
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      xb[j] = *reinterpret_cast<const u32x4_t*>(buf + b_code[sub][j]);
-      yb[j] = e4m3x2_to_f16x2(*reinterpret_cast<const uint16_t*>(buf + b_sc[j] + 4 * sub));
-    }
+      fb[j] = *reinterpret_cast<const f16x8_t*>(lds + buf * kOpBytes + rb[t] + j * 32 * kRowBytes);
   };
-  read_sub(lds, 0, ca, cb, sa, sb);
-  f16x8_t a_op[FM], b_op[FN];
-#pragma unroll
-  for (int i = 0; i < FM; ++i) a_op[i] = dequant8(ca[i][0], f16x2_t{sa[i][0], sa[i][0]});
-#pragma unroll
-  for (int j = 0; j < FN; ++j) b_op[j] = dequant8(cb[j][0], f16x2_t{sb[j][0], sb[j][0]});
 
-  for (int64_t s = 0; s < nstage; ++s) {
-    // stage s+3 into the buffer computed in the previous iteration (all waves passed the
-    // barrier after it)
-    if (s + 3 < nstage)
-      stage_issue(lds + ((s + 3) % kStages) * kStageBytes, A, As, B, Bs, M, m0, n0, kb, ks, s + 3,
-                  wave, lane);
+  // prologue: scale chunks 0, 1 and code rounds 0, 1 in flight, low-rank term into the
+  // accumulators, stage 0 converted into buffer 0
+  const float gsc = g_a[0] * g_w[0];
+  load_scales(0, 0);
+  load_scales(1, nchunk > 1 ? 1 : 0);
+  u32x4_t g0[4], g1[4];
+  load_round(g0, 0);
+  load_round(g1, nround > 1 ? 1 : 0);
+  f32x16_t acc[FM][FN];
+  gemm_lowrank_init<FM, FN>(acc, 1.0f / gsc, M, m_base, n_base, r32, h, D, up, r);
+  wait_vmcnt<0>();
+  barrier_lds();
+  {
+    f16x2_t s01, s23;
+    stage_scales(0, s01, s23);
+    const uint32_t* w = reinterpret_cast<const uint32_t*>(g0);
 #pragma unroll
-    for (int sub = 0; sub < 2; ++sub) {
-      // raw fragments of the next sub-stage (past the end: this one again, never used)
-      u32x4_t na[FM], nb[FN];
-      f16x2_t nsa[FM], nsb[FN];
-      const bool more = sub == 0 || s + 1 < nstage;
-      const uint8_t* nbuf = lds + ((sub == 0 || !more ? s : s + 1) % kStages) * kStageBytes;
-      read_sub(nbuf, more ? sub ^ 1 : sub, na, nb, nsa, nsb);
+    for (int d = 0; d < 8; ++d) convert(w, s01, s23, 0, d);
+  }
+  barrier_lds();
+  f16x8_t a_op[FM], b_op[FN];
+  read_frags(0, 0, a_op, b_op);
+
+  // Iteration s computes stage s from buffer s % 2 while converting stage s+1 (words w of a
+  // register round) into the other buffer.  Extra work of the four-stage pattern, by s % 4:
+  //   0: round s/2 + 2 loaded into g0 at the end (g0 consumed)
+  //   2: round s/2 + 2 loaded into g1 at the end; scale chunk s/4 + 1 waited for before the
+  //      barrier (read from iteration s + 1 on)
+  //   3: scale chunk s/4 + 2 requested at the end.  (Issued here, the chunk is older than the
+  //      code round that iteration s + 2 waits for, so the compiler's wait there stays partial.)
+  // Past the end, loads repeat the last round / chunk into idle registers and buffers.
+  auto iteration = [&](auto phase, int64_t s, const uint32_t* w, u32x4_t (&refill)[4]) {
+    constexpr int ph = decltype(phase)::value;  // s % 4
+    constexpr int p = ph & 1;
+    f16x2_t s01, s23;
+    stage_scales(s + 1, s01, s23);
 #pragma unroll
-      for (int t = 0; t < 4; ++t) {
+    for (int t = 0; t < 4; ++t) {
+      // next step's fragments are requested before this step's MFMAs (the scheduling barriers
+      // keep the compiler from sinking the reads to their use)
+      f16x8_t na[FM], nb[FN];
+      if (t < 3) read_frags(p, t + 1, na, nb);
+      __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
-        for (int i = 0; i < FM; ++i)
+      for (int i = 0; i < FM; ++i)
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[i], b_op[j], acc[i][j], 0, 0, 0);
-        // operands of the next step
-        if (t < 3) {
-          const int hi = (t + 1) >> 1;
+        for (int j = 0; j < FN; ++j)
+          acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[i], b_op[j], acc[i][j], 0, 0, 0);
+      convert(w, s01, s23, p ^ 1, 2 * t);
+      convert(w, s01, s23, p ^ 1, 2 * t + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      if (t < 3) {
 #pragma unroll
-          for (int i = 0; i < FM; ++i)
-            a_op[i] = dequant8(ca[i][t + 1], hi ? f16x2_t{sa[i][1], sa[i][1]} : f16x2_t{sa[i][0], sa[i][0]});
+        for (int i = 0; i < FM; ++i) a_op[i] = na[i];
 #pragma unroll
-          for (int j = 0; j < FN; ++j)
-            b_op[j] = dequant8(cb[j][t + 1], hi ? f16x2_t{sb[j][1], sb[j][1]} : f16x2_t{sb[j][0], sb[j][0]});
-        } else {
-#pragma unroll
-          for (int i = 0; i < FM; ++i) a_op[i] = dequant8(na[i][0], f16x2_t{nsa[i][0], nsa[i][0]});
-#pragma unroll
-          for (int j = 0; j < FN; ++j) b_op[j] = dequant8(nb[j][0], f16x2_t{nsb[j][0], nsb[j][0]});
-        }
-      }
-#pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        ca[i] = na[i];
-        sa[i] = nsa[i];
-      }
-#pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        cb[j] = nb[j];
-        sb[j] = nsb[j];
+        for (int j = 0; j < FN; ++j) b_op[j] = nb[j];
       }
     }
-    // iteration s+1 reads ahead into stage s+2: it must have landed (in every wave) before the
-    // barrier; only the loads of stage s+3 may still be in flight
-    if (s + 3 < nstage)
-      wait_vmcnt<kLoadsPerStage>();
-    else
-      wait_vmcnt<0>();
+    if (ph == 0 || ph == 2) {
+      const int64_t q = s / 2 + 2;
+      load_round(refill, q < nround ? q : nround - 1);
+    }
+    // all but the round just issued: at phase 2 the scale chunk read from the next iteration
+    // on has landed; at phase 0 the round of g1 (used next) has, which spares the next iteration
+    // a full wait (the compiler, unable to place the older scale chunk in the count, would
+    // wait for everything)
+    if (ph == 0 || ph == 2) wait_vmcnt<4>();
+    if (ph == 3) {
+      // chunk s/4 + 2 into the buffer of chunk s/4, whose last stage was converted in the
+      // previous iteration
+      const int64_t c = s / 4 + 2;
+      load_scales((int)(c & 1), c < nchunk ? c : nchunk - 1);
+    }
     barrier_lds();
+    read_frags(p ^ 1, 0, a_op, b_op);
+  };
+  for (int64_t s = 0; s < nstage; s += 4) {
+    // stage s+1: second half of round s/2 (g0); s+2, s+3: round s/2 + 1 (g1); s+4: g0 again
+    iteration(std::integral_constant<int, 0>{}, s, reinterpret_cast<const uint32_t*>(g0) + 8, g0);
+    iteration(std::integral_constant<int, 1>{}, s + 1, reinterpret_cast<const uint32_t*>(g1), g1);
+    iteration(std::integral_constant<int, 2>{}, s + 2, reinterpret_cast<const uint32_t*>(g1) + 8, g1);
+    iteration(std::integral_constant<int, 3>{}, s + 3, reinterpret_cast<const uint32_t*>(g0), g0);
   }
 
-  gemm_epilogue<FM, FN>(acc, g_a[0] * g_w[0], M, N, m_base, n_base, r32, h, D, up, r, core_out,
-                        row_to_cube, Y, ldy);
+  // Every wave passed the last barrier after its final fragment reads: the fp16 buffers are
+  // free for the output staging (each wave its own 16 KB).
+  static_assert(8 * gemm_store_bytes<FM, FN>() <= kScaleOffset, "output staging fits the LDS");
+  gemm_store<FM, FN>(acc, gsc, lds + wave * gemm_store_bytes<FM, FN>(), lane, M, N, m_base, n_base,
+                     core_out, row_to_cube, Y, ldy);
 }
 
 }  // namespace
