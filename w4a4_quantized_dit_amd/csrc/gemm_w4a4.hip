@@ -42,10 +42,10 @@ constexpr int kThreads = 512;  // 8 waves, 2 x 4 over the workgroup tile (two pe
 // about once per two stages instead of twice per stage.
 //
 // LDS: [A fp16 buf 0][A buf 1][W buf 0][W buf 1] (256 rows x 64 fp16 = 128 bytes each), then
-// two scale chunks [operand][row][16 bytes].  The 16-byte chunk c (elements [8c, 8c + 8)) of
-// row R sits at chunk c ^ ((R >> 1) & 7), and at c ^ ((R >> 1) & 7) ^ 4 in W: the fragment
-// reads (32 consecutive rows, one chunk) and the conversion stores (A and W rows interleaved
-// in a wave, one chunk each) are free of bank conflicts.
+// two scale chunks [row][operand][16 bytes].  The 16-byte chunk c (elements [8c, 8c + 8)) of
+// row R sits at chunk c ^ swz(R), and at c ^ swz(R) ^ 4 in W, which keeps the fragment reads
+// (32 consecutive rows, one chunk) and the conversion stores (A and W rows interleaved in a
+// wave, one chunk each) free of bank conflicts.
 constexpr int kBM = 256, kBN = 256, kBK = 64;
 constexpr int kRowBytes = kBK * 2;          // fp16 row of one stage
 constexpr int kOpBytes = kBM * kRowBytes;   // one operand, one buffer: 32 KB
@@ -61,6 +61,12 @@ typedef __attribute__((address_space(3))) void lvoid_t;
 // chunks) or where their registers are used (codes), so the barrier must not wait for them,
 // which a full __syncthreads() fence would do.  (The memory clobber keeps the compiler from
 // moving memory accesses across it.)
+// Chunk swizzle of fp16 row R (W rows additionally flip bit 2).  Fragment reads are served 16
+// lanes (256 bytes) per pass and the conversion stores 8 lanes (128 bytes) per pass; this
+// function gives distinct chunks to the 8 even and the 8 odd rows of 16 consecutive rows (reads)
+// and to the rows of any aligned group of 4 (stores, A and W rows interleaved).
+__device__ __forceinline__ int swz(int row) { return (row & 7) ^ ((row >> 3) & 1); }
+
 __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
@@ -101,14 +107,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
   ar = ar < M ? ar : M - 1;
   const uint8_t* pcode = co ? B + (n0 + crow) * kb : A + ar * kb;
   const int w_base = co * kWOffset + crow * kRowBytes;
-  const int w_swz = ((crow >> 1) & 7) ^ (co << 2);
-  const int s_rd = kScaleOffset + co * (kBM * 16) + crow * 16;
+  const int w_swz = swz(crow) ^ (co << 2);
 
-  // Scale chunk loads: wave w fetches 64 rows (16 bytes each) of operand w / 4.
-  const int srow = (wave & 3) * 64 + lane;
-  int64_t sr = (wave < 4 ? m0 : n0) + srow;
-  if (wave < 4) sr = sr < M ? sr : M - 1;
-  const uint8_t* pscale = (wave < 4 ? As : Bs) + sr * ks;
+  // Scale chunks: the thread fetches the 16 scale bytes (four stages) of its own row and operand
+  // into LDS slot tid (global_load_lds puts lane l of wave w at w * 1024 + 16 l) and reads them
+  // back from there.
+  const uint8_t* pscale = co ? Bs + (n0 + crow) * ks : As + ar * ks;
   auto load_scales = [&](int buf, int64_t c) {
     __builtin_amdgcn_global_load_lds((gvoid_t*)(pscale + c * 16),
                                      (lvoid_t*)(lds + kScaleOffset + buf * kScaleChunk +
@@ -117,8 +121,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
   };
 
   // Fragment reads: step t (elements [16t, 16t + 16) of a stage) of the lane's row is chunk
-  // 2t + h; fragments i (j) of the wave are 32 rows apart.
-  const int x = (r32 >> 1) & 7;
+  // 2t + h; fragments i (j) of the wave are 32 rows apart (same low row bits, same swizzle).
+  const int x = swz(r32);
   int ra[4], rb[4];
 #pragma unroll
   for (int t = 0; t < 4; ++t) {
@@ -137,9 +141,12 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
     *reinterpret_cast<f16x8_t*>(lds + buf * kOpBytes + w_base + 16 * (d ^ w_swz)) =
         dequant8(w[d], f16x2_t{sc, sc});
   };
-  auto stage_scales = [&](int64_t st, f16x2_t& s01, f16x2_t& s23) {
-    const uint32_t v = *reinterpret_cast<const uint32_t*>(
-        lds + s_rd + ((st >> 2) & 1) * kScaleChunk + (st & 3) * 4);
+  // the thread's scale chunk of four stages, read back from LDS once per chunk
+  auto read_chunk = [&](int64_t c) {
+    return *reinterpret_cast<const u32x4_t*>(lds + kScaleOffset + (int)(c & 1) * kScaleChunk +
+                                             tid * 16);
+  };
+  auto stage_scales = [&](uint32_t v, f16x2_t& s01, f16x2_t& s23) {
     s01 = e4m3x2_to_f16x2(v & 0xFFFFu);
     s23 = e4m3x2_to_f16x2(v >> 16);
   };
@@ -164,9 +171,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
   gemm_lowrank_init<FM, FN>(acc, 1.0f / gsc, M, m_base, n_base, r32, h, D, up, r);
   wait_vmcnt<0>();
   barrier_lds();
+  u32x4_t sq = read_chunk(0);  // scales of stages 4c .. 4c + 3 (chunk c of the stage converted)
   {
     f16x2_t s01, s23;
-    stage_scales(0, s01, s23);
+    stage_scales(sq[0], s01, s23);
     const uint32_t* w = reinterpret_cast<const uint32_t*>(g0);
 #pragma unroll
     for (int d = 0; d < 8; ++d) convert(w, s01, s23, 0, d);
@@ -186,8 +194,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
   auto iteration = [&](auto phase, int64_t s, const uint32_t* w, u32x4_t (&refill)[4]) {
     constexpr int ph = decltype(phase)::value;  // s % 4
     constexpr int p = ph & 1;
+    // stage s+1 opens chunk s/4 + 1 at phase 3; that chunk landed before the previous barrier
+    if (ph == 3) sq = read_chunk(s / 4 + 1);
     f16x2_t s01, s23;
-    stage_scales(s + 1, s01, s23);
+    stage_scales(sq[(ph + 1) & 3], s01, s23);
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       // next step's fragments are requested before this step's MFMAs (the scheduling barriers
