@@ -84,7 +84,7 @@ constexpr int gemm_store_bytes() {
 // Store y = bf16(gsc·acc (+ core_out[cube(m)][n])) of the wave's tile at (m_base, n_base).  The
 // elements go one by one, in the accumulator layout, into the wave's own LDS region (row-major,
 // 64 FN bytes per row), and come back as 16-byte row pieces that are written to Y with
-// full-width stores, eight lanes per 128-byte row segment.  Piece c of staged row R sits at
+// full-width stores, 4 FN lanes per row segment.  Piece c of staged row R sits at
 // c ^ (4 ((R >> 2) & 1)), so the two half-waves of one element write (rows 4 apart) use
 // different banks.  Rows past M are not stored.  Y rows must be 16-byte aligned (ldy % 8 == 0).
 template <int FM, int FN>
@@ -94,7 +94,7 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[FM][FN], float 
                                            const float* __restrict__ core_out,
                                            const int32_t* __restrict__ row_to_cube,
                                            uint16_t* __restrict__ Y, int64_t ldy) {
-  static_assert(FN == 2, "row pieces assume 64-column wave tiles");
+  static_assert(FN >= 2, "the piece swizzle needs at least 8 pieces per staged row");
   constexpr int kRowB = FN * 64;
   const int r32 = lane & 31, h = lane >> 5;
 #pragma unroll

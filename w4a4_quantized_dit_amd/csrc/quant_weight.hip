@@ -20,9 +20,11 @@ namespace svdq {
 namespace {
 
 constexpr int kThreads = 256;
-constexpr int kTileRows = 128;       // weight rows per tile
-constexpr int kTileCols = 128;       // channels per tile
-constexpr int kRowsPerThread = 4;    // rows of one thread (a 16-channel block each)
+constexpr int kTileRows = 128;  // weight rows per tile
+constexpr int kTileCols = 128;  // channels per tile
+constexpr int kRankChunk = 32;  // ranks staged in LDS at a time
+
+typedef __attribute__((ext_vector_type(2))) double f64x2_t;
 
 // MODE 0: max|R32| over the whole weight (one atomic per block)
 // MODE 1: NVFP4 codes and scales with g = amax / 2688
@@ -36,80 +38,124 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
                                                     float* __restrict__ amax_io,
                                                     uint8_t* __restrict__ codes,
                                                     void* __restrict__ scales) {
-  // dynamic LDS: lora_down slice fp32 [r][128] | lora_up transposed bf16 [r][128] | λ [128]
+  // dynamic LDS: down fp64 [chunk][128] (pieces rotated) | -up fp64 [chunk][128] | lambda [128]
   extern __shared__ __attribute__((aligned(16))) uint8_t s_dyn[];
-  float* s_down = reinterpret_cast<float*>(s_dyn);
-  uint16_t* s_upT = reinterpret_cast<uint16_t*>(s_dyn + (size_t)r * kTileCols * 4);
-  float* s_lam = reinterpret_cast<float*>(s_dyn + (size_t)r * kTileCols * 6);
+  double* s_down = reinterpret_cast<double*>(s_dyn);
+  double* s_up = reinterpret_cast<double*>(s_dyn + kRankChunk * kTileCols * 8);
+  float* s_lam = reinterpret_cast<float*>(s_dyn + 2 * kRankChunk * kTileCols * 8);
   __shared__ float s_red[kThreads / 64];
 
   const int tid = threadIdx.x;
   const int64_t tiles_k = K / kTileCols;
   const int64_t n0 = (int64_t)(blockIdx.x / tiles_k) * kTileRows;
   const int64_t c0 = (int64_t)(blockIdx.x % tiles_k) * kTileCols;
-  const int cb = tid & 7, rg = tid >> 3;  // 16-channel block, group of 4 rows
+  const int cb = tid & 15, rg = tid >> 4;  // channels 8 cb .. 8 cb + 7, rows 8 rg .. 8 rg + 7
 
-  // stage lora_down[:, c0:c0+128] as fp32: piece p = rank p / 16, channels 8·(p % 16) .. +8
-  for (int p = tid; p < r * (kTileCols / 8); p += kThreads) {
-    const int i = p >> 4, part = p & 15;
-    const u32x4_t v = *reinterpret_cast<const u32x4_t*>(down + (int64_t)i * K + c0 + 8 * part);
-    float* dst = s_down + i * kTileCols + 8 * part;
-    *reinterpret_cast<f32x4_t*>(dst) =
-        f32x4_t{bf16_lo(v[0]), bf16_hi(v[0]), bf16_lo(v[1]), bf16_hi(v[1])};
-    *reinterpret_cast<f32x4_t*>(dst + 4) =
-        f32x4_t{bf16_lo(v[2]), bf16_hi(v[2]), bf16_lo(v[3]), bf16_hi(v[3])};
-  }
-  // stage lora_up[n0:n0+128, :] transposed: element (row, i) -> s_upT[i][row] (rows past N: 0)
-  for (int e = tid; e < kTileRows * r; e += kThreads) {
-    const int row = e / r, i = e % r;
-    const int64_t n = n0 + row;
-    s_upT[i * kTileRows + row] = n < N ? up[n * r + i] : (uint16_t)0;
-  }
-  if (tid < kTileCols) s_lam[tid] = lambda ? lambda[c0 + tid] : 1.0f;
-  __syncthreads();
-
-  // initial values λ_k·W[n, k] (exact in fp64); rows past N read row N-1 and are never used
-  double R[kRowsPerThread][16];
-  const int64_t kc = c0 + 16 * cb;
+  // A rank chunk is staged from 16-byte pieces, two per thread per factor: down piece p = rank
+  // p / 16, channels 8 (p % 16) .. +8; up piece p = row p % 128, ranks 8 (p / 128) .. +8.
+  // The pieces of the next chunk are loaded into registers while the current one is applied.
+  auto load_chunk = [&](int i0, int rc, u32x4_t (&pd)[2], u32x4_t (&pu)[2]) {
 #pragma unroll
-  for (int j = 0; j < kRowsPerThread; ++j) {
-    int64_t n = n0 + kRowsPerThread * rg + j;
+    for (int k = 0; k < 2; ++k) {
+      const int p = tid + kThreads * k;
+      pd[k] = u32x4_t{0u, 0u, 0u, 0u};
+      pu[k] = u32x4_t{0u, 0u, 0u, 0u};
+      if (p < rc * 16)
+        pd[k] = *reinterpret_cast<const u32x4_t*>(down + (int64_t)(i0 + p / 16) * K + c0 +
+                                                  8 * (p % 16));
+      const int row = p % kTileRows, k8 = p / kTileRows;
+      if (8 * k8 < rc && n0 + row < N)
+        pu[k] = *reinterpret_cast<const u32x4_t*>(up + (n0 + row) * r + i0 + 8 * k8);
+    }
+  };
+  auto store_chunk = [&](int rc, const u32x4_t (&pd)[2], const u32x4_t (&pu)[2]) {
+#pragma unroll
+    for (int k = 0; k < 2; ++k) {
+      const int p = tid + kThreads * k;
+      if (p < rc * 16) {
+        const int i = p / 16, g = p % 16;
+#pragma unroll
+        for (int q = 0; q < 4; ++q)
+          *reinterpret_cast<f64x2_t*>(s_down + i * kTileCols + g * 8 + ((q + (g >> 2)) & 3) * 2) =
+              f64x2_t{(double)bf16_lo(pd[k][q]), (double)bf16_hi(pd[k][q])};
+      }
+      const int row = p % kTileRows, k8 = p / kTileRows;
+      if (8 * k8 < rc) {
+#pragma unroll
+        for (int q = 0; q < 4; ++q) {
+          s_up[(8 * k8 + 2 * q) * kTileRows + row] = -(double)bf16_lo(pu[k][q]);
+          s_up[(8 * k8 + 2 * q + 1) * kTileRows + row] = -(double)bf16_hi(pu[k][q]);
+        }
+      }
+    }
+  };
+
+  // W tile and the first chunk in flight together; lambda; then the initial values
+  // lambda_k W[n, k] (exact in fp64).  Rows past N read row N-1 and are never stored.
+  const int64_t kc = c0 + 8 * cb;
+  u32x4_t wt[8];
+#pragma unroll
+  for (int j = 0; j < 8; ++j) {
+    int64_t n = n0 + 8 * rg + j;
     n = n < N ? n : N - 1;
-    const u32x4_t* wp = reinterpret_cast<const u32x4_t*>(W + n * ldw + kc);
-    const u32x4_t w0 = wp[0], w1 = wp[1];
-    const uint32_t w[8] = {w0[0], w0[1], w0[2], w0[3], w1[0], w1[1], w1[2], w1[3]};
+    wt[j] = *reinterpret_cast<const u32x4_t*>(W + n * ldw + kc);
+  }
+  u32x4_t pd[2], pu[2];
+  int rc = r < kRankChunk ? r : kRankChunk;
+  if (r > 0) load_chunk(0, rc, pd, pu);
+  if (tid < kTileCols) s_lam[tid] = lambda ? lambda[c0 + tid] : 1.0f;
+  if (r > 0) store_chunk(rc, pd, pu);
+  __syncthreads();
+  double R[8][8];
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      R[j][2 * e] = (double)s_lam[16 * cb + 2 * e] * (double)bf16_lo(w[e]);
-      R[j][2 * e + 1] = (double)s_lam[16 * cb + 2 * e + 1] * (double)bf16_hi(w[e]);
+  for (int j = 0; j < 8; ++j) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      R[j][2 * e] = (double)s_lam[8 * cb + 2 * e] * (double)bf16_lo(wt[j][e]);
+      R[j][2 * e + 1] = (double)s_lam[8 * cb + 2 * e + 1] * (double)bf16_hi(wt[j][e]);
     }
   }
-  // R ← R − up·down, rank by rank in ascending order
-  for (int i = 0; i < r; ++i) {
-    const f32x4_t* dp = reinterpret_cast<const f32x4_t*>(s_down + i * kTileCols + 16 * cb);
-    double d[16];
+
+  // R <- R - up·down, rank by rank in ascending order.  The thread's 16-byte piece q of a
+  // staged down row sits at piece (q + cb / 4) % 4 of its 64 bytes.
+  const int rot = cb >> 2;
+  for (int i0 = 0; i0 < r; i0 += kRankChunk) {
+    const int next = i0 + kRankChunk;
+    const int rn = r - next < kRankChunk ? r - next : kRankChunk;
+    if (next < r) load_chunk(next, rn, pd, pu);
+    for (int i = 0; i < rc; ++i) {
+      const double* dp = s_down + i * kTileCols + cb * 8;
+      const double* upp = s_up + i * kTileRows + rg * 8;
+      double d[8], u[8];
 #pragma unroll
-    for (int e4 = 0; e4 < 4; ++e4) {
-      const f32x4_t v = dp[e4];
+      for (int q = 0; q < 4; ++q) {
+        const f64x2_t v = *reinterpret_cast<const f64x2_t*>(dp + ((q + rot) & 3) * 2);
+        d[2 * q] = v[0];
+        d[2 * q + 1] = v[1];
+        const f64x2_t w = *reinterpret_cast<const f64x2_t*>(upp + 2 * q);
+        u[2 * q] = w[0];
+        u[2 * q + 1] = w[1];
+      }
 #pragma unroll
-      for (int e = 0; e < 4; ++e) d[4 * e4 + e] = (double)v[e];
+      for (int j = 0; j < 8; ++j)
+#pragma unroll
+        for (int e = 0; e < 8; ++e) R[j][e] = __builtin_fma(u[j], d[e], R[j][e]);
     }
-    const uint2 uw = *reinterpret_cast<const uint2*>(s_upT + i * kTileRows + kRowsPerThread * rg);
-    const double u[4] = {-(double)bf16_lo(uw.x), -(double)bf16_hi(uw.x), -(double)bf16_lo(uw.y),
-                         -(double)bf16_hi(uw.y)};
-#pragma unroll
-    for (int j = 0; j < kRowsPerThread; ++j)
-#pragma unroll
-      for (int e = 0; e < 16; ++e) R[j][e] = __builtin_fma(u[j], d[e], R[j][e]);
+    if (next < r) {
+      __syncthreads();  // every thread is done with this chunk
+      store_chunk(rn, pd, pu);
+      __syncthreads();
+      rc = rn;
+    }
   }
 
   if (MODE == 0) {
     float m = 0.0f;
 #pragma unroll
-    for (int j = 0; j < kRowsPerThread; ++j) {
-      if (n0 + kRowsPerThread * rg + j < N) {
+    for (int j = 0; j < 8; ++j) {
+      if (n0 + 8 * rg + j < N) {
 #pragma unroll
-        for (int e = 0; e < 16; ++e) m = fmaxf(m, fabsf((float)R[j][e]));
+        for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)R[j][e]));
       }
     }
     for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
@@ -121,56 +167,55 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
       if (b > 0.0f) atomic_max_pos(amax_io, b);
     }
   } else if (MODE == 1) {
+    // an NVFP4 block of 16 channels is held by lanes cb = 2b, 2b + 1
     const float amax = amax_io[0];
     const float g = amax == 0.0f ? 1.0f : amax / 2688.0f;
     const float d6 = 6.0f * g;
 #pragma unroll
-    for (int j = 0; j < kRowsPerThread; ++j) {
-      const int64_t n = n0 + kRowsPerThread * rg + j;
-      float x[16];
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + 8 * rg + j;
+      float x[8];
       float a = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < 8; ++e) {
         x[e] = (float)R[j][e];
         a = fmaxf(a, fabsf(x[e]));
       }
+      a = fmaxf(a, __shfl_xor(a, 1));
       float inv;
       const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
-      float y[16];
+      float y[8];
 #pragma unroll
-      for (int e = 0; e < 16; ++e) y[e] = x[e] * inv;
+      for (int e = 0; e < 8; ++e) y[e] = x[e] * inv;
       if (n < N) {
-        *reinterpret_cast<uint2*>(codes + n * (K / 2) + kc / 2) =
-            uint2{e2m1_pack8(y), e2m1_pack8(y + 8)};
-        reinterpret_cast<uint8_t*>(scales)[n * (K / 16) + kc / 16] = (uint8_t)sc;
+        *reinterpret_cast<uint32_t*>(codes + n * (K / 2) + kc / 2) = e2m1_pack8(y);
+        if ((cb & 1) == 0) reinterpret_cast<uint8_t*>(scales)[n * (K / 16) + kc / 16] = (uint8_t)sc;
       }
     }
   } else {
-    // int4-g64: the group's four 16-channel blocks are held by lanes cb = 4g .. 4g+3
+    // an int4-g64 group is held by lanes cb = 8g .. 8g + 7
 #pragma unroll
-    for (int j = 0; j < kRowsPerThread; ++j) {
-      const int64_t n = n0 + kRowsPerThread * rg + j;
-      float x[16];
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + 8 * rg + j;
+      float x[8];
       float a = 0.0f;
 #pragma unroll
-      for (int e = 0; e < 16; ++e) {
+      for (int e = 0; e < 8; ++e) {
         x[e] = (float)R[j][e];
         a = fmaxf(a, fabsf(x[e]));
       }
       a = fmaxf(a, __shfl_xor(a, 1));
       a = fmaxf(a, __shfl_xor(a, 2));
+      a = fmaxf(a, __shfl_xor(a, 4));
       const __half s = __float2half_rn(a / 7.0f);
       const float sf = __half2float(s);
       const float inv = sf != 0.0f ? 1.0f / sf : 0.0f;
-      uint32_t w0 = 0, w1 = 0;
+      uint32_t w0 = 0;
 #pragma unroll
-      for (int e = 0; e < 8; ++e) {
-        w0 |= int4_code(x[e] * inv) << (4 * e);
-        w1 |= int4_code(x[8 + e] * inv) << (4 * e);
-      }
+      for (int e = 0; e < 8; ++e) w0 |= int4_code(x[e] * inv) << (4 * e);
       if (n < N) {
-        *reinterpret_cast<uint2*>(codes + n * (K / 2) + kc / 2) = uint2{w0, w1};
-        if ((cb & 3) == 0) reinterpret_cast<__half*>(scales)[n * (K / 64) + kc / 64] = s;
+        *reinterpret_cast<uint32_t*>(codes + n * (K / 2) + kc / 2) = w0;
+        if ((cb & 7) == 0) reinterpret_cast<__half*>(scales)[n * (K / 64) + kc / 64] = s;
       }
     }
   }
@@ -183,7 +228,8 @@ __global__ void k_amax_to_g(float* t) {
 
 __global__ void k_zero1(float* t) { t[0] = 0.0f; }
 
-size_t lds_bytes(int64_t r) { return (size_t)r * kTileCols * 6 + kTileCols * 4; }
+// fixed layout: a full rank chunk of down and up values (fp64), then lambda
+size_t lds_bytes(int64_t) { return (size_t)kRankChunk * kTileCols * 16 + kTileCols * 4; }
 
 template <int MODE>
 hipError_t allow_lds(size_t bytes) {
