@@ -37,8 +37,9 @@ PEAK_I8_TOPS = 5000.0         # MI355X dense int8 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
 WORKLOADS = {"attn": 1, "mlp-up-int4": 2, "delta": 4}
 # Sources of each GEMM kernel: the PMC traffic figure is valid only for the source it was taken on.
-GEMM_SOURCES = {"attn": ("gemm_w4a4.hip", "device.h"), "mlp-up-int4": ("gemm_int4.hip", "device.h"),
-                "delta": ("gemm_w4a4.hip", "device.h")}
+GEMM_SOURCES = {"attn": ("gemm_w4a4.hip", "gemm_common.h", "device.h"),
+                "mlp-up-int4": ("gemm_int4.hip", "gemm_common.h", "device.h"),
+                "delta": ("gemm_w4a4.hip", "gemm_common.h", "device.h")}
 
 
 def source_digest(files):
