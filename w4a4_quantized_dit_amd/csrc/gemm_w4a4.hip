@@ -4,17 +4,16 @@
 // "DeltaQuant on MiniMax-H3").
 //
 // NVFP4 operands (E2M1 code × E4M3 block scale) need at most 6 significant bits and lie in
-// [2^-10, 2688], so they are EXACT in fp16.  The kernel dequantises both operands to fp16 in
-// registers (v_cvt_scalef32_pk_f16_fp4 with unit scale, then a packed fp16 multiply by the
-// block scale) and runs v_mfma_f32_32x32x16_f16; every product is exact in the fp32
-// accumulator, and the two tensor scales are applied once in the epilogue.  The hardware
-// block-scaled FP4 MFMA takes power-of-two (E8M0) scales per 32 elements, which cannot carry an
-// E4M3 scale per 16 exactly, so it is not used for this format.
+// [2^-10, 2688], so they are EXACT in fp16.  The kernel dequantises both operands to fp16
+// (v_cvt_scalef32_pk_f16_fp4 with unit scale, then a packed fp16 multiply by the block scale)
+// and runs v_mfma_f32_32x32x16_f16; every product is exact in the fp32 accumulator, and the two
+// tensor scales are applied once at the store.  The hardware block-scaled FP4 MFMA takes
+// power-of-two (E8M0) scales per 32 elements, which cannot carry an E4M3 scale per 16 exactly,
+// so it is not used for this format.
 //
-// K mapping: within each 64-element half of a stage, lane (row = lane % 32, h = lane / 32) holds
-// elements [32h, 32h + 32) of its row (16 contiguous bytes of codes).  MFMA step t (0..3) takes the lane's
-// elements [8t, 8t + 8) as its k-slots; the weight operand uses the identical mapping, so every
-// product pairs equal K indices.
+// K mapping: MFMA step t of a 64-element stage covers elements [16t, 16t + 16); lane (row =
+// lane % 32, h = lane / 32) supplies elements [16t + 8h, 16t + 8h + 8) of its row, for A and W
+// alike, so every product pairs equal K indices.
 #include "device.h"
 #include "gemm_common.h"
 #include "launch.h"
