@@ -31,7 +31,8 @@ typedef __attribute__((ext_vector_type(8))) uint16_t u16x8;
 // ax[mu*K + k] = max(ax, max over the chunk's rows of |X[row, k]|) for the three modality
 // segments, and aw[k] = max(aw, max |W[row, k]|) for the fourth (W's rows).  bf16 magnitudes
 // compare as unsigned 15-bit patterns, so the max is taken on integers; the four waves of a
-// block take interleaved rows and combine through LDS before one atomic per channel.
+// block take interleaved rows and combine through LDS before one atomic per channel.  The rows
+// are streamed once: nontemporal loads.
 __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint16_t* __restrict__ X,
                                                            int64_t ldx,
                                                            const uint16_t* __restrict__ W,
@@ -61,7 +62,8 @@ __global__ __launch_bounds__(kAbsmaxThreads) void k_absmax(const uint16_t* __res
     for (; r + (kUnroll - 1) * kAbsmaxWaves < r1; r += kUnroll * kAbsmaxWaves) {
       u16x8 v[kUnroll];
 #pragma unroll
-      for (int u = 0; u < kUnroll; ++u) v[u] = *(const u16x8*)(p + (r + u * kAbsmaxWaves) * ld);
+      for (int u = 0; u < kUnroll; ++u)
+        v[u] = __builtin_nontemporal_load((const u16x8*)(p + (r + u * kAbsmaxWaves) * ld));
 #pragma unroll
       for (int u = 0; u < kUnroll; ++u) m = __builtin_elementwise_max(m, v[u] & mask);
     }

@@ -68,21 +68,23 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
 
   // coalesced X loads: instruction i covers rows 2i, 2i+1 of the wave, lane piece = lane % 32
   // (rows past M read row M-1; their results are never stored)
-  const uint16_t* xg[8];
+  // (element offsets from the block's first row fit 32 bits: 64 rows of at most ldx each)
+  const uint16_t* xblk = X + (int64_t)blockIdx.x * kRowsPerBlock * ldx;
+  uint32_t xo[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int64_t xrow = row0 + 2 * i + (lane >> 5);
     xrow = xrow < M ? xrow : M - 1;
-    xg[i] = X + xrow * ldx + 8 * (lane & 31);
+    xo[i] = (uint32_t)((xrow - (int64_t)blockIdx.x * kRowsPerBlock) * ldx + 8 * (lane & 31));
   }
   // L1 staging within the K group: piece p = rank p / 32, channels 8 * (p % 32) .. +8 (ranks
   // past r read rank r-1 and are zeroed)
-  const uint16_t* lg[kLPieces > 0 ? kLPieces : 1];
+  uint32_t lo[kLPieces > 0 ? kLPieces : 1];
 #pragma unroll
   for (int u = 0; u < kLPieces; ++u) {
     const int p = gtid + kGroupThreads * u;
     const int n = p >> 5;
-    lg[u] = down + (int64_t)(n < r ? n : r - 1) * K + 8 * (p & 31);
+    lo[u] = (uint32_t)((n < r ? n : r - 1) * K + 8 * (p & 31));
   }
 
   f32x4_t acc[NTc];
@@ -94,9 +96,10 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
   if (ks < nchunk) {
     const int64_t k0 = (int64_t)ks * kChunk;
 #pragma unroll
-    for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + k0);
+    for (int i = 0; i < 8; ++i)
+      xr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xblk + k0 + xo[i]));
 #pragma unroll
-    for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + k0);
+    for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(down + k0 + lo[u]);
   }
   __syncthreads();  // s_inv complete
 
@@ -120,9 +123,10 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
     if (kc + kSplit < nchunk) {
       const int64_t kn = (kc + kSplit) * kChunk;
 #pragma unroll
-      for (int i = 0; i < 8; ++i) xr[i] = *reinterpret_cast<const u32x4_t*>(xg[i] + kn);
+      for (int i = 0; i < 8; ++i)
+        xr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xblk + kn + xo[i]));
 #pragma unroll
-      for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(lg[u] + kn);
+      for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(down + kn + lo[u]);
     }
     if (has) {
       const int64_t kb = kc * kChunk + 64 * q;  // first channel of this lane
@@ -132,7 +136,7 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
         const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&s_x[wave][rl * kPitch + 64 * q + 8 * i]);
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
-          const uint32_t w = valid ? v[c] : 0u;
+          const uint32_t w = v[c];
           x[8 * i + 2 * c] = bf16_lo(w) * s_inv[kb + 8 * i + 2 * c];
           x[8 * i + 2 * c + 1] = bf16_hi(w) * s_inv[kb + 8 * i + 2 * c + 1];
         }
@@ -146,7 +150,7 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
           float a = 0.0f;
 #pragma unroll
           for (int j = 0; j < 16; ++j) a = fmaxf(a, fabsf(x[16 * b + j]));
-          nsat += (a > amax) ? 1u : 0u;
+          nsat += (valid && a > amax) ? 1u : 0u;
           float inv;
           const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
           float y[16];
