@@ -10,8 +10,8 @@ namespace {
 
 constexpr int kAbsmaxWaves = 4;
 constexpr int kAbsmaxThreads = 64 * kAbsmaxWaves;  // a block covers 512 channels (8 per lane)
-constexpr int kAbsmaxRows = 128;                    // rows per block (never straddling a segment)
-constexpr int kUnroll = 8;                          // loads in flight per lane
+constexpr int kAbsmaxRows = 512;                    // rows per block (never straddling a segment)
+constexpr int kUnroll = 16;                         // loads in flight per lane
 
 // Row chunks of one launch: X's three modality segments, then (optionally) W as a fourth.
 struct SegChunks {
