@@ -2,7 +2,7 @@
 
 TEST INFRASTRUCTURE ONLY.  This package is a plain, slow, obviously correct CPU statement of
 what the GPU path computes: smoothing, λ calibration, truncated SVD, NVFP4 / int4
-round-to-nearest-even quantisation, a float64 GEMM, per-modality scoring and the DeltaQuant
+round-to-nearest-even quantisation, the MX (E8M0 per 32) variant, a float64 GEMM, per-modality scoring and the DeltaQuant
 (cube core + delta) variant.  Only the tests, the smoke check and the CPU-baseline leg of the
 benchmark may import it.  It shares no code with the HIP library and imports nothing from it.
 
@@ -14,6 +14,8 @@ Sources (cited by page title and section):
     per-modality relative L2).
   * "MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph (outliers absorbed
     by a 16-bit low-rank branch, 4-bit residual, activations quantised per token at run time).
+  * "MiniMax-H3 — MXFP8 (weight-quantized, vLLM-Omni native layout)", section "Quant format"
+    (E4M3 elements, E8M0 scale per 32, round to nearest, dynamic activations): the MX variant.
   * "DeltaQuant on MiniMax-H3", sections "Why DeltaQuant does not beat SVDQuant here" (cube
     core + delta), "The audio win has a mechanism" (1-D cubes of consecutive rows for
     non-video rows), "The activation scale bound held" (|x − core| ≤ 2·max|x|, saturated
@@ -24,4 +26,4 @@ Every reading taken where the pages are silent is listed in the module that take
 Float32 steps use numpy float32 operations (each one IEEE round-to-nearest-even); exact
 steps use float64.
 """
-from . import formats, quant, calib, svd, gemm, delta, score, layer  # noqa: F401
+from . import formats, quant, mx, calib, svd, gemm, delta, score, layer  # noqa: F401

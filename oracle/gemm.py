@@ -16,6 +16,7 @@ import numpy as np
 
 from .formats import bf16_bits_to_f32, bf16_rne, bf16_round_f32
 from .quant import nvfp4_dequantize, int4_dequantize
+from .mx import mx_dequantize
 
 
 def lowrank_down(xhat32, lora_down_bits):
@@ -53,6 +54,14 @@ def linear_int4(a_codes, a_scales16, w_codes, w_scales16, D, lora_up_bits):
     """int4-g64 W4A4 layer output: (Y64, Y bf16 bits)."""
     A = int4_dequantize(a_codes, a_scales16)
     W = int4_dequantize(w_codes, w_scales16)
+    y64 = linear_f64(A, W, D, lora_up_bits)
+    return y64, bf16_rne(y64)
+
+
+def linear_mx(a_codes, a_scales, w_codes, w_scales, D, lora_up_bits, elem):
+    """MX (MXFP4 W4A4 or MXFP8 W8A8) layer output: (Y64, Y bf16 bits)."""
+    A = mx_dequantize(a_codes, a_scales, elem)
+    W = mx_dequantize(w_codes, w_scales, elem)
     y64 = linear_f64(A, W, D, lora_up_bits)
     return y64, bf16_rne(y64)
 
