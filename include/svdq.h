@@ -55,9 +55,21 @@ typedef enum svdq_status {
 } svdq_status;
 
 typedef enum svdq_format {
-  SVDQ_NVFP4 = 0,    /* E2M1 codes, E4M3 scale per 16 along K, fp32 tensor scale */
-  SVDQ_INT4_G64 = 1  /* symmetric int4 codes, fp16 scale per 64 along K */
+  SVDQ_NVFP4 = 0,     /* E2M1 codes, E4M3 scale per 16 along K, fp32 tensor scale */
+  SVDQ_INT4_G64 = 1,  /* symmetric int4 codes, fp16 scale per 64 along K */
+  SVDQ_MXFP4 = 2,     /* E2M1 codes, E8M0 scale per 32 along K (W4A4 MX variant) */
+  SVDQ_MXFP8 = 3      /* E4M3 codes, E8M0 scale per 32 along K (W8A8 MX variant) */
 } svdq_format;
+
+/*
+ * MX formats ("MiniMax-H3 — MXFP8 (weight-quantized, vLLM-Omni native layout)", section "Quant
+ * format": E8M0 block scales per 32, round to nearest, dynamic activations).  Per block of 32
+ * along K: a = max|x|; e = floor(log2 a) − emax (emax 2 for E2M1, 8 for E4M3; a == 0 gives
+ * −127), clamped to [−127, 127]; scale byte = e + 127; code = element(x · 2^−e), nearest even,
+ * saturating, sign bit = sign of x.  MXFP4 codes are packed two per byte (even element in the
+ * low nibble, [rows, K/2]); MXFP8 codes are one byte per element ([rows, K]).  Scales are
+ * [rows, K/32] bytes.  No tensor scale.
+ */
 
 /* Modality bits of a calibration mask (rows are packed text | video | audio). */
 #define SVDQ_MOD_TEXT 1u
@@ -104,9 +116,11 @@ svdq_status svdq_calibrate_lambda(const uint16_t* X, int64_t M, int64_t K, int64
  *     NVFP4: tensor amax = max |R32|; g = amax/2688; per 16-block s = E4M3(max|x| / (6g)),
  *            codes = E2M1(x · 1/(s·g)), round to nearest even, satfinite.
  *     INT4_G64: s = fp16(max|x| / 7); codes = clamp(rint(x · 1/s), −8, 7).
+ *     MXFP4 / MXFP8: per 32-block as described at svdq_format.
  * lambda may be NULL (λ = 1).  lora_down [r, K] and lora_up [N, r] are bf16 (ignored when
- * r == 0).  Outputs: codes [N, K/2]; scales ([N, K/16] E4M3 bytes or [N, K/64] fp16);
- * tensor_scale (device float[1], g; required for NVFP4, ignored for INT4_G64).  Bit-exact.
+ * r == 0).  Outputs: codes ([N, K/2], MXFP8 [N, K]); scales ([N, K/16] E4M3 bytes, [N, K/64]
+ * fp16, or [N, K/32] E8M0 bytes); tensor_scale (device float[1], g; required for NVFP4,
+ * ignored otherwise).  Bit-exact.
  */
 svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                                  const float* lambda, const uint16_t* lora_down,
@@ -122,11 +136,14 @@ svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t 
  *          static amax from svdq_calibrate_lambda; NULL selects a dynamic pre-pass computing
  *          max |X̂| over all M rows.  tensor_scale (device float[1]) receives g_a.
  *   INT4_G64: per 64-group scales; tensor_scale and act_amax are ignored.
+ *   MXFP4 / MXFP8: per 32-block E8M0 scales (see svdq_format); tensor_scale, act_amax and
+ *          sat_count are ignored.
  *   D = bf16(X̂) · lora_downᵀ         [M, r] fp32: products of bf16 operands accumulated in
  *                                     fp32 and NOT rounded to bf16 (D may be NULL iff r == 0)
  * sat_count (nullable, device uint32[1]): the number of NVFP4 blocks whose absmax exceeds the
  * tensor amax is ADDED to it (the caller zeroes it).
- * Outputs: codes [M, K/2], scales, tensor_scale, D.  Codes and scales bit-exact.
+ * Outputs: codes [M, K/2] (MXFP8: [M, K]), scales, tensor_scale, D.  Codes and scales
+ * bit-exact.
  */
 svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, int64_t K,
                                         int64_t ldx, const float* lambda, const float* act_amax,
@@ -139,6 +156,8 @@ svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, i
  *
  *   NVFP4:    Y = bf16( g_a·g_w · Σ_k (c_a·s_a)(c_w·s_w) + D·lora_upᵀ [+ core_out[cube(m)]] )
  *   INT4_G64: Y = bf16( Σ_groups s_a·s_w · Σ_k c_a·c_w + D·lora_upᵀ )
+ *   MXFP4 / MXFP8: Y = bf16( Σ_blocks 2^(e_a + e_w) · Σ_k c_a·c_w + D·lora_upᵀ ) on the
+ *            hardware block-scaled MFMA (v_mfma_scale_f32_32x32x64_f8f6f4)
  * a_codes/a_scales [M, ...] from svdq_quant_act_lowrank_down, w_codes/w_scales [N, ...] from
  * svdq_quantize_weight; g_a / g_w device float[1] (NVFP4 only).  D [M, r] fp32 (from the
  * activation kernel), lora_up [N, r] bf16.

@@ -13,7 +13,7 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(HERE, "libsvdq.so")
 HEADER = os.path.join(os.path.dirname(HERE), "include", "svdq.h")
 
-NVFP4, INT4_G64 = 0, 1
+NVFP4, INT4_G64, MXFP4, MXFP8 = 0, 1, 2, 3
 
 _c_p = ctypes.c_void_p
 _i64 = ctypes.c_int64
@@ -127,7 +127,17 @@ def _bf16():
 
 def _scale_dtype(fmt):
     torch = _torch()
-    return torch.uint8 if fmt == NVFP4 else torch.float16
+    return torch.float16 if fmt == INT4_G64 else torch.uint8
+
+
+def _block(fmt):
+    """Elements per scale along K."""
+    return {NVFP4: 16, INT4_G64: 64, MXFP4: 32, MXFP8: 32}[int(fmt)]
+
+
+def _code_bytes(fmt, rows, K):
+    """Bytes of codes for rows x K elements (MXFP8: one per element, else two per byte)."""
+    return rows * K if int(fmt) == MXFP8 else rows * K // 2
 
 
 # ------------------------------------------------------------------------------------------
@@ -155,12 +165,12 @@ def svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, tens
     """Residual weight quantisation; W [N, K] bf16; outputs codes [N, K/2] u8, scales, g_w."""
     torch = _torch()
     N, K = W.shape
-    blk = 16 if fmt == NVFP4 else 64
+    blk = _block(fmt)
     _check(load().svdq_quantize_weight(
         int(fmt), _ptr(W, _bf16(), "W"), N, K, W.stride(0), _ptr(lam, torch.float32, "lambda", K),
         _ptr(lora_down if r else None, _bf16(), "lora_down", r * K),
         _ptr(lora_up if r else None, _bf16(), "lora_up", N * r), int(r),
-        _ptr(codes, torch.uint8, "codes", N * K // 2),
+        _ptr(codes, torch.uint8, "codes", _code_bytes(fmt, N, K)),
         _ptr(scales, _scale_dtype(fmt), "scales", N * K // blk),
         _ptr(tensor_scale, torch.float32, "tensor_scale", 1), _stream(stream)))
 
@@ -170,12 +180,12 @@ def svdq_quant_act_lowrank_down(fmt, X, lam, act_amax, lora_down, r, codes, scal
     """Activation quantisation + D = bf16(X̂)·L1 (fp32 [M, r]); X [M, K] bf16."""
     torch = _torch()
     M, K = X.shape
-    blk = 16 if fmt == NVFP4 else 64
+    blk = _block(fmt)
     _check(load().svdq_quant_act_lowrank_down(
         int(fmt), _ptr(X, _bf16(), "X"), M, K, X.stride(0),
         _ptr(lam, torch.float32, "lambda", K), _ptr(act_amax, torch.float32, "act_amax", 1),
         _ptr(lora_down if r else None, _bf16(), "lora_down", r * K), int(r),
-        _ptr(codes, torch.uint8, "codes", M * K // 2),
+        _ptr(codes, torch.uint8, "codes", _code_bytes(fmt, M, K)),
         _ptr(scales, _scale_dtype(fmt), "scales", M * K // blk),
         _ptr(tensor_scale, torch.float32, "tensor_scale", 1),
         _ptr(D if r else None, torch.float32, "D", M * r),
@@ -186,11 +196,11 @@ def svdq_w4a4_gemm(fmt, M, N, K, a_codes, a_scales, g_a, w_codes, w_scales, g_w,
                    Y, core_out=None, row_to_cube=None, stream=None):
     """Y [M, N] bf16 = W4A4 GEMM + D·L2 (+ core term)."""
     torch = _torch()
-    blk = 16 if fmt == NVFP4 else 64
+    blk = _block(fmt)
     _check(load().svdq_w4a4_gemm(
-        int(fmt), M, N, K, _ptr(a_codes, torch.uint8, "a_codes", M * K // 2),
+        int(fmt), M, N, K, _ptr(a_codes, torch.uint8, "a_codes", _code_bytes(fmt, M, K)),
         _ptr(a_scales, _scale_dtype(fmt), "a_scales", M * K // blk),
-        _ptr(g_a, torch.float32, "g_a", 1), _ptr(w_codes, torch.uint8, "w_codes", N * K // 2),
+        _ptr(g_a, torch.float32, "g_a", 1), _ptr(w_codes, torch.uint8, "w_codes", _code_bytes(fmt, N, K)),
         _ptr(w_scales, _scale_dtype(fmt), "w_scales", N * K // blk),
         _ptr(g_w, torch.float32, "g_w", 1), _ptr(D if r else None, torch.float32, "D", M * r),
         _ptr(lora_up if r else None, _bf16(), "lora_up", N * r), int(r),

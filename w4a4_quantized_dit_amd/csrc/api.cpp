@@ -73,7 +73,7 @@ svdq_status check_rank(const char* fn, int64_t r) {
 }
 
 svdq_status check_fmt(const char* fn, int fmt) {
-  if (fmt != SVDQ_NVFP4 && fmt != SVDQ_INT4_G64)
+  if (fmt != SVDQ_NVFP4 && fmt != SVDQ_INT4_G64 && fmt != SVDQ_MXFP4 && fmt != SVDQ_MXFP8)
     return fail(SVDQ_INVALID_ARG, "%s: unknown format %d", fn, fmt);
   return SVDQ_OK;
 }

@@ -58,6 +58,23 @@ __device__ __forceinline__ uint32_t e4m3_encode_pos(float q, float* val) {
   return (b >> 20) - (120u << 3);
 }
 
+// Signed E4M3 element code: the magnitude as above (satfinite at 448), bit 7 the sign of q
+// (also for zero).
+__device__ __forceinline__ uint32_t e4m3_encode_signed(float q) {
+  float v;
+  return e4m3_encode_pos(fabsf(q), &v) | ((__float_as_uint(q) >> 31) << 7);
+}
+
+// MX block exponent ("MiniMax-H3 — MXFP8 (weight-quantized, vLLM-Omni native layout)", section
+// "Quant format": E8M0 scale per 32; block exponent by the OCP microscaling rule):
+// floor(log2 a) − emax for a block maximum a > 0, −127 for a == 0, clamped to [−127, 127].
+// frexp's exponent is floor(log2 a) + 1, subnormal a included.
+__device__ __forceinline__ int mx_exponent(float a, int emax) {
+  if (a == 0.0f) return -127;
+  const int e = __builtin_amdgcn_frexp_expf(a) - 1 - emax;
+  return e < -127 ? -127 : (e > 127 ? 127 : e);
+}
+
 // NVFP4 block scale: q = a / d6, s = E4M3(q), S = s·g, inv = 1/S (0 when S == 0).
 __device__ __forceinline__ uint32_t nvfp4_block_scale(float a, float g, float d6, float* inv) {
   float sval;

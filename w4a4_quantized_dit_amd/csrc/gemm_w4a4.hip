@@ -259,6 +259,11 @@ hipError_t launch_gemm_int4(int64_t M, int64_t N, int64_t K, const uint8_t* a_co
                             const float* D, const uint16_t* up, int64_t r, uint16_t* Y,
                             int64_t ldy, hipStream_t s);
 
+hipError_t launch_gemm_mx(int fp8, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
+                          const uint8_t* a_scales, const uint8_t* w_codes,
+                          const uint8_t* w_scales, const float* D, const uint16_t* up, int64_t r,
+                          uint16_t* Y, int64_t ldy, hipStream_t s);
+
 hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const void* a_scales, const float* g_a, const uint8_t* w_codes,
                        const void* w_scales, const float* g_w, const float* D,
@@ -266,6 +271,10 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
                        const int32_t* row_to_cube, uint16_t* Y, int64_t ldy, hipStream_t s) {
   if (fmt == 1)
     return launch_gemm_int4(M, N, K, a_codes, a_scales, w_codes, w_scales, D, up, r, Y, ldy, s);
+  if (fmt == 2 || fmt == 3)
+    return launch_gemm_mx(fmt == 3, M, N, K, a_codes, reinterpret_cast<const uint8_t*>(a_scales),
+                          w_codes, reinterpret_cast<const uint8_t*>(w_scales), D, up, r, Y, ldy,
+                          s);
   const dim3 grid(grid_of_tiles((M + kBM - 1) / kBM, N / kBN));
   k_gemm_nvfp4<<<grid, dim3(kThreads), 0, s>>>(
       M, N, K, a_codes, reinterpret_cast<const uint8_t*>(a_scales), g_a, w_codes,

@@ -13,7 +13,9 @@
 // k0 + 64q + 8t .. +8, and the block stages the matching slice of L1 (lora_down[:, k0:k0+256])
 // in LDS once for its waves.  The next chunk's global loads are issued before the current
 // chunk is processed, and two K groups of waves walk alternate chunks of the same rows.  FMT 2 computes D alone (the DeltaQuant path quantises its deltas in its
-// own kernel and takes D from here).
+// own kernel and takes D from here); FMT 3 / 4 are the MX formats (E8M0 scale per 32 with E2M1
+// / E4M3 elements: "MiniMax-H3 — MXFP8 (weight-quantized, vLLM-Omni native layout)", section
+// "Quant format"), each lane's 64 channels being two whole blocks.
 #include "device.h"
 #include "launch.h"
 
@@ -187,6 +189,55 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
           cp[1] = u32x4_t{cw[4], cw[5], cw[6], cw[7]};
           reinterpret_cast<__half*>(scales)[row * (K / 64) + kb / 64] = s;
         }
+      } else if (FMT == 3 || FMT == 4) {
+        // MX: the lane's 64 channels are two blocks of 32, each with an E8M0 exponent from its
+        // maximum; codes of x · 2^-e (exact scaling), E2M1 (FMT 3) or E4M3 (FMT 4)
+        constexpr int kEmax = FMT == 3 ? 2 : 8;
+        uint32_t sb = 0;
+#pragma unroll
+        for (int b = 0; b < 2; ++b) {
+          float a = 0.0f;
+#pragma unroll
+          for (int j = 0; j < 32; ++j) a = fmaxf(a, fabsf(x[32 * b + j]));
+          const int e = mx_exponent(a, kEmax);
+          sb |= (uint32_t)(e + 127) << (8 * b);
+          // each 16-byte piece of codes is encoded and stored before the next, keeping the
+          // E4M3 encodings' temporaries short-lived
+          if (FMT == 3) {
+            uint32_t cw[4];
+#pragma unroll
+            for (int d = 0; d < 4; ++d) {
+              float y[8];
+#pragma unroll
+              for (int j = 0; j < 8; ++j) y[j] = __builtin_ldexpf(x[32 * b + 8 * d + j], -e);
+              cw[d] = e2m1_pack8(y);
+            }
+            if (valid)
+              reinterpret_cast<u32x4_t*>(codes + row * (K / 2) + kb / 2)[b] =
+                  u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+          } else {
+#pragma unroll
+            for (int v = 0; v < 2; ++v) {
+              uint32_t cw[4];
+#pragma unroll
+              for (int d = 0; d < 4; ++d) {
+                uint32_t w = 0;
+#pragma unroll
+                for (int t = 0; t < 4; ++t)
+                  w |= e4m3_encode_signed(__builtin_ldexpf(x[32 * b + 16 * v + 4 * d + t], -e))
+                       << (8 * t);
+                cw[d] = w;
+              }
+              if (valid)
+                reinterpret_cast<u32x4_t*>(codes + row * K + kb)[2 * b + v] =
+                    u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+            }
+          }
+        }
+        if (valid) {
+          *reinterpret_cast<uint16_t*>(reinterpret_cast<uint8_t*>(scales) + row * (K / 32) +
+                                       kb / 32) = (uint16_t)sb;
+        }
       }
 
       if (NT > 0) {
@@ -355,6 +406,12 @@ hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, in
   const size_t lds = (size_t)K * sizeof(float);
   if (fmt == 1)
     return dispatch<1>(nt, grid, lds, s, X, M, K, ldx, lambda, nullptr, down, (int)r, codes,
+                       scales, nullptr, 0, D, nullptr);
+  if (fmt == 2)  // MXFP4
+    return dispatch<3>(nt, grid, lds, s, X, M, K, ldx, lambda, nullptr, down, (int)r, codes,
+                       scales, nullptr, 0, D, nullptr);
+  if (fmt == 3)  // MXFP8
+    return dispatch<4>(nt, grid, lds, s, X, M, K, ldx, lambda, nullptr, down, (int)r, codes,
                        scales, nullptr, 0, D, nullptr);
   const float* amax_p = act_amax;
   int write_g = 1;

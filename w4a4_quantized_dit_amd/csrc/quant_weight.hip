@@ -29,6 +29,7 @@ typedef __attribute__((ext_vector_type(2))) double f64x2_t;
 // MODE 0: max|R32| over the whole weight (one atomic per block)
 // MODE 1: NVFP4 codes and scales with g = amax / 2688
 // MODE 2: int4-g64 codes and fp16 scales
+// MODE 3 / 4: MX codes (E2M1 / E4M3) with E8M0 scales per 32 (single pass)
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__ W, int64_t N,
                                                     int64_t K, int64_t ldw,
@@ -192,6 +193,41 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
         if ((cb & 1) == 0) reinterpret_cast<uint8_t*>(scales)[n * (K / 16) + kc / 16] = (uint8_t)sc;
       }
     }
+  } else if (MODE == 3 || MODE == 4) {
+    // an MX block of 32 channels is held by lanes cb = 4b .. 4b + 3: E8M0 exponent from the
+    // block maximum, codes of x · 2^-e, E2M1 (MODE 3) or E4M3 (MODE 4)
+    constexpr int kEmax = MODE == 3 ? 2 : 8;
+#pragma unroll
+    for (int j = 0; j < 8; ++j) {
+      const int64_t n = n0 + 8 * rg + j;
+      float x[8];
+      float a = 0.0f;
+#pragma unroll
+      for (int e = 0; e < 8; ++e) {
+        x[e] = (float)R[j][e];
+        a = fmaxf(a, fabsf(x[e]));
+      }
+      a = fmaxf(a, __shfl_xor(a, 1));
+      a = fmaxf(a, __shfl_xor(a, 2));
+      const int ex = mx_exponent(a, kEmax);
+      float y[8];
+#pragma unroll
+      for (int e = 0; e < 8; ++e) y[e] = __builtin_ldexpf(x[e], -ex);
+      if (n < N) {
+        if (MODE == 3) {
+          *reinterpret_cast<uint32_t*>(codes + n * (K / 2) + kc / 2) = e2m1_pack8(y);
+        } else {
+          uint32_t w0 = 0, w1 = 0;
+#pragma unroll
+          for (int t = 0; t < 4; ++t) {
+            w0 |= e4m3_encode_signed(y[t]) << (8 * t);
+            w1 |= e4m3_encode_signed(y[4 + t]) << (8 * t);
+          }
+          *reinterpret_cast<uint2*>(codes + n * K + kc) = uint2{w0, w1};
+        }
+        if ((cb & 3) == 0) reinterpret_cast<uint8_t*>(scales)[n * (K / 32) + kc / 32] = (uint8_t)(ex + 127);
+      }
+    }
   } else {
     // an int4-g64 group is held by lanes cb = 8g .. 8g + 7
 #pragma unroll
@@ -245,6 +281,17 @@ hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t
                                   hipStream_t s) {
   const int64_t tiles = ((N + kTileRows - 1) / kTileRows) * (K / kTileCols);
   const size_t lds = lds_bytes(r);
+  if (fmt == 2 || fmt == 3) {  // MX: one pass, no tensor scale
+    hipError_t e = fmt == 2 ? allow_lds<3>(lds) : allow_lds<4>(lds);
+    if (e != hipSuccess) return e;
+    if (fmt == 2)
+      k_resid<3><<<dim3((unsigned)tiles), dim3(kThreads), lds, s>>>(W, N, K, ldw, lambda, down, up,
+                                                                   (int)r, nullptr, codes, scales);
+    else
+      k_resid<4><<<dim3((unsigned)tiles), dim3(kThreads), lds, s>>>(W, N, K, ldw, lambda, down, up,
+                                                                   (int)r, nullptr, codes, scales);
+    return hipGetLastError();
+  }
   if (fmt == 1) {
     hipError_t e = allow_lds<2>(lds);
     if (e != hipSuccess) return e;

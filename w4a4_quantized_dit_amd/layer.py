@@ -7,7 +7,7 @@ low-rank down-projection -> W4A4 GEMM.
 from dataclasses import dataclass
 
 from . import _lib
-from ._lib import NVFP4, INT4_G64  # noqa: F401
+from ._lib import NVFP4, INT4_G64, MXFP4, MXFP8  # noqa: F401
 
 
 def _torch():
@@ -21,10 +21,25 @@ class PreparedWeight:
     N: int
     K: int
     r: int
-    codes: object        # uint8 [N, K/2]
-    scales: object       # uint8 [N, K/16] (E4M3) or float16 [N, K/64]
+    codes: object        # uint8 [N, K/2] (MXFP8: [N, K])
+    scales: object       # uint8 [N, K/16] (E4M3), float16 [N, K/64] or uint8 [N, K/32] (E8M0)
     g: object            # float32 [1] (NVFP4) or None
     lora_up: object      # bf16 [N, r] or None
+
+
+def _alloc_codes_scales(fmt, rows, K, dev):
+    """Code and scale tensors of one format; the NVFP4 tensor scale (else None)."""
+    torch = _torch()
+    codes = torch.empty(rows, K if fmt == MXFP8 else K // 2, dtype=torch.uint8, device=dev)
+    g = None
+    if fmt == NVFP4:
+        scales = torch.empty(rows, K // 16, dtype=torch.uint8, device=dev)
+        g = torch.empty(1, dtype=torch.float32, device=dev)
+    elif fmt == INT4_G64:
+        scales = torch.empty(rows, K // 64, dtype=torch.float16, device=dev)
+    else:
+        scales = torch.empty(rows, K // 32, dtype=torch.uint8, device=dev)
+    return codes, scales, g
 
 
 def calibrate(X, seg, W=None, mask=7, alpha=0.5, state=None):
@@ -49,14 +64,7 @@ def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
     torch = _torch()
     N, K = W.shape
     r = 0 if lora_down is None else lora_down.shape[0]
-    dev = W.device
-    codes = torch.empty(N, K // 2, dtype=torch.uint8, device=dev)
-    if fmt == NVFP4:
-        scales = torch.empty(N, K // 16, dtype=torch.uint8, device=dev)
-        g = torch.empty(1, dtype=torch.float32, device=dev)
-    else:
-        scales = torch.empty(N, K // 64, dtype=torch.float16, device=dev)
-        g = None
+    codes, scales, g = _alloc_codes_scales(fmt, N, K, W.device)
     _lib.svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, g)
     return PreparedWeight(fmt, N, K, r, codes, scales, g, lora_up)
 
@@ -67,13 +75,7 @@ def quantize_activation(X, lam, act_amax, lora_down, fmt=NVFP4, sat_count=None):
     M, K = X.shape
     r = 0 if lora_down is None else lora_down.shape[0]
     dev = X.device
-    codes = torch.empty(M, K // 2, dtype=torch.uint8, device=dev)
-    if fmt == NVFP4:
-        scales = torch.empty(M, K // 16, dtype=torch.uint8, device=dev)
-        g = torch.empty(1, dtype=torch.float32, device=dev)
-    else:
-        scales = torch.empty(M, K // 64, dtype=torch.float16, device=dev)
-        g = None
+    codes, scales, g = _alloc_codes_scales(fmt, M, K, dev)
     D = torch.empty(M, r, dtype=torch.float32, device=dev) if r else None
     _lib.svdq_quant_act_lowrank_down(fmt, X, lam, act_amax, lora_down, r, codes, scales, g, D,
                                      sat_count)
