@@ -9,8 +9,9 @@ whole per-batch path:
 Inputs are seeded synthetic tensors resident in HBM before the timed region; copies of X are
 rotated so the 256 MB last-level cache cannot serve the activation reads.
 
-`--workload` also times the int4-g64 MLP up-projection (M = 32768, K = 5120, N = 13824) and
-the DeltaQuant cube-field layer (31x24x42 grid, K = N = 5120, rank 128) for profiling; the
+`--workload` also times the int4-g64 MLP up-projection (M = 32768, K = 5120, N = 13824), the
+DeltaQuant cube-field layer (31x24x42 grid, K = N = 5120, rank 128) and the MX formats (MXFP4
+W4A4, MXFP8 W8A8) on the attention-projection shape, for profiling; the
 `--copy-probe` mode runs a plain 1 GiB device copy whose hardware byte counters calibrate the
 per-kernel traffic figures.
 
@@ -34,12 +35,30 @@ sys.path.insert(0, ROOT)
 METRIC = "W4A4 SVDQuant linear TFLOP/s + % MFMA peak; quant kernel GB/s, 5120² M=16k"
 PEAK_F16_TFLOPS = 2500.0      # MI355X dense fp16 / bf16 MFMA
 PEAK_I8_TOPS = 5000.0         # MI355X dense int8 MFMA
+PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
+PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 / fp6 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
-WORKLOADS = {"attn": 1, "mlp-up-int4": 2, "delta": 4}
+WORKLOADS = {"attn": 1, "attn-mxfp4": 1, "attn-mxfp8": 1, "mlp-up-int4": 2, "delta": 4}
+MX_FORMATS = {"attn-mxfp4": (2, "mxfp4"), "attn-mxfp8": (3, "mxfp8")}
 # Sources of each GEMM kernel: the PMC traffic figure is valid only for the source it was taken on.
 GEMM_SOURCES = {"attn": ("gemm_w4a4.hip", "gemm_common.h", "device.h"),
                 "mlp-up-int4": ("gemm_int4.hip", "gemm_common.h", "device.h"),
-                "delta": ("gemm_w4a4.hip", "gemm_common.h", "device.h")}
+                "delta": ("gemm_w4a4.hip", "gemm_common.h", "device.h"),
+                "attn-mxfp4": ("gemm_mx.hip", "gemm_common.h", "device.h"),
+                "attn-mxfp8": ("gemm_mx.hip", "gemm_common.h", "device.h")}
+GEMM_KERNELS = {"mlp-up-int4": "k_gemm_int4", "attn-mxfp4": "k_gemm_mxfp4",
+                "attn-mxfp8": "k_gemm_mx_dma"}
+
+
+def workload_config(workload):
+    """The synthetic configuration of a workload (the MX ones: the attention projection in that
+    format)."""
+    import synth
+    cfg = synth.config(WORKLOADS[workload])
+    if workload in MX_FORMATS:
+        cfg["fmt"] = MX_FORMATS[workload][1]
+        cfg["name"] = f"{cfg['name']}-{cfg['fmt']}"
+    return cfg
 
 
 def source_digest(files):
@@ -53,9 +72,8 @@ def source_digest(files):
 def measured_traffic(workload):
     """HBM bytes per GEMM launch from the committed hardware-counter summary, if it was taken on
     the current kernel source; otherwise None."""
-    import synth
-    kern = "k_gemm_int4" if workload == "mlp-up-int4" else "k_gemm_nvfp4"
-    name = synth.config(WORKLOADS[workload])["name"]
+    kern = GEMM_KERNELS.get(workload, "k_gemm_nvfp4")
+    name = workload_config(workload)["name"]
     path = os.path.join(ROOT, "profiles", f"{kern}_{name}_traffic.md")
     if not os.path.exists(path):
         return None
@@ -91,7 +109,7 @@ def cpu_baseline(cfg, X, W, down, up, rows):
     s = cfg["seg"]
     seg = (0, min(s[1], rows), min(s[2], rows), rows)
     Xs = X[:rows]
-    fmt = "int4" if cfg["fmt"] == "int4" else "nvfp4"
+    fmt = cfg["fmt"] if cfg["fmt"] in ("int4", "mxfp4", "mxfp8") else "nvfp4"
     t0 = time.perf_counter()
     ax, aw, lam, amax = OC.calibrate(Xs, seg, W, 7)
     wt = OL.prepare_weight(W, lam, down, up, fmt)
@@ -128,7 +146,8 @@ def setup(torch, workload, n_rot):
     """Inputs, outputs and the per-step launch list of one workload."""
     import synth
     from w4a4_quantized_dit_amd import _lib
-    cfg = synth.config(WORKLOADS[workload])
+    from w4a4_quantized_dit_amd import layer
+    cfg = workload_config(workload)
     M, K, N, r = cfg["M"], cfg["K"], cfg["N"], cfg["r"]
     seg = cfg["seg"]
     dev = "cuda"
@@ -172,6 +191,27 @@ def setup(torch, workload, n_rot):
         st["qa_bytes"] = M * K * 2 + M * K // 2 + M * K // 16 + M * r * 4 + r * K * 2 + K * 4
         st["gemm_flops"] = 2.0 * M * N * K + 2.0 * M * r * N
         st["gemm_peak"] = PEAK_F16_TFLOPS
+    elif workload in MX_FORMATS:
+        f = MX_FORMATS[workload][0]
+        w_codes, w_scales, _ = layer._alloc_codes_scales(f, N, K, dev)
+        a_codes, a_scales, _ = layer._alloc_codes_scales(f, M, K, dev)
+        D = torch.empty(M, r, device=dev)
+
+        def wq(Xi):
+            _lib.svdq_quantize_weight(f, Wd, lam, downd, upd, r, w_codes, w_scales, None)
+
+        def qa(Xi):
+            _lib.svdq_quant_act_lowrank_down(f, Xi, lam, None, downd, r, a_codes, a_scales, None,
+                                             D)
+
+        def gemm(Xi):
+            _lib.svdq_w4a4_gemm(f, M, N, K, a_codes, a_scales, None, w_codes, w_scales, None, D,
+                                upd, r, Y)
+        st["steps"] = [("cal", cal), ("wq", wq), ("qa", qa), ("gemm", gemm)]
+        code_bytes = M * K if f == 3 else M * K // 2
+        st["qa_bytes"] = M * K * 2 + code_bytes + M * K // 32 + M * r * 4 + r * K * 2 + K * 4
+        st["gemm_flops"] = 2.0 * M * N * K + 2.0 * M * r * N
+        st["gemm_peak"] = PEAK_FP8_TFLOPS if f == 3 else PEAK_FP4_TFLOPS
     elif workload == "mlp-up-int4":
         w_codes = torch.empty(N, K // 2, dtype=u8, device=dev)
         w_scales = torch.empty(N, K // 64, dtype=torch.float16, device=dev)
@@ -290,7 +330,8 @@ def main():
     gemm_tflops = gemm_flops / (ms["gemm"] * 1e-3) / 1e12
     peak = st["gemm_peak"]
     qa_gbs = st["qa_bytes"] / (ms["qa"] * 1e-3) / 1e9
-    dtype = {"attn": "f16", "mlp-up-int4": "i8", "delta": "f16"}[args.workload]
+    dtype = {"attn": "f16", "mlp-up-int4": "i8", "delta": "f16", "attn-mxfp4": "fp4",
+             "attn-mxfp8": "fp8"}[args.workload]
     out = {
         "metric": METRIC,
         "value": round(layer_flops / (ms_step * 1e-3) / 1e12, 2),

@@ -6,20 +6,32 @@
 //
 // This is the scale layout v_mfma_scale_f32_32x32x64_f8f6f4 takes natively: one MFMA covers 64
 // elements of K, i.e. two scale blocks per row, and each lane supplies the E8M0 byte of its
-// (row, block).  The codes go from global memory straight into LDS (global_load_lds) and from
-// LDS into the MFMA with no conversion at all.  Operand layout (measured): lane (row = lane % 32,
+// (row, block).  The codes go from global memory through LDS into the MFMA with no conversion at
+// all.  Operand layout (measured): lane (row = lane % 32,
 // h = lane / 32) holds, for FP4, elements [32h, 32h + 32) of the 64 in dwords 0..3 (element 8d
 // + j in nibble j of dword d); for FP8, dwords 0..3 hold elements [16h, 16h + 16) of block 0 and
 // dwords 4..7 the same positions of block 1, with lane h supplying block h's scale.  Inside a
 // block the element order only has to agree between A and W.
 //
-// Tiling: workgroup 256 x 256, 8 waves (two per SIMD) of 128 x 64 (4 x 2 tiles of 32x32),
-// XCD-grouped tile order; K advances 128 elements per stage (two MFMA steps), staged through a
-// ring of LDS buffers (four for FP4, two for FP8), with one LDS-only barrier per stage.  A row's
-// 16-byte code chunk c of a stage is stored at chunk c ^ f(row) (f = (row >> 2) & 3 for 4 chunks
-// per row, (row >> 1) & 7 for 8), which keeps the fragment reads (32 consecutive rows, one
-// chunk) free of bank conflicts.  The E8M0 bytes of a row's four blocks of the stage are one
-// dword.  The low-rank term and the LDS-staged bf16 store are the ones of the NVFP4 GEMM.
+// MXFP4 kernel.  Tiling: workgroup 256 x 256, 8 waves (two per SIMD) of 128 x 64 (4 x 2 tiles of
+// 32x32), XCD-grouped tile order.  K advances 256 elements per stage (four MFMA steps of 64).  A
+// stage goes global -> registers (one stage ahead) -> LDS (two buffers); the fragments are
+// double-buffered per MFMA step, so the LDS reads of the next step run under the MFMAs of the
+// current one, with one LDS-only barrier per stage.
+//
+// What bounds the loads is the rate at which a CU issues requests to L2 (measured: about one per
+// four clocks whatever their size, i.e. about 64 GB/s per CU with full 128-byte lines), not
+// their bytes: a row's contiguous code bytes of a stage go out as one request, and so do its
+// scale bytes.  The deep stage makes these 128 bytes and 8 bytes per row and stage, and eight
+// consecutive lanes read one row's 128 bytes in order.
+//
+// LDS layout of one operand's stage: region g (g = 0..3, one per MFMA step) holds bytes
+// [32g, 32g + 32) of every row's 128, as two 16-byte halves swapped on rows with bit 3 set;
+// regions are 64 bytes longer than their 8 KB of data.  A fragment read (32 consecutive rows,
+// one half each) then touches every bank once per 16 lanes, the eight lanes of one row write
+// four regions on disjoint banks, and every fragment address is one per-lane base plus a
+// constant.  A row's eight E8M0 bytes of the stage are one 8-byte word.  The low-rank term and
+// the LDS-staged bf16 store are the ones of the NVFP4 GEMM.
 #include "device.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -29,10 +41,252 @@ namespace svdq {
 namespace {
 
 constexpr int kThreads = 512;
-constexpr int kBM = 256, kBN = 256, kBK = 128;
+constexpr int kBM = 256, kBN = 256;
+constexpr int FM = 4, FN = 2;
+
+struct Fp4Cfg {
+  static constexpr int kBK = 256;                         // K per stage
+  static constexpr int kSteps = kBK / 64;                 // MFMA steps per stage
+  static constexpr int kRowBytes = kBK / 2;               // codes of a row per stage
+  static constexpr int kRegionBytes = kBM * 32 + 64;      // one step's 32 bytes of every row
+  static constexpr int kCodeBuf = kSteps * kRegionBytes;  // one operand, one stage
+  static constexpr int kScaleRow = kBK / 32;              // E8M0 bytes of a row per stage
+  static constexpr int kScaleBuf = kBM * kScaleRow;
+  static constexpr int kStageBytes = 2 * kCodeBuf + 2 * kScaleBuf;
+  static constexpr int kPerThread = kBM * kRowBytes / 16 / kThreads;  // 16-byte loads per operand
+  static constexpr int kStoreBytes = 8 * gemm_store_bytes<FM, FN>();
+  static constexpr int kLdsBytes = 2 * kStageBytes > kStoreBytes ? 2 * kStageBytes : kStoreBytes;
+};
+
+// stored half of a row's region: the logical half XOR this
+__device__ __forceinline__ int half_swz(int row) { return (row >> 3) & 1; }
+
+// Workgroup barrier ordering LDS accesses only (the next stage's global loads stay in flight,
+// which a full __syncthreads() fence would drain).  The memory clobber keeps the compiler from
+// moving memory accesses across it.
+__device__ __forceinline__ void barrier_lds() {
+  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
+}
+
+// One stage in registers.  Load q of thread tid is 16-byte chunk c = 512q + tid of the operand
+// tile: row c / 8, bytes 16 (c % 8) onward of the row's stage slab; thread tid also loads the
+// stage's scale word of row tid (A) or tid - 256 (W).  A's loads go through range-checked buffer
+// resources whose base and record count carry the row slice and the stage, with only the
+// lane's own offset in the VGPR (the scalar offset is not part of the range check), so rows past
+// M read as zero without touching memory; their results are never stored.
+struct StageRegs {
+  u32x4_t a[Fp4Cfg::kPerThread], b[Fp4Cfg::kPerThread];
+  uint32_t sc[2];
+};
+
+struct StageSrc {
+  const uint8_t* a;   // A codes of the tile's first row
+  const uint8_t* b;   // W codes of the tile's first row
+  const uint8_t* s;   // scale row 0 of this wave's operand (A: waves 0..3, W: 4..7)
+  int64_t a_rows;     // valid rows of the A tile
+  int64_t s_rows;     // valid rows of this wave's scale operand
+  uint32_t kb, ks, voff, s_voff;
+};
+
+constexpr int kRaw = 0x00020000;  // raw buffer resource, word 3
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t rows_rsrc(const uint8_t* base, int64_t rows,
+                                                            uint32_t pitch, uint32_t skip) {
+  const int64_t n = rows > 0 ? rows * (int64_t)pitch - skip : 0;
+  return __builtin_amdgcn_make_buffer_rsrc((void*)(base + skip), (short)0, (int)n, kRaw);
+}
+
+__device__ __forceinline__ void stage_load(StageRegs& R, const StageSrc& src, uint32_t stage) {
+  using C = Fp4Cfg;
+  const __amdgpu_buffer_rsrc_t rb =
+      __builtin_amdgcn_make_buffer_rsrc((void*)src.b, (short)0, (int)(kBN * src.kb), kRaw);
+#pragma unroll
+  for (int q = 0; q < C::kPerThread; ++q) {
+    const uint32_t skip = stage * C::kRowBytes;
+    const __amdgpu_buffer_rsrc_t ra =
+        rows_rsrc(src.a + (int64_t)q * 64 * src.kb, src.a_rows - 64 * q, src.kb, skip);
+    R.a[q] = __builtin_bit_cast(u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(ra, src.voff, 0, 0));
+    R.b[q] = __builtin_bit_cast(
+        u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(rb, src.voff, (int)(q * 64 * src.kb + skip), 0));
+  }
+  const __amdgpu_buffer_rsrc_t rs = rows_rsrc(src.s, src.s_rows, src.ks, stage * C::kScaleRow);
+  const auto v = __builtin_amdgcn_raw_buffer_load_b64(rs, src.s_voff, 0, 0);
+  R.sc[0] = v[0];
+  R.sc[1] = v[1];
+}
+
+__device__ __forceinline__ void stage_store(const StageRegs& R, uint8_t* buf, int st_off,
+                                            int tid) {
+  using C = Fp4Cfg;
+#pragma unroll
+  for (int q = 0; q < C::kPerThread; ++q) {
+    *reinterpret_cast<u32x4_t*>(buf + st_off + q * 64 * 32) = R.a[q];
+    *reinterpret_cast<u32x4_t*>(buf + C::kCodeBuf + st_off + q * 64 * 32) = R.b[q];
+  }
+  *reinterpret_cast<uint2*>(buf + 2 * C::kCodeBuf + tid * C::kScaleRow) = uint2{R.sc[0], R.sc[1]};
+}
+
+// Fragments of one MFMA step: the lane's 16 bytes of each of the wave's 4 + 2 tiles.
+struct Frags {
+  u32x4_t a[FM], b[FN];
+};
+
+__device__ __forceinline__ void frags_read(Frags& F, const uint8_t* a_lds, const uint8_t* b_lds,
+                                           int t) {
+  using C = Fp4Cfg;
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+    F.a[i] = *reinterpret_cast<const u32x4_t*>(a_lds + t * C::kRegionBytes + i * 32 * 32);
+#pragma unroll
+  for (int j = 0; j < FN; ++j)
+    F.b[j] = *reinterpret_cast<const u32x4_t*>(b_lds + t * C::kRegionBytes + j * 32 * 32);
+}
+
+// The fragments' rows' scale words of a stage, shifted so that step t takes byte 2 (t % 2) of
+// word t / 2 (lane h uses block 2t + h).
+struct Scales {
+  uint32_t a[FM][2], b[FN][2];
+};
+
+__device__ __forceinline__ void scales_read(Scales& S, const uint8_t* buf, int a_row0, int b_row0,
+                                            int h) {
+  using C = Fp4Cfg;
+#pragma unroll
+  for (int i = 0; i < FM; ++i) {
+    const uint2 v = *reinterpret_cast<const uint2*>(buf + 2 * C::kCodeBuf +
+                                                    (a_row0 + 32 * i) * C::kScaleRow);
+    S.a[i][0] = v.x >> (8 * h);
+    S.a[i][1] = v.y >> (8 * h);
+  }
+#pragma unroll
+  for (int j = 0; j < FN; ++j) {
+    const uint2 v = *reinterpret_cast<const uint2*>(buf + 2 * C::kCodeBuf + C::kScaleBuf +
+                                                    (b_row0 + 32 * j) * C::kScaleRow);
+    S.b[j][0] = v.x >> (8 * h);
+    S.b[j][1] = v.y >> (8 * h);
+  }
+}
+
+__device__ __forceinline__ i32x8_t fp4_op(u32x4_t v) {
+  return i32x8_t{(int)v[0], (int)v[1], (int)v[2], (int)v[3], 0, 0, 0, 0};
+}
+
+__device__ __forceinline__ void mfma_step(f32x16_t (&acc)[FM][FN], const Frags& F, const Scales& S,
+                                          int t) {
+  constexpr int kFp4 = 4;  // MFMA operand format E2M1
+#pragma unroll
+  for (int i = 0; i < FM; ++i)
+#pragma unroll
+    for (int j = 0; j < FN; ++j)
+      acc[i][j] = __builtin_amdgcn_mfma_scale_f32_32x32x64_f8f6f4(
+          fp4_op(F.a[i]), fp4_op(F.b[j]), acc[i][j], kFp4, kFp4, 0,
+          (int)((S.a[i][t >> 1] >> (16 * (t & 1))) & 0xFFu), 0,
+          (int)((S.b[j][t >> 1] >> (16 * (t & 1))) & 0xFFu));
+}
+
+__global__ __launch_bounds__(kThreads) void k_gemm_mxfp4(
+    int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
+    const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
+    const uint8_t* __restrict__ Bs, const float* __restrict__ D,
+    const uint16_t* __restrict__ up, int r, uint16_t* __restrict__ Y, int64_t ldy) {
+  using C = Fp4Cfg;
+  __shared__ __attribute__((aligned(16))) uint8_t lds[C::kLdsBytes];
+  int64_t tm, tn;
+  if (!tile_of_block((M + kBM - 1) / kBM, N / kBN, tm, tn)) return;
+  const int64_t m0 = tm * kBM, n0 = tn * kBN;
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
+  const int wm = wave >> 2, wn = wave & 3;
+  const int64_t m_base = m0 + wm * 128, n_base = n0 + wn * 64;
+  const int r32 = lane & 31, h = lane >> 5;
+  const int64_t kb = K / 2, ks = K / 32;
+  const int64_t nstage = K / C::kBK;
+
+  // stage sources: this thread's 16-byte part of its row (row q·64 + tid / 8 of load q) and its
+  // scale row; and the LDS offset of its stores (region part / 2, row, swizzled half part % 2)
+  const int part = tid & 7;
+  const int lrow = tid >> 3;  // row within each load's 64-row slice (same swizzle for every q)
+  const int64_t a_rows = M - m0 < kBM ? M - m0 : kBM;
+  const bool a_side = __builtin_amdgcn_readfirstlane(wave) < 4;
+  StageSrc src;
+  src.a = A + m0 * kb;
+  src.b = B + n0 * kb;
+  src.s = a_side ? As + m0 * ks : Bs + n0 * ks;
+  src.a_rows = a_rows;
+  src.s_rows = a_side ? a_rows : kBN;
+  src.kb = (uint32_t)kb;
+  src.ks = (uint32_t)ks;
+  src.voff = (uint32_t)(lrow * kb + 16 * part);
+  src.s_voff = (uint32_t)((tid & 255) * ks);
+  const int st_off = (part >> 1) * C::kRegionBytes + lrow * 32 + 16 * ((part & 1) ^ half_swz(lrow));
+  // LDS bases of this lane's fragments (the fragment rows share their low 5 bits with r32)
+  const int frag_off = r32 * 32 + 16 * (h ^ half_swz(r32));
+  const int a_lds = wm * 128 * 32 + frag_off;
+  const int b_lds = C::kCodeBuf + wn * 64 * 32 + frag_off;
+  const int a_row0 = wm * 128 + r32, b_row0 = wn * 64 + r32;
+
+  f32x16_t acc[FM][FN];
+  gemm_lowrank_init<FM, FN>(acc, 1.0f, M, m_base, n_base, r32, h, D, up, r);
+
+  // prologue: stage 0 in LDS buffer 0, stage 1 in registers, step (0, 0) in F0
+  const uint32_t last = (uint32_t)(nstage - 1);
+  StageRegs R;
+  stage_load(R, src, 0);
+  stage_store(R, lds, st_off, tid);
+  stage_load(R, src, last < 1 ? last : 1);
+  barrier_lds();
+  Frags F0, F1;
+  Scales Sc;
+  scales_read(Sc, lds, a_row0, b_row0, h);
+  frags_read(F0, lds + a_lds, lds + b_lds, 0);
+
+  // The body has no branches, so the MFMAs stay where they are placed: past the last stage the
+  // loads repeat the last stage (in bounds) and the stores and reads of the next buffer touch a
+  // buffer nobody reads any more.
+  for (uint32_t s = 0; s < (uint32_t)nstage; ++s) {
+    uint8_t* cur = lds + (s & 1) * C::kStageBytes;
+    uint8_t* nxt = lds + ((s + 1) & 1) * C::kStageBytes;
+    frags_read(F1, cur + a_lds, cur + b_lds, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(acc, F0, Sc, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    frags_read(F0, cur + a_lds, cur + b_lds, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(acc, F1, Sc, 1);
+    __builtin_amdgcn_sched_barrier(0);
+    frags_read(F1, cur + a_lds, cur + b_lds, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(acc, F0, Sc, 2);
+    __builtin_amdgcn_sched_barrier(0);
+    // the next buffer held stage s-1, which every wave finished reading before the previous
+    // barrier; stage s+1 is in registers
+    stage_store(R, nxt, st_off, tid);
+    stage_load(R, src, s + 2 < last ? s + 2 : last);
+    barrier_lds();
+    frags_read(F0, nxt + a_lds, nxt + b_lds, 0);
+    __builtin_amdgcn_sched_barrier(0);
+    mfma_step(acc, F1, Sc, 3);
+    __builtin_amdgcn_sched_barrier(0);
+    // the scale words of stage s+1 (their LDS latency runs under the next fragment reads)
+    scales_read(Sc, nxt, a_row0, b_row0, h);
+  }
+
+  // every wave's fragment reads completed before its last MFMAs; after this barrier the LDS is
+  // free for the output staging (each wave its own 16 KB)
+  barrier_lds();
+  static_assert(C::kStoreBytes <= C::kLdsBytes, "output staging fits the LDS");
+  gemm_store<FM, FN>(acc, 1.0f, lds + wave * gemm_store_bytes<FM, FN>(), lane, M, N, m_base,
+                     n_base, nullptr, nullptr, Y, ldy);
+}
+
+// MXFP8 kernel: the codes go from global memory straight into LDS (global_load_lds), 128 elements
+// of K per stage in a ring of two stages, 16-byte chunk c of a row stored at chunk c ^ ((row >> 1)
+// & 7).  (The register-staged pipeline of the FP4 kernel needs twice the fragment registers with
+// 8-bit codes and does not fit the register file at this tile shape.)
+constexpr int kBK = 128;  // K per stage of this variant
 
 template <int FP8>
-struct MxCfg {
+struct DmaCfg {
   static constexpr int kRowBytes = FP8 ? 128 : 64;       // codes of a row per stage
   static constexpr int kChunks = kRowBytes / 16;         // 16-byte chunks per row per stage
   static constexpr int kStages = FP8 ? 2 : 4;
@@ -47,16 +301,8 @@ typedef __attribute__((address_space(1))) void gvoid_t;
 typedef __attribute__((address_space(3))) void lvoid_t;
 
 template <int FP8>
-__device__ __forceinline__ int chunk_swz(int row) {
+__device__ __forceinline__ int dma_chunk_swz(int row) {
   return FP8 ? (row >> 1) & 7 : (row >> 2) & 3;
-}
-
-// Workgroup barrier ordering LDS accesses only; the stage loads are completed with explicit
-// vmcnt waits before it, so it must not drain the stages still in flight, which a full
-// __syncthreads() fence would do.  (The memory clobber keeps the compiler from moving memory
-// accesses across it.)
-__device__ __forceinline__ void barrier_lds() {
-  asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
 // s_waitcnt vmcnt(n) (other counters untouched), gfx9 encoding
@@ -70,17 +316,17 @@ __device__ __forceinline__ void wait_vmcnt() {
 // part c % kChunks holding logical part (c % kChunks) ^ f(row)); then the scale dwords of 64 rows
 // (waves 0..3: A, 4..7: W).  Rows of A past M read row M-1 (never stored).
 template <int FP8>
-__device__ __forceinline__ void stage_issue(uint8_t* buf, const uint8_t* __restrict__ A,
+__device__ __forceinline__ void dma_stage_issue(uint8_t* buf, const uint8_t* __restrict__ A,
                                             const uint8_t* __restrict__ As,
                                             const uint8_t* __restrict__ B,
                                             const uint8_t* __restrict__ Bs, int64_t M, int64_t m0,
                                             int64_t n0, int64_t kb, int64_t ks, int64_t stage,
                                             int wave, int lane) {
-  using C = MxCfg<FP8>;
+  using C = DmaCfg<FP8>;
 #pragma unroll
   for (int q = 0; q < C::kPerWave; ++q) {
     const int c = (wave * C::kPerWave + q) * 64 + lane;
-    const int row = c / C::kChunks, part = (c % C::kChunks) ^ chunk_swz<FP8>(row);
+    const int row = c / C::kChunks, part = (c % C::kChunks) ^ dma_chunk_swz<FP8>(row);
     int64_t ar = m0 + row;
     ar = ar < M ? ar : M - 1;
     __builtin_amdgcn_global_load_lds(
@@ -100,13 +346,12 @@ __device__ __forceinline__ void stage_issue(uint8_t* buf, const uint8_t* __restr
 }
 
 template <int FP8>
-__global__ __launch_bounds__(kThreads) void k_gemm_mx(
+__global__ __launch_bounds__(kThreads) void k_gemm_mx_dma(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,
     const uint8_t* __restrict__ As, const uint8_t* __restrict__ B,
     const uint8_t* __restrict__ Bs, const float* __restrict__ D,
     const uint16_t* __restrict__ up, int r, uint16_t* __restrict__ Y, int64_t ldy) {
-  using C = MxCfg<FP8>;
-  constexpr int FM = 4, FN = 2;
+  using C = DmaCfg<FP8>;
   constexpr int kFmt = FP8 ? 0 : 4;  // MFMA operand format: 0 E4M3, 4 E2M1
   __shared__ __attribute__((aligned(16))) uint8_t lds[C::kStages * C::kStageBytes];
   int64_t tm, tn;
@@ -121,7 +366,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
   const int64_t nstage = K / kBK;
 
   // the lane's fragment rows share their low 5 bits with r32, hence one swizzle for all
-  const int sw = chunk_swz<FP8>(r32);
+  const int sw = dma_chunk_swz<FP8>(r32);
   int a_row[FM], b_row[FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i) a_row[i] = (wm * 128 + 32 * i + r32);
@@ -135,7 +380,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
 #pragma unroll
   for (int p = 0; p < C::kStages - 1; ++p)
     if (p < nstage)
-      stage_issue<FP8>(lds + p * C::kStageBytes, A, As, B, Bs, M, m0, n0, kb, ks, p, wave, lane);
+      dma_stage_issue<FP8>(lds + p * C::kStageBytes, A, As, B, Bs, M, m0, n0, kb, ks, p, wave, lane);
   if (nstage >= C::kStages - 1)
     wait_vmcnt<(C::kStages - 2) * C::kLoads>();
   else
@@ -146,7 +391,7 @@ __global__ __launch_bounds__(kThreads) void k_gemm_mx(
     // stage s+S-1 into the buffer computed in the previous iteration (all waves passed the
     // barrier after it)
     if (s + C::kStages - 1 < nstage)
-      stage_issue<FP8>(lds + ((s + C::kStages - 1) % C::kStages) * C::kStageBytes, A, As, B, Bs,
+      dma_stage_issue<FP8>(lds + ((s + C::kStages - 1) % C::kStages) * C::kStageBytes, A, As, B, Bs,
                        M, m0, n0, kb, ks, s + C::kStages - 1, wave, lane);
     const uint8_t* buf = lds + (s % C::kStages) * C::kStageBytes;
     // E8M0 bytes of the fragments' rows for the stage's four blocks; step t, lane h uses block
@@ -215,11 +460,11 @@ hipError_t launch_gemm_mx(int fp8, int64_t M, int64_t N, int64_t K, const uint8_
                           uint16_t* Y, int64_t ldy, hipStream_t s) {
   const dim3 grid(grid_of_tiles((M + kBM - 1) / kBM, N / kBN));
   if (fp8)
-    k_gemm_mx<1><<<grid, dim3(kThreads), 0, s>>>(M, N, K, a_codes, a_scales, w_codes, w_scales, D,
-                                                 up, (int)r, Y, ldy);
+    k_gemm_mx_dma<1><<<grid, dim3(kThreads), 0, s>>>(M, N, K, a_codes, a_scales, w_codes,
+                                                     w_scales, D, up, (int)r, Y, ldy);
   else
-    k_gemm_mx<0><<<grid, dim3(kThreads), 0, s>>>(M, N, K, a_codes, a_scales, w_codes, w_scales, D,
-                                                 up, (int)r, Y, ldy);
+    k_gemm_mxfp4<<<grid, dim3(kThreads), 0, s>>>(M, N, K, a_codes, a_scales, w_codes, w_scales,
+                                                  D, up, (int)r, Y, ldy);
   return hipGetLastError();
 }
 
