@@ -46,10 +46,13 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
   constexpr int kSplit = SPLIT;
   constexpr int kThreads = kGroupThreads * SPLIT;
   constexpr int kLPieces = NT * 16 * (kChunk / 8) / kGroupThreads;  // 16-B L1 pieces per thread
-  extern __shared__ float s_inv[];  // 1/λ for all K channels
+  // 1/λ for all K channels, 4 floats of padding after every 64: the four lane groups of a row
+  // (64 channels apart) then read different banks instead of one
+  extern __shared__ float s_inv[];
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kWaves * kSplit][16 * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t s_l[kSplit][NTc * 16 * kPitch];
-  for (int64_t k = threadIdx.x; k < K; k += kThreads) s_inv[k] = lambda ? 1.0f / lambda[k] : 1.0f;
+  for (int64_t k = threadIdx.x; k < K; k += kThreads)
+    s_inv[k + 4 * (k >> 6)] = lambda ? 1.0f / lambda[k] : 1.0f;
 
   float amax = 0.0f, g = 1.0f, d6 = 6.0f;
   if (FMT == 0) {
@@ -132,6 +135,7 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
     }
     if (has) {
       const int64_t kb = kc * kChunk + 64 * q;  // first channel of this lane
+      const int64_t kbp = kb + 4 * (kb >> 6);   // its padded index in s_inv
       float x[64];
 #pragma unroll
       for (int i = 0; i < 8; ++i) {
@@ -139,8 +143,8 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
 #pragma unroll
         for (int c = 0; c < 4; ++c) {
           const uint32_t w = v[c];
-          x[8 * i + 2 * c] = bf16_lo(w) * s_inv[kb + 8 * i + 2 * c];
-          x[8 * i + 2 * c + 1] = bf16_hi(w) * s_inv[kb + 8 * i + 2 * c + 1];
+          x[8 * i + 2 * c] = bf16_lo(w) * s_inv[kbp + 8 * i + 2 * c];
+          x[8 * i + 2 * c + 1] = bf16_hi(w) * s_inv[kbp + 8 * i + 2 * c + 1];
         }
       }
 
@@ -335,6 +339,9 @@ __global__ void k_amax_to_g(float* t) {
 }
 
 // Static LDS of an instantiation (the X staging and L1 slices of every K group).
+// dynamic LDS of the padded 1/λ table
+inline size_t inv_lds_bytes(int64_t K) { return (size_t)(K + 4 * (K / 64)) * sizeof(float); }
+
 constexpr size_t static_lds(int nt, int split) {
   return (size_t)kWaves * split * 16 * kPitch * 2 + (size_t)split * (nt > 0 ? nt : 1) * 16 * kPitch * 2;
 }
@@ -393,7 +400,7 @@ hipError_t launch_lowrank_down(const uint16_t* X, int64_t M, int64_t K, int64_t 
                                hipStream_t s) {
   const int nt = (int)((r + 15) / 16);
   const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
-  return dispatch<2>(nt, grid, (size_t)K * sizeof(float), s, X, M, K, ldx, lambda, nullptr, down,
+  return dispatch<2>(nt, grid, inv_lds_bytes(K), s, X, M, K, ldx, lambda, nullptr, down,
                      (int)r, nullptr, nullptr, nullptr, 0, D, nullptr);
 }
 
@@ -403,7 +410,7 @@ hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, in
                             float* D, uint32_t* sat, hipStream_t s) {
   const int nt = (int)((r + 15) / 16);
   const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
-  const size_t lds = (size_t)K * sizeof(float);
+  const size_t lds = inv_lds_bytes(K);
   if (fmt == 1)
     return dispatch<1>(nt, grid, lds, s, X, M, K, ldx, lambda, nullptr, down, (int)r, codes,
                        scales, nullptr, 0, D, nullptr);
