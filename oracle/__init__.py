@@ -9,8 +9,8 @@ benchmark may import it.  It shares no code with the HIP library and imports not
 Sources (cited by page title and section):
   * "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", sections
     "Why" (NVFP4: 16 consecutive channels under one FP8 scale set by the group absmax; the
-    kernel sees X / λ), "Calibration" (activation statistics accumulated under a modality
-    mask feed λ), "The metric that picks the winner also hides the cost" (uniform-row and
+    kernel sees X / λ; the statistics-only bits-lost proxy), "Calibration" (activation
+    statistics accumulated under a modality mask feed λ), "The metric that picks the winner also hides the cost" (uniform-row and
     per-modality relative L2).
   * "MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph (outliers absorbed
     by a 16-bit low-rank branch, 4-bit residual, activations quantised per token at run time).
@@ -26,4 +26,4 @@ Every reading taken where the pages are silent is listed in the module that take
 Float32 steps use numpy float32 operations (each one IEEE round-to-nearest-even); exact
 steps use float64.
 """
-from . import formats, quant, mx, calib, svd, gemm, delta, score, layer  # noqa: F401
+from . import formats, quant, mx, calib, proxy, svd, gemm, delta, score, layer  # noqa: F401
