@@ -108,6 +108,22 @@ svdq_status svdq_calibrate_lambda(const uint16_t* X, int64_t M, int64_t K, int64
                                   svdq_stream_t stream);
 
 /*
+ * Statistics-only "bits lost" proxy of a smoothing scale, per modality ("MiniMax-H3 NVFP4 —
+ * what the smoothing scale should be calibrated on", section "Why": a channel whose absmax lies
+ * below its quantisation group's loses log2(group absmax / channel absmax) bits, and λ reshapes
+ * that profile because the kernel sees X / λ).
+ *
+ *   c[μ, k] = fp32(ax[μ, k] · fp32(1/λ[k]))                  (lambda may be NULL: λ = 1)
+ *   out[μ]  = mean over k with c[μ, k] > 0 of log2(max_{j in k's group} c[μ, j] / c[μ, k])
+ *             (fp64; 0 when no channel is live)
+ * Groups are `block` consecutive channels: 16 (NVFP4), 32 (MX) or 64 (int4); K % block == 0.
+ * ax: device fp32 [3, K] (from svdq_calibrate_lambda); out: device fp64 [3].  Summation order
+ * differs from a sequential sum (results agree to fp64 rounding).
+ */
+svdq_status svdq_bits_lost(const float* ax, const float* lambda, int64_t K, int64_t block,
+                           double* out, svdq_stream_t stream);
+
+/*
  * Weight preparation ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph:
  * low-rank branch plus a 4-bit residual; here rounded to nearest).
  *

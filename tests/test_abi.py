@@ -110,3 +110,12 @@ def test_cube_geometry_rejects_bad_sizes(lib):
     assert lib.svdq_cube_geometry(2, 2, 2, 4, 4, 2, 0, 0, 4, None, None, None, pn) == SHAPE
     assert lib.svdq_cube_geometry(31, 24, 42, 2, 2, 2, 312, 128, 4, None, None, None, pn) == OK
     assert n.value == 4142
+
+
+def test_bits_lost_validation(lib):
+    f = lib.svdq_bits_lost
+    assert f(None, None, 256, 16, P, None) == NULLP and "ax" in _err(lib)
+    assert f(P, None, 256, 16, None, None) == NULLP
+    assert f(P, None, 256, 24, P, None) == INVALID
+    assert f(P, None, 200, 16, P, None) == SHAPE
+    assert f(P, None, 32, 64, P, None) == SHAPE

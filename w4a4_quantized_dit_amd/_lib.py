@@ -24,6 +24,7 @@ _SIGS = {
     "svdq_calibrate_lambda": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _i64, _i64,
                                              ctypes.c_uint32, ctypes.c_float, ctypes.c_int,
                                              _c_p, _c_p, _c_p, _c_p, _c_p]),
+    "svdq_bits_lost": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p]),
     "svdq_quantize_weight": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p, _c_p,
                                             _c_p, _i64, _c_p, _c_p, _c_p, _c_p]),
     "svdq_quant_act_lowrank_down": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p,
@@ -158,6 +159,15 @@ def svdq_calibrate_lambda(X, seg, W, modality_mask, alpha, accumulate, ax, aw, l
         int(modality_mask), float(alpha), int(accumulate),
         _ptr(ax, f32, "ax", 3 * K), _ptr(aw, f32, "aw", K), _ptr(lam, f32, "lambda", K),
         _ptr(act_amax, f32, "act_amax", 1), _stream(stream)))
+
+
+def svdq_bits_lost(ax, lam, block, out, stream=None):
+    """Bits-lost proxy per modality; ax [3, K] fp32, lam [K] fp32 or None; out [3] fp64."""
+    torch = _torch()
+    K = ax.shape[1]
+    _check(load().svdq_bits_lost(
+        _ptr(ax, torch.float32, "ax", 3 * K), _ptr(lam, torch.float32, "lambda", K), K,
+        int(block), _ptr(out, torch.float64, "out", 3), _stream(stream)))
 
 
 def svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, tensor_scale,

@@ -132,6 +132,20 @@ svdq_status svdq_calibrate_lambda(const uint16_t* X, int64_t M, int64_t K, int64
                     fn);
 }
 
+svdq_status svdq_bits_lost(const float* ax, const float* lambda, int64_t K, int64_t block,
+                           double* out, svdq_stream_t stream) {
+  const char* fn = "svdq_bits_lost";
+  REQUIRE_PTR(ax); REQUIRE_PTR(out);
+  if (block != 16 && block != 32 && block != 64)
+    return fail(SVDQ_INVALID_ARG, "%s: block=%lld must be 16, 32 or 64", fn, (long long)block);
+  if (K < block || K % block != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: K=%lld must be a positive multiple of block=%lld", fn,
+                (long long)K, (long long)block);
+  return hip_result(svdq::launch_bits_lost(ax, lambda, K, (int)block, out,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                                  const float* lambda, const uint16_t* lora_down,
                                  const uint16_t* lora_up, int64_t r, uint8_t* codes,

@@ -128,6 +128,48 @@ SegChunks make_chunks(const int64_t seg[4], int64_t n_w) {
   return sc;
 }
 
+// Bits-lost proxy ("MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on",
+// section "Why"): one workgroup per modality, a thread per group of `block` channels at a time.
+// The smoothed channel maximum is fp32(ax · fp32(1/λ)) as in the activation kernel (correctly
+// rounded reciprocal, no contraction); each live channel adds log2(group max / its max) in fp64.
+constexpr int kBitsThreads = 256;
+__global__ __launch_bounds__(kBitsThreads) void k_bits_lost(const float* __restrict__ ax,
+                                                            const float* __restrict__ lambda,
+                                                            int64_t K, int block,
+                                                            double* __restrict__ out) {
+  const float* a = ax + (int64_t)blockIdx.x * K;
+  double sum = 0.0;
+  int64_t live = 0;
+  for (int64_t g = threadIdx.x; g < K / block; g += kBitsThreads) {
+    const int64_t k0 = g * block;
+    float gmax = 0.0f;
+    for (int j = 0; j < block; ++j) {
+      const float c = a[k0 + j] * (lambda ? 1.0f / lambda[k0 + j] : 1.0f);
+      gmax = fmaxf(gmax, c);
+    }
+    for (int j = 0; j < block; ++j) {
+      const float c = a[k0 + j] * (lambda ? 1.0f / lambda[k0 + j] : 1.0f);
+      if (c > 0.0f) {
+        sum += log2((double)gmax / (double)c);
+        ++live;
+      }
+    }
+  }
+  __shared__ double s_sum[kBitsThreads];
+  __shared__ int64_t s_live[kBitsThreads];
+  s_sum[threadIdx.x] = sum;
+  s_live[threadIdx.x] = live;
+  __syncthreads();
+  for (int w = kBitsThreads / 2; w > 0; w >>= 1) {
+    if ((int)threadIdx.x < w) {
+      s_sum[threadIdx.x] += s_sum[threadIdx.x + w];
+      s_live[threadIdx.x] += s_live[threadIdx.x + w];
+    }
+    __syncthreads();
+  }
+  if (threadIdx.x == 0) out[blockIdx.x] = s_live[0] ? s_sum[0] / (double)s_live[0] : 0.0;
+}
+
 }  // namespace
 
 hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
@@ -153,6 +195,12 @@ hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx
     if ((e = hipGetLastError()) != hipSuccess) return e;
   }
   k_lambda<<<dim3(1), dim3(1024), 0, s>>>(ax, aw, K, mask, alpha, lambda, act_amax);
+  return hipGetLastError();
+}
+
+hipError_t launch_bits_lost(const float* ax, const float* lambda, int64_t K, int block,
+                            double* out, hipStream_t s) {
+  k_bits_lost<<<dim3(3), dim3(kBitsThreads), 0, s>>>(ax, lambda, K, block, out);
   return hipGetLastError();
 }
 

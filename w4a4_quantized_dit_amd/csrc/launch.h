@@ -11,6 +11,8 @@ hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx
                             const int64_t seg[4], const uint16_t* W, int64_t N, int64_t ldw,
                             uint32_t mask, float alpha, int accumulate, float* ax, float* aw,
                             float* lambda, float* act_amax, hipStream_t s);
+hipError_t launch_bits_lost(const float* ax, const float* lambda, int64_t K, int block,
+                            double* out, hipStream_t s);
 
 hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                                   const float* lambda, const uint16_t* down, const uint16_t* up,

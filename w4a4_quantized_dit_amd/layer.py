@@ -59,6 +59,15 @@ def calibrate(X, seg, W=None, mask=7, alpha=0.5, state=None):
     return state
 
 
+def bits_lost(ax, lam=None, block=16):
+    """Bits-lost proxy per modality (float64 [3]) of the smoothing λ for per-modality channel
+    maxima ax [3, K] (the `ax` of a calibration state); block = the quantiser's group size."""
+    torch = _torch()
+    out = torch.empty(3, dtype=torch.float64, device=ax.device)
+    _lib.svdq_bits_lost(ax, lam, block, out)
+    return out
+
+
 def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
     """Quantised residual of diag(λ)·W − L1·L2 (W [N, K] bf16)."""
     torch = _torch()
