@@ -16,6 +16,16 @@ The residual uses the ROUNDED factors:
     R32 = float32(R)
 SVD factors are not unique (signs, rotations of equal singular values), so both the oracle and
 the GPU path take lora_down / lora_up as inputs.
+
+Randomized factors (computing the branch on the GPU; the pages give no method for it, so the
+reading is the randomized range finder with power iterations and a small SVD, Halko, Martinsson
+and Tropp 2011, Algorithms 4.4 and 5.1):
+    A = W'ᵀ (K x N),  Ω (N x ℓ, ℓ = r + oversampling) a given random matrix
+    Q = orth(A Ω);  q times: Q = orth(A · orth(Aᵀ Q))
+    B = Qᵀ A = U_B Σ V_Bᵀ,   L1 = Q U_B[:, :r] Σ_r,   L2 = V_B[:, :r]ᵀ
+Ω is an input (both sides draw nothing).  The span of each Q, hence L1·L2 and Σ, does not
+depend on how a basis is orthonormalised; the factors themselves are compared only through
+these unique quantities.
 """
 import numpy as np
 
@@ -57,6 +67,26 @@ def lowrank_factors(W_bits, lam, r):
     L1 = U * s[None, :]                            # K x r
     L2 = Vt                                        # r x N
     return bf16_rne(L1.T), bf16_rne(L2.T)
+
+
+def _orth(M):
+    """An orthonormal basis of the columns of M (a library QR is the step)."""
+    return np.linalg.qr(M)[0]
+
+
+def randomized_factors(W_bits, lam, r, omega, power_iters):
+    """Randomized rank-r factors: (lora_down bf16 bits [r, K], lora_up bf16 bits [N, r],
+    σ float64 [r], the unrounded L1 [K, r] and L2 [r, N] in float64)."""
+    A = smoothed_weight(W_bits, lam).T                 # K x N
+    omega = np.asarray(omega, dtype=np.float64)        # N x ℓ
+    Q = _orth(A @ omega)
+    for _ in range(power_iters):
+        Q = _orth(A @ _orth(A.T @ Q))
+    B = Q.T @ A                                        # ℓ x N
+    Ub, s, Vt = np.linalg.svd(B, full_matrices=False)
+    L1 = (Q @ Ub[:, :r]) * s[None, :r]
+    L2 = Vt[:r]
+    return bf16_rne(L1.T), bf16_rne(L2.T), s[:r], L1, L2
 
 
 def residual_f32(W_bits, lam, lora_down_bits, lora_up_bits):
