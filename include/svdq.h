@@ -124,6 +124,28 @@ svdq_status svdq_bits_lost(const float* ax, const float* lambda, int64_t K, int6
                            double* out, svdq_stream_t stream);
 
 /*
+ * Low-rank factors on the GPU ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening
+ * paragraph: a 16-bit rank-r branch absorbs the outliers of the smoothed weight).  The pages give
+ * no method; this is a randomized truncated SVD of A = diag(λ)·Wᵀ (K x N):
+ *   Y = A Ω, Q = orth(Y); power_iters times: Q = orth(A · orth(Aᵀ Q));  Z = Aᵀ Q
+ *   ZᵀZ = U Σ² Uᵀ (ℓ x ℓ);  lora_down = bf16((Q U_r Σ_r)ᵀ) [r, K];  lora_up = bf16(Z U_r Σ_r⁻¹) [N, r]
+ * W: bf16 [N, K] with row stride ldw; lambda: fp32 [K] or NULL (λ = 1); omega: fp32 [N, ell]
+ * (the caller's random matrix, e.g. Gaussian); 1 <= r <= ell <= min(N, K, 160);
+ * 0 <= power_iters <= 8.  Outputs (device): lora_down, lora_up (bf16), sigma (fp32 [r], the
+ * estimated singular values in decreasing order; may be NULL).  workspace: device memory of at
+ * least svdq_lowrank_workspace_bytes(N, K, ell) bytes, 256-byte aligned, owned by the caller and
+ * free again when the stream reaches the end of the call.  Deterministic.  Factors are unique
+ * only up to signs and rotations among equal singular values; the product and σ are what the
+ * method fixes.
+ */
+int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int64_t ell);
+svdq_status svdq_lowrank_factors(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                 const float* lambda, const float* omega, int64_t ell, int64_t r,
+                                 int power_iters, uint16_t* lora_down, uint16_t* lora_up,
+                                 float* sigma, void* workspace, int64_t workspace_bytes,
+                                 svdq_stream_t stream);
+
+/*
  * Weight preparation ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph:
  * low-rank branch plus a 4-bit residual; here rounded to nearest).
  *

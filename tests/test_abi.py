@@ -119,3 +119,27 @@ def test_bits_lost_validation(lib):
     assert f(P, None, 256, 24, P, None) == INVALID
     assert f(P, None, 200, 16, P, None) == SHAPE
     assert f(P, None, 32, 64, P, None) == SHAPE
+
+
+def test_lowrank_validation(lib):
+    f = lib.svdq_lowrank_factors
+    ws = 1 << 30                  # a fake 256-byte aligned workspace address
+    need = lib.svdq_lowrank_workspace_bytes(512, 256, 40)
+    assert need > 0 and lib.svdq_lowrank_workspace_bytes(512, 256, 161) == -1
+
+    def call(**kw):
+        a = dict(W=P, N=512, K=256, ldw=256, lam=None, om=P, ell=40, r=32, q=2, down=P, up=P,
+                 sig=None, ws=ws, wsb=need)
+        a.update(kw)
+        return f(a["W"], a["N"], a["K"], a["ldw"], a["lam"], a["om"], a["ell"], a["r"], a["q"],
+                 a["down"], a["up"], a["sig"], a["ws"], a["wsb"], None)
+    assert call(W=None) == NULLP
+    assert call(om=None) == NULLP
+    assert call(ws=ws + 16) == SHAPE                     # not 256-byte aligned
+    assert call(r=48) == SHAPE                           # r > ell
+    assert call(r=0) == SHAPE
+    assert call(ell=161, r=32) == SHAPE
+    assert call(N=32, ldw=256) == SHAPE                  # ell > N
+    assert call(q=9) == INVALID
+    assert call(wsb=need - 1) == SHAPE and "workspace" in _err(lib)
+    assert call(ldw=250) == SHAPE

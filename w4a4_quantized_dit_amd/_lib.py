@@ -25,6 +25,9 @@ _SIGS = {
                                              ctypes.c_uint32, ctypes.c_float, ctypes.c_int,
                                              _c_p, _c_p, _c_p, _c_p, _c_p]),
     "svdq_bits_lost": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p]),
+    "svdq_lowrank_workspace_bytes": (_i64, [_i64, _i64, _i64]),
+    "svdq_lowrank_factors": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _i64, _i64,
+                                            ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
     "svdq_quantize_weight": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p, _c_p,
                                             _c_p, _i64, _c_p, _c_p, _c_p, _c_p]),
     "svdq_quant_act_lowrank_down": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p,
@@ -168,6 +171,25 @@ def svdq_bits_lost(ax, lam, block, out, stream=None):
     _check(load().svdq_bits_lost(
         _ptr(ax, torch.float32, "ax", 3 * K), _ptr(lam, torch.float32, "lambda", K), K,
         int(block), _ptr(out, torch.float64, "out", 3), _stream(stream)))
+
+
+def svdq_lowrank_workspace_bytes(N, K, ell):
+    return int(load().svdq_lowrank_workspace_bytes(int(N), int(K), int(ell)))
+
+
+def svdq_lowrank_factors(W, lam, omega, r, power_iters, lora_down, lora_up, sigma, workspace,
+                         stream=None):
+    """Randomized rank-r factors of diag(λ)·Wᵀ; W [N, K] bf16, omega [N, ell] fp32; outputs
+    lora_down [r, K] bf16, lora_up [N, r] bf16, sigma [r] fp32 or None; workspace uint8."""
+    torch = _torch()
+    N, K = W.shape
+    ell = omega.shape[1]
+    _check(load().svdq_lowrank_factors(
+        _ptr(W, _bf16(), "W"), N, K, W.stride(0), _ptr(lam, torch.float32, "lambda", K),
+        _ptr(omega, torch.float32, "omega", N * ell), ell, int(r), int(power_iters),
+        _ptr(lora_down, _bf16(), "lora_down", r * K), _ptr(lora_up, _bf16(), "lora_up", N * r),
+        _ptr(sigma, torch.float32, "sigma", r), _ptr(workspace, torch.uint8, "workspace"),
+        workspace.numel(), _stream(stream)))
 
 
 def svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, tensor_scale,

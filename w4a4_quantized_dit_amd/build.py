@@ -13,7 +13,8 @@ LIB = os.path.join(HERE, "libsvdq.so")
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "geometry.cpp", "calib.hip", "quant_weight.hip", "quant_act.hip",
-           "gemm_w4a4.hip", "gemm_int4.hip", "gemm_mx.hip", "delta.hip", "score.hip"]
+           "gemm_w4a4.hip", "gemm_int4.hip", "gemm_mx.hip", "delta.hip", "score.hip",
+           "lowrank.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

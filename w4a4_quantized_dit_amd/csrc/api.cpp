@@ -132,6 +132,43 @@ svdq_status svdq_calibrate_lambda(const uint16_t* X, int64_t M, int64_t K, int64
                     fn);
 }
 
+int64_t svdq_lowrank_workspace_bytes(int64_t N, int64_t K, int64_t ell) {
+  if (N < 1 || K < 1 || ell < 1 || ell > svdq::lowrank_max_ell()) return -1;
+  return svdq::lowrank_workspace_bytes(N, K, ell);
+}
+
+svdq_status svdq_lowrank_factors(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                 const float* lambda, const float* omega, int64_t ell, int64_t r,
+                                 int power_iters, uint16_t* lora_down, uint16_t* lora_up,
+                                 float* sigma, void* workspace, int64_t workspace_bytes,
+                                 svdq_stream_t stream) {
+  const char* fn = "svdq_lowrank_factors";
+  REQUIRE_PTR(W); REQUIRE_PTR(omega); REQUIRE_PTR(lora_down); REQUIRE_PTR(lora_up);
+  REQUIRE_PTR(workspace);
+  REQUIRE_ALIGNED(W); REQUIRE_ALIGNED(omega); REQUIRE_ALIGNED(lambda); REQUIRE_ALIGNED(sigma);
+  REQUIRE_ALIGNED(lora_down); REQUIRE_ALIGNED(lora_up);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+  if (N < 1 || K < 1)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld, K=%lld must be >= 1", fn, (long long)N,
+                (long long)K);
+  TRY(check_ld(fn, "ldw", ldw, K));
+  const int64_t lim = svdq::lowrank_max_ell();
+  if (r < 1 || ell < r || ell > lim || ell > N || ell > K)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: need 1 <= r (%lld) <= ell (%lld) <= min(N, K, %lld)",
+                fn, (long long)r, (long long)ell, (long long)lim);
+  if (power_iters < 0 || power_iters > 8)
+    return fail(SVDQ_INVALID_ARG, "%s: power_iters=%d must lie in [0, 8]", fn, power_iters);
+  const int64_t need = svdq::lowrank_workspace_bytes(N, K, ell);
+  if (workspace_bytes < need)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace of %lld bytes, needs %lld", fn,
+                (long long)workspace_bytes, (long long)need);
+  return hip_result(svdq::launch_lowrank(W, N, K, ldw, lambda, omega, ell, r, power_iters,
+                                         lora_down, lora_up, sigma, workspace,
+                                         reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 svdq_status svdq_bits_lost(const float* ax, const float* lambda, int64_t K, int64_t block,
                            double* out, svdq_stream_t stream) {
   const char* fn = "svdq_bits_lost";

@@ -13,6 +13,12 @@ hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx
                             float* lambda, float* act_amax, hipStream_t s);
 hipError_t launch_bits_lost(const float* ax, const float* lambda, int64_t K, int block,
                             double* out, hipStream_t s);
+int64_t lowrank_workspace_bytes(int64_t N, int64_t K, int64_t ell);
+int lowrank_max_ell();
+hipError_t launch_lowrank(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                          const float* lambda, const float* omega, int64_t ell, int64_t r,
+                          int power_iters, uint16_t* lora_down, uint16_t* lora_up, float* sigma,
+                          void* workspace, hipStream_t s);
 
 hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                                   const float* lambda, const uint16_t* down, const uint16_t* up,

@@ -1,0 +1,504 @@
+// Randomized rank-r factors of the smoothed weight A = diag(λ)·Wᵀ (K x N) on the GPU: the branch
+// the layer adds in 16 bits ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening
+// paragraph).  The pages give no method for computing it; this is the randomized range finder
+// with power iterations followed by a small SVD (Halko, Martinsson and Tropp 2011, Algorithms 4.4
+// and 5.1):
+//   Y = A Ω, Q = orth(Y); q times: Q = orth(A · orth(Aᵀ Q));  Z = Aᵀ Q  (= Bᵀ, B = Qᵀ A)
+//   ZᵀZ = B Bᵀ = U Σ² Uᵀ;  L1 = Q U_r Σ_r (K x r);  L2 = (Z U_r Σ_r⁻¹)ᵀ (r x N)
+// Ω (N x ℓ) is the caller's.  The large products are fp32 (bf16 W exact, fp32 fused
+// multiply-adds) split over their reduction dimension, the splits summed in a fixed order
+// (deterministic).  orth() is Cholesky-QR applied twice: Gram matrix in fp64 from fp32 rows,
+// Cholesky and triangular inverse in fp64 (one workgroup), rows times the inverse in fp64.  The
+// ℓ x ℓ eigenproblem is parallel cyclic Jacobi in fp64 (one workgroup, round-robin pairs).
+// None of this is on the layer's per-batch path; it prepares the factors that
+// svdq_quantize_weight and the GEMM take.
+#include "device.h"
+#include "launch.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kMaxEll = 160;
+constexpr int kColTile = 40;       // columns of the sketch handled by one thread
+constexpr int kSplitRows = 512;    // reduction rows per partial sum of the sketch products
+constexpr int kGramRows = 64;      // rows per partial Gram matrix
+constexpr int kJacobiThreads = 1024;
+constexpr int kMaxSweeps = 40;
+
+// Yp[s][k][j] = Σ_{n in split s} W[n, k] · X[n, j]: thread = column k, 40 columns of X per
+// workgroup (blockIdx.z), rows of X staged 64 at a time.
+__global__ __launch_bounds__(256) void k_sketch_wt(const uint16_t* __restrict__ W, int64_t N,
+                                                   int64_t K, int64_t ldw,
+                                                   const float* __restrict__ X, int ell,
+                                                   float* __restrict__ Yp) {
+  __shared__ float xs[64][kColTile];
+  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t s = blockIdx.y;
+  const int j0 = blockIdx.z * kColTile;
+  const int jn = ell - j0 < kColTile ? ell - j0 : kColTile;
+  const int64_t n_begin = s * kSplitRows;
+  const int64_t n_end = n_begin + kSplitRows < N ? n_begin + kSplitRows : N;
+  float acc[kColTile];
+#pragma unroll
+  for (int c = 0; c < kColTile; ++c) acc[c] = 0.0f;
+  for (int64_t n0 = n_begin; n0 < n_end; n0 += 64) {
+    const int nn = n_end - n0 < 64 ? (int)(n_end - n0) : 64;
+    __syncthreads();
+    for (int t = threadIdx.x; t < 64 * kColTile; t += 256) {
+      const int rr = t / kColTile, c = t % kColTile;
+      xs[rr][c] = (rr < nn && c < jn) ? X[(n0 + rr) * ell + j0 + c] : 0.0f;
+    }
+    __syncthreads();
+    if (k < K) {
+      for (int rr = 0; rr < nn; ++rr) {
+        const float w = bf16_to_f32(W[(n0 + rr) * ldw + k]);
+#pragma unroll
+        for (int c = 0; c < kColTile; ++c) acc[c] = __builtin_fmaf(w, xs[rr][c], acc[c]);
+      }
+    }
+  }
+  if (k < K) {
+#pragma unroll
+    for (int c = 0; c < kColTile; ++c)
+      if (c < jn) Yp[(s * K + k) * ell + j0 + c] = acc[c];
+  }
+}
+
+// Zp[s][n][j] = Σ_{k in split s} W[n, k] · λ_k · Q[k, j]: 64 rows n x 40 columns per workgroup,
+// thread = (row, column residue mod 4), W and λ∘Q staged 64 channels at a time.
+__global__ __launch_bounds__(256) void k_sketch_w(const uint16_t* __restrict__ W, int64_t N,
+                                                  int64_t K, int64_t ldw,
+                                                  const float* __restrict__ lambda,
+                                                  const float* __restrict__ Q, int ell,
+                                                  float* __restrict__ Zp) {
+  __shared__ float ws[64][65];
+  __shared__ float qs[64][kColTile];
+  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t s = blockIdx.y;
+  const int j0 = blockIdx.z * kColTile;
+  const int jn = ell - j0 < kColTile ? ell - j0 : kColTile;
+  const int64_t k_begin = s * kSplitRows;
+  const int64_t k_end = k_begin + kSplitRows < K ? k_begin + kSplitRows : K;
+  const int row = threadIdx.x >> 2, cq = threadIdx.x & 3;
+  constexpr int kPer = kColTile / 4;
+  float acc[kPer];
+#pragma unroll
+  for (int m = 0; m < kPer; ++m) acc[m] = 0.0f;
+  for (int64_t k0 = k_begin; k0 < k_end; k0 += 64) {
+    const int kn = k_end - k0 < 64 ? (int)(k_end - k0) : 64;
+    __syncthreads();
+    for (int t = threadIdx.x; t < 64 * 64; t += 256) {
+      const int rr = t >> 6, kk = t & 63;
+      ws[rr][kk] = (n0 + rr < N && kk < kn) ? bf16_to_f32(W[(n0 + rr) * ldw + k0 + kk]) : 0.0f;
+    }
+    for (int t = threadIdx.x; t < 64 * kColTile; t += 256) {
+      const int kk = t / kColTile, c = t % kColTile;
+      float v = 0.0f;
+      if (kk < kn && c < jn) {
+        v = Q[(k0 + kk) * ell + j0 + c];
+        if (lambda) v *= lambda[k0 + kk];
+      }
+      qs[kk][c] = v;
+    }
+    __syncthreads();
+    for (int kk = 0; kk < kn; ++kk) {
+      const float w = ws[row][kk];
+#pragma unroll
+      for (int m = 0; m < kPer; ++m) acc[m] = __builtin_fmaf(w, qs[kk][cq + 4 * m], acc[m]);
+    }
+  }
+  if (n0 + row < N) {
+#pragma unroll
+    for (int m = 0; m < kPer; ++m) {
+      const int c = cq + 4 * m;
+      if (c < jn) Zp[(s * N + n0 + row) * ell + j0 + c] = acc[m];
+    }
+  }
+}
+
+// out[i] = scale(row) · Σ_s P[s][i] (splits in ascending order), i over rows x ell
+__global__ __launch_bounds__(256) void k_reduce_splits(const float* __restrict__ P, int64_t rows,
+                                                       int ell, int64_t nsplit,
+                                                       const float* __restrict__ row_scale,
+                                                       float* __restrict__ out) {
+  const int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t total = rows * ell;
+  if (i >= total) return;
+  float acc = 0.0f;
+  for (int64_t s = 0; s < nsplit; ++s) acc += P[s * total + i];
+  if (row_scale) acc *= row_scale[i / ell];
+  out[i] = acc;
+}
+
+// Gp[b][i][j] = Σ over rows of chunk b (64 rows) of M[row][i]·M[row][j] in fp64 (both triangles)
+__global__ __launch_bounds__(256) void k_gram_partial(const float* __restrict__ M, int64_t rows,
+                                                      int ell, double* __restrict__ Gp) {
+  __shared__ float ms[kGramRows][kMaxEll];
+  const int64_t r0 = (int64_t)blockIdx.x * kGramRows;
+  const int rn = rows - r0 < kGramRows ? (int)(rows - r0) : kGramRows;
+  for (int t = threadIdx.x; t < kGramRows * ell; t += 256) {
+    const int rr = t / ell, c = t % ell;
+    ms[rr][c] = rr < rn ? M[(r0 + rr) * ell + c] : 0.0f;
+  }
+  __syncthreads();
+  double* g = Gp + (int64_t)blockIdx.x * ell * ell;
+  const int npairs = ell * (ell + 1) / 2;
+  for (int p = threadIdx.x; p < npairs; p += 256) {
+    // pair p -> (i, j), i <= j, row-major over the upper triangle
+    int i = 0, rem = p;
+    while (rem >= ell - i) {
+      rem -= ell - i;
+      ++i;
+    }
+    const int j = i + rem;
+    double acc = 0.0;
+    for (int rr = 0; rr < rn; ++rr) acc += (double)ms[rr][i] * (double)ms[rr][j];
+    g[i * ell + j] = acc;
+    g[j * ell + i] = acc;
+  }
+}
+
+// G = Σ_b Gp[b] (ascending b)
+__global__ __launch_bounds__(256) void k_gram_reduce(const double* __restrict__ Gp, int64_t nb,
+                                                     int ell, double* __restrict__ G) {
+  const int i = blockIdx.x * 256 + threadIdx.x;
+  if (i >= ell * ell) return;
+  double acc = 0.0;
+  for (int64_t b = 0; b < nb; ++b) acc += Gp[b * ell * ell + i];
+  G[i] = acc;
+}
+
+// Cholesky G = RᵀR (R upper) and Rinv = R⁻¹ (upper), fp64, one workgroup.  A pivot that is not
+// positive (a rank-deficient block) is raised to a tiny positive value relative to the trace,
+// which keeps every value finite; such directions have singular values at rounding level and
+// end up at the bottom of the spectrum.
+__global__ __launch_bounds__(256) void k_chol_inv(const double* __restrict__ G, int ell,
+                                                  double* __restrict__ R,
+                                                  double* __restrict__ Rinv) {
+  __shared__ double s_tiny;
+  if (threadIdx.x == 0) {
+    double tr = 0.0;
+    for (int i = 0; i < ell; ++i) tr += G[i * ell + i];
+    s_tiny = (tr > 1e-300 ? tr : 1e-300) * 1e-28;
+  }
+  for (int t = threadIdx.x; t < ell * ell; t += 256) R[t] = 0.0;
+  __syncthreads();
+  for (int j = 0; j < ell; ++j) {
+    if (threadIdx.x == 0) {
+      double d = G[j * ell + j];
+      for (int k = 0; k < j; ++k) d -= R[k * ell + j] * R[k * ell + j];
+      R[j * ell + j] = sqrt(d > s_tiny ? d : s_tiny);
+    }
+    __syncthreads();
+    const double rjj = R[j * ell + j];
+    for (int i = j + 1 + threadIdx.x; i < ell; i += 256) {
+      double v = G[j * ell + i];
+      for (int k = 0; k < j; ++k) v -= R[k * ell + j] * R[k * ell + i];
+      R[j * ell + i] = v / rjj;
+    }
+    __syncthreads();
+  }
+  // column c of R⁻¹ by back substitution (thread per column)
+  for (int c = threadIdx.x; c < ell; c += 256) {
+    for (int i = ell - 1; i > c; --i) Rinv[i * ell + c] = 0.0;
+    Rinv[c * ell + c] = 1.0 / R[c * ell + c];
+    for (int i = c - 1; i >= 0; --i) {
+      double v = 0.0;
+      for (int k = i + 1; k <= c; ++k) v += R[i * ell + k] * Rinv[k * ell + c];
+      Rinv[i * ell + c] = -v / R[i * ell + i];
+    }
+  }
+}
+
+// Mo[row][j] = Σ_{i <= j} M[row][i] · Rinv[i][j]  (fp64 accumulation)
+__global__ __launch_bounds__(256) void k_apply_rinv(const float* __restrict__ M, int64_t rows,
+                                                    int ell, const double* __restrict__ Rinv,
+                                                    float* __restrict__ Mo) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= rows * ell) return;
+  const int64_t row = t / ell;
+  const int j = (int)(t % ell);
+  double acc = 0.0;
+  for (int i = 0; i <= j; ++i) acc += (double)M[row * ell + i] * Rinv[i * ell + j];
+  Mo[t] = (float)acc;
+}
+
+// Parallel cyclic Jacobi on the symmetric H (ell x ell, fp64, in place; both in global memory,
+// one workgroup), eigenvectors accumulated in V; then the eigenpairs sorted by decreasing
+// eigenvalue: eig[i], U[:, i].  Rounds pair the indices by the circle method (index 0 fixed,
+// the others rotating); an odd ell gets a dummy index that sits out its pairs.
+__global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ H, int ell,
+                                                           double* __restrict__ V,
+                                                           double* __restrict__ U,
+                                                           double* __restrict__ eig) {
+  __shared__ double s_c[kMaxEll / 2], s_s[kMaxEll / 2];
+  __shared__ int s_p[kMaxEll / 2], s_q[kMaxEll / 2];
+  __shared__ double s_red[kJacobiThreads], s_red2[kJacobiThreads];
+  __shared__ int s_order[kMaxEll];
+  __shared__ int s_done;
+  const int tid = threadIdx.x;
+  const int m = (ell + 1) & ~1;  // even player count
+  const int half = m / 2;
+  for (int t = tid; t < ell * ell; t += kJacobiThreads) V[t] = (t / ell == t % ell) ? 1.0 : 0.0;
+  if (tid == 0) s_done = 0;
+  __syncthreads();
+  for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
+    // convergence: off-diagonal mass against the whole matrix
+    double off = 0.0, all = 0.0;
+    for (int t = tid; t < ell * ell; t += kJacobiThreads) {
+      const double h = H[t];
+      all += h * h;
+      if (t / ell != t % ell) off += h * h;
+    }
+    s_red[tid] = off;
+    s_red2[tid] = all;
+    __syncthreads();
+    for (int w = kJacobiThreads / 2; w > 0; w >>= 1) {
+      if (tid < w) {
+        s_red[tid] += s_red[tid + w];
+        s_red2[tid] += s_red2[tid + w];
+      }
+      __syncthreads();
+    }
+    if (tid == 0) s_done = (s_red[0] <= 1e-30 * s_red2[0]) ? 1 : 0;
+    __syncthreads();
+    if (s_done) break;
+    for (int round = 0; round < m - 1; ++round) {
+      if (tid < half) {
+        int a, b;
+        if (tid == 0) {
+          a = 0;
+          b = 1 + round % (m - 1);
+        } else {
+          a = 1 + (round + tid) % (m - 1);
+          b = 1 + (round - tid + (m - 1)) % (m - 1);
+        }
+        const int p = a < b ? a : b, q = a < b ? b : a;
+        double c = 1.0, s = 0.0;
+        if (q < ell) {
+          const double hpq = H[p * ell + q];
+          if (hpq != 0.0) {
+            const double tau = (H[q * ell + q] - H[p * ell + p]) / (2.0 * hpq);
+            const double tt = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
+            c = 1.0 / sqrt(1.0 + tt * tt);
+            s = tt * c;
+          }
+        }
+        s_p[tid] = p;
+        s_q[tid] = q < ell ? q : -1;
+        s_c[tid] = c;
+        s_s[tid] = s;
+      }
+      __syncthreads();
+      // rows: H <- Jᵀ H
+      for (int t = tid; t < half * ell; t += kJacobiThreads) {
+        const int pr = t / ell, j = t % ell;
+        const int p = s_p[pr], q = s_q[pr];
+        if (q < 0) continue;
+        const double c = s_c[pr], s = s_s[pr];
+        const double hp = H[p * ell + j], hq = H[q * ell + j];
+        H[p * ell + j] = c * hp - s * hq;
+        H[q * ell + j] = s * hp + c * hq;
+      }
+      __syncthreads();
+      // columns: H <- H J, V <- V J
+      for (int t = tid; t < half * ell; t += kJacobiThreads) {
+        const int pr = t / ell, i = t % ell;
+        const int p = s_p[pr], q = s_q[pr];
+        if (q < 0) continue;
+        const double c = s_c[pr], s = s_s[pr];
+        const double hp = H[i * ell + p], hq = H[i * ell + q];
+        H[i * ell + p] = c * hp - s * hq;
+        H[i * ell + q] = s * hp + c * hq;
+        const double vp = V[i * ell + p], vq = V[i * ell + q];
+        V[i * ell + p] = c * vp - s * vq;
+        V[i * ell + q] = s * vp + c * vq;
+      }
+      __syncthreads();
+    }
+  }
+  // sort by decreasing eigenvalue (ties by index)
+  if (tid == 0) {
+    for (int i = 0; i < ell; ++i) s_order[i] = i;
+    for (int i = 0; i < ell; ++i) {
+      int best = i;
+      for (int j = i + 1; j < ell; ++j)
+        if (H[s_order[j] * ell + s_order[j]] > H[s_order[best] * ell + s_order[best]]) best = j;
+      const int tmp = s_order[i];
+      s_order[i] = s_order[best];
+      s_order[best] = tmp;
+    }
+  }
+  __syncthreads();
+  for (int t = tid; t < ell * ell; t += kJacobiThreads) {
+    const int i = t / ell, c = t % ell;
+    U[i * ell + c] = V[i * ell + s_order[c]];
+  }
+  for (int c = tid; c < ell; c += kJacobiThreads) eig[c] = H[s_order[c] * ell + s_order[c]];
+}
+
+// lora_down[i][k] = bf16(σ_i Σ_j Q[k][j] U[j][i]);  lora_up[n][i] = bf16(Σ_j Z[n][j] U[j][i] / σ_i)
+// (0 when σ_i == 0);  sigma[i] = σ_i = sqrt(max(eig_i, 0)).
+__global__ __launch_bounds__(256) void k_factors(const float* __restrict__ Q,
+                                                 const float* __restrict__ Z, int64_t N,
+                                                 int64_t K, int ell, int r,
+                                                 const double* __restrict__ U,
+                                                 const double* __restrict__ eig,
+                                                 uint16_t* __restrict__ down,
+                                                 uint16_t* __restrict__ up,
+                                                 float* __restrict__ sigma) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  const int64_t nd = (int64_t)r * K, nu = N * (int64_t)r;
+  if (t < nd) {
+    const int i = (int)(t / K);
+    const int64_t k = t % K;
+    const double sg = sqrt(eig[i] > 0.0 ? eig[i] : 0.0);
+    double acc = 0.0;
+    for (int j = 0; j < ell; ++j) acc += (double)Q[k * ell + j] * U[j * ell + i];
+    down[(int64_t)i * K + k] = f32_to_bf16((float)(acc * sg));
+    if (sigma && k == 0) sigma[i] = (float)sg;
+  } else if (t < nd + nu) {
+    const int64_t u = t - nd;
+    const int64_t n = u / r;
+    const int i = (int)(u % r);
+    const double sg = sqrt(eig[i] > 0.0 ? eig[i] : 0.0);
+    double acc = 0.0;
+    for (int j = 0; j < ell; ++j) acc += (double)Z[n * ell + j] * U[j * ell + i];
+    up[n * r + i] = f32_to_bf16(sg > 0.0 ? (float)(acc / sg) : 0.0f);
+  }
+}
+
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+
+struct Workspace {
+  float *y, *yt, *z, *zt, *p;
+  double *gp, *g, *r, *rinv, *v, *u, *eig;
+};
+
+Workspace carve(void* base, int64_t N, int64_t K, int64_t ell) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  Workspace w;
+  auto take = [&](int64_t bytes) {
+    uint8_t* p = b;
+    b += align256(bytes);
+    return p;
+  };
+  w.y = reinterpret_cast<float*>(take(K * ell * 4));
+  w.yt = reinterpret_cast<float*>(take(K * ell * 4));
+  w.z = reinterpret_cast<float*>(take(N * ell * 4));
+  w.zt = reinterpret_cast<float*>(take(N * ell * 4));
+  const int64_t splits = ceil_div(N, kSplitRows) * K > ceil_div(K, kSplitRows) * N
+                             ? ceil_div(N, kSplitRows) * K
+                             : ceil_div(K, kSplitRows) * N;
+  w.p = reinterpret_cast<float*>(take(splits * ell * 4));
+  const int64_t nb = ceil_div(K > N ? K : N, kGramRows);
+  w.gp = reinterpret_cast<double*>(take(nb * ell * ell * 8));
+  w.g = reinterpret_cast<double*>(take(ell * ell * 8));
+  w.r = reinterpret_cast<double*>(take(ell * ell * 8));
+  w.rinv = reinterpret_cast<double*>(take(ell * ell * 8));
+  w.v = reinterpret_cast<double*>(take(ell * ell * 8));
+  w.u = reinterpret_cast<double*>(take(ell * ell * 8));
+  w.eig = reinterpret_cast<double*>(take(ell * 8));
+  return w;
+}
+
+}  // namespace
+
+int64_t lowrank_workspace_bytes(int64_t N, int64_t K, int64_t ell) {
+  int64_t total = 0;
+  total += 2 * align256(K * ell * 4) + 2 * align256(N * ell * 4);
+  const int64_t splits = ceil_div(N, kSplitRows) * K > ceil_div(K, kSplitRows) * N
+                             ? ceil_div(N, kSplitRows) * K
+                             : ceil_div(K, kSplitRows) * N;
+  total += align256(splits * ell * 4);
+  total += align256(ceil_div(K > N ? K : N, kGramRows) * ell * ell * 8);
+  total += 5 * align256(ell * ell * 8) + align256(ell * 8);
+  return total;
+}
+
+int lowrank_max_ell() { return kMaxEll; }
+
+hipError_t launch_lowrank(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                          const float* lambda, const float* omega, int64_t ell, int64_t r,
+                          int power_iters, uint16_t* lora_down, uint16_t* lora_up, float* sigma,
+                          void* workspace, hipStream_t s) {
+  Workspace w = carve(workspace, N, K, ell);
+  const int e = (int)ell;
+  const unsigned ztiles = (unsigned)ceil_div(ell, kColTile);
+  hipError_t err;
+#define SVDQ_CHECK_LAUNCH() \
+  do {                      \
+    err = hipGetLastError(); \
+    if (err != hipSuccess) return err; \
+  } while (0)
+
+  // Y (K x ell) = diag(λ) Wᵀ X  for X (N x ell)
+  auto a_times = [&](const float* X, float* Y) -> hipError_t {
+    const int64_t nsplit = ceil_div(N, kSplitRows);
+    k_sketch_wt<<<dim3((unsigned)ceil_div(K, 256), (unsigned)nsplit, ztiles), dim3(256), 0, s>>>(
+        W, N, K, ldw, X, e, w.p);
+    SVDQ_CHECK_LAUNCH();
+    k_reduce_splits<<<dim3((unsigned)ceil_div(K * ell, 256)), dim3(256), 0, s>>>(
+        w.p, K, e, nsplit, lambda, Y);
+    SVDQ_CHECK_LAUNCH();
+    return hipSuccess;
+  };
+  // Z (N x ell) = W diag(λ) Q  for Q (K x ell)
+  auto at_times = [&](const float* Qm, float* Z) -> hipError_t {
+    const int64_t nsplit = ceil_div(K, kSplitRows);
+    k_sketch_w<<<dim3((unsigned)ceil_div(N, 64), (unsigned)nsplit, ztiles), dim3(256), 0, s>>>(
+        W, N, K, ldw, lambda, Qm, e, w.p);
+    SVDQ_CHECK_LAUNCH();
+    k_reduce_splits<<<dim3((unsigned)ceil_div(N * ell, 256)), dim3(256), 0, s>>>(
+        w.p, N, e, nsplit, nullptr, Z);
+    SVDQ_CHECK_LAUNCH();
+    return hipSuccess;
+  };
+  auto gram = [&](const float* M, int64_t rows, double* G) -> hipError_t {
+    const int64_t nb = ceil_div(rows, kGramRows);
+    k_gram_partial<<<dim3((unsigned)nb), dim3(256), 0, s>>>(M, rows, e, w.gp);
+    SVDQ_CHECK_LAUNCH();
+    k_gram_reduce<<<dim3((unsigned)ceil_div(ell * ell, 256)), dim3(256), 0, s>>>(w.gp, nb, e, G);
+    SVDQ_CHECK_LAUNCH();
+    return hipSuccess;
+  };
+  // M (rows x ell) <- an orthonormal basis of its columns (Cholesky-QR twice); tmp is scratch
+  auto orth = [&](float*& M, float*& tmp, int64_t rows) -> hipError_t {
+    for (int pass = 0; pass < 2; ++pass) {
+      if ((err = gram(M, rows, w.g)) != hipSuccess) return err;
+      k_chol_inv<<<dim3(1), dim3(256), 0, s>>>(w.g, e, w.r, w.rinv);
+      SVDQ_CHECK_LAUNCH();
+      k_apply_rinv<<<dim3((unsigned)ceil_div(rows * ell, 256)), dim3(256), 0, s>>>(M, rows, e,
+                                                                                  w.rinv, tmp);
+      SVDQ_CHECK_LAUNCH();
+      float* t = M;
+      M = tmp;
+      tmp = t;
+    }
+    return hipSuccess;
+  };
+
+  float *y = w.y, *yt = w.yt, *z = w.z, *zt = w.zt;
+  if ((err = a_times(omega, y)) != hipSuccess) return err;
+  if ((err = orth(y, yt, K)) != hipSuccess) return err;
+  for (int it = 0; it < power_iters; ++it) {
+    if ((err = at_times(y, z)) != hipSuccess) return err;
+    if ((err = orth(z, zt, N)) != hipSuccess) return err;
+    if ((err = a_times(z, y)) != hipSuccess) return err;
+    if ((err = orth(y, yt, K)) != hipSuccess) return err;
+  }
+  if ((err = at_times(y, z)) != hipSuccess) return err;       // Z = Aᵀ Q = Bᵀ
+  if ((err = gram(z, N, w.g)) != hipSuccess) return err;      // B Bᵀ
+  k_jacobi<<<dim3(1), dim3(kJacobiThreads), 0, s>>>(w.g, e, w.v, w.u, w.eig);
+  SVDQ_CHECK_LAUNCH();
+  const int64_t nout = (r * K) + (N * r);
+  k_factors<<<dim3((unsigned)ceil_div(nout, 256)), dim3(256), 0, s>>>(
+      y, z, N, K, e, (int)r, w.u, w.eig, lora_down, lora_up, sigma);
+  SVDQ_CHECK_LAUNCH();
+#undef SVDQ_CHECK_LAUNCH
+  return hipSuccess;
+}
+
+}  // namespace svdq

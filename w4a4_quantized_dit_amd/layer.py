@@ -68,6 +68,26 @@ def bits_lost(ax, lam=None, block=16):
     return out
 
 
+def lowrank_factors(W, lam, omega, r, power_iters=2):
+    """Randomized rank-r factors of diag(λ)·Wᵀ on the GPU: (lora_down [r, K], lora_up [N, r],
+    sigma [r]).  omega [N, ell] fp32 is the caller's random matrix (ell >= r)."""
+    torch = _torch()
+    N, K = W.shape
+    ell = omega.shape[1]
+    dev = W.device
+    down = torch.empty(r, K, dtype=torch.bfloat16, device=dev)
+    up = torch.empty(N, r, dtype=torch.bfloat16, device=dev)
+    sigma = torch.empty(r, dtype=torch.float32, device=dev)
+    nbytes = _lib.svdq_lowrank_workspace_bytes(N, K, ell)
+    if nbytes < 0:
+        raise ValueError(f"unsupported sketch width {ell}")
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    _lib.svdq_lowrank_factors(W, lam, omega, r, power_iters, down, up, sigma,
+                              ws[off:off + nbytes])
+    return down, up, sigma
+
+
 def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
     """Quantised residual of diag(λ)·W − L1·L2 (W [N, K] bf16)."""
     torch = _torch()
