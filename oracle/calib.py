@@ -13,7 +13,9 @@ Readings where the pages are silent:
   * λ formula: the SmoothQuant α-migration, λ_k = ax_k^α / aw_k^(1-α), with ax the selected
     per-channel activation absmax and aw the per-input-channel absmax of the original weight.
     For α = 0.5 it is computed as sqrt(ax / aw) in float32 (division and square root each
-    correctly rounded); other α use float64 powers rounded once to float32.
+    correctly rounded); other α use float64 powers rounded once to float32.  α itself is a
+    float32 value (the migration strength as the layer stores it), and both exponents α and
+    1 − α are exact in float64.
   * zero guard: λ_k = 1 when ax_k == 0 or aw_k == 0; modality mask 0 means λ = 1.
   * mask selection: ax_sel = max over the modalities whose bit is set (bit 0 text, bit 1 video,
     bit 2 audio) of that modality's absmax (rows of the other modalities are ignored).
@@ -73,6 +75,7 @@ def lambda_from_stats(ax, aw, mask, alpha=0.5):
     aw = np.asarray(aw, dtype=F32)
     ok = (sel != 0) & (aw != 0)
     lam = np.ones(K, dtype=F32)
+    alpha = float(F32(alpha))                 # the float32 α, widened exactly
     if alpha == 0.5:
         ratio = (sel[ok] / aw[ok]).astype(F32)
         lam[ok] = np.sqrt(ratio).astype(F32)
