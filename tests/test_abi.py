@@ -143,3 +143,42 @@ def test_lowrank_validation(lib):
     assert call(q=9) == INVALID
     assert call(wsb=need - 1) == SHAPE and "workspace" in _err(lib)
     assert call(ldw=250) == SHAPE
+
+
+def test_lambda_search_validation(lib):
+    import ctypes
+    f = lib.svdq_lambda_search
+    ws = 1 << 30
+    need = lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 40, 32, 1024, 39)
+    assert need > 0
+    assert lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 161, 32, 1024, 39) == -1
+    assert lib.svdq_lambda_search_workspace_bytes(4, 512, 256, 40, 32, 1024, 39) == -1
+    assert lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 0, 0, 1024, 39) > 0
+    grid = (ctypes.c_float * 39)(*[i / 40 for i in range(1, 40)])
+    bad = (ctypes.c_float * 2)(0.5, 1.0)
+
+    def call(**kw):
+        a = dict(X=P, M=4096, K=256, ldx=256, W=P, N=512, ldw=256, ax=P, aw=P, mask=7,
+                 al=ctypes.cast(grid, ctypes.c_void_p), na=39, fmt=0, om=P, ell=40, r=32, q=2,
+                 rows=P, nr=1024, sc=P, best=P, idx=P, ws=ws, wsb=need)
+        a.update(kw)
+        return f(a["X"], a["M"], a["K"], a["ldx"], a["W"], a["N"], a["ldw"], a["ax"], a["aw"],
+                 a["mask"], a["al"], a["na"], a["fmt"], a["om"], a["ell"], a["r"], a["q"],
+                 a["rows"], a["nr"], a["sc"], a["best"], a["idx"], a["ws"], a["wsb"], None)
+    assert call(X=None) == NULLP
+    assert call(al=None) == NULLP
+    assert call(om=None) == NULLP                        # r > 0 needs Ω
+    assert call(fmt=7) == INVALID
+    assert call(N=500) == SHAPE
+    assert call(K=200, ldx=200, ldw=200) == SHAPE
+    assert call(ldx=128) == SHAPE
+    assert call(mask=8) == INVALID
+    assert call(na=0) == INVALID
+    assert call(al=ctypes.cast(bad, ctypes.c_void_p), na=2) == INVALID and "alphas[1]" in _err(lib)
+    assert call(r=12) == SHAPE                           # rank not a multiple of 8
+    assert call(ell=24) == SHAPE                         # ell < r
+    assert call(q=9) == INVALID
+    assert call(nr=0) == SHAPE
+    assert call(M=0) == SHAPE
+    assert call(ws=ws + 64) == SHAPE
+    assert call(wsb=need - 1) == SHAPE and "workspace" in _err(lib)

@@ -169,6 +169,64 @@ svdq_status svdq_lowrank_factors(const uint16_t* W, int64_t N, int64_t K, int64_
                     fn);
 }
 
+int64_t svdq_lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
+                                           int64_t n_rows, int64_t n_alpha) {
+  if (fmt < 0 || fmt > 3 || N < 1 || K < 1 || n_rows < 1 || n_alpha < 1 || r < 0) return -1;
+  if (r > 0 && (ell < r || ell > svdq::lowrank_max_ell())) return -1;
+  return svdq::lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha);
+}
+
+svdq_status svdq_lambda_search(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                               const uint16_t* W, int64_t N, int64_t ldw, const float* ax,
+                               const float* aw, uint32_t modality_mask, const float* alphas,
+                               int64_t n_alpha, int fmt, const float* omega, int64_t ell,
+                               int64_t r, int power_iters, const int32_t* rows, int64_t n_rows,
+                               double* scores, float* best_lambda, int32_t* best_index,
+                               void* workspace, int64_t workspace_bytes, svdq_stream_t stream) {
+  const char* fn = "svdq_lambda_search";
+  TRY(check_fmt(fn, fmt));
+  REQUIRE_PTR(X); REQUIRE_PTR(W); REQUIRE_PTR(ax); REQUIRE_PTR(aw); REQUIRE_PTR(alphas);
+  REQUIRE_PTR(rows); REQUIRE_PTR(scores); REQUIRE_PTR(best_lambda); REQUIRE_PTR(best_index);
+  REQUIRE_PTR(workspace);
+  REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(W); REQUIRE_ALIGNED(omega);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+  if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldx", ldx, K));
+  TRY(check_ld(fn, "ldw", ldw, K));
+  if (N < 1 || N % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn,
+                (long long)N);
+  if (modality_mask > 7u) return fail(SVDQ_INVALID_ARG, "%s: modality_mask=%u > 7", fn, modality_mask);
+  if (n_alpha < 1 || n_alpha > 1024)
+    return fail(SVDQ_INVALID_ARG, "%s: n_alpha=%lld must lie in [1, 1024]", fn, (long long)n_alpha);
+  for (int64_t i = 0; i < n_alpha; ++i)
+    if (!(alphas[i] > 0.0f && alphas[i] < 1.0f))
+      return fail(SVDQ_INVALID_ARG, "%s: alphas[%lld] must lie in (0, 1)", fn, (long long)i);
+  TRY(check_rank(fn, r));
+  if (r > 0) {
+    REQUIRE_PTR(omega);
+    const int64_t lim = svdq::lowrank_max_ell();
+    if (ell < r || ell > lim || ell > N || ell > K)
+      return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: need r (%lld) <= ell (%lld) <= min(N, K, %lld)",
+                  fn, (long long)r, (long long)ell, (long long)lim);
+    if (power_iters < 0 || power_iters > 8)
+      return fail(SVDQ_INVALID_ARG, "%s: power_iters=%d must lie in [0, 8]", fn, power_iters);
+  }
+  if (n_rows < 1)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: n_rows=%lld must be >= 1", fn, (long long)n_rows);
+  const int64_t need = svdq::lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha);
+  if (workspace_bytes < need)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace of %lld bytes, needs %lld", fn,
+                (long long)workspace_bytes, (long long)need);
+  return hip_result(svdq::launch_lambda_search(X, M, ldx, W, N, K, ldw, ax, aw, modality_mask, alphas,
+                                               n_alpha, fmt, omega, ell, r, power_iters, rows,
+                                               n_rows, scores, best_lambda, best_index, workspace,
+                                               reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 svdq_status svdq_bits_lost(const float* ax, const float* lambda, int64_t K, int64_t block,
                            double* out, svdq_stream_t stream) {
   const char* fn = "svdq_bits_lost";

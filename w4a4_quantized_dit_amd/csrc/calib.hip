@@ -198,6 +198,12 @@ hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx
   return hipGetLastError();
 }
 
+hipError_t launch_lambda(const float* ax, const float* aw, int64_t K, uint32_t mask, float alpha,
+                         float* lambda, float* act_amax, hipStream_t s) {
+  k_lambda<<<dim3(1), dim3(1024), 0, s>>>(ax, aw, K, mask, alpha, lambda, act_amax);
+  return hipGetLastError();
+}
+
 hipError_t launch_bits_lost(const float* ax, const float* lambda, int64_t K, int block,
                             double* out, hipStream_t s) {
   k_bits_lost<<<dim3(3), dim3(kBitsThreads), 0, s>>>(ax, lambda, K, block, out);

@@ -11,6 +11,10 @@ hipError_t launch_calibrate(const uint16_t* X, int64_t M, int64_t K, int64_t ldx
                             const int64_t seg[4], const uint16_t* W, int64_t N, int64_t ldw,
                             uint32_t mask, float alpha, int accumulate, float* ax, float* aw,
                             float* lambda, float* act_amax, hipStream_t s);
+// λ and the static activation amax from the calibration statistics (the last step of
+// launch_calibrate).
+hipError_t launch_lambda(const float* ax, const float* aw, int64_t K, uint32_t mask, float alpha,
+                         float* lambda, float* act_amax, hipStream_t s);
 hipError_t launch_bits_lost(const float* ax, const float* lambda, int64_t K, int block,
                             double* out, hipStream_t s);
 int64_t lowrank_workspace_bytes(int64_t N, int64_t K, int64_t ell);
@@ -61,5 +65,15 @@ hipError_t launch_score(const uint16_t* Y, int64_t ldy, const uint16_t* X, int64
                         const uint16_t* W, int64_t ldw, int64_t M, int64_t N, int64_t K,
                         const int32_t* rows, const int8_t* grp, int64_t n_rows, double* sums,
                         hipStream_t s);
+
+int64_t lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
+                                      int64_t n_rows, int64_t n_alpha);
+hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W, int64_t N,
+                                int64_t K, int64_t ldw, const float* ax, const float* aw,
+                                uint32_t mask, const float* alphas, int64_t n_alpha, int fmt,
+                                const float* omega, int64_t ell, int64_t r, int power_iters,
+                                const int32_t* rows, int64_t n_rows, double* scores,
+                                float* best_lambda, int32_t* best_index, void* workspace,
+                                hipStream_t s);
 
 }  // namespace svdq

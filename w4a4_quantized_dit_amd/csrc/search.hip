@@ -1,0 +1,178 @@
+// λ grid search against the layer's output error ("MiniMax-H3 NVFP4 — what the smoothing scale
+// should be calibrated on", sections "Calibration" — a grid of candidate λ scored against the
+// OutputsError objective — and "The metric that picks the winner also hides the cost" — that
+// objective is the relative L2 of the layer output against bf16 on rows drawn uniformly from the
+// packed sequence).  For each α of the grid, entirely on the device and in stream order:
+//   λ_α from the calibration statistics; rank-r factors of diag(λ_α)·Wᵀ (randomized SVD);
+//   residual weight quantisation; activation quantisation of the sampled rows (static amax of
+//   λ_α) with the low-rank down-projection; the W4A4 GEMM; relative L2 against bf16(X·Wᵀ)
+// then the first α of smallest error is selected and its λ copied out.  The per-candidate
+// steps are the library's own launches; this file adds the row gather and the bookkeeping.
+#include "device.h"
+#include "launch.h"
+
+namespace svdq {
+
+namespace {
+
+// Xs[i, :] = X[rows[i], :]  (16 bytes per thread; an index outside [0, M) reads the nearest row)
+__global__ __launch_bounds__(256) void k_gather_rows(const uint16_t* __restrict__ X, int64_t M,
+                                                     int64_t ldx, const int32_t* __restrict__ rows,
+                                                     int64_t n_rows, int64_t K,
+                                                     uint16_t* __restrict__ Xs) {
+  const int64_t per_row = K / 8;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= n_rows * per_row) return;
+  const int64_t i = t / per_row, c = (t % per_row) * 8;
+  int64_t m = rows[i];
+  m = m < 0 ? 0 : (m < M ? m : M - 1);
+  *reinterpret_cast<u32x4_t*>(Xs + i * K + c) =
+      *reinterpret_cast<const u32x4_t*>(X + m * ldx + c);
+}
+
+// identity row list and one scoring group (3: the uniform rows) for the gathered rows
+__global__ __launch_bounds__(256) void k_rows_setup(int64_t n_rows, int32_t* __restrict__ ids,
+                                                    int8_t* __restrict__ grp) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < n_rows) {
+    ids[t] = (int32_t)t;
+    grp[t] = 3;
+  }
+}
+
+__global__ void k_zero_sums(double* __restrict__ sums) {
+  if (threadIdx.x < 8) sums[threadIdx.x] = 0.0;
+}
+
+// score = sqrt(Σ(Y−Y_ref)²) / sqrt(ΣY_ref²) of group 3; +inf when the reference is all zero
+__global__ void k_finish_score(const double* __restrict__ sums, double* __restrict__ score) {
+  if (threadIdx.x == 0) {
+    const double d = sums[6], r = sums[7];
+    *score = r > 0.0 ? sqrt(d) / sqrt(r) : __builtin_huge_val();
+  }
+}
+
+// first index of the smallest score (NaN never wins); its λ copied to best_lambda
+__global__ __launch_bounds__(256) void k_pick(const double* __restrict__ scores, int64_t n,
+                                              const float* __restrict__ lam_all, int64_t K,
+                                              float* __restrict__ best_lambda,
+                                              int32_t* __restrict__ best_index) {
+  __shared__ int64_t s_best;
+  if (threadIdx.x == 0) {
+    int64_t b = 0;
+    for (int64_t i = 1; i < n; ++i)
+      if (scores[i] < scores[b] || scores[b] != scores[b]) b = i;
+    s_best = b;
+    *best_index = (int32_t)b;
+  }
+  __syncthreads();
+  for (int64_t k = threadIdx.x; k < K; k += 256) best_lambda[k] = lam_all[s_best * K + k];
+}
+
+int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+int64_t code_bytes(int fmt, int64_t rows, int64_t K) { return fmt == 3 ? rows * K : rows * K / 2; }
+int64_t scale_bytes(int fmt, int64_t rows, int64_t K) {
+  return fmt == 0 ? rows * K / 16 : fmt == 1 ? rows * (K / 64) * 2 : rows * K / 32;
+}
+
+struct SearchWs {
+  float *lam_all, *amax, *g_w, *g_a, *D;
+  uint16_t *down, *up, *xs, *ys;
+  uint8_t *w_codes, *w_scales, *a_codes, *a_scales;
+  int32_t* ids;
+  int8_t* grp;
+  double* sums;
+  void* lowrank;
+  int64_t bytes;
+};
+
+SearchWs carve(void* base, int fmt, int64_t N, int64_t K, int64_t ell, int64_t r, int64_t S,
+               int64_t n_alpha) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    void* p = b ? b + off : nullptr;
+    off += align256(bytes > 0 ? bytes : 1);
+    return p;
+  };
+  SearchWs w;
+  w.lowrank = r > 0 ? take(lowrank_workspace_bytes(N, K, ell)) : nullptr;
+  w.lam_all = static_cast<float*>(take(n_alpha * K * 4));
+  w.amax = static_cast<float*>(take(n_alpha * 4));
+  w.g_w = static_cast<float*>(take(4));
+  w.g_a = static_cast<float*>(take(4));
+  w.D = static_cast<float*>(take(S * (r > 0 ? r : 1) * 4));
+  w.down = static_cast<uint16_t*>(take((r > 0 ? r : 1) * K * 2));
+  w.up = static_cast<uint16_t*>(take(N * (r > 0 ? r : 1) * 2));
+  w.xs = static_cast<uint16_t*>(take(S * K * 2));
+  w.ys = static_cast<uint16_t*>(take(S * N * 2));
+  w.w_codes = static_cast<uint8_t*>(take(code_bytes(fmt, N, K)));
+  w.w_scales = static_cast<uint8_t*>(take(scale_bytes(fmt, N, K)));
+  w.a_codes = static_cast<uint8_t*>(take(code_bytes(fmt, S, K)));
+  w.a_scales = static_cast<uint8_t*>(take(scale_bytes(fmt, S, K)));
+  w.ids = static_cast<int32_t*>(take(S * 4));
+  w.grp = static_cast<int8_t*>(take(S));
+  w.sums = static_cast<double*>(take(8 * 8));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+int64_t lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
+                                      int64_t n_rows, int64_t n_alpha) {
+  return carve(nullptr, fmt, N, K, ell, r, n_rows, n_alpha).bytes;
+}
+
+hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W, int64_t N,
+                                int64_t K, int64_t ldw, const float* ax, const float* aw,
+                                uint32_t mask, const float* alphas, int64_t n_alpha, int fmt,
+                                const float* omega, int64_t ell, int64_t r, int power_iters,
+                                const int32_t* rows, int64_t n_rows, double* scores,
+                                float* best_lambda, int32_t* best_index, void* workspace,
+                                hipStream_t s) {
+  const SearchWs w = carve(workspace, fmt, N, K, ell, r, n_rows, n_alpha);
+  hipError_t e;
+#define SVDQ_TRY_HIP(x)                  \
+  do {                                   \
+    if ((e = (x)) != hipSuccess) return e; \
+  } while (0)
+  k_gather_rows<<<dim3((unsigned)ceil_div(n_rows * (K / 8), 256)), dim3(256), 0, s>>>(
+      X, M, ldx, rows, n_rows, K, w.xs);
+  SVDQ_TRY_HIP(hipGetLastError());
+  k_rows_setup<<<dim3((unsigned)ceil_div(n_rows, 256)), dim3(256), 0, s>>>(n_rows, w.ids, w.grp);
+  SVDQ_TRY_HIP(hipGetLastError());
+  const uint16_t* down = r > 0 ? w.down : nullptr;
+  const uint16_t* up = r > 0 ? w.up : nullptr;
+  float* D = r > 0 ? w.D : nullptr;
+  for (int64_t i = 0; i < n_alpha; ++i) {
+    float* lam = w.lam_all + i * K;
+    float* amax = w.amax + i;
+    SVDQ_TRY_HIP(launch_lambda(ax, aw, K, mask, alphas[i], lam, amax, s));
+    if (r > 0)
+      SVDQ_TRY_HIP(launch_lowrank(W, N, K, ldw, lam, omega, ell, r, power_iters, w.down, w.up,
+                                  nullptr, w.lowrank, s));
+    SVDQ_TRY_HIP(launch_quantize_weight(fmt, W, N, K, ldw, lam, down, up, r, w.w_codes,
+                                        w.w_scales, fmt == 0 ? w.g_w : nullptr, s));
+    SVDQ_TRY_HIP(launch_quant_act(fmt, w.xs, n_rows, K, K, lam, fmt == 0 ? amax : nullptr, down,
+                                  r, w.a_codes, w.a_scales, fmt == 0 ? w.g_a : nullptr, D,
+                                  nullptr, s));
+    SVDQ_TRY_HIP(launch_gemm(fmt, n_rows, N, K, w.a_codes, w.a_scales,
+                             fmt == 0 ? w.g_a : nullptr, w.w_codes, w.w_scales,
+                             fmt == 0 ? w.g_w : nullptr, D, up, r, nullptr, nullptr, w.ys, N, s));
+    k_zero_sums<<<dim3(1), dim3(64), 0, s>>>(w.sums);
+    SVDQ_TRY_HIP(hipGetLastError());
+    SVDQ_TRY_HIP(launch_score(w.ys, N, w.xs, K, W, ldw, n_rows, N, K, w.ids, w.grp, n_rows,
+                              w.sums, s));
+    k_finish_score<<<dim3(1), dim3(64), 0, s>>>(w.sums, scores + i);
+    SVDQ_TRY_HIP(hipGetLastError());
+  }
+  k_pick<<<dim3(1), dim3(256), 0, s>>>(scores, n_alpha, w.lam_all, K, best_lambda, best_index);
+  SVDQ_TRY_HIP(hipGetLastError());
+#undef SVDQ_TRY_HIP
+  return hipSuccess;
+}
+
+}  // namespace svdq

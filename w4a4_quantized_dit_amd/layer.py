@@ -88,6 +88,32 @@ def lowrank_factors(W, lam, omega, r, power_iters=2):
     return down, up, sigma
 
 
+# The 39 migration strengths α = i/40 of the λ grid (λ_k = a_k^α / w_k^(1−α)).
+ALPHA_GRID = tuple(i / 40.0 for i in range(1, 40))
+
+
+def lambda_search(X, W, state, alphas, rows, fmt=NVFP4, omega=None, r=32, power_iters=2,
+                  mask=7):
+    """λ grid search on the GPU: for each α the layer's output error on the sampled rows
+    (device int32 indices into X); returns (scores fp64 [len(alphas)], best λ, best index)."""
+    torch = _torch()
+    N, K = W.shape
+    dev = X.device
+    ell = omega.shape[1] if omega is not None else 0
+    scores = torch.empty(len(alphas), dtype=torch.float64, device=dev)
+    best = torch.empty(K, dtype=torch.float32, device=dev)
+    idx = torch.empty(1, dtype=torch.int32, device=dev)
+    nbytes = _lib.svdq_lambda_search_workspace_bytes(fmt, N, K, ell, r, rows.numel(),
+                                                     len(alphas))
+    if nbytes < 0:
+        raise ValueError("unsupported search shape")
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
+    off = (-ws.data_ptr()) % 256
+    _lib.svdq_lambda_search(X, W, state["ax"], state["aw"], mask, alphas, fmt, omega, r,
+                            power_iters, rows, scores, best, idx, ws[off:off + nbytes])
+    return scores, best, idx
+
+
 def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
     """Quantised residual of diag(λ)·W − L1·L2 (W [N, K] bf16)."""
     torch = _torch()
