@@ -77,7 +77,12 @@ def _orth(M):
 def randomized_factors(W_bits, lam, r, omega, power_iters):
     """Randomized rank-r factors: (lora_down bf16 bits [r, K], lora_up bf16 bits [N, r],
     σ float64 [r], the unrounded L1 [K, r] and L2 [r, N] in float64)."""
-    A = smoothed_weight(W_bits, lam).T                 # K x N
+    return randomized_factors_of(smoothed_weight(W_bits, lam).T, r, omega, power_iters)
+
+
+def randomized_factors_of(A, r, omega, power_iters):
+    """The same factors for any K x N matrix A (float64)."""
+    A = np.asarray(A, dtype=np.float64)
     omega = np.asarray(omega, dtype=np.float64)        # N x ℓ
     Q = _orth(A @ omega)
     for _ in range(power_iters):

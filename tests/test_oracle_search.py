@@ -117,3 +117,63 @@ def test_the_low_rank_branch_lowers_the_error_on_outlier_data():
     s0, _, _ = OSe.lambda_search(X, W, ax, aw, 7, alphas, "nvfp4", rows)
     s8, _, _ = OSe.lambda_search(X, W, ax, aw, 7, alphas, "nvfp4", rows, omega, 8, 2)
     assert np.all(s8 < s0), (s0, s8)
+
+
+@pytest.mark.parametrize("fmt", ["nvfp4", "int4", "mxfp4"])
+def test_each_refit_step_lowers_the_weight_error_for_the_fixed_quantised_residual(fmt):
+    # iterate t + 1 takes the best rank-r approximation of E_t = W' − deq(Q(R_t)), so for that
+    # fixed quantised residual it is no worse than iterate t's branch (Eckart–Young; the power
+    # iterations make the randomized factors optimal to rounding at this size), up to the bf16
+    # rounding of the new factors
+    from oracle import svd as OS
+    from oracle.formats import bf16_bits_to_f32
+    cfg = synth.config(0)
+    X = synth.gen.x_bits(cfg)
+    W = synth.gen.weight_bits(cfg["N"], cfg["K"])
+    ax, aw, _, _ = OC.calibrate(X, cfg["seg"], W, 7)
+    r = 8
+    omega = np.random.default_rng(4).standard_normal((cfg["N"], 24)).astype(F32)
+    s, lam, facs = OSe.candidate_iterates(X, W, ax, aw, 7, F32(0.5), fmt, np.arange(64), omega,
+                                          r, power_iters=6, refit_iters=3)
+    Wp = OS.smoothed_weight(W, lam)
+
+    def branch(f):
+        d = bf16_bits_to_f32(f[0]).astype(np.float64)
+        u = bf16_bits_to_f32(f[1]).astype(np.float64)
+        return u @ d                                          # [N, K]
+
+    for t in range(3):
+        wt = OL.prepare_weight(W, lam, facs[t][0], facs[t][1], fmt)
+        E = Wp - OSe.dequantized_weight(wt, fmt)
+        # bf16 rounding moves each factor by at most 2^-9 of itself, so the branch moves by at
+        # most about 2^-8 · ||up||_F · ||down||_F
+        d = bf16_bits_to_f32(facs[t + 1][0]).astype(np.float64)
+        u = bf16_bits_to_f32(facs[t + 1][1]).astype(np.float64)
+        rounding = 1.01 * 2.0 ** -8 * np.linalg.norm(u) * np.linalg.norm(d)
+        before = np.linalg.norm(E - branch(facs[t]))
+        after = np.linalg.norm(E - branch(facs[t + 1]))
+        assert after <= before + rounding, (fmt, t, before, after, rounding)
+        # the unrounded new branch is the best rank-r approximation of E_t (an exact SVD; the
+        # singular values fall from about 20 to about 2 after the r-th, so it is unique)
+        U, sv, Vt = np.linalg.svd(E, full_matrices=False)
+        best_r = (U[:, :r] * sv[:r]) @ Vt[:r]
+        assert sv[r - 1] > 5 * sv[r]
+        assert np.linalg.norm(facs[t + 1][2] - best_r) <= 1e-9 * np.linalg.norm(best_r)
+    assert len(s) == 4 and np.all(np.isfinite(s))
+
+
+def test_refit_needs_a_branch_and_zero_iterations_is_the_plain_candidate():
+    cfg = synth.config(0)
+    X = synth.gen.x_bits(cfg)
+    W = synth.gen.weight_bits(cfg["N"], cfg["K"])
+    ax, aw, _, _ = OC.calibrate(X, cfg["seg"], W, 7)
+    with pytest.raises(ValueError):
+        OSe.candidate(X, W, ax, aw, 7, F32(0.5), "nvfp4", np.arange(8), refit_iters=2)
+    omega = np.random.default_rng(5).standard_normal((cfg["N"], 16)).astype(F32)
+    s3, _, f3 = OSe.candidate_iterates(X, W, ax, aw, 7, F32(0.5), "nvfp4", np.arange(64), omega,
+                                       8, 2, 3)
+    s0, _, f0 = OSe.candidate_iterates(X, W, ax, aw, 7, F32(0.5), "nvfp4", np.arange(64), omega,
+                                       8, 2, 0)
+    assert s3[0] == s0[0] and np.array_equal(f3[0][0], f0[0][0])
+    sc, _ = OSe.candidate(X, W, ax, aw, 7, F32(0.5), "nvfp4", np.arange(64), omega, 8, 2, 3)
+    assert sc == s3.min()
