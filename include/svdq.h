@@ -148,31 +148,42 @@ svdq_status svdq_lowrank_factors(const uint16_t* W, int64_t N, int64_t K, int64_
 /*
  * λ grid search against the layer's output error ("MiniMax-H3 NVFP4 — what the smoothing scale
  * should be calibrated on", sections "Calibration": candidate λ scored against the OutputsError
- * objective, and "The metric that picks the winner also hides the cost": that objective is the
- * relative L2 against bf16 on rows drawn uniformly from the packed sequence).  For each
- * alphas[i] (host array, each in (0, 1)), in stream order on the device:
+ * objective with a number of low-rank refit iterations each, and "The metric that picks the
+ * winner also hides the cost": that objective is the relative L2 against bf16 on rows drawn
+ * uniformly from the packed sequence).  For each alphas[i] (host array, each in (0, 1)), in
+ * stream order on the device:
  *   λ_i, act_amax_i from the statistics ax [3, K] and aw [K] (as svdq_calibrate_lambda, same
  *   modality_mask); when r > 0 the factors of svdq_lowrank_factors (omega [N, ell], ell,
- *   power_iters); svdq_quantize_weight; svdq_quant_act_lowrank_down on the n_rows sampled rows
- *   X[rows[j], :] (NVFP4 with the static act_amax_i); svdq_w4a4_gemm;
- *   scores[i] = sqrt(Σ(Y − Y_ref)²) / sqrt(ΣY_ref²) over those rows, Y_ref = bf16(X·Wᵀ)
- * then best_index = the first i of smallest score and best_lambda = λ_best.
+ *   power_iters); then for iterates t = 0 .. refit_iters:
+ *     svdq_quantize_weight; svdq_quant_act_lowrank_down on the n_rows sampled rows X[rows[j], :]
+ *     (NVFP4 with the static act_amax_i); svdq_w4a4_gemm;
+ *     s_it = sqrt(Σ(Y − Y_ref)²) / sqrt(ΣY_ref²) over those rows, Y_ref = bf16(X·Wᵀ);
+ *     unless t is the last iterate, the factors are refit: the rank-r factors (same omega,
+ *     power_iters) of E = λ_i·W − deq(Q(R)), what the quantised residual leaves of the
+ *     smoothed weight, rounded once to fp32 (the page does not define its refit; this is the
+ *     alternating reading);
+ *   scores[i] = min over t of s_it (iter_scores[i·(refit_iters+1) + t] = s_it when given)
+ * then best_index = the first i of smallest score, best_lambda = λ_best and, when best_down /
+ * best_up are given (r > 0), the factors of the best iterate of that candidate ([r, K], [N, r]
+ * bf16).  refit_iters > 0 needs r > 0.
  * X [M, K], W [N, K] bf16; rows device int32 [n_rows], each in [0, M) (an index outside reads
- * the nearest row); scores device fp64
- * [n_alpha]; best_lambda device fp32 [K]; best_index device int32 [1].  K and N multiples of
- * 256; r as svdq_quantize_weight.  workspace: at least svdq_lambda_search_workspace_bytes(...)
- * bytes, 256-byte aligned, the caller's.  The sums behind a score are fp64 atomics, so scores
- * repeat to fp64 rounding; everything else (λ, factors, codes, Y) is bit-reproducible.
+ * the nearest row); scores / iter_scores device fp64; best_lambda device fp32 [K]; best_index
+ * device int32 [1].  K and N multiples of 256; r as svdq_quantize_weight.  workspace: at least
+ * svdq_lambda_search_workspace_bytes(...) bytes (−1: unsupported), 256-byte aligned, the
+ * caller's.  The sums behind a score are fp64 atomics, so scores repeat to fp64 rounding; λ is
+ * bit-reproducible.
  */
 int64_t svdq_lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
-                                           int64_t n_rows, int64_t n_alpha);
+                                           int64_t n_rows, int64_t n_alpha, int refit_iters);
 svdq_status svdq_lambda_search(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                const uint16_t* W, int64_t N, int64_t ldw, const float* ax,
                                const float* aw, uint32_t modality_mask, const float* alphas,
                                int64_t n_alpha, int fmt, const float* omega, int64_t ell,
-                               int64_t r, int power_iters, const int32_t* rows, int64_t n_rows,
-                               double* scores, float* best_lambda, int32_t* best_index,
-                               void* workspace, int64_t workspace_bytes, svdq_stream_t stream);
+                               int64_t r, int power_iters, int refit_iters, const int32_t* rows,
+                               int64_t n_rows, double* scores, double* iter_scores,
+                               float* best_lambda, int32_t* best_index, uint16_t* best_down,
+                               uint16_t* best_up, void* workspace, int64_t workspace_bytes,
+                               svdq_stream_t stream);
 
 /*
  * Weight preparation ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph:

@@ -149,22 +149,27 @@ def test_lambda_search_validation(lib):
     import ctypes
     f = lib.svdq_lambda_search
     ws = 1 << 30
-    need = lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 40, 32, 1024, 39)
+    need = lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 40, 32, 1024, 39, 0)
     assert need > 0
-    assert lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 161, 32, 1024, 39) == -1
-    assert lib.svdq_lambda_search_workspace_bytes(4, 512, 256, 40, 32, 1024, 39) == -1
-    assert lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 0, 0, 1024, 39) > 0
+    need_refit = lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 40, 32, 1024, 39, 100)
+    assert need_refit >= need + 512 * 256 * 4            # the fp32 refit target
+    assert lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 161, 32, 1024, 39, 0) == -1
+    assert lib.svdq_lambda_search_workspace_bytes(4, 512, 256, 40, 32, 1024, 39, 0) == -1
+    assert lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 0, 0, 1024, 39, 0) > 0
+    assert lib.svdq_lambda_search_workspace_bytes(0, 512, 256, 0, 0, 1024, 39, 3) == -1
     grid = (ctypes.c_float * 39)(*[i / 40 for i in range(1, 40)])
     bad = (ctypes.c_float * 2)(0.5, 1.0)
 
     def call(**kw):
         a = dict(X=P, M=4096, K=256, ldx=256, W=P, N=512, ldw=256, ax=P, aw=P, mask=7,
                  al=ctypes.cast(grid, ctypes.c_void_p), na=39, fmt=0, om=P, ell=40, r=32, q=2,
-                 rows=P, nr=1024, sc=P, best=P, idx=P, ws=ws, wsb=need)
+                 T=0, rows=P, nr=1024, sc=P, its=None, best=P, idx=P, bd=None, bu=None, ws=ws,
+                 wsb=need)
         a.update(kw)
         return f(a["X"], a["M"], a["K"], a["ldx"], a["W"], a["N"], a["ldw"], a["ax"], a["aw"],
-                 a["mask"], a["al"], a["na"], a["fmt"], a["om"], a["ell"], a["r"], a["q"],
-                 a["rows"], a["nr"], a["sc"], a["best"], a["idx"], a["ws"], a["wsb"], None)
+                 a["mask"], a["al"], a["na"], a["fmt"], a["om"], a["ell"], a["r"], a["q"], a["T"],
+                 a["rows"], a["nr"], a["sc"], a["its"], a["best"], a["idx"], a["bd"], a["bu"],
+                 a["ws"], a["wsb"], None)
     assert call(X=None) == NULLP
     assert call(al=None) == NULLP
     assert call(om=None) == NULLP                        # r > 0 needs Ω
@@ -182,3 +187,10 @@ def test_lambda_search_validation(lib):
     assert call(M=0) == SHAPE
     assert call(ws=ws + 64) == SHAPE
     assert call(wsb=need - 1) == SHAPE and "workspace" in _err(lib)
+    assert call(T=-1) == INVALID
+    assert call(T=1001) == INVALID
+    assert call(T=3, r=0, om=None) == INVALID            # refit needs a branch
+    assert call(T=3, wsb=need) == SHAPE                  # the refit target needs room
+    assert call(bd=P) == NULLP                           # best factors go in pairs
+    assert call(bd=P, bu=P, r=0, om=None) == INVALID
+    assert call(bd=MIS, bu=P) == SHAPE

@@ -40,27 +40,34 @@ def _case(M, K, N, seed=0):
     return X, W, ax, aw
 
 
-def _run(L, X, W, ax, aw, alphas, fmt, rows, omega, r, q, mask=7):
+def _run(L, X, W, ax, aw, alphas, fmt, rows, omega, r, q, mask=7, refit=0):
     torch = torch_mod()
     state = dict(ax=dev(ax), aw=dev(aw))
     om = dev(omega) if r > 0 else None
-    scores, best, idx = L.lambda_search(dev_bf16(X), dev_bf16(W), state, [float(a) for a in alphas],
-                                        dev(rows.astype(np.int32)), FMT[fmt], om, r, q, mask)
+    out = L.lambda_search(dev_bf16(X), dev_bf16(W), state, [float(a) for a in alphas],
+                          dev(rows.astype(np.int32)), FMT[fmt], om, r, q, mask, refit_iters=refit,
+                          per_iterate=True)
     torch.cuda.synchronize()
-    return scores.cpu().numpy(), best.cpu().numpy(), int(idx.cpu().numpy()[0])
+    return {k: v.cpu() for k, v in out.items()}
 
 
-def _check(L, X, W, ax, aw, alphas, fmt, rows, r, q=2, ell=None, mask=7, seed=5):
+def _check(L, X, W, ax, aw, alphas, fmt, rows, r, q=2, ell=None, mask=7, seed=5, refit=0):
     N = W.shape[0]
     ell = ell or r + 8
     omega = np.random.default_rng(seed).standard_normal((N, ell)).astype(F32) if r else None
-    g_scores, g_lam, g_idx = _run(L, X, W, ax, aw, alphas, fmt, rows, omega, r, q, mask)
-    o_scores, o_lam, o_idx = OSe.lambda_search(X, W, ax, aw, mask, alphas, fmt, rows, omega, r, q)
+    g = _run(L, X, W, ax, aw, alphas, fmt, rows, omega, r, q, mask, refit)
+    g_scores, g_lam, g_idx = g["scores"].numpy(), g["lam"].numpy(), int(g["index"][0])
+    o_scores, o_lam, o_idx, det = OSe.lambda_search(X, W, ax, aw, mask, alphas, fmt, rows, omega,
+                                                    r, q, refit, details=True)
+    g_it, o_it = g["iter_scores"].numpy(), det["iter_scores"]
+    tol_it = 1e-3 * (1 + o_it) + (0.02 * o_it if r else 0.0)
     tol = 1e-3 * (1 + o_scores) + (0.02 * o_scores if r else 0.0)
-    worst = np.max(np.abs(g_scores - o_scores) / o_scores)
-    print(f"[search] {fmt} r={r} {X.shape}x{W.shape} rows={len(rows)} n_alpha={len(alphas)}: "
-          f"worst relative score difference {worst:.3e}, GPU best {g_idx} ({g_scores[g_idx]:.5f})"
-          f", oracle best {o_idx} ({o_scores[o_idx]:.5f})", flush=True)
+    worst = np.max(np.abs(g_it - o_it) / o_it)
+    print(f"[search] {fmt} r={r} refit={refit} {X.shape}x{W.shape} rows={len(rows)} "
+          f"n_alpha={len(alphas)}: worst relative score difference {worst:.3e}, GPU best {g_idx} "
+          f"({g_scores[g_idx]:.5f}), oracle best {o_idx} ({o_scores[o_idx]:.5f})", flush=True)
+    assert np.all(np.abs(g_it - o_it) <= tol_it), (g_it, o_it)
+    assert np.array_equal(g_scores, g_it.min(axis=1))
     assert np.all(np.abs(g_scores - o_scores) <= tol), (g_scores, o_scores)
     assert g_idx == int(np.argmin(g_scores))
     assert o_scores[g_idx] <= o_scores[o_idx] + 2 * tol[o_idx]
@@ -69,6 +76,7 @@ def _check(L, X, W, ax, aw, alphas, fmt, rows, r, q=2, ell=None, mask=7, seed=5)
     o_lam = OC.lambda_from_stats(ax, aw, mask, F32(alphas[g_idx]))
     ulp = np.abs(g_lam.view(np.int32).astype(np.int64) - o_lam.view(np.int32).astype(np.int64))
     assert ulp.max() <= 1
+    return g, det, (o_scores, o_idx)
 
 
 @pytest.fixture(scope="module")
@@ -107,9 +115,45 @@ def test_one_sampled_row_and_one_candidate(L, small):
     _check(L, X, W, ax, aw, [F32(0.5)], "nvfp4", np.array([17]), r=0)
 
 
+@pytest.mark.parametrize("fmt,r", [("nvfp4", 8), ("int4", 8), ("mxfp4", 16), ("mxfp8", 8)])
+def test_refit_iterations(L, small, fmt, r):
+    X, W, ax, aw = small
+    rows = np.sort(np.random.default_rng(8).choice(X.shape[0], 160, replace=False))
+    g, det, _ = _check(L, X, W, ax, aw, OSe.alpha_grid()[3::9], fmt, rows, r=r, refit=4)
+    assert g["lora_down"].shape == (r, X.shape[1]) and g["lora_up"].shape == (W.shape[0], r)
+
+
+def test_best_factors_reproduce_the_best_score(L, small):
+    """The factors the search returns, run through the layer's own entry points with the
+    winner's λ, give the winner's score again."""
+    torch = torch_mod()
+    X, W, ax, aw = small
+    rows = np.sort(np.random.default_rng(9).choice(X.shape[0], 192, replace=False))
+    omega = np.random.default_rng(10).standard_normal((W.shape[0], 16)).astype(F32)
+    g = _run(L, X, W, ax, aw, OSe.alpha_grid()[::6], "nvfp4", rows, omega, 8, 2, refit=5)
+    i = int(g["index"][0])
+    Xd, Wd = dev_bf16(X), dev_bf16(W)
+    lam = g["lam"].cuda()
+    amax = torch.tensor([OC.act_amax_from_stats(ax, g["lam"].numpy())], device="cuda")
+    down, up = g["lora_down"].cuda(), g["lora_up"].cuda()
+    pw = L.prepare_weight(Wd, lam, down, up, 0)
+    Xs = Xd[torch.from_numpy(rows).long().cuda()].contiguous()
+    codes, scales, ga, D = L.quantize_activation(Xs, lam, amax, down, 0)
+    Y = L.gemm(codes, scales, ga, D, pw, len(rows))
+    torch.cuda.synchronize()
+    from oracle import score as OSc
+    from tests.gpu_common import host_bits
+    sums = OSc.modal_sums(host_bits(Y), OSc.reference_rows(X, W, rows), np.full(len(rows), 3))
+    again = np.sqrt(sums[3, 0]) / np.sqrt(sums[3, 1])
+    best = float(g["scores"][i])
+    print(f"[search] best factors: search score {best:.6f}, layer again {again:.6f}", flush=True)
+    assert abs(again - best) <= 1e-3 * (1 + best)
+
+
 def test_full_size_attention_projection(L):
-    """5120 x 5120, rank 32, 1024 uniform rows of a 16384-row packed sequence: three candidates
-    against the oracle, then the whole 39-point grid timed."""
+    """5120 x 5120, rank 32, 1024 uniform rows of a 16384-row packed sequence: three candidates,
+    and one with two refit iterations, against the oracle; then the whole 39-point grid and 100
+    refit iterations of one candidate timed."""
     torch = torch_mod()
     cfg = synth.config(1)
     M, K, N = cfg["M"], cfg["K"], cfg["N"]
@@ -119,6 +163,7 @@ def test_full_size_attention_projection(L):
     ax, aw, _, _ = OC.calibrate(X, cfg["seg"], W, 7)
     rows = np.sort(np.random.default_rng(6).choice(M, 1024, replace=False))
     _check(L, X, W, ax, aw, [F32(0.25), F32(0.5), F32(0.75)], "nvfp4", rows, r=32, ell=40)
+    _check(L, X, W, ax, aw, [F32(0.5)], "nvfp4", rows, r=32, ell=40, refit=2)
 
     omega = np.random.default_rng(7).standard_normal((N, 40)).astype(F32)
     Xd, Wd, od = dev_bf16(X), dev_bf16(W), dev(omega)
@@ -129,11 +174,22 @@ def test_full_size_attention_projection(L):
     torch.cuda.synchronize()
     t0, t1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     t0.record()
-    scores, best, idx = L.lambda_search(Xd, Wd, state, grid, rd, 0, od, 32, 2)
+    out = L.lambda_search(Xd, Wd, state, grid, rd, 0, od, 32, 2)
     t1.record()
     torch.cuda.synchronize()
-    s = scores.cpu().numpy()
-    assert np.all(np.isfinite(s)) and int(idx.cpu()[0]) == int(np.argmin(s))
+    s, i = out["scores"].cpu().numpy(), int(out["index"].cpu()[0])
+    assert np.all(np.isfinite(s)) and i == int(np.argmin(s))
     print(f"[search] 39 candidates at 5120x5120 r=32, 1024 rows: {t0.elapsed_time(t1):.1f} ms, "
-          f"best α = {grid[int(idx.cpu()[0])]:.3f} (score {s.min():.5f}, α=0.5: {s[19]:.5f})",
-          flush=True)
+          f"best α = {grid[i]:.3f} (score {s.min():.5f}, α=0.5: {s[19]:.5f})", flush=True)
+
+    # 100 refit iterations of the branch for one candidate, timed
+    t0.record()
+    out = L.lambda_search(Xd, Wd, state, [0.5], rd, 0, od, 32, 2, refit_iters=100,
+                          per_iterate=True)
+    t1.record()
+    torch.cuda.synchronize()
+    it = out["iter_scores"].cpu().numpy()[0]
+    assert np.all(np.isfinite(it)) and out["scores"].cpu().numpy()[0] == it.min()
+    print(f"[search] α=0.5 with 100 refits at 5120x5120 r=32: {t0.elapsed_time(t1):.1f} ms; "
+          f"score {it[0]:.5f} -> best {it.min():.5f} at iterate {int(np.argmin(it))} "
+          f"(iterates 1-5: {np.round(it[1:6], 5).tolist()})", flush=True)

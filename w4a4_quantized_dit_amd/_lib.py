@@ -27,11 +27,11 @@ _SIGS = {
     "svdq_bits_lost": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p]),
     "svdq_lowrank_workspace_bytes": (_i64, [_i64, _i64, _i64]),
     "svdq_lambda_search_workspace_bytes": (_i64, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
-                                                  _i64]),
+                                                  _i64, ctypes.c_int]),
     "svdq_lambda_search": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _i64, _i64, _c_p, _c_p,
                                           ctypes.c_uint32, _c_p, _i64, ctypes.c_int, _c_p, _i64,
-                                          _i64, ctypes.c_int, _c_p, _i64, _c_p, _c_p, _c_p, _c_p,
-                                          _i64, _c_p]),
+                                          _i64, ctypes.c_int, ctypes.c_int, _c_p, _i64, _c_p, _c_p,
+                                          _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
     "svdq_lowrank_factors": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _i64, _i64,
                                             ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
     "svdq_quantize_weight": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p, _c_p,
@@ -198,29 +198,36 @@ def svdq_lowrank_factors(W, lam, omega, r, power_iters, lora_down, lora_up, sigm
         workspace.numel(), _stream(stream)))
 
 
-def svdq_lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha):
+def svdq_lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha, refit_iters=0):
     return int(load().svdq_lambda_search_workspace_bytes(int(fmt), int(N), int(K), int(ell),
-                                                         int(r), int(n_rows), int(n_alpha)))
+                                                         int(r), int(n_rows), int(n_alpha),
+                                                         int(refit_iters)))
 
 
-def svdq_lambda_search(X, W, ax, aw, mask, alphas, fmt, omega, r, power_iters, rows, scores,
-                       best_lambda, best_index, workspace, stream=None):
+def svdq_lambda_search(X, W, ax, aw, mask, alphas, fmt, omega, r, power_iters, refit_iters, rows,
+                       scores, iter_scores, best_lambda, best_index, best_down, best_up,
+                       workspace, stream=None):
     """λ grid search (alphas: host floats) scored by the output error on the sampled rows."""
     torch = _torch()
     M, K = X.shape
     N = W.shape[0]
     ell = omega.shape[1] if omega is not None else 0
-    arr = (ctypes.c_float * len(alphas))(*[float(a) for a in alphas])
+    n = len(alphas)
+    arr = (ctypes.c_float * n)(*[float(a) for a in alphas])
     _check(load().svdq_lambda_search(
         _ptr(X, _bf16(), "X"), M, K, X.stride(0), _ptr(W, _bf16(), "W"), N, W.stride(0),
         _ptr(ax, torch.float32, "ax", 3 * K), _ptr(aw, torch.float32, "aw", K), int(mask),
-        ctypes.cast(arr, _c_p), len(alphas), int(fmt),
+        ctypes.cast(arr, _c_p), n, int(fmt),
         _ptr(omega, torch.float32, "omega", N * ell) if omega is not None else None, ell, int(r),
-        int(power_iters), _ptr(rows, torch.int32, "rows"), rows.numel(),
-        _ptr(scores, torch.float64, "scores", len(alphas)),
+        int(power_iters), int(refit_iters), _ptr(rows, torch.int32, "rows"), rows.numel(),
+        _ptr(scores, torch.float64, "scores", n),
+        _ptr(iter_scores, torch.float64, "iter_scores", n * (refit_iters + 1))
+        if iter_scores is not None else None,
         _ptr(best_lambda, torch.float32, "best_lambda", K),
-        _ptr(best_index, torch.int32, "best_index", 1), _ptr(workspace, torch.uint8, "workspace"),
-        workspace.numel(), _stream(stream)))
+        _ptr(best_index, torch.int32, "best_index", 1),
+        _ptr(best_down, _bf16(), "best_down", r * K) if best_down is not None else None,
+        _ptr(best_up, _bf16(), "best_up", N * r) if best_up is not None else None,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, tensor_scale,

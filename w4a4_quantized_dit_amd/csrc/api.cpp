@@ -170,19 +170,22 @@ svdq_status svdq_lowrank_factors(const uint16_t* W, int64_t N, int64_t K, int64_
 }
 
 int64_t svdq_lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
-                                           int64_t n_rows, int64_t n_alpha) {
+                                           int64_t n_rows, int64_t n_alpha, int refit_iters) {
   if (fmt < 0 || fmt > 3 || N < 1 || K < 1 || n_rows < 1 || n_alpha < 1 || r < 0) return -1;
+  if (refit_iters < 0 || (refit_iters > 0 && r == 0)) return -1;
   if (r > 0 && (ell < r || ell > svdq::lowrank_max_ell())) return -1;
-  return svdq::lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha);
+  return svdq::lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha, refit_iters);
 }
 
 svdq_status svdq_lambda_search(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                const uint16_t* W, int64_t N, int64_t ldw, const float* ax,
                                const float* aw, uint32_t modality_mask, const float* alphas,
                                int64_t n_alpha, int fmt, const float* omega, int64_t ell,
-                               int64_t r, int power_iters, const int32_t* rows, int64_t n_rows,
-                               double* scores, float* best_lambda, int32_t* best_index,
-                               void* workspace, int64_t workspace_bytes, svdq_stream_t stream) {
+                               int64_t r, int power_iters, int refit_iters, const int32_t* rows,
+                               int64_t n_rows, double* scores, double* iter_scores,
+                               float* best_lambda, int32_t* best_index, uint16_t* best_down,
+                               uint16_t* best_up, void* workspace, int64_t workspace_bytes,
+                               svdq_stream_t stream) {
   const char* fn = "svdq_lambda_search";
   TRY(check_fmt(fn, fmt));
   REQUIRE_PTR(X); REQUIRE_PTR(W); REQUIRE_PTR(ax); REQUIRE_PTR(aw); REQUIRE_PTR(alphas);
@@ -214,17 +217,28 @@ svdq_status svdq_lambda_search(const uint16_t* X, int64_t M, int64_t K, int64_t 
     if (power_iters < 0 || power_iters > 8)
       return fail(SVDQ_INVALID_ARG, "%s: power_iters=%d must lie in [0, 8]", fn, power_iters);
   }
+  if (refit_iters < 0 || refit_iters > 1000)
+    return fail(SVDQ_INVALID_ARG, "%s: refit_iters=%d must lie in [0, 1000]", fn, refit_iters);
+  if (refit_iters > 0 && r == 0)
+    return fail(SVDQ_INVALID_ARG, "%s: refit iterations need a low-rank branch (r > 0)", fn);
+  if ((best_down == nullptr) != (best_up == nullptr))
+    return fail(SVDQ_NULL_POINTER, "%s: best_down and best_up go together", fn);
+  if (best_down != nullptr && r == 0)
+    return fail(SVDQ_INVALID_ARG, "%s: best factors need a low-rank branch (r > 0)", fn);
+  REQUIRE_ALIGNED(best_down); REQUIRE_ALIGNED(best_up);
   if (n_rows < 1)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: n_rows=%lld must be >= 1", fn, (long long)n_rows);
-  const int64_t need = svdq::lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha);
+  const int64_t need =
+      svdq::lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha, refit_iters);
   if (workspace_bytes < need)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace of %lld bytes, needs %lld", fn,
                 (long long)workspace_bytes, (long long)need);
-  return hip_result(svdq::launch_lambda_search(X, M, ldx, W, N, K, ldw, ax, aw, modality_mask, alphas,
-                                               n_alpha, fmt, omega, ell, r, power_iters, rows,
-                                               n_rows, scores, best_lambda, best_index, workspace,
-                                               reinterpret_cast<hipStream_t>(stream)),
-                    fn);
+  return hip_result(
+      svdq::launch_lambda_search(X, M, ldx, W, N, K, ldw, ax, aw, modality_mask, alphas, n_alpha,
+                                 fmt, omega, ell, r, power_iters, refit_iters, rows, n_rows,
+                                 scores, iter_scores, best_lambda, best_index, best_down,
+                                 best_up, workspace, reinterpret_cast<hipStream_t>(stream)),
+      fn);
 }
 
 svdq_status svdq_bits_lost(const float* ax, const float* lambda, int64_t K, int64_t block,

@@ -24,6 +24,13 @@ hipError_t launch_lowrank(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                           int power_iters, uint16_t* lora_down, uint16_t* lora_up, float* sigma,
                           void* workspace, hipStream_t s);
 
+// The same factors for an fp32 matrix E [N, K] (row stride lde) in place of diag(λ)·Wᵀ's
+// transpose: the rank-r approximation of Eᵀ.
+hipError_t launch_lowrank_f32(const float* E, int64_t N, int64_t K, int64_t lde,
+                              const float* omega, int64_t ell, int64_t r, int power_iters,
+                              uint16_t* lora_down, uint16_t* lora_up, float* sigma,
+                              void* workspace, hipStream_t s);
+
 hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                                   const float* lambda, const uint16_t* down, const uint16_t* up,
                                   int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
@@ -67,13 +74,15 @@ hipError_t launch_score(const uint16_t* Y, int64_t ldy, const uint16_t* X, int64
                         hipStream_t s);
 
 int64_t lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
-                                      int64_t n_rows, int64_t n_alpha);
-hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W, int64_t N,
-                                int64_t K, int64_t ldw, const float* ax, const float* aw,
-                                uint32_t mask, const float* alphas, int64_t n_alpha, int fmt,
-                                const float* omega, int64_t ell, int64_t r, int power_iters,
+                                      int64_t n_rows, int64_t n_alpha, int refit_iters);
+hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W,
+                                int64_t N, int64_t K, int64_t ldw, const float* ax,
+                                const float* aw, uint32_t mask, const float* alphas,
+                                int64_t n_alpha, int fmt, const float* omega, int64_t ell,
+                                int64_t r, int power_iters, int refit_iters,
                                 const int32_t* rows, int64_t n_rows, double* scores,
-                                float* best_lambda, int32_t* best_index, void* workspace,
+                                double* iter_scores, float* best_lambda, int32_t* best_index,
+                                uint16_t* best_down, uint16_t* best_up, void* workspace,
                                 hipStream_t s);
 
 }  // namespace svdq

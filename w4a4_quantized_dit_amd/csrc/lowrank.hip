@@ -26,9 +26,15 @@ constexpr int kGramRows = 64;      // rows per partial Gram matrix
 constexpr int kJacobiThreads = 1024;
 constexpr int kMaxSweeps = 40;
 
+// The matrix is either the bf16 weight (scaled by λ per channel) or an fp32 matrix (the refit
+// target of the layer's low-rank branch), read through one of these.
+__device__ __forceinline__ float ld_elem(const uint16_t* p) { return bf16_to_f32(*p); }
+__device__ __forceinline__ float ld_elem(const float* p) { return *p; }
+
 // Yp[s][k][j] = Σ_{n in split s} W[n, k] · X[n, j]: thread = column k, 40 columns of X per
 // workgroup (blockIdx.z), rows of X staged 64 at a time.
-__global__ __launch_bounds__(256) void k_sketch_wt(const uint16_t* __restrict__ W, int64_t N,
+template <typename T>
+__global__ __launch_bounds__(256) void k_sketch_wt(const T* __restrict__ W, int64_t N,
                                                    int64_t K, int64_t ldw,
                                                    const float* __restrict__ X, int ell,
                                                    float* __restrict__ Yp) {
@@ -52,7 +58,7 @@ __global__ __launch_bounds__(256) void k_sketch_wt(const uint16_t* __restrict__ 
     __syncthreads();
     if (k < K) {
       for (int rr = 0; rr < nn; ++rr) {
-        const float w = bf16_to_f32(W[(n0 + rr) * ldw + k]);
+        const float w = ld_elem(W + (n0 + rr) * ldw + k);
 #pragma unroll
         for (int c = 0; c < kColTile; ++c) acc[c] = __builtin_fmaf(w, xs[rr][c], acc[c]);
       }
@@ -67,7 +73,8 @@ __global__ __launch_bounds__(256) void k_sketch_wt(const uint16_t* __restrict__ 
 
 // Zp[s][n][j] = Σ_{k in split s} W[n, k] · λ_k · Q[k, j]: 64 rows n x 40 columns per workgroup,
 // thread = (row, column residue mod 4), W and λ∘Q staged 64 channels at a time.
-__global__ __launch_bounds__(256) void k_sketch_w(const uint16_t* __restrict__ W, int64_t N,
+template <typename T>
+__global__ __launch_bounds__(256) void k_sketch_w(const T* __restrict__ W, int64_t N,
                                                   int64_t K, int64_t ldw,
                                                   const float* __restrict__ lambda,
                                                   const float* __restrict__ Q, int ell,
@@ -90,7 +97,7 @@ __global__ __launch_bounds__(256) void k_sketch_w(const uint16_t* __restrict__ W
     __syncthreads();
     for (int t = threadIdx.x; t < 64 * 64; t += 256) {
       const int rr = t >> 6, kk = t & 63;
-      ws[rr][kk] = (n0 + rr < N && kk < kn) ? bf16_to_f32(W[(n0 + rr) * ldw + k0 + kk]) : 0.0f;
+      ws[rr][kk] = (n0 + rr < N && kk < kn) ? ld_elem(W + (n0 + rr) * ldw + k0 + kk) : 0.0f;
     }
     for (int t = threadIdx.x; t < 64 * kColTile; t += 256) {
       const int kk = t / kColTile, c = t % kColTile;
@@ -420,10 +427,13 @@ int64_t lowrank_workspace_bytes(int64_t N, int64_t K, int64_t ell) {
 
 int lowrank_max_ell() { return kMaxEll; }
 
-hipError_t launch_lowrank(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
-                          const float* lambda, const float* omega, int64_t ell, int64_t r,
-                          int power_iters, uint16_t* lora_down, uint16_t* lora_up, float* sigma,
-                          void* workspace, hipStream_t s) {
+namespace {
+
+template <typename T>
+hipError_t lowrank_impl(const T* W, int64_t N, int64_t K, int64_t ldw, const float* lambda,
+                        const float* omega, int64_t ell, int64_t r, int power_iters,
+                        uint16_t* lora_down, uint16_t* lora_up, float* sigma, void* workspace,
+                        hipStream_t s) {
   Workspace w = carve(workspace, N, K, ell);
   const int e = (int)ell;
   const unsigned ztiles = (unsigned)ceil_div(ell, kColTile);
@@ -499,6 +509,24 @@ hipError_t launch_lowrank(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
   SVDQ_CHECK_LAUNCH();
 #undef SVDQ_CHECK_LAUNCH
   return hipSuccess;
+}
+
+}  // namespace
+
+hipError_t launch_lowrank(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                          const float* lambda, const float* omega, int64_t ell, int64_t r,
+                          int power_iters, uint16_t* lora_down, uint16_t* lora_up, float* sigma,
+                          void* workspace, hipStream_t s) {
+  return lowrank_impl(W, N, K, ldw, lambda, omega, ell, r, power_iters, lora_down, lora_up, sigma,
+                      workspace, s);
+}
+
+hipError_t launch_lowrank_f32(const float* E, int64_t N, int64_t K, int64_t lde,
+                              const float* omega, int64_t ell, int64_t r, int power_iters,
+                              uint16_t* lora_down, uint16_t* lora_up, float* sigma,
+                              void* workspace, hipStream_t s) {
+  return lowrank_impl(E, N, K, lde, nullptr, omega, ell, r, power_iters, lora_down, lora_up,
+                      sigma, workspace, s);
 }
 
 }  // namespace svdq

@@ -6,8 +6,18 @@
 //   λ_α from the calibration statistics; rank-r factors of diag(λ_α)·Wᵀ (randomized SVD);
 //   residual weight quantisation; activation quantisation of the sampled rows (static amax of
 //   λ_α) with the low-rank down-projection; the W4A4 GEMM; relative L2 against bf16(X·Wᵀ)
-// then the first α of smallest error is selected and its λ copied out.  The per-candidate
-// steps are the library's own launches; this file adds the row gather and the bookkeeping.
+// then the first α of smallest error is selected and its λ copied out.
+//
+// Low-rank refit (the same page, section "Calibration", runs a number of refit iterations of the
+// branch against the same objective for every candidate; it does not define them).  Reading: the
+// alternating refit, where iterate t + 1 takes the rank-r factors of E_t = λ·W − deq(Q(R_t)),
+// what the quantised residual of iterate t leaves of the smoothed weight, so that branch and
+// quantised residual are fitted to each other; every iterate is scored like the first, and a
+// candidate's score is the smallest over its iterates.  The factors of the best iterate of the
+// winning candidate can be copied out.
+//
+// The per-candidate steps are the library's own launches; this file adds the row gather, the
+// refit target and the bookkeeping.
 #include "device.h"
 #include "launch.h"
 
@@ -44,11 +54,98 @@ __global__ void k_zero_sums(double* __restrict__ sums) {
   if (threadIdx.x < 8) sums[threadIdx.x] = 0.0;
 }
 
-// score = sqrt(Σ(Y−Y_ref)²) / sqrt(ΣY_ref²) of group 3; +inf when the reference is all zero
-__global__ void k_finish_score(const double* __restrict__ sums, double* __restrict__ score) {
+__global__ void k_set_inf(double* __restrict__ v) {
+  if (threadIdx.x == 0) *v = __builtin_huge_val();
+}
+
+// The score of iterate t of a candidate, sqrt(Σ(Y−Y_ref)²) / sqrt(ΣY_ref²) over group 3 (+inf
+// when the reference is all zero), into cur and iter_score (when given); the candidate's score
+// is the smallest over its iterates (a NaN is replaced by any later number).
+__global__ void k_finish_iter(const double* __restrict__ sums, int t, double* __restrict__ score,
+                              double* __restrict__ iter_score, double* __restrict__ cur) {
   if (threadIdx.x == 0) {
     const double d = sums[6], r = sums[7];
-    *score = r > 0.0 ? sqrt(d) / sqrt(r) : __builtin_huge_val();
+    const double v = r > 0.0 ? sqrt(d) / sqrt(r) : __builtin_huge_val();
+    *cur = v;
+    if (iter_score) *iter_score = v;
+    const double old = *score;
+    if (t == 0 || v < old || old != old) *score = v;
+  }
+}
+
+// Factors of an iterate that beats every earlier iterate of every earlier candidate are copied
+// out (strictly smaller: the first of equal scores is kept, as in the choice of α) ...
+__global__ __launch_bounds__(256) void k_keep_factors(const double* __restrict__ cur,
+                                                      const double* __restrict__ best,
+                                                      const uint16_t* __restrict__ down,
+                                                      const uint16_t* __restrict__ up,
+                                                      int64_t n_down, int64_t n_up,
+                                                      uint16_t* __restrict__ best_down,
+                                                      uint16_t* __restrict__ best_up) {
+  if (!(*cur < *best)) return;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < n_down) best_down[t] = down[t];
+  else if (t < n_down + n_up) best_up[t - n_down] = up[t - n_down];
+}
+
+// ... and the running best score follows once the copy has been made.
+__global__ void k_commit_best(const double* __restrict__ cur, double* __restrict__ best) {
+  if (threadIdx.x == 0 && *cur < *best) *best = *cur;
+}
+
+// Exact values of the stored codes.
+__device__ __forceinline__ double e2m1_value(uint32_t nib) {
+  const uint32_t m = nib & 7u;
+  const double mag = m < 4u ? 0.5 * (double)m : (m == 4u ? 2.0 : m == 5u ? 3.0 : m == 6u ? 4.0 : 6.0);
+  return (nib & 8u) ? -mag : mag;
+}
+__device__ __forceinline__ double e4m3_value(uint32_t b) {
+  const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (b & 0x80u) ? -mag : mag;
+}
+
+// Refit target of the low-rank branch: E = λ·W − deq(Q(R)), the smoothed weight less the
+// dequantised residual, in fp64 (every term exact), rounded once to fp32.  One thread per 16
+// consecutive channels of a row.  FMT: 0 NVFP4, 1 int4-g64, 2 MXFP4, 3 MXFP8.
+template <int FMT>
+__global__ __launch_bounds__(256) void k_refit_target(const uint16_t* __restrict__ W, int64_t N,
+                                                      int64_t K, int64_t ldw,
+                                                      const float* __restrict__ lambda,
+                                                      const uint8_t* __restrict__ codes,
+                                                      const void* __restrict__ scales,
+                                                      const float* __restrict__ g,
+                                                      float* __restrict__ E) {
+  const int64_t per_row = K / 16;
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= N * per_row) return;
+  const int64_t n = t / per_row, k0 = (t % per_row) * 16;
+  double mult;
+  if (FMT == 0) {
+    mult = e4m3_value(static_cast<const uint8_t*>(scales)[n * (K / 16) + k0 / 16]) * (double)*g;
+  } else if (FMT == 1) {
+    const uint16_t h = static_cast<const uint16_t*>(scales)[n * (K / 64) + k0 / 64];
+    mult = (double)(float)__builtin_bit_cast(_Float16, h);
+  } else {
+    mult = ldexp(1.0, (int)static_cast<const uint8_t*>(scales)[n * (K / 32) + k0 / 32] - 127);
+  }
+  uint8_t b[16];
+  if (FMT == 3) {
+    *reinterpret_cast<u32x4_t*>(b) = *reinterpret_cast<const u32x4_t*>(codes + n * K + k0);
+  } else {
+    const uint64_t q = *reinterpret_cast<const uint64_t*>(codes + n * (K / 2) + k0 / 2);
+#pragma unroll
+    for (int j = 0; j < 16; ++j) b[j] = (uint8_t)((q >> (4 * j)) & 0xFu);
+  }
+  const uint16_t* wr = W + n * ldw + k0;
+  float* er = E + n * K + k0;
+#pragma unroll
+  for (int j = 0; j < 16; ++j) {
+    double v;
+    if (FMT == 3) v = e4m3_value(b[j]);
+    else if (FMT == 1) v = (double)((int)b[j] - (b[j] >= 8 ? 16 : 0));
+    else v = e2m1_value(b[j]);
+    er[j] = (float)((double)lambda[k0 + j] * (double)bf16_to_f32(wr[j]) - v * mult);
   }
 }
 
@@ -78,7 +175,8 @@ int64_t scale_bytes(int fmt, int64_t rows, int64_t K) {
 }
 
 struct SearchWs {
-  float *lam_all, *amax, *g_w, *g_a, *D;
+  float *lam_all, *amax, *g_w, *g_a, *D, *E;
+  double *cur, *best;
   uint16_t *down, *up, *xs, *ys;
   uint8_t *w_codes, *w_scales, *a_codes, *a_scales;
   int32_t* ids;
@@ -89,7 +187,7 @@ struct SearchWs {
 };
 
 SearchWs carve(void* base, int fmt, int64_t N, int64_t K, int64_t ell, int64_t r, int64_t S,
-               int64_t n_alpha) {
+               int64_t n_alpha, int refit_iters) {
   uint8_t* b = static_cast<uint8_t*>(base);
   int64_t off = 0;
   auto take = [&](int64_t bytes) {
@@ -115,6 +213,9 @@ SearchWs carve(void* base, int fmt, int64_t N, int64_t K, int64_t ell, int64_t r
   w.ids = static_cast<int32_t*>(take(S * 4));
   w.grp = static_cast<int8_t*>(take(S));
   w.sums = static_cast<double*>(take(8 * 8));
+  w.cur = static_cast<double*>(take(8));
+  w.best = static_cast<double*>(take(8));
+  w.E = refit_iters > 0 ? static_cast<float*>(take(N * K * 4)) : nullptr;
   w.bytes = off;
   return w;
 }
@@ -122,21 +223,23 @@ SearchWs carve(void* base, int fmt, int64_t N, int64_t K, int64_t ell, int64_t r
 }  // namespace
 
 int64_t lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
-                                      int64_t n_rows, int64_t n_alpha) {
-  return carve(nullptr, fmt, N, K, ell, r, n_rows, n_alpha).bytes;
+                                      int64_t n_rows, int64_t n_alpha, int refit_iters) {
+  return carve(nullptr, fmt, N, K, ell, r, n_rows, n_alpha, refit_iters).bytes;
 }
 
-hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W, int64_t N,
-                                int64_t K, int64_t ldw, const float* ax, const float* aw,
-                                uint32_t mask, const float* alphas, int64_t n_alpha, int fmt,
-                                const float* omega, int64_t ell, int64_t r, int power_iters,
+hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W,
+                                int64_t N, int64_t K, int64_t ldw, const float* ax,
+                                const float* aw, uint32_t mask, const float* alphas,
+                                int64_t n_alpha, int fmt, const float* omega, int64_t ell,
+                                int64_t r, int power_iters, int refit_iters,
                                 const int32_t* rows, int64_t n_rows, double* scores,
-                                float* best_lambda, int32_t* best_index, void* workspace,
+                                double* iter_scores, float* best_lambda, int32_t* best_index,
+                                uint16_t* best_down, uint16_t* best_up, void* workspace,
                                 hipStream_t s) {
-  const SearchWs w = carve(workspace, fmt, N, K, ell, r, n_rows, n_alpha);
+  const SearchWs w = carve(workspace, fmt, N, K, ell, r, n_rows, n_alpha, refit_iters);
   hipError_t e;
-#define SVDQ_TRY_HIP(x)                  \
-  do {                                   \
+#define SVDQ_TRY_HIP(x)                    \
+  do {                                     \
     if ((e = (x)) != hipSuccess) return e; \
   } while (0)
   k_gather_rows<<<dim3((unsigned)ceil_div(n_rows * (K / 8), 256)), dim3(256), 0, s>>>(
@@ -144,9 +247,16 @@ hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const
   SVDQ_TRY_HIP(hipGetLastError());
   k_rows_setup<<<dim3((unsigned)ceil_div(n_rows, 256)), dim3(256), 0, s>>>(n_rows, w.ids, w.grp);
   SVDQ_TRY_HIP(hipGetLastError());
+  const bool keep = r > 0 && best_down != nullptr;
+  if (keep) {
+    k_set_inf<<<dim3(1), dim3(64), 0, s>>>(w.best);
+    SVDQ_TRY_HIP(hipGetLastError());
+  }
   const uint16_t* down = r > 0 ? w.down : nullptr;
   const uint16_t* up = r > 0 ? w.up : nullptr;
   float* D = r > 0 ? w.D : nullptr;
+  float* g_w = fmt == 0 ? w.g_w : nullptr;
+  const int64_t n_tgt = N * (K / 16);
   for (int64_t i = 0; i < n_alpha; ++i) {
     float* lam = w.lam_all + i * K;
     float* amax = w.amax + i;
@@ -154,20 +264,49 @@ hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const
     if (r > 0)
       SVDQ_TRY_HIP(launch_lowrank(W, N, K, ldw, lam, omega, ell, r, power_iters, w.down, w.up,
                                   nullptr, w.lowrank, s));
-    SVDQ_TRY_HIP(launch_quantize_weight(fmt, W, N, K, ldw, lam, down, up, r, w.w_codes,
-                                        w.w_scales, fmt == 0 ? w.g_w : nullptr, s));
-    SVDQ_TRY_HIP(launch_quant_act(fmt, w.xs, n_rows, K, K, lam, fmt == 0 ? amax : nullptr, down,
-                                  r, w.a_codes, w.a_scales, fmt == 0 ? w.g_a : nullptr, D,
-                                  nullptr, s));
-    SVDQ_TRY_HIP(launch_gemm(fmt, n_rows, N, K, w.a_codes, w.a_scales,
-                             fmt == 0 ? w.g_a : nullptr, w.w_codes, w.w_scales,
-                             fmt == 0 ? w.g_w : nullptr, D, up, r, nullptr, nullptr, w.ys, N, s));
-    k_zero_sums<<<dim3(1), dim3(64), 0, s>>>(w.sums);
-    SVDQ_TRY_HIP(hipGetLastError());
-    SVDQ_TRY_HIP(launch_score(w.ys, N, w.xs, K, W, ldw, n_rows, N, K, w.ids, w.grp, n_rows,
-                              w.sums, s));
-    k_finish_score<<<dim3(1), dim3(64), 0, s>>>(w.sums, scores + i);
-    SVDQ_TRY_HIP(hipGetLastError());
+    for (int t = 0; t <= refit_iters; ++t) {
+      SVDQ_TRY_HIP(launch_quantize_weight(fmt, W, N, K, ldw, lam, down, up, r, w.w_codes,
+                                          w.w_scales, g_w, s));
+      SVDQ_TRY_HIP(launch_quant_act(fmt, w.xs, n_rows, K, K, lam, fmt == 0 ? amax : nullptr,
+                                    down, r, w.a_codes, w.a_scales, fmt == 0 ? w.g_a : nullptr,
+                                    D, nullptr, s));
+      SVDQ_TRY_HIP(launch_gemm(fmt, n_rows, N, K, w.a_codes, w.a_scales,
+                               fmt == 0 ? w.g_a : nullptr, w.w_codes, w.w_scales, g_w, D, up, r,
+                               nullptr, nullptr, w.ys, N, s));
+      k_zero_sums<<<dim3(1), dim3(64), 0, s>>>(w.sums);
+      SVDQ_TRY_HIP(hipGetLastError());
+      SVDQ_TRY_HIP(launch_score(w.ys, N, w.xs, K, W, ldw, n_rows, N, K, w.ids, w.grp, n_rows,
+                                w.sums, s));
+      k_finish_iter<<<dim3(1), dim3(64), 0, s>>>(
+          w.sums, t, scores + i,
+          iter_scores ? iter_scores + i * (refit_iters + 1) + t : nullptr, w.cur);
+      SVDQ_TRY_HIP(hipGetLastError());
+      if (keep) {
+        k_keep_factors<<<dim3((unsigned)ceil_div(r * K + N * r, 256)), dim3(256), 0, s>>>(
+            w.cur, w.best, w.down, w.up, r * K, N * r, best_down, best_up);
+        SVDQ_TRY_HIP(hipGetLastError());
+        k_commit_best<<<dim3(1), dim3(64), 0, s>>>(w.cur, w.best);
+        SVDQ_TRY_HIP(hipGetLastError());
+      }
+      if (t < refit_iters) {   // refit the branch to what the quantised residual leaves
+        const dim3 grid((unsigned)ceil_div(n_tgt, 256));
+        if (fmt == 0)
+          k_refit_target<0><<<grid, dim3(256), 0, s>>>(W, N, K, ldw, lam, w.w_codes, w.w_scales,
+                                                      g_w, w.E);
+        else if (fmt == 1)
+          k_refit_target<1><<<grid, dim3(256), 0, s>>>(W, N, K, ldw, lam, w.w_codes, w.w_scales,
+                                                      g_w, w.E);
+        else if (fmt == 2)
+          k_refit_target<2><<<grid, dim3(256), 0, s>>>(W, N, K, ldw, lam, w.w_codes, w.w_scales,
+                                                      g_w, w.E);
+        else
+          k_refit_target<3><<<grid, dim3(256), 0, s>>>(W, N, K, ldw, lam, w.w_codes, w.w_scales,
+                                                      g_w, w.E);
+        SVDQ_TRY_HIP(hipGetLastError());
+        SVDQ_TRY_HIP(launch_lowrank_f32(w.E, N, K, K, omega, ell, r, power_iters, w.down, w.up,
+                                        nullptr, w.lowrank, s));
+      }
+    }
   }
   k_pick<<<dim3(1), dim3(256), 0, s>>>(scores, n_alpha, w.lam_all, K, best_lambda, best_index);
   SVDQ_TRY_HIP(hipGetLastError());

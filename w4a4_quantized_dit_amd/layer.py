@@ -93,25 +93,36 @@ ALPHA_GRID = tuple(i / 40.0 for i in range(1, 40))
 
 
 def lambda_search(X, W, state, alphas, rows, fmt=NVFP4, omega=None, r=32, power_iters=2,
-                  mask=7):
+                  mask=7, refit_iters=0, per_iterate=False):
     """λ grid search on the GPU: for each α the layer's output error on the sampled rows
-    (device int32 indices into X); returns (scores fp64 [len(alphas)], best λ, best index)."""
+    (device int32 indices into X), the smallest over refit_iters refits of the low-rank branch.
+    Returns dict(scores fp64 [n_alpha], lam (the winner's λ), index, and when r > 0 the
+    winner's best factors lora_down [r, K] / lora_up [N, r]; with per_iterate the score of
+    every iterate, fp64 [n_alpha, refit_iters + 1])."""
     torch = _torch()
     N, K = W.shape
     dev = X.device
     ell = omega.shape[1] if omega is not None else 0
-    scores = torch.empty(len(alphas), dtype=torch.float64, device=dev)
-    best = torch.empty(K, dtype=torch.float32, device=dev)
-    idx = torch.empty(1, dtype=torch.int32, device=dev)
-    nbytes = _lib.svdq_lambda_search_workspace_bytes(fmt, N, K, ell, r, rows.numel(),
-                                                     len(alphas))
+    n = len(alphas)
+    out = dict(scores=torch.empty(n, dtype=torch.float64, device=dev),
+               lam=torch.empty(K, dtype=torch.float32, device=dev),
+               index=torch.empty(1, dtype=torch.int32, device=dev))
+    if per_iterate:
+        out["iter_scores"] = torch.empty(n, refit_iters + 1, dtype=torch.float64, device=dev)
+    if r > 0:
+        out["lora_down"] = torch.empty(r, K, dtype=torch.bfloat16, device=dev)
+        out["lora_up"] = torch.empty(N, r, dtype=torch.bfloat16, device=dev)
+    nbytes = _lib.svdq_lambda_search_workspace_bytes(fmt, N, K, ell, r, rows.numel(), n,
+                                                     refit_iters)
     if nbytes < 0:
         raise ValueError("unsupported search shape")
     ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=dev)
     off = (-ws.data_ptr()) % 256
     _lib.svdq_lambda_search(X, W, state["ax"], state["aw"], mask, alphas, fmt, omega, r,
-                            power_iters, rows, scores, best, idx, ws[off:off + nbytes])
-    return scores, best, idx
+                            power_iters, refit_iters, rows, out["scores"], out.get("iter_scores"),
+                            out["lam"], out["index"], out.get("lora_down"), out.get("lora_up"),
+                            ws[off:off + nbytes])
+    return out
 
 
 def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
