@@ -26,4 +26,4 @@ Every reading taken where the pages are silent is listed in the module that take
 Float32 steps use numpy float32 operations (each one IEEE round-to-nearest-even); exact
 steps use float64.
 """
-from . import formats, quant, mx, calib, proxy, svd, gemm, delta, score, layer, search  # noqa: F401
+from . import formats, quant, mx, calib, proxy, svd, gemm, delta, score, layer, search, gptq  # noqa: F401

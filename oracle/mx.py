@@ -51,16 +51,21 @@ def mx_quantize(x32, elem):
     xb = x32.reshape(R, K // BLOCK, BLOCK)
     a = np.abs(xb).max(axis=2)
     e = mx_exponent(a, elem)                                  # [R, K/32]
-    q = np.ldexp(xb, (-e)[:, :, None].astype(np.int32)).astype(F32)
-    neg = np.signbit(xb)
-    if elem == "e2m1":
-        mag = e2m1_encode_mag(np.abs(q))
-        nib = (mag | (neg.astype(np.uint8) << 3)).astype(np.uint8).reshape(R, K)
-        codes = pack_nibbles(nib)
-    else:
-        codes = e4m3_encode_signed(q).reshape(R, K)
+    el = mx_element_codes(xb, np.broadcast_to(e[:, :, None], xb.shape), elem).reshape(R, K)
+    codes = pack_nibbles(el) if elem == "e2m1" else el
     scales = (e + 127).astype(np.uint8)
     return codes, scales
+
+
+def mx_element_codes(x32, e, elem):
+    """Element codes (E2M1 nibble with the sign in bit 3, or E4M3 byte) of float32 x in blocks
+    of exponent e (same shape)."""
+    x32 = np.asarray(x32, dtype=F32)
+    q = np.ldexp(x32, (-np.asarray(e)).astype(np.int32)).astype(F32)
+    if elem == "e2m1":
+        mag = e2m1_encode_mag(np.abs(q))
+        return (mag | (np.signbit(x32).astype(np.uint8) << 3)).astype(np.uint8)
+    return e4m3_encode_signed(q)
 
 
 def mx_dequantize(codes, scales, elem):

@@ -55,6 +55,28 @@ def nvfp4_tensor_scale(amax_t):
     return F32(amax_t / F32(2688.0))
 
 
+def nvfp4_block_scales(a, g):
+    """E4M3 codes s and float32 values S = value(s)·g of the block scales for block maxima a."""
+    d6 = F32(F32(6.0) * F32(g))
+    q = (np.asarray(a, dtype=F32) / d6).astype(F32)
+    s = e4m3_encode(q)
+    S = (e4m3_decode(s).astype(F32) * F32(g)).astype(F32)
+    return s, S
+
+
+def nvfp4_nibbles(x32, S):
+    """E2M1 nibbles (sign in bit 3) of float32 x under block scale values S (same shape)."""
+    x32 = np.asarray(x32, dtype=F32)
+    S = np.asarray(S, dtype=F32)
+    nz = S != 0
+    inv = np.zeros_like(S)
+    inv[nz] = (F32(1.0) / S[nz]).astype(F32)
+    y = (np.abs(x32) * inv).astype(F32)
+    mag = e2m1_encode_mag(y)
+    mag[~nz] = 0
+    return (mag | (np.signbit(x32).astype(np.uint8) << np.uint8(3))).astype(np.uint8)
+
+
 def nvfp4_quantize(x32, amax_t):
     """Quantise float32 rows [R, K] to NVFP4 with tensor amax `amax_t`.
 
@@ -65,20 +87,11 @@ def nvfp4_quantize(x32, amax_t):
     if K % NVFP4_BLOCK:
         raise ValueError("K must be a multiple of 16")
     g = nvfp4_tensor_scale(amax_t)
-    d6 = F32(F32(6.0) * g)
     xb = x32.reshape(R, K // NVFP4_BLOCK, NVFP4_BLOCK)
     a = np.abs(xb).max(axis=2)                              # exact
-    q = (a / d6).astype(F32)
     n_sat = int(np.count_nonzero(a > F32(amax_t)))
-    s = e4m3_encode(q)                                      # [R, K/16]
-    S = (e4m3_decode(s).astype(F32) * g).astype(F32)
-    nz = S != 0
-    inv = np.zeros_like(S)
-    inv[nz] = (F32(1.0) / S[nz]).astype(F32)
-    y = (np.abs(xb) * inv[:, :, None]).astype(F32)
-    mag = e2m1_encode_mag(y)
-    mag[~nz] = 0
-    nib = mag | (np.signbit(xb).astype(np.uint8) << np.uint8(3))
+    s, S = nvfp4_block_scales(a, g)                         # [R, K/16]
+    nib = nvfp4_nibbles(xb, np.broadcast_to(S[:, :, None], xb.shape))
     codes = pack_nibbles(nib.reshape(R, K))
     return codes, s.astype(np.uint8), g, n_sat
 
@@ -102,18 +115,29 @@ def int4_quantize(x32):
     if K % INT4_GROUP:
         raise ValueError("K must be a multiple of 64")
     xg = x32.reshape(R, K // INT4_GROUP, INT4_GROUP)
-    a = np.abs(xg).max(axis=2)
-    s16 = fp16_rne((a / F32(7.0)).astype(F32))
-    sf = s16.astype(F32)
-    nz = sf != 0
-    inv = np.zeros_like(sf)
-    with np.errstate(divide="ignore"):
-        inv[nz] = (F32(1.0) / sf[nz]).astype(F32)
-    v = (xg * inv[:, :, None]).astype(F32)
-    c = np.clip(np.rint(v), -8, 7).astype(np.int8)
-    c[~nz] = 0
+    s16 = int4_scale(np.abs(xg).max(axis=2))
+    c = int4_codes(xg, np.broadcast_to(s16[:, :, None], xg.shape))
     nib = (c.astype(np.uint8) & np.uint8(0xF)).reshape(R, K)
     return pack_nibbles(nib), s16
+
+
+def int4_scale(a):
+    """fp16 scales fp16(a / 7) of groups with float32 absmax a."""
+    return fp16_rne((np.asarray(a, dtype=F32) / F32(7.0)).astype(F32))
+
+
+def int4_codes(x32, s16):
+    """int8 codes clamp(rint(x · fl32(1/s)), −8, 7) of float32 x under fp16 scales s16 of the
+    same shape (0 where s == 0)."""
+    x32 = np.asarray(x32, dtype=F32)
+    sf = np.asarray(s16, dtype=np.float16).astype(F32)
+    nz = sf != 0
+    inv = np.zeros_like(sf)
+    inv[nz] = (F32(1.0) / sf[nz]).astype(F32)
+    v = (x32 * inv).astype(F32)
+    c = np.clip(np.rint(v), -8, 7).astype(np.int8)
+    c[~nz] = 0
+    return c
 
 
 def int4_dequantize(codes, scales16):
