@@ -146,6 +146,37 @@ svdq_status svdq_lowrank_factors(const uint16_t* W, int64_t N, int64_t K, int64_
                                  svdq_stream_t stream);
 
 /*
+ * GPTQ rounding of the weight residual ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)",
+ * opening paragraph: the residual left by the low-rank branch is GPTQ-rounded; GPTQ as
+ * published by Frantar et al. 2022).
+ *
+ * svdq_gptq_hessian: H [K, K] fp64 row-major (device) = Σ_m x̂_m·x̂_mᵀ over the M rows of X
+ * [M, K] bf16, x̂ = fl32(x · fl32(1/λ)) (lambda may be NULL: λ = 1); accumulate != 0 adds to
+ * H (calibration batches), else overwrites it.  Symmetric by construction.
+ *
+ * svdq_gptq_quantize_weight: the codes, scales and (NVFP4) tensor scale of
+ * svdq_quantize_weight, same formats and layouts, with the residual R32 (computed exactly as
+ * there from W, lambda, lora_down [r, K], lora_up [N, r]) rounded by GPTQ under H: damping
+ * H + 0.01·mean(diag H)·I (an all-zero diagonal: H = I), natural column order, each quantiser
+ * group's scale fixed when the sweep reaches its first column from the current values, the
+ * round-to-nearest element rule applied to fl32 of each fp64 working value; the NVFP4 tensor
+ * scale is the round-to-nearest one, max|R32|/2688.  H must be symmetric positive
+ * semi-definite (as svdq_gptq_hessian makes it).  N a multiple of 256, K of 256.  workspace:
+ * at least svdq_gptq_workspace_bytes(N, K) bytes (about 16·K² + 12·N·K), 256-byte aligned, the
+ * caller's.  Deterministic.
+ */
+svdq_status svdq_gptq_hessian(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                              const float* lambda, int accumulate, double* H,
+                              svdq_stream_t stream);
+int64_t svdq_gptq_workspace_bytes(int64_t N, int64_t K);
+svdq_status svdq_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K,
+                                      int64_t ldw, const float* lambda,
+                                      const uint16_t* lora_down, const uint16_t* lora_up,
+                                      int64_t r, const double* H, uint8_t* codes, void* scales,
+                                      float* tensor_scale, void* workspace,
+                                      int64_t workspace_bytes, svdq_stream_t stream);
+
+/*
  * λ grid search against the layer's output error ("MiniMax-H3 NVFP4 — what the smoothing scale
  * should be calibrated on", sections "Calibration": candidate λ scored against the OutputsError
  * objective with a number of low-rank refit iterations each, and "The metric that picks the

@@ -26,7 +26,7 @@ Readings where the pages are silent:
 import numpy as np
 
 from . import calib, quant, mx
-from .formats import e2m1_decode, e4m3_decode, pack_nibbles
+from .formats import bf16_bits_to_f32, e2m1_decode, e4m3_decode, pack_nibbles
 
 F32 = np.float32
 GROUP = {"int4": 64, "nvfp4": 16, "mxfp4": 32, "mxfp8": 32}
@@ -35,8 +35,11 @@ PERCDAMP = 0.01
 
 
 def hessian(X_bits, lam):
-    """H = X̂ᵀ X̂ over the given rows, float64 [K, K]."""
-    xhat = calib.smooth(X_bits, lam).astype(np.float64)
+    """H = X̂ᵀ X̂ over the given rows, float64 [K, K] (lam None: λ = 1, X̂ = X)."""
+    if lam is None:
+        xhat = bf16_bits_to_f32(X_bits).astype(np.float64)
+    else:
+        xhat = calib.smooth(X_bits, lam).astype(np.float64)
     return xhat.T @ xhat
 
 
@@ -78,16 +81,19 @@ def _group_scale(x32, fmt, g):
     return (e + 127).astype(np.uint8), enc
 
 
-def gptq_quantize(R32, H, fmt):
+def gptq_quantize(R32, H, fmt, amax=None):
     """GPTQ codes and scales of the residual R32 [N, K] under the Hessian H [K, K] (damped here):
-    dict(codes, scales, g (NVFP4) / None, deq (exact float64 values of the codes))."""
+    dict(codes, scales, g (NVFP4) / None, deq (exact float64 values of the codes)).  Rows are
+    independent given H, so R32 may be a subset of a residual's rows; amax is then the whole
+    residual's max|R32| for the NVFP4 tensor scale (default: this R32's)."""
     W = np.asarray(R32, dtype=F32).astype(np.float64)
     N, K = W.shape
     G = GROUP[fmt]
     if K % G:
         raise ValueError(f"K={K} is not a multiple of the group size {G}")
-    g = quant.nvfp4_tensor_scale(np.abs(np.asarray(R32, dtype=F32)).max()) if fmt == "nvfp4" \
-        else None
+    if amax is None:
+        amax = np.abs(np.asarray(R32, dtype=F32)).max()
+    g = quant.nvfp4_tensor_scale(amax) if fmt == "nvfp4" else None
     U = np.linalg.cholesky(np.linalg.inv(damped(H))).T          # H⁻¹ = UᵀU, U upper
     el = np.zeros((N, K), dtype=np.int16)
     deq = np.zeros((N, K))

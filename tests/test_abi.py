@@ -194,3 +194,36 @@ def test_lambda_search_validation(lib):
     assert call(bd=P) == NULLP                           # best factors go in pairs
     assert call(bd=P, bu=P, r=0, om=None) == INVALID
     assert call(bd=MIS, bu=P) == SHAPE
+
+
+def test_gptq_validation(lib):
+    hx = lib.svdq_gptq_hessian
+    assert hx(None, 16, 256, 256, None, 0, P, None) == NULLP
+    assert hx(P, 16, 256, 256, None, 0, None, None) == NULLP
+    assert hx(P, 0, 256, 256, None, 0, P, None) == SHAPE
+    assert hx(P, 16, 200, 200, None, 0, P, None) == SHAPE
+    assert hx(P, 16, 256, 100, None, 0, P, None) == SHAPE
+    ws = 1 << 30
+    need = lib.svdq_gptq_workspace_bytes(512, 256)
+    assert need >= 16 * 256 * 256 + 12 * 512 * 256
+    assert lib.svdq_gptq_workspace_bytes(0, 256) == -1
+    f = lib.svdq_gptq_quantize_weight
+
+    def call(**kw):
+        a = dict(fmt=0, W=P, N=512, K=256, ldw=256, lam=P, down=P, up=P, r=32, H=P, codes=P,
+                 scales=P, g=P, ws=ws, wsb=need)
+        a.update(kw)
+        return f(a["fmt"], a["W"], a["N"], a["K"], a["ldw"], a["lam"], a["down"], a["up"], a["r"],
+                 a["H"], a["codes"], a["scales"], a["g"], a["ws"], a["wsb"], None)
+    assert call(fmt=9) == INVALID
+    assert call(W=None) == NULLP
+    assert call(H=None) == NULLP
+    assert call(g=None) == NULLP                          # NVFP4 needs its tensor scale
+    assert call(down=None) == NULLP
+    assert call(r=12) == SHAPE
+    assert call(N=300) == SHAPE
+    assert call(K=200, ldw=200) == SHAPE
+    assert call(ldw=128) == SHAPE
+    assert call(ws=ws + 8) == SHAPE
+    assert call(wsb=need - 1) == SHAPE and "workspace" in _err(lib)
+    assert call(W=MIS) == SHAPE

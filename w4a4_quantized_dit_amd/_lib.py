@@ -26,6 +26,12 @@ _SIGS = {
                                              _c_p, _c_p, _c_p, _c_p, _c_p]),
     "svdq_bits_lost": (ctypes.c_int, [_c_p, _c_p, _i64, _i64, _c_p, _c_p]),
     "svdq_lowrank_workspace_bytes": (_i64, [_i64, _i64, _i64]),
+    "svdq_gptq_hessian": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, ctypes.c_int, _c_p,
+                                         _c_p]),
+    "svdq_gptq_workspace_bytes": (_i64, [_i64, _i64]),
+    "svdq_gptq_quantize_weight": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p, _c_p,
+                                                 _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _i64,
+                                                 _c_p]),
     "svdq_lambda_search_workspace_bytes": (_i64, [ctypes.c_int, _i64, _i64, _i64, _i64, _i64,
                                                   _i64, ctypes.c_int]),
     "svdq_lambda_search": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _i64, _i64, _c_p, _c_p,
@@ -196,6 +202,35 @@ def svdq_lowrank_factors(W, lam, omega, r, power_iters, lora_down, lora_up, sigm
         _ptr(lora_down, _bf16(), "lora_down", r * K), _ptr(lora_up, _bf16(), "lora_up", N * r),
         _ptr(sigma, torch.float32, "sigma", r), _ptr(workspace, torch.uint8, "workspace"),
         workspace.numel(), _stream(stream)))
+
+
+def svdq_gptq_hessian(X, lam, H, accumulate=False, stream=None):
+    torch = _torch()
+    M, K = X.shape
+    _check(load().svdq_gptq_hessian(
+        _ptr(X, _bf16(), "X"), M, K, X.stride(0),
+        _ptr(lam, torch.float32, "lambda", K) if lam is not None else None, int(bool(accumulate)),
+        _ptr(H, torch.float64, "H", K * K), _stream(stream)))
+
+
+def svdq_gptq_workspace_bytes(N, K):
+    return int(load().svdq_gptq_workspace_bytes(int(N), int(K)))
+
+
+def svdq_gptq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, H, codes, scales, tensor_scale,
+                              workspace, stream=None):
+    torch = _torch()
+    N, K = W.shape
+    _check(load().svdq_gptq_quantize_weight(
+        int(fmt), _ptr(W, _bf16(), "W"), N, K, W.stride(0),
+        _ptr(lam, torch.float32, "lambda", K) if lam is not None else None,
+        _ptr(lora_down, _bf16(), "lora_down", r * K) if r else None,
+        _ptr(lora_up, _bf16(), "lora_up", N * r) if r else None, int(r),
+        _ptr(H, torch.float64, "H", K * K),
+        _ptr(codes, torch.uint8, "codes", _code_bytes(fmt, N, K)),
+        _ptr(scales, _scale_dtype(fmt), "scales", N * K // _block(fmt)),
+        _ptr(tensor_scale, torch.float32, "tensor_scale", 1) if tensor_scale is not None else None,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def svdq_lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha, refit_iters=0):

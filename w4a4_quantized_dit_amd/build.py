@@ -14,7 +14,7 @@ HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "geometry.cpp", "calib.hip", "quant_weight.hip", "quant_act.hip",
            "gemm_w4a4.hip", "gemm_int4.hip", "gemm_mx.hip", "delta.hip", "score.hip",
-           "lowrank.hip", "search.hip"]
+           "lowrank.hip", "search.hip", "gptq.hip"]
 
 FLAGS = [
     "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",

@@ -169,6 +169,55 @@ svdq_status svdq_lowrank_factors(const uint16_t* W, int64_t N, int64_t K, int64_
                     fn);
 }
 
+svdq_status svdq_gptq_hessian(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                              const float* lambda, int accumulate, double* H,
+                              svdq_stream_t stream) {
+  const char* fn = "svdq_gptq_hessian";
+  REQUIRE_PTR(X); REQUIRE_PTR(H);
+  if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldx", ldx, K));
+  return hip_result(svdq::launch_gptq_hessian(X, M, K, ldx, lambda, accumulate ? 1 : 0, H,
+                                              reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+int64_t svdq_gptq_workspace_bytes(int64_t N, int64_t K) {
+  if (N < 1 || K < 1) return -1;
+  return svdq::gptq_workspace_bytes(N, K);
+}
+
+svdq_status svdq_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K,
+                                      int64_t ldw, const float* lambda,
+                                      const uint16_t* lora_down, const uint16_t* lora_up,
+                                      int64_t r, const double* H, uint8_t* codes, void* scales,
+                                      float* tensor_scale, void* workspace,
+                                      int64_t workspace_bytes, svdq_stream_t stream) {
+  const char* fn = "svdq_gptq_quantize_weight";
+  TRY(check_fmt(fn, fmt));
+  REQUIRE_PTR(W); REQUIRE_PTR(H); REQUIRE_PTR(codes); REQUIRE_PTR(scales); REQUIRE_PTR(workspace);
+  REQUIRE_ALIGNED(W); REQUIRE_ALIGNED(codes);
+  if (fmt == SVDQ_NVFP4) REQUIRE_PTR(tensor_scale);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldw", ldw, K));
+  if (N < 1 || N % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn,
+                (long long)N);
+  TRY(check_rank(fn, r));
+  if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(lora_up); }
+  const int64_t need = svdq::gptq_workspace_bytes(N, K);
+  if (workspace_bytes < need)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace of %lld bytes, needs %lld", fn,
+                (long long)workspace_bytes, (long long)need);
+  return hip_result(svdq::launch_gptq_quantize_weight(fmt, W, N, K, ldw, lambda, lora_down,
+                                                      lora_up, r, H, codes, scales, tensor_scale,
+                                                      workspace,
+                                                      reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 int64_t svdq_lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
                                            int64_t n_rows, int64_t n_alpha, int refit_iters) {
   if (fmt < 0 || fmt > 3 || N < 1 || K < 1 || n_rows < 1 || n_alpha < 1 || r < 0) return -1;

@@ -155,6 +155,19 @@ __device__ __forceinline__ f16x2_t e4m3x2_to_f16x2(uint32_t x) {
   return __builtin_bit_cast(f16x2_t, bits) * f16x2_t{(_Float16)256.0f, (_Float16)256.0f};
 }
 
+// Exact values of stored element codes: an E2M1 nibble (sign in bit 3) and an E4M3 byte (sign in
+// bit 7; normal (8 + m)·2^(e − 10), subnormal m·2^-9).
+__device__ __forceinline__ double e2m1_value(uint32_t nib) {
+  const uint32_t m = nib & 7u;
+  const double mag = m < 4u ? 0.5 * (double)m : (m == 4u ? 2.0 : m == 5u ? 3.0 : m == 6u ? 4.0 : 6.0);
+  return (nib & 8u) ? -mag : mag;
+}
+__device__ __forceinline__ double e4m3_value(uint32_t b) {
+  const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
+  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
+  return (b & 0x80u) ? -mag : mag;
+}
+
 // Running maximum of non-negative floats stored as their bit patterns (monotone for >= 0).
 __device__ __forceinline__ void atomic_max_pos(float* addr, float v) {
   atomicMax(reinterpret_cast<unsigned int*>(addr), __float_as_uint(v));

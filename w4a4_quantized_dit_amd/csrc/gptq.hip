@@ -1,0 +1,523 @@
+// GPTQ rounding of the low-rank branch's residual ("MiniMax-H3 · SVDQuant W4A4 (int4, rank 32,
+// GPTQ)", opening paragraph: the residual is GPTQ-rounded; GPTQ as published by Frantar et al.
+// 2022: columns quantised in order, each column's rounding error compensated in the columns not
+// yet quantised through the inverse Hessian).
+//
+// Hessian: H = Σ_m x̂_m x̂_mᵀ with x̂ = fl32(x · fl32(1/λ)), in fp64 (each product of two fp32
+// values is exact), 64 x 64 tiles of the lower triangle mirrored to the upper.
+//
+// The sweep without an inverse.  With H = Ũ Ũᵀ, Ũ upper triangular (the Cholesky factor taken
+// from the last row up), the published update (error of column j over the diagonal of the upper
+// Cholesky factor of H⁻¹, along that factor's row) adds up to
+//     w̃_k = w_k + Σ_{j<k} (w_j − q_j) · C_jk,      C_jk = Ũ_jk / Ũ_kk,
+// where w is the residual before the sweep and q_j the dequantised code of column j: writing
+// the published sweep's errors e and its unit-diagonal factor V (row j of the factor over its
+// diagonal), w̃ = w − e(V − I) and e = w̃ − q give e·V = w − q, and V⁻¹ = Ũ·diag(1/Ũ_kk)
+// column-normalised because the factor of H⁻¹ is Ũ⁻¹.  So only one Cholesky factorisation is
+// needed: Ũ is the lower Cholesky factor of the index-reversed H, reversed back.
+//
+// Steps on the device, all fp64 except the fp32 residual and the quantiser:
+//   damping H + 0.01 · mean(diag H) · I, copied index-reversed;  blocked lower Cholesky
+//   (64-column panels: a one-workgroup diagonal factor, a forward-substituted panel, a rank-64
+//   update of the trailing lower triangle);  C;  R32 (as the round-to-nearest path) and, for
+//   NVFP4, its tensor scale;  then per block of 64 columns: one thread per weight row
+//   quantises the block's columns in order, keeps w̃ of the block in LDS and updates it
+//   in-block, and writes the block's w − q;  a rank-64 product adds those to the running sums
+//   T of all later columns.  A group's scale is fixed at its first column from the values the
+//   published sweep holds there; those differ from the partial sums above for every column but
+//   the first, and are recovered by a forward substitution inside the group (see the block
+//   kernel).
+#include "device.h"
+#include "launch.h"
+
+namespace svdq {
+
+namespace {
+
+constexpr int kB = 64;           // panel / sweep block width
+constexpr double kPercDamp = 0.01;
+
+int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
+int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
+
+// H (+)= X̂ᵀX̂ on one lower tile (ti >= tj) of 64 x 64, mirrored.  Thread (ty, tx) = 4 x 4
+// outputs; rows of X̂ staged 32 at a time as fp32.
+__global__ __launch_bounds__(256) void k_hessian(const uint16_t* __restrict__ X, int64_t M,
+                                                 int64_t K, int64_t ldx,
+                                                 const float* __restrict__ lambda,
+                                                 int accumulate, double* __restrict__ H) {
+  __shared__ float xi[32][kB];
+  __shared__ float xj[32][kB];
+  const int64_t b = blockIdx.x;
+  int64_t ti = (int64_t)((__builtin_sqrt(8.0 * (double)b + 1.0) - 1.0) * 0.5);
+  while (ti * (ti + 1) / 2 > b) --ti;
+  while ((ti + 1) * (ti + 2) / 2 <= b) ++ti;
+  const int64_t tj = b - ti * (ti + 1) / 2;
+  const int64_t i0 = ti * kB, j0 = tj * kB;
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  double acc[4][4];
+#pragma unroll
+  for (int a = 0; a < 4; ++a)
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[a][c] = 0.0;
+  for (int64_t m0 = 0; m0 < M; m0 += 32) {
+    __syncthreads();
+    for (int t = tid; t < 32 * kB; t += 256) {
+      const int rr = t / kB, cc = t % kB;
+      const int64_t m = m0 + rr;
+      float vi = 0.0f, vj = 0.0f;
+      if (m < M) {
+        const float li = lambda ? 1.0f / lambda[i0 + cc] : 1.0f;
+        const float lj = lambda ? 1.0f / lambda[j0 + cc] : 1.0f;
+        vi = bf16_to_f32(X[m * ldx + i0 + cc]) * li;
+        vj = bf16_to_f32(X[m * ldx + j0 + cc]) * lj;
+      }
+      xi[rr][cc] = vi;
+      xj[rr][cc] = vj;
+    }
+    __syncthreads();
+    const int mn = M - m0 < 32 ? (int)(M - m0) : 32;
+    for (int mm = 0; mm < mn; ++mm) {
+      const f32x4_t a = *reinterpret_cast<const f32x4_t*>(&xi[mm][ty * 4]);
+      const f32x4_t c = *reinterpret_cast<const f32x4_t*>(&xj[mm][tx * 4]);
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fma((double)a[p], (double)c[q], acc[p][q]);
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      const int64_t i = i0 + ty * 4 + p, j = j0 + tx * 4 + q;
+      double v = acc[p][q];
+      if (accumulate) v += H[i * K + j];
+      H[i * K + j] = v;
+      if (ti != tj) H[j * K + i] = v;   // the mirrored entry: same sum, same order
+    }
+}
+
+// damp = 0.01 · mean(diag H), or −1 when the diagonal is all zero (H taken as the identity)
+__global__ __launch_bounds__(256) void k_damping(const double* __restrict__ H, int64_t K,
+                                                 double* __restrict__ damp) {
+  __shared__ double red[4];
+  double s = 0.0;
+  for (int64_t k = threadIdx.x; k < K; k += 256) s += H[k * K + k];
+  for (int off = 32; off > 0; off >>= 1) s += __shfl_xor(s, off);
+  if ((threadIdx.x & 63) == 0) red[threadIdx.x >> 6] = s;
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double t = (red[0] + red[1]) + (red[2] + red[3]);
+    *damp = t == 0.0 ? -1.0 : kPercDamp * (t / (double)K);
+  }
+}
+
+// A[i][j] = Hd[K−1−i][K−1−j]: the damped Hessian with its indices reversed
+__global__ __launch_bounds__(256) void k_reverse_damped(const double* __restrict__ H, int64_t K,
+                                                        const double* __restrict__ damp,
+                                                        double* __restrict__ A) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= K * K) return;
+  const int64_t i = t / K, j = t % K;
+  const double d = *damp;
+  double v;
+  if (d < 0.0) {
+    v = i == j ? 1.0 : 0.0;
+  } else {
+    v = H[(K - 1 - i) * K + (K - 1 - j)];
+    if (i == j) v += d;
+  }
+  A[t] = v;
+}
+
+// Unblocked Cholesky of the 64 x 64 diagonal block at (j0, j0), in LDS; the upper part is zeroed.
+__global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ A, int64_t K, int64_t j0) {
+  __shared__ double a[kB][kB + 1];
+  const int tid = threadIdx.x;
+  for (int t = tid; t < kB * kB; t += 256) a[t / kB][t % kB] = A[(j0 + t / kB) * K + j0 + t % kB];
+  __syncthreads();
+  for (int c = 0; c < kB; ++c) {
+    if (tid == 0) a[c][c] = __builtin_sqrt(a[c][c]);
+    __syncthreads();
+    const double d = a[c][c];
+    for (int i = c + 1 + tid; i < kB; i += 256) a[i][c] /= d;
+    __syncthreads();
+    const int n = kB - 1 - c;   // trailing lower triangle of size n
+    for (int t = tid; t < n * n; t += 256) {
+      const int i = c + 1 + t / n, j = c + 1 + t % n;
+      if (j <= i) a[i][j] -= a[i][c] * a[j][c];
+    }
+    __syncthreads();
+  }
+  for (int t = tid; t < kB * kB; t += 256) {
+    const int i = t / kB, j = t % kB;
+    A[(j0 + i) * K + j0 + j] = j <= i ? a[i][j] : 0.0;
+  }
+}
+
+// Panel rows i >= j0 + 64: L[i, j0 .. j0+64) by forward substitution against the factored
+// diagonal block; one thread per row.
+__global__ __launch_bounds__(64) void k_chol_panel(double* __restrict__ A, int64_t K, int64_t j0) {
+  __shared__ double l[kB][kB + 1];
+  const int tid = threadIdx.x;
+  for (int t = tid; t < kB * kB; t += 64) l[t / kB][t % kB] = A[(j0 + t / kB) * K + j0 + t % kB];
+  __syncthreads();
+  const int64_t i = j0 + kB + (int64_t)blockIdx.x * 64 + tid;
+  if (i >= K) return;
+  double* row = A + i * K + j0;
+  double x[kB];
+#pragma unroll
+  for (int c = 0; c < kB; ++c) x[c] = row[c];
+#pragma unroll
+  for (int c = 0; c < kB; ++c) {
+    double v = x[c];
+#pragma unroll
+    for (int p = 0; p < c; ++p) v = __builtin_fma(-x[p], l[c][p], v);
+    x[c] = v / l[c][c];
+  }
+#pragma unroll
+  for (int c = 0; c < kB; ++c) row[c] = x[c];
+}
+
+// Out[i][j] += sign · Σ_{c<64} A[i][c] · B(c, j) on 64 x 64 output tiles, B(c, j) = B[c][j]
+// (row-major, ldb) or, TRANSB, Bt[j][c].  LOWER: tiles above the diagonal (tile row < tile
+// column) are skipped.  Thread (ty, tx) = 4 x 4 outputs; both operands staged in LDS with the
+// output index contiguous.
+template <bool TRANSB, bool LOWER>
+__global__ __launch_bounds__(256) void k_rank64(const double* __restrict__ A, int64_t lda,
+                                                const double* __restrict__ B, int64_t ldb,
+                                                double* __restrict__ Out, int64_t ldo,
+                                                double sign) {
+  if (LOWER && blockIdx.y < blockIdx.x) return;
+  __shared__ double as[kB][kB + 2];   // as[c][i]
+  __shared__ double bs[kB][kB + 2];   // bs[c][j]
+  const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
+  const int64_t i0 = (int64_t)blockIdx.y * kB, j0 = (int64_t)blockIdx.x * kB;
+  for (int t = tid; t < kB * kB; t += 256) {
+    const int r = t / kB, c = t % kB;
+    as[c][r] = A[(i0 + r) * lda + c];
+    if (TRANSB) bs[c][r] = B[(j0 + r) * ldb + c];
+    else bs[r][c] = B[(int64_t)r * ldb + j0 + c];
+  }
+  __syncthreads();
+  double acc[4][4];
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) acc[p][q] = 0.0;
+#pragma unroll 4
+  for (int c = 0; c < kB; ++c) {
+    double a[4], b[4];
+#pragma unroll
+    for (int p = 0; p < 4; ++p) {
+      a[p] = as[c][ty * 4 + p];
+      b[p] = bs[c][tx * 4 + p];
+    }
+#pragma unroll
+    for (int p = 0; p < 4; ++p)
+#pragma unroll
+      for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fma(a[p], b[q], acc[p][q]);
+  }
+#pragma unroll
+  for (int p = 0; p < 4; ++p)
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      double* o = Out + (i0 + ty * 4 + p) * ldo + j0 + tx * 4 + q;
+      *o = __builtin_fma(sign, acc[p][q], *o);
+    }
+}
+
+// C[j][k] = Ũ_jk / Ũ_kk for j < k (else 0), Ũ_jk = L[K−1−j][K−1−k]
+__global__ __launch_bounds__(256) void k_make_c(const double* __restrict__ L, int64_t K,
+                                                double* __restrict__ C) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t >= K * K) return;
+  const int64_t j = t / K, k = t % K;
+  C[t] = j < k ? L[(K - 1 - j) * K + (K - 1 - k)] / L[(K - 1 - k) * K + (K - 1 - k)] : 0.0;
+}
+
+// R32 = fl32(λ·W − Σ_i up[:, i]·down[i, :]) in fp64, rank by rank ascending (the round-to-
+// nearest path's residual); amax (NVFP4) = max|R32| as a running maximum.
+__global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ W, int64_t N,
+                                                  int64_t K, int64_t ldw,
+                                                  const float* __restrict__ lambda,
+                                                  const uint16_t* __restrict__ down,
+                                                  const uint16_t* __restrict__ up, int64_t r,
+                                                  float* __restrict__ R32,
+                                                  float* __restrict__ amax) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  float m = 0.0f;
+  if (t < N * K) {
+    const int64_t n = t / K, k = t % K;
+    double v = (double)bf16_to_f32(W[n * ldw + k]);
+    if (lambda) v *= (double)lambda[k];
+    for (int64_t i = 0; i < r; ++i)
+      v = __builtin_fma(-(double)bf16_to_f32(up[n * r + i]), (double)bf16_to_f32(down[i * K + k]), v);
+    const float f = (float)v;
+    R32[t] = f;
+    m = fabsf(f);
+  }
+  if (amax) {
+    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((threadIdx.x & 63) == 0 && m > 0.0f) atomic_max_pos(amax, m);
+  }
+}
+
+__global__ void k_set_zero_f32(float* p) { if (threadIdx.x == 0) *p = 0.0f; }
+
+__global__ void k_amax_g(float* p) {
+  if (threadIdx.x == 0) {
+    const float a = *p;
+    *p = a == 0.0f ? 1.0f : a / 2688.0f;
+  }
+}
+
+__global__ __launch_bounds__(256) void k_fill_f64(double* __restrict__ p, int64_t n) {
+  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  if (t < n) p[t] = 0.0;
+}
+
+// Scale of one quantiser group from the fp32 values x[0 .. G) of a row, and the element rule.
+template <int FMT>
+struct GroupQuant {
+  float inv;        // NVFP4 / int4: inverse block scale
+  double mult;      // exact value of one code unit
+  int ex;           // MX exponent
+  uint32_t stored;  // the stored scale (E4M3 byte, fp16 bits or E8M0 byte)
+
+  __device__ __forceinline__ void set(float a, float g) {
+    if (FMT == 0) {
+      const float d6 = 6.0f * g;
+      float sval;
+      stored = e4m3_encode_pos(a / d6, &sval);
+      const float S = sval * g;
+      inv = S != 0.0f ? 1.0f / S : 0.0f;
+      mult = (double)sval * (double)g;
+    } else if (FMT == 1) {
+      const __half s = __float2half_rn(a / 7.0f);
+      const float sf = __half2float(s);
+      inv = sf != 0.0f ? 1.0f / sf : 0.0f;
+      mult = (double)sf;
+      stored = (uint32_t)__builtin_bit_cast(uint16_t, s);
+    } else {
+      ex = mx_exponent(a, FMT == 2 ? 2 : 8);
+      mult = ldexp(1.0, ex);
+      stored = (uint32_t)(ex + 127);
+    }
+  }
+  // element code of x and its exact value
+  __device__ __forceinline__ uint32_t code(float x, double* val) const {
+    if (FMT == 0 || FMT == 2) {
+      const float y = FMT == 0 ? x * inv : __builtin_ldexpf(x, -ex);
+      const uint32_t c = __builtin_amdgcn_cvt_scalef32_pk_fp4_f32(0u, y, 0.0f, 1.0f, 0) & 0xFu;
+      *val = (FMT == 0 && inv == 0.0f) ? 0.0 : e2m1_value(c) * mult;
+      return (FMT == 0 && inv == 0.0f) ? (c & 8u) : c;
+    } else if (FMT == 1) {
+      const uint32_t c = int4_code(x * inv);
+      *val = (double)((int)c - (c >= 8u ? 16 : 0)) * mult;
+      return c;
+    } else {
+      const uint32_t c = e4m3_encode_signed(__builtin_ldexpf(x, -ex));
+      *val = e4m3_value(c) * mult;
+      return c;
+    }
+  }
+};
+
+// One block of 64 columns of the sweep; one thread per weight row.  The row's working values
+// w̃ of the block and its element codes live in LDS (lane-contiguous), the in-block
+// coefficients C[b0 + c][b0 + m] are shared by the workgroup.
+template <int FMT>
+__global__ __launch_bounds__(64) void k_gptq_block(const float* __restrict__ R32,
+                                                   const double* __restrict__ T,
+                                                   const double* __restrict__ C, int64_t N,
+                                                   int64_t K, int64_t b0,
+                                                   const float* __restrict__ tensor_g,
+                                                   uint8_t* __restrict__ codes,
+                                                   void* __restrict__ scales,
+                                                   double* __restrict__ D) {
+  constexpr int G = FMT == 0 ? 16 : (FMT == 1 ? 64 : 32);
+  __shared__ double cb[kB][kB + 1];
+  __shared__ double vs[kB][64];
+  __shared__ double zs[G][64];
+  __shared__ uint8_t cs[kB][64];
+  const int tid = threadIdx.x;
+  for (int t = tid; t < kB * kB; t += 64) cb[t / kB][t % kB] = C[(b0 + t / kB) * K + b0 + t % kB];
+  const int64_t n = (int64_t)blockIdx.x * 64 + tid;
+  const bool live = n < N;
+  const int64_t row = live ? n : N - 1;
+  for (int m = 0; m < kB; ++m) vs[m][tid] = (double)R32[row * K + b0 + m] + T[row * K + b0 + m];
+  __syncthreads();
+  const float g = FMT == 0 ? *tensor_g : 1.0f;
+  GroupQuant<FMT> gq;
+  for (int m = 0; m < kB; ++m) {
+    if (m % G == 0) {
+      // The group's current values as the published sweep has them at this column: the sums
+      // in vs are complete only for column m; for the later columns of the group the
+      // compensation of the columns already quantised is z = Ũ_FF⁻ᵀ·s (F the columns from m
+      // on), and with y = vs − w = diag(1/Ũ)·s the first G entries of z follow by forward
+      // substitution, z_j = y_j − Σ_{m<=l<j} C_lj·z_l.
+      float a = 0.0f;
+      for (int j = 0; j < G; ++j) {
+        const double wj = (double)R32[row * K + b0 + m + j];
+        double z = vs[m + j][tid] - wj;
+        for (int l = 0; l < j; ++l) z = __builtin_fma(-zs[l][tid], cb[m + l][m + j], z);
+        zs[j][tid] = z;
+        a = fmaxf(a, fabsf((float)(wj + z)));
+      }
+      gq.set(a, g);
+      if (live) {
+        const int64_t gi = (b0 + m) / G;
+        if (FMT == 1)
+          reinterpret_cast<uint16_t*>(scales)[n * (K / G) + gi] = (uint16_t)gq.stored;
+        else
+          reinterpret_cast<uint8_t*>(scales)[n * (K / G) + gi] = (uint8_t)gq.stored;
+      }
+    }
+    double q;
+    cs[m][tid] = (uint8_t)gq.code((float)vs[m][tid], &q);
+    const double d = (double)R32[row * K + b0 + m] - q;
+    if (live) D[n * kB + m] = d;
+    for (int m2 = m + 1; m2 < kB; ++m2) vs[m2][tid] = __builtin_fma(d, cb[m][m2], vs[m2][tid]);
+  }
+  if (!live) return;
+  if (FMT == 3) {
+#pragma unroll
+    for (int w = 0; w < 4; ++w) {
+      u32x4_t o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p)
+        o[p] = (uint32_t)cs[16 * w + 4 * p][tid] | ((uint32_t)cs[16 * w + 4 * p + 1][tid] << 8) |
+               ((uint32_t)cs[16 * w + 4 * p + 2][tid] << 16) |
+               ((uint32_t)cs[16 * w + 4 * p + 3][tid] << 24);
+      reinterpret_cast<u32x4_t*>(codes + n * K + b0)[w] = o;
+    }
+  } else {
+#pragma unroll
+    for (int w = 0; w < 2; ++w) {
+      u32x4_t o;
+#pragma unroll
+      for (int p = 0; p < 4; ++p) {
+        uint32_t word = 0u;
+#pragma unroll
+        for (int e = 0; e < 8; ++e) word |= (uint32_t)cs[32 * w + 8 * p + e][tid] << (4 * e);
+        o[p] = word;
+      }
+      reinterpret_cast<u32x4_t*>(codes + n * (K / 2) + b0 / 2)[w] = o;
+    }
+  }
+}
+
+struct GptqWs {
+  double *A, *C, *T, *D, *damp;
+  float* R32;
+  int64_t bytes;
+};
+
+GptqWs carve(void* base, int64_t N, int64_t K) {
+  uint8_t* b = static_cast<uint8_t*>(base);
+  int64_t off = 0;
+  auto take = [&](int64_t bytes) {
+    void* p = b ? b + off : nullptr;
+    off += align256(bytes);
+    return p;
+  };
+  GptqWs w;
+  w.A = static_cast<double*>(take(K * K * 8));
+  w.C = static_cast<double*>(take(K * K * 8));
+  w.T = static_cast<double*>(take(N * K * 8));
+  w.D = static_cast<double*>(take(N * kB * 8));
+  w.R32 = static_cast<float*>(take(N * K * 4));
+  w.damp = static_cast<double*>(take(8));
+  w.bytes = off;
+  return w;
+}
+
+}  // namespace
+
+hipError_t launch_gptq_hessian(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                               const float* lambda, int accumulate, double* H, hipStream_t s) {
+  const int64_t T = K / kB;
+  k_hessian<<<dim3((unsigned)(T * (T + 1) / 2)), dim3(256), 0, s>>>(X, M, K, ldx, lambda,
+                                                                   accumulate, H);
+  return hipGetLastError();
+}
+
+int64_t gptq_workspace_bytes(int64_t N, int64_t K) { return carve(nullptr, N, K).bytes; }
+
+hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K,
+                                       int64_t ldw, const float* lambda, const uint16_t* down,
+                                       const uint16_t* up, int64_t r, const double* H,
+                                       uint8_t* codes, void* scales, float* tensor_scale,
+                                       void* workspace, hipStream_t s) {
+  const GptqWs w = carve(workspace, N, K);
+  hipError_t e;
+#define SVDQ_TRY_HIP(x)                    \
+  do {                                     \
+    if ((e = (x)) != hipSuccess) return e; \
+  } while (0)
+  // Ũ from the index-reversed damped Hessian
+  k_damping<<<dim3(1), dim3(256), 0, s>>>(H, K, w.damp);
+  SVDQ_TRY_HIP(hipGetLastError());
+  k_reverse_damped<<<dim3((unsigned)ceil_div(K * K, 256)), dim3(256), 0, s>>>(H, K, w.damp, w.A);
+  SVDQ_TRY_HIP(hipGetLastError());
+  for (int64_t j0 = 0; j0 < K; j0 += kB) {
+    k_chol_diag<<<dim3(1), dim3(256), 0, s>>>(w.A, K, j0);
+    SVDQ_TRY_HIP(hipGetLastError());
+    const int64_t rest = K - j0 - kB;
+    if (rest > 0) {
+      k_chol_panel<<<dim3((unsigned)ceil_div(rest, 64)), dim3(64), 0, s>>>(w.A, K, j0);
+      SVDQ_TRY_HIP(hipGetLastError());
+      const unsigned tiles = (unsigned)(rest / kB);
+      const int64_t p = (j0 + kB) * K + j0;   // the panel rows below the diagonal block
+      k_rank64<true, true><<<dim3(tiles, tiles), dim3(256), 0, s>>>(
+          w.A + p, K, w.A + p, K, w.A + (j0 + kB) * K + j0 + kB, K, -1.0);
+      SVDQ_TRY_HIP(hipGetLastError());
+    }
+  }
+  k_make_c<<<dim3((unsigned)ceil_div(K * K, 256)), dim3(256), 0, s>>>(w.A, K, w.C);
+  SVDQ_TRY_HIP(hipGetLastError());
+  // the residual, the NVFP4 tensor scale, and T = 0
+  float* amax = fmt == 0 ? tensor_scale : nullptr;
+  if (amax) {
+    k_set_zero_f32<<<dim3(1), dim3(64), 0, s>>>(amax);
+    SVDQ_TRY_HIP(hipGetLastError());
+  }
+  k_residual<<<dim3((unsigned)ceil_div(N * K, 256)), dim3(256), 0, s>>>(W, N, K, ldw, lambda,
+                                                                        down, up, r, w.R32, amax);
+  SVDQ_TRY_HIP(hipGetLastError());
+  if (amax) {
+    k_amax_g<<<dim3(1), dim3(64), 0, s>>>(amax);
+    SVDQ_TRY_HIP(hipGetLastError());
+  }
+  k_fill_f64<<<dim3((unsigned)ceil_div(N * K, 256)), dim3(256), 0, s>>>(w.T, N * K);
+  SVDQ_TRY_HIP(hipGetLastError());
+  // the sweep
+  const dim3 rows_grid((unsigned)ceil_div(N, 64));
+  for (int64_t b0 = 0; b0 < K; b0 += kB) {
+    if (fmt == 0)
+      k_gptq_block<0><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, tensor_scale,
+                                                     codes, scales, w.D);
+    else if (fmt == 1)
+      k_gptq_block<1><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
+                                                     scales, w.D);
+    else if (fmt == 2)
+      k_gptq_block<2><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
+                                                     scales, w.D);
+    else
+      k_gptq_block<3><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
+                                                     scales, w.D);
+    SVDQ_TRY_HIP(hipGetLastError());
+    const int64_t rest = K - b0 - kB;
+    if (rest > 0) {
+      k_rank64<false, false><<<dim3((unsigned)(rest / kB), (unsigned)(N / kB)), dim3(256), 0, s>>>(
+          w.D, kB, w.C + b0 * K + b0 + kB, K, w.T + b0 + kB, K, 1.0);
+      SVDQ_TRY_HIP(hipGetLastError());
+    }
+  }
+#undef SVDQ_TRY_HIP
+  return hipSuccess;
+}
+
+}  // namespace svdq

@@ -73,6 +73,15 @@ hipError_t launch_score(const uint16_t* Y, int64_t ldy, const uint16_t* X, int64
                         const int32_t* rows, const int8_t* grp, int64_t n_rows, double* sums,
                         hipStream_t s);
 
+hipError_t launch_gptq_hessian(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                               const float* lambda, int accumulate, double* H, hipStream_t s);
+int64_t gptq_workspace_bytes(int64_t N, int64_t K);
+hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K,
+                                       int64_t ldw, const float* lambda, const uint16_t* down,
+                                       const uint16_t* up, int64_t r, const double* H,
+                                       uint8_t* codes, void* scales, float* tensor_scale,
+                                       void* workspace, hipStream_t s);
+
 int64_t lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
                                       int64_t n_rows, int64_t n_alpha, int refit_iters);
 hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W,

@@ -93,18 +93,6 @@ __global__ void k_commit_best(const double* __restrict__ cur, double* __restrict
   if (threadIdx.x == 0 && *cur < *best) *best = *cur;
 }
 
-// Exact values of the stored codes.
-__device__ __forceinline__ double e2m1_value(uint32_t nib) {
-  const uint32_t m = nib & 7u;
-  const double mag = m < 4u ? 0.5 * (double)m : (m == 4u ? 2.0 : m == 5u ? 3.0 : m == 6u ? 4.0 : 6.0);
-  return (nib & 8u) ? -mag : mag;
-}
-__device__ __forceinline__ double e4m3_value(uint32_t b) {
-  const int e = (int)((b >> 3) & 15u), m = (int)(b & 7u);
-  const double mag = e == 0 ? ldexp((double)m, -9) : ldexp((double)(8 + m), e - 10);
-  return (b & 0x80u) ? -mag : mag;
-}
-
 // Refit target of the low-rank branch: E = λ·W − deq(Q(R)), the smoothed weight less the
 // dequantised residual, in fp64 (every term exact), rounded once to fp32.  One thread per 16
 // consecutive channels of a row.  FMT: 0 NVFP4, 1 int4-g64, 2 MXFP4, 3 MXFP8.

@@ -135,6 +135,32 @@ def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
     return PreparedWeight(fmt, N, K, r, codes, scales, g, lora_up)
 
 
+def gptq_hessian(X, lam, H=None):
+    """H [K, K] fp64 (+)= X̂ᵀX̂ of the calibration rows X; pass H back to accumulate batches."""
+    torch = _torch()
+    K = X.shape[1]
+    if H is None:
+        H = torch.empty(K, K, dtype=torch.float64, device=X.device)
+        _lib.svdq_gptq_hessian(X, lam, H, accumulate=False)
+    else:
+        _lib.svdq_gptq_hessian(X, lam, H, accumulate=True)
+    return H
+
+
+def prepare_weight_gptq(W, lam, lora_down, lora_up, H, fmt=NVFP4):
+    """prepare_weight with the residual GPTQ-rounded under the Hessian H."""
+    torch = _torch()
+    N, K = W.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    codes, scales, g = _alloc_codes_scales(fmt, N, K, W.device)
+    nbytes = _lib.svdq_gptq_workspace_bytes(N, K)
+    ws = torch.empty(nbytes + 256, dtype=torch.uint8, device=W.device)
+    off = (-ws.data_ptr()) % 256
+    _lib.svdq_gptq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, H, codes, scales, g,
+                                   ws[off:off + nbytes])
+    return PreparedWeight(fmt, N, K, r, codes, scales, g, lora_up)
+
+
 def quantize_activation(X, lam, act_amax, lora_down, fmt=NVFP4, sat_count=None):
     """(codes, scales, g_a, D) of X [M, K]."""
     torch = _torch()
