@@ -20,6 +20,7 @@ HIP events on the launch stream, the roofline of the dominant kernel, and the CP
 baseline.
 """
 import argparse
+import gc
 import hashlib
 import json
 import os
@@ -102,6 +103,35 @@ def lowrank_factors_gpu(torch, layer, Wd, lam, r, seed=0, power_iters=2, reps=5)
     return down, up, float(np.median(times[1:]))
 
 
+def weight_side_gpu(torch, layer, st, fmt, seed=0):
+    """One-off (set-up side, outside the timed step) times in milliseconds of the calibration
+    search and GPTQ on the benchmark inputs: the 39-point λ grid scored on 1024 uniform rows
+    with the rank-r branch, and GPTQ of the residual under the Hessian of 2048 rows."""
+    cfg = st["cfg"]
+    M, K, N, r = cfg["M"], cfg["K"], cfg["N"], cfg["r"]
+    Xd, Wd = st["Xs"][0], st["Wd"]
+    rng = np.random.default_rng([seed, 10])
+    rows = torch.from_numpy(np.sort(rng.choice(M, 1024, replace=False)).astype(np.int32)).cuda()
+    omega = torch.from_numpy(rng.standard_normal((N, r + 8)).astype(np.float32)).cuda()
+    state = dict(ax=st["ax"], aw=st["aw"])
+    grid = list(layer.ALPHA_GRID)
+    t = [torch.cuda.Event(enable_timing=True) for _ in range(4)]
+    layer.lambda_search(Xd, Wd, state, grid[:1], rows, fmt, omega, r)       # warm-up
+    t[0].record()
+    out = layer.lambda_search(Xd, Wd, state, grid, rows, fmt, omega, r)
+    t[1].record()
+    n_cal = min(2048, M)
+    H = layer.gptq_hessian(Xd[:n_cal], st["lam"])
+    t[2].record()
+    layer.prepare_weight_gptq(Wd, st["lam"], st["downd"], st["upd"], H, fmt)
+    t[3].record()
+    torch.cuda.synchronize()
+    return {"lambda_search_39": round(t[0].elapsed_time(t[1]), 2),
+            "lambda_search_best_alpha": grid[int(out["index"].cpu()[0])],
+            "gptq_hessian_2048_rows": round(t[1].elapsed_time(t[2]), 2),
+            "gptq": round(t[2].elapsed_time(t[3]), 2)}
+
+
 def cpu_baseline(cfg, X, W, down, up, rows):
     """The oracle, as it stands, on the first `rows` rows of the workload (whole weight)."""
     from oracle import calib as OC, layer as OL
@@ -164,7 +194,8 @@ def setup(torch, workload, n_rot):
     up = upd.view(torch.int16).cpu().numpy().view(np.uint16)
     Y = torch.empty(M, N, dtype=torch.bfloat16, device=dev)
     u8 = torch.uint8
-    st = dict(cfg=cfg, X=X, W=W, down=down, up=up, Y=Y, lowrank_ms=lowrank_ms)
+    st = dict(cfg=cfg, X=X, W=W, down=down, up=up, Y=Y, lowrank_ms=lowrank_ms, Wd=Wd, ax=ax,
+              aw=aw, lam=lam, downd=downd, upd=upd)
 
     def cal(Xi):
         _lib.svdq_calibrate_lambda(Xi, seg, Wd, 7, 0.5, 0, ax, aw, lam, amax)
@@ -278,6 +309,8 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--copy-probe", action="store_true")
+    ap.add_argument("--no-weight-side", action="store_true",
+                    help="skip the one-off λ search and GPTQ timings")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer is "
@@ -299,13 +332,22 @@ def main():
     names = [n for n, _ in st["steps"]]
     ev = {k: [] for k in names}
 
+    # every timing event exists (and has been recorded once) before the timed region: the
+    # first creation of a timing event costs tens of milliseconds of host time
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+           for _ in range(args.steps)]
+    for e in evs:
+        for x in e:
+            x.record()
+    torch.cuda.synchronize()
+
     def step(i, record):
         Xi = st["Xs"][i % n_rot]
         if not record:
             for _, fn in st["steps"]:
                 fn(Xi)
             return
-        e = [torch.cuda.Event(enable_timing=True) for _ in range(len(names) + 1)]
+        e = evs[i]
         e[0].record()
         for j, (name, fn) in enumerate(st["steps"]):
             fn(Xi)
@@ -317,11 +359,14 @@ def main():
         step(i, False)
     torch.cuda.synchronize()
     print("[bench] timed steps", file=sys.stderr, flush=True)
+    gc.collect()
+    gc.disable()           # no collector pause inside the timed region
     t0 = time.perf_counter()
     for i in range(args.steps):
         step(i, True)
     torch.cuda.synchronize()
     wall = time.perf_counter() - t0
+    gc.enable()
     ms = {k: float(np.mean([a.elapsed_time(b) for a, b in v])) for k, v in ev.items()}
     ms_step = wall * 1e3 / args.steps
 
@@ -363,6 +408,11 @@ def main():
     }
     if "core" in ms:
         out["core_gemm_tflops"] = round(st["core_flops"] / (ms["core"] * 1e-3) / 1e12, 2)
+    if not args.no_weight_side:
+        from w4a4_quantized_dit_amd import layer
+        print("[bench] weight side: λ search and GPTQ", file=sys.stderr, flush=True)
+        fmt = {"nvfp4": 0, "nvfp4-delta": 0, "int4": 1, "mxfp4": 2, "mxfp8": 3}[cfg["fmt"]]
+        out["weight_side_ms"] = weight_side_gpu(torch, layer, st, fmt)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         if cfg["fmt"] == "nvfp4-delta":
