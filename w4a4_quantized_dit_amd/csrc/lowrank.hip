@@ -21,84 +21,152 @@ namespace {
 
 constexpr int kMaxEll = 160;
 constexpr int kColTile = 40;       // columns of the sketch handled by one thread
-constexpr int kSplitRows = 512;    // reduction rows per partial sum of the sketch products
+constexpr int kSplitWt = 128;      // reduction rows (of W) per partial sum of Wᵀ·X
+constexpr int kSplitW = 256;       // reduction channels per partial sum of W·Q
 constexpr int kGramRows = 64;      // rows per partial Gram matrix
 constexpr int kJacobiThreads = 1024;
 constexpr int kMaxSweeps = 40;
+constexpr int kLdsEll = 80;        // the small factorisations run in LDS up to this ell
 
 // The matrix is either the bf16 weight (scaled by λ per channel) or an fp32 matrix (the refit
-// target of the layer's low-rank branch), read through one of these.
-__device__ __forceinline__ float ld_elem(const uint16_t* p) { return bf16_to_f32(*p); }
-__device__ __forceinline__ float ld_elem(const float* p) { return *p; }
+// target of the layer's low-rank branch).
 
-// Yp[s][k][j] = Σ_{n in split s} W[n, k] · X[n, j]: thread = column k, 40 columns of X per
-// workgroup (blockIdx.z), rows of X staged 64 at a time.
+// Stage a ROWS x COLS tile of W (rows r0 .. r_end, columns c0 .. c_end; the rest reads as 0)
+// into LDS as fp32 with 16-byte loads, all of a thread's loads in flight before the first
+// store.  COLS and c0 are multiples of the elements per 16 bytes and the rows are 16-byte
+// aligned (ldw a multiple of 8); a 16-byte piece that crosses c_end is read element by element.
+template <typename T, int ROWS, int COLS, int LDS_LD>
+__device__ __forceinline__ void stage_tile(const T* __restrict__ W, int64_t ldw, int64_t r0,
+                                           int64_t r_end, int64_t c0, int64_t c_end,
+                                           float* lds) {
+  constexpr int V = 16 / (int)sizeof(T);          // elements per 16 bytes
+  constexpr int PER = ROWS * COLS / V / 256;       // 16-byte loads per thread
+  static_assert(PER * 256 * V == ROWS * COLS, "tile must split evenly over 256 threads");
+  u32x4_t buf[PER];
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int idx = threadIdx.x + 256 * p;
+    const int rr = idx / (COLS / V), cv = idx % (COLS / V);
+    const int64_t c = c0 + cv * V;
+    buf[p] = u32x4_t{0u, 0u, 0u, 0u};
+    if (r0 + rr < r_end) {
+      const T* src = W + (r0 + rr) * ldw + c;
+      if (c + V <= c_end) {
+        buf[p] = *reinterpret_cast<const u32x4_t*>(src);
+      } else if (c < c_end) {
+        T part[V];
+#pragma unroll
+        for (int e = 0; e < V; ++e) part[e] = c + e < c_end ? src[e] : (T)0;
+        __builtin_memcpy(&buf[p], part, 16);
+      }
+    }
+  }
+#pragma unroll
+  for (int p = 0; p < PER; ++p) {
+    const int idx = threadIdx.x + 256 * p;
+    const int rr = idx / (COLS / V), cv = idx % (COLS / V);
+    float* dst = lds + rr * LDS_LD + cv * V;
+    if (sizeof(T) == 2) {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        dst[2 * e] = bf16_lo(buf[p][e]);
+        dst[2 * e + 1] = bf16_hi(buf[p][e]);
+      }
+    } else {
+#pragma unroll
+      for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(buf[p][e]);
+    }
+  }
+}
+
+// Yp[s][k][j] = Σ_{n in split s} W[n, k] · X[n, j]: 256 columns k per workgroup (thread =
+// column), 40 columns of X per workgroup (blockIdx.z); W and X staged 32 rows at a time.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sketch_wt(const T* __restrict__ W, int64_t N,
                                                    int64_t K, int64_t ldw,
                                                    const float* __restrict__ X, int ell,
                                                    float* __restrict__ Yp) {
-  __shared__ float xs[64][kColTile];
-  const int64_t k = (int64_t)blockIdx.x * 256 + threadIdx.x;
+  constexpr int kR = 32;
+  // the W chunk [kR][256] while accumulating, then the block of sums [256][kColTile]
+  __shared__ __attribute__((aligned(16))) float s_buf[256 * kColTile];
+  float (*ws)[256] = reinterpret_cast<float (*)[256]>(s_buf);
+  __shared__ float xs[kR][kColTile];
+  const int64_t kb = (int64_t)blockIdx.x * 256;
   const int64_t s = blockIdx.y;
   const int j0 = blockIdx.z * kColTile;
   const int jn = ell - j0 < kColTile ? ell - j0 : kColTile;
-  const int64_t n_begin = s * kSplitRows;
-  const int64_t n_end = n_begin + kSplitRows < N ? n_begin + kSplitRows : N;
+  const int64_t n_begin = s * kSplitWt;
+  const int64_t n_end = n_begin + kSplitWt < N ? n_begin + kSplitWt : N;
   float acc[kColTile];
 #pragma unroll
   for (int c = 0; c < kColTile; ++c) acc[c] = 0.0f;
-  for (int64_t n0 = n_begin; n0 < n_end; n0 += 64) {
-    const int nn = n_end - n0 < 64 ? (int)(n_end - n0) : 64;
+  for (int64_t n0 = n_begin; n0 < n_end; n0 += kR) {
     __syncthreads();
-    for (int t = threadIdx.x; t < 64 * kColTile; t += 256) {
+    stage_tile<T, kR, 256, 256>(W, ldw, n0, n_end, kb, K, &ws[0][0]);
+    for (int t = threadIdx.x; t < kR * kColTile; t += 256) {
       const int rr = t / kColTile, c = t % kColTile;
-      xs[rr][c] = (rr < nn && c < jn) ? X[(n0 + rr) * ell + j0 + c] : 0.0f;
+      xs[rr][c] = (n0 + rr < n_end && c < jn) ? X[(n0 + rr) * ell + j0 + c] : 0.0f;
     }
     __syncthreads();
-    if (k < K) {
-      for (int rr = 0; rr < nn; ++rr) {
-        const float w = ld_elem(W + (n0 + rr) * ldw + k);
+#pragma unroll 4
+    for (int rr = 0; rr < kR; ++rr) {
+      const float w = ws[rr][threadIdx.x];
 #pragma unroll
-        for (int c = 0; c < kColTile; ++c) acc[c] = __builtin_fmaf(w, xs[rr][c], acc[c]);
-      }
+      for (int c = 0; c < kColTile; ++c) acc[c] = __builtin_fmaf(w, xs[rr][c], acc[c]);
     }
   }
-  if (k < K) {
+  // The sums leave through LDS so that the stores are row-contiguous (a thread's 40 sums are
+  // one row of the output; storing them directly would touch a cache line per lane).
+  __syncthreads();
 #pragma unroll
-    for (int c = 0; c < kColTile; ++c)
-      if (c < jn) Yp[(s * K + k) * ell + j0 + c] = acc[c];
+  for (int c = 0; c < kColTile; ++c) s_buf[threadIdx.x * kColTile + ((c + threadIdx.x) % kColTile)] = acc[c];
+  __syncthreads();
+  auto sum_at = [&](int row, int c) { return s_buf[row * kColTile + ((c + row) % kColTile)]; };
+  if (ell == kColTile && kb + 256 <= K) {
+    // the block is one contiguous run of 256 x 40 floats
+    float* dst = Yp + (s * K + kb) * ell;
+    for (int t = threadIdx.x; t < 256 * kColTile / 4; t += 256) {
+      const int e = 4 * t, row = e / kColTile, c = e % kColTile;
+      *reinterpret_cast<f32x4_t*>(dst + e) =
+          f32x4_t{sum_at(row, c), sum_at(row, c + 1), sum_at(row, c + 2), sum_at(row, c + 3)};
+    }
+  } else {
+    for (int t = threadIdx.x; t < 256 * kColTile; t += 256) {
+      const int row = t / kColTile, c = t % kColTile;
+      const int64_t k = kb + row;
+      if (k < K && c < jn) Yp[(s * K + k) * ell + j0 + c] = sum_at(row, c);
+    }
   }
 }
 
-// Zp[s][n][j] = Σ_{k in split s} W[n, k] · λ_k · Q[k, j]: 64 rows n x 40 columns per workgroup,
-// thread = (row, column residue mod 4), W and λ∘Q staged 64 channels at a time.
+// Zp[s][n][j] = Σ_{k in split s} W[n, k] · λ_k · Q[k, j]: 128 rows n x 40 columns per
+// workgroup; thread = 4 rows (tid / 8) x 5 columns (tid % 8 + 8m), W and λ∘Q staged 64 channels
+// at a time.
 template <typename T>
 __global__ __launch_bounds__(256) void k_sketch_w(const T* __restrict__ W, int64_t N,
                                                   int64_t K, int64_t ldw,
                                                   const float* __restrict__ lambda,
                                                   const float* __restrict__ Q, int ell,
                                                   float* __restrict__ Zp) {
-  __shared__ float ws[64][65];
+  constexpr int kRows = 128, kPr = 4, kPc = kColTile / 8;
+  __shared__ float ws[kRows][65];
   __shared__ float qs[64][kColTile];
-  const int64_t n0 = (int64_t)blockIdx.x * 64;
+  const int64_t n0 = (int64_t)blockIdx.x * kRows;
   const int64_t s = blockIdx.y;
   const int j0 = blockIdx.z * kColTile;
   const int jn = ell - j0 < kColTile ? ell - j0 : kColTile;
-  const int64_t k_begin = s * kSplitRows;
-  const int64_t k_end = k_begin + kSplitRows < K ? k_begin + kSplitRows : K;
-  const int row = threadIdx.x >> 2, cq = threadIdx.x & 3;
-  constexpr int kPer = kColTile / 4;
-  float acc[kPer];
+  const int64_t k_begin = s * kSplitW;
+  const int64_t k_end = k_begin + kSplitW < K ? k_begin + kSplitW : K;
+  const int rg = threadIdx.x >> 3, cg = threadIdx.x & 7;
+  float acc[kPr][kPc];
 #pragma unroll
-  for (int m = 0; m < kPer; ++m) acc[m] = 0.0f;
+  for (int a = 0; a < kPr; ++a)
+#pragma unroll
+    for (int m = 0; m < kPc; ++m) acc[a][m] = 0.0f;
   for (int64_t k0 = k_begin; k0 < k_end; k0 += 64) {
     const int kn = k_end - k0 < 64 ? (int)(k_end - k0) : 64;
     __syncthreads();
-    for (int t = threadIdx.x; t < 64 * 64; t += 256) {
-      const int rr = t >> 6, kk = t & 63;
-      ws[rr][kk] = (n0 + rr < N && kk < kn) ? ld_elem(W + (n0 + rr) * ldw + k0 + kk) : 0.0f;
-    }
+    stage_tile<T, kRows, 64, 65>(W, ldw, n0, N, k0, k_end, &ws[0][0]);
     for (int t = threadIdx.x; t < 64 * kColTile; t += 256) {
       const int kk = t / kColTile, c = t % kColTile;
       float v = 0.0f;
@@ -110,16 +178,26 @@ __global__ __launch_bounds__(256) void k_sketch_w(const T* __restrict__ W, int64
     }
     __syncthreads();
     for (int kk = 0; kk < kn; ++kk) {
-      const float w = ws[row][kk];
+      float w[kPr], q[kPc];
 #pragma unroll
-      for (int m = 0; m < kPer; ++m) acc[m] = __builtin_fmaf(w, qs[kk][cq + 4 * m], acc[m]);
+      for (int a = 0; a < kPr; ++a) w[a] = ws[rg * kPr + a][kk];
+#pragma unroll
+      for (int m = 0; m < kPc; ++m) q[m] = qs[kk][cg + 8 * m];
+#pragma unroll
+      for (int a = 0; a < kPr; ++a)
+#pragma unroll
+        for (int m = 0; m < kPc; ++m) acc[a][m] = __builtin_fmaf(w[a], q[m], acc[a][m]);
     }
   }
-  if (n0 + row < N) {
 #pragma unroll
-    for (int m = 0; m < kPer; ++m) {
-      const int c = cq + 4 * m;
-      if (c < jn) Zp[(s * N + n0 + row) * ell + j0 + c] = acc[m];
+  for (int a = 0; a < kPr; ++a) {
+    const int64_t n = n0 + rg * kPr + a;
+    if (n < N) {
+#pragma unroll
+      for (int m = 0; m < kPc; ++m) {
+        const int c = cg + 8 * m;
+        if (c < jn) Zp[(s * N + n) * ell + j0 + c] = acc[a][m];
+      }
     }
   }
 }
@@ -179,41 +257,63 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const double* __restrict__ 
 // Cholesky G = RᵀR (R upper) and Rinv = R⁻¹ (upper), fp64, one workgroup.  A pivot that is not
 // positive (a rank-deficient block) is raised to a tiny positive value relative to the trace,
 // which keeps every value finite; such directions have singular values at rounding level and
-// end up at the bottom of the spectrum.
+// end up at the bottom of the spectrum.  Both factorisations are right-looking: every step is a
+// pivot, a scaled row and a rank-1 update of the trailing part, each spread over the workgroup,
+// so a step costs a few barriers instead of a serial dot product.
 __global__ __launch_bounds__(256) void k_chol_inv(const double* __restrict__ G, int ell,
-                                                  double* __restrict__ R,
-                                                  double* __restrict__ Rinv) {
+                                                  double* __restrict__ Rg,
+                                                  double* __restrict__ Rinvg) {
   __shared__ double s_tiny;
-  if (threadIdx.x == 0) {
+  __shared__ double s_r[kLdsEll * kLdsEll], s_ri[kLdsEll * kLdsEll];
+  // R and R⁻¹ are built in LDS when they fit, in the output buffers otherwise (same arithmetic)
+  const bool in_lds = ell <= kLdsEll;
+  double* R = in_lds ? s_r : Rg;
+  double* X = in_lds ? s_ri : Rinvg;
+  const int tid = threadIdx.x;
+  if (tid == 0) {
     double tr = 0.0;
     for (int i = 0; i < ell; ++i) tr += G[i * ell + i];
     s_tiny = (tr > 1e-300 ? tr : 1e-300) * 1e-28;
   }
-  for (int t = threadIdx.x; t < ell * ell; t += 256) R[t] = 0.0;
+  // R starts as the upper triangle of G, X as the identity
+  for (int t = tid; t < ell * ell; t += 256) {
+    const int i = t / ell, j = t % ell;
+    R[t] = j >= i ? G[t] : 0.0;
+    X[t] = i == j ? 1.0 : 0.0;
+  }
   __syncthreads();
   for (int j = 0; j < ell; ++j) {
-    if (threadIdx.x == 0) {
-      double d = G[j * ell + j];
-      for (int k = 0; k < j; ++k) d -= R[k * ell + j] * R[k * ell + j];
+    if (tid == 0) {
+      const double d = R[j * ell + j];
       R[j * ell + j] = sqrt(d > s_tiny ? d : s_tiny);
     }
     __syncthreads();
     const double rjj = R[j * ell + j];
-    for (int i = j + 1 + threadIdx.x; i < ell; i += 256) {
-      double v = G[j * ell + i];
-      for (int k = 0; k < j; ++k) v -= R[k * ell + j] * R[k * ell + i];
-      R[j * ell + i] = v / rjj;
+    for (int i = j + 1 + tid; i < ell; i += 256) R[j * ell + i] /= rjj;
+    __syncthreads();
+    const int n = ell - 1 - j;   // trailing upper triangle: rows/columns j+1 .. ell-1
+    for (int t = tid; t < n * n; t += 256) {
+      const int k = j + 1 + t / n, i = j + 1 + t % n;
+      if (i >= k) R[k * ell + i] -= R[j * ell + k] * R[j * ell + i];
     }
     __syncthreads();
   }
-  // column c of R⁻¹ by back substitution (thread per column)
-  for (int c = threadIdx.x; c < ell; c += 256) {
-    for (int i = ell - 1; i > c; --i) Rinv[i * ell + c] = 0.0;
-    Rinv[c * ell + c] = 1.0 / R[c * ell + c];
-    for (int i = c - 1; i >= 0; --i) {
-      double v = 0.0;
-      for (int k = i + 1; k <= c; ++k) v += R[i * ell + k] * Rinv[k * ell + c];
-      Rinv[i * ell + c] = -v / R[i * ell + i];
+  // X = R⁻¹ from the bottom row up: row k of X is divided by R_kk, then removed from the rows
+  // above it in proportion to column k of R
+  for (int k = ell - 1; k >= 0; --k) {
+    const double rkk = R[k * ell + k];
+    for (int c = k + tid; c < ell; c += 256) X[k * ell + c] /= rkk;
+    __syncthreads();
+    for (int t = tid; t < k * (ell - k); t += 256) {
+      const int i = t / (ell - k), c = k + t % (ell - k);
+      X[i * ell + c] -= R[i * ell + k] * X[k * ell + c];
+    }
+    __syncthreads();
+  }
+  if (in_lds) {
+    for (int t = tid; t < ell * ell; t += 256) {
+      Rg[t] = s_r[t];
+      Rinvg[t] = s_ri[t];
     }
   }
 }
@@ -235,8 +335,8 @@ __global__ __launch_bounds__(256) void k_apply_rinv(const float* __restrict__ M,
 // one workgroup), eigenvectors accumulated in V; then the eigenpairs sorted by decreasing
 // eigenvalue: eig[i], U[:, i].  Rounds pair the indices by the circle method (index 0 fixed,
 // the others rotating); an odd ell gets a dummy index that sits out its pairs.
-__global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ H, int ell,
-                                                           double* __restrict__ V,
+__global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ Hg, int ell,
+                                                           double* __restrict__ Vg,
                                                            double* __restrict__ U,
                                                            double* __restrict__ eig) {
   __shared__ double s_c[kMaxEll / 2], s_s[kMaxEll / 2];
@@ -244,7 +344,14 @@ __global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ 
   __shared__ double s_red[kJacobiThreads], s_red2[kJacobiThreads];
   __shared__ int s_order[kMaxEll];
   __shared__ int s_done;
+  __shared__ double s_h[kLdsEll * kLdsEll], s_v[kLdsEll * kLdsEll];
   const int tid = threadIdx.x;
+  // H and V live in LDS when they fit, in the caller's buffers otherwise (same arithmetic)
+  const bool in_lds = ell <= kLdsEll;
+  double* H = in_lds ? s_h : Hg;
+  double* V = in_lds ? s_v : Vg;
+  if (in_lds)
+    for (int t = tid; t < ell * ell; t += kJacobiThreads) s_h[t] = Hg[t];
   const int m = (ell + 1) & ~1;  // even player count
   const int half = m / 2;
   for (int t = tid; t < ell * ell; t += kJacobiThreads) V[t] = (t / ell == t % ell) ? 1.0 : 0.0;
@@ -396,9 +503,9 @@ Workspace carve(void* base, int64_t N, int64_t K, int64_t ell) {
   w.yt = reinterpret_cast<float*>(take(K * ell * 4));
   w.z = reinterpret_cast<float*>(take(N * ell * 4));
   w.zt = reinterpret_cast<float*>(take(N * ell * 4));
-  const int64_t splits = ceil_div(N, kSplitRows) * K > ceil_div(K, kSplitRows) * N
-                             ? ceil_div(N, kSplitRows) * K
-                             : ceil_div(K, kSplitRows) * N;
+  const int64_t splits = ceil_div(N, kSplitWt) * K > ceil_div(K, kSplitW) * N
+                             ? ceil_div(N, kSplitWt) * K
+                             : ceil_div(K, kSplitW) * N;
   w.p = reinterpret_cast<float*>(take(splits * ell * 4));
   const int64_t nb = ceil_div(K > N ? K : N, kGramRows);
   w.gp = reinterpret_cast<double*>(take(nb * ell * ell * 8));
@@ -416,9 +523,9 @@ Workspace carve(void* base, int64_t N, int64_t K, int64_t ell) {
 int64_t lowrank_workspace_bytes(int64_t N, int64_t K, int64_t ell) {
   int64_t total = 0;
   total += 2 * align256(K * ell * 4) + 2 * align256(N * ell * 4);
-  const int64_t splits = ceil_div(N, kSplitRows) * K > ceil_div(K, kSplitRows) * N
-                             ? ceil_div(N, kSplitRows) * K
-                             : ceil_div(K, kSplitRows) * N;
+  const int64_t splits = ceil_div(N, kSplitWt) * K > ceil_div(K, kSplitW) * N
+                             ? ceil_div(N, kSplitWt) * K
+                             : ceil_div(K, kSplitW) * N;
   total += align256(splits * ell * 4);
   total += align256(ceil_div(K > N ? K : N, kGramRows) * ell * ell * 8);
   total += 5 * align256(ell * ell * 8) + align256(ell * 8);
@@ -446,7 +553,7 @@ hipError_t lowrank_impl(const T* W, int64_t N, int64_t K, int64_t ldw, const flo
 
   // Y (K x ell) = diag(λ) Wᵀ X  for X (N x ell)
   auto a_times = [&](const float* X, float* Y) -> hipError_t {
-    const int64_t nsplit = ceil_div(N, kSplitRows);
+    const int64_t nsplit = ceil_div(N, kSplitWt);
     k_sketch_wt<<<dim3((unsigned)ceil_div(K, 256), (unsigned)nsplit, ztiles), dim3(256), 0, s>>>(
         W, N, K, ldw, X, e, w.p);
     SVDQ_CHECK_LAUNCH();
@@ -457,8 +564,8 @@ hipError_t lowrank_impl(const T* W, int64_t N, int64_t K, int64_t ldw, const flo
   };
   // Z (N x ell) = W diag(λ) Q  for Q (K x ell)
   auto at_times = [&](const float* Qm, float* Z) -> hipError_t {
-    const int64_t nsplit = ceil_div(K, kSplitRows);
-    k_sketch_w<<<dim3((unsigned)ceil_div(N, 64), (unsigned)nsplit, ztiles), dim3(256), 0, s>>>(
+    const int64_t nsplit = ceil_div(K, kSplitW);
+    k_sketch_w<<<dim3((unsigned)ceil_div(N, 128), (unsigned)nsplit, ztiles), dim3(256), 0, s>>>(
         W, N, K, ldw, lambda, Qm, e, w.p);
     SVDQ_CHECK_LAUNCH();
     k_reduce_splits<<<dim3((unsigned)ceil_div(N * ell, 256)), dim3(256), 0, s>>>(
