@@ -237,42 +237,6 @@ __global__ __launch_bounds__(256) void k_make_c(const double* __restrict__ L, in
   C[t] = j < k ? L[(K - 1 - j) * K + (K - 1 - k)] / L[(K - 1 - k) * K + (K - 1 - k)] : 0.0;
 }
 
-// R32 = fl32(λ·W − Σ_i up[:, i]·down[i, :]) in fp64, rank by rank ascending (the round-to-
-// nearest path's residual); amax (NVFP4) = max|R32| as a running maximum.
-__global__ __launch_bounds__(256) void k_residual(const uint16_t* __restrict__ W, int64_t N,
-                                                  int64_t K, int64_t ldw,
-                                                  const float* __restrict__ lambda,
-                                                  const uint16_t* __restrict__ down,
-                                                  const uint16_t* __restrict__ up, int64_t r,
-                                                  float* __restrict__ R32,
-                                                  float* __restrict__ amax) {
-  const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
-  float m = 0.0f;
-  if (t < N * K) {
-    const int64_t n = t / K, k = t % K;
-    double v = (double)bf16_to_f32(W[n * ldw + k]);
-    if (lambda) v *= (double)lambda[k];
-    for (int64_t i = 0; i < r; ++i)
-      v = __builtin_fma(-(double)bf16_to_f32(up[n * r + i]), (double)bf16_to_f32(down[i * K + k]), v);
-    const float f = (float)v;
-    R32[t] = f;
-    m = fabsf(f);
-  }
-  if (amax) {
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if ((threadIdx.x & 63) == 0 && m > 0.0f) atomic_max_pos(amax, m);
-  }
-}
-
-__global__ void k_set_zero_f32(float* p) { if (threadIdx.x == 0) *p = 0.0f; }
-
-__global__ void k_amax_g(float* p) {
-  if (threadIdx.x == 0) {
-    const float a = *p;
-    *p = a == 0.0f ? 1.0f : a / 2688.0f;
-  }
-}
-
 __global__ __launch_bounds__(256) void k_fill_f64(double* __restrict__ p, int64_t n) {
   const int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x;
   if (t < n) p[t] = 0.0;
@@ -478,19 +442,9 @@ hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, in
   }
   k_make_c<<<dim3((unsigned)ceil_div(K * K, 256)), dim3(256), 0, s>>>(w.A, K, w.C);
   SVDQ_TRY_HIP(hipGetLastError());
-  // the residual, the NVFP4 tensor scale, and T = 0
-  float* amax = fmt == 0 ? tensor_scale : nullptr;
-  if (amax) {
-    k_set_zero_f32<<<dim3(1), dim3(64), 0, s>>>(amax);
-    SVDQ_TRY_HIP(hipGetLastError());
-  }
-  k_residual<<<dim3((unsigned)ceil_div(N * K, 256)), dim3(256), 0, s>>>(W, N, K, ldw, lambda,
-                                                                        down, up, r, w.R32, amax);
-  SVDQ_TRY_HIP(hipGetLastError());
-  if (amax) {
-    k_amax_g<<<dim3(1), dim3(64), 0, s>>>(amax);
-    SVDQ_TRY_HIP(hipGetLastError());
-  }
+  // the residual (the round-to-nearest path's own kernel), the NVFP4 tensor scale, and T = 0
+  SVDQ_TRY_HIP(launch_residual_f32(W, N, K, ldw, lambda, down, up, r, w.R32,
+                                   fmt == 0 ? tensor_scale : nullptr, s));
   k_fill_f64<<<dim3((unsigned)ceil_div(N * K, 256)), dim3(256), 0, s>>>(w.T, N * K);
   SVDQ_TRY_HIP(hipGetLastError());
   // the sweep

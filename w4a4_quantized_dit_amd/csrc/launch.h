@@ -36,6 +36,12 @@ hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t
                                   int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
                                   hipStream_t s);
 
+// R32 = fl32(λ·W − up·down) exactly as launch_quantize_weight forms it, into R32 [N, K]; with
+// tensor_scale, also the NVFP4 tensor scale max|R32| / 2688 (1 when the residual is zero).
+hipError_t launch_residual_f32(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                               const float* lambda, const uint16_t* down, const uint16_t* up,
+                               int64_t r, float* R32, float* tensor_scale, hipStream_t s);
+
 hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                             const float* lambda, const float* act_amax, const uint16_t* down,
                             int64_t r, uint8_t* codes, void* scales, float* tensor_scale,

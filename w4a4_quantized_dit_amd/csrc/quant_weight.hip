@@ -30,6 +30,7 @@ typedef __attribute__((ext_vector_type(2))) double f64x2_t;
 // MODE 1: NVFP4 codes and scales with g = amax / 2688
 // MODE 2: int4-g64 codes and fp16 scales
 // MODE 3 / 4: MX codes (E2M1 / E4M3) with E8M0 scales per 32 (single pass)
+// MODE 5: R32 itself (fp32 [N, K], through `codes`), and max|R32| when amax_io is given
 template <int MODE>
 __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__ W, int64_t N,
                                                     int64_t K, int64_t ldw,
@@ -150,22 +151,32 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
     }
   }
 
-  if (MODE == 0) {
+  if (MODE == 0 || MODE == 5) {
     float m = 0.0f;
 #pragma unroll
     for (int j = 0; j < 8; ++j) {
-      if (n0 + 8 * rg + j < N) {
+      const int64_t n = n0 + 8 * rg + j;
+      if (n < N) {
 #pragma unroll
         for (int e = 0; e < 8; ++e) m = fmaxf(m, fabsf((float)R[j][e]));
+        if (MODE == 5) {
+          float* dst = reinterpret_cast<float*>(codes) + n * K + kc;
+          reinterpret_cast<f32x4_t*>(dst)[0] =
+              f32x4_t{(float)R[j][0], (float)R[j][1], (float)R[j][2], (float)R[j][3]};
+          reinterpret_cast<f32x4_t*>(dst)[1] =
+              f32x4_t{(float)R[j][4], (float)R[j][5], (float)R[j][6], (float)R[j][7]};
+        }
       }
     }
-    for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if ((tid & 63) == 0) s_red[tid >> 6] = m;
-    __syncthreads();
-    if (tid == 0) {
-      float b = 0.0f;
-      for (int w = 0; w < kThreads / 64; ++w) b = fmaxf(b, s_red[w]);
-      if (b > 0.0f) atomic_max_pos(amax_io, b);
+    if (amax_io) {
+      for (int off = 32; off > 0; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+      if ((tid & 63) == 0) s_red[tid >> 6] = m;
+      __syncthreads();
+      if (tid == 0) {
+        float b = 0.0f;
+        for (int w = 0; w < kThreads / 64; ++w) b = fmaxf(b, s_red[w]);
+        if (b > 0.0f) atomic_max_pos(amax_io, b);
+      }
     }
   } else if (MODE == 1) {
     // an NVFP4 block of 16 channels is held by lanes cb = 2b, 2b + 1
@@ -274,6 +285,21 @@ hipError_t allow_lds(size_t bytes) {
 }
 
 }  // namespace
+
+hipError_t launch_residual_f32(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                               const float* lambda, const uint16_t* down, const uint16_t* up,
+                               int64_t r, float* R32, float* tensor_scale, hipStream_t s) {
+  const int64_t tiles = ((N + kTileRows - 1) / kTileRows) * (K / kTileCols);
+  const size_t lds = lds_bytes(r);
+  hipError_t e = allow_lds<5>(lds);
+  if (e != hipSuccess) return e;
+  if (tensor_scale) k_zero1<<<1, 1, 0, s>>>(tensor_scale);
+  k_resid<5><<<dim3((unsigned)tiles), dim3(kThreads), lds, s>>>(
+      W, N, K, ldw, lambda, down, up, (int)r, tensor_scale, reinterpret_cast<uint8_t*>(R32),
+      nullptr);
+  if (tensor_scale) k_amax_to_g<<<1, 1, 0, s>>>(tensor_scale);
+  return hipGetLastError();
+}
 
 hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
                                   const float* lambda, const uint16_t* down, const uint16_t* up,
