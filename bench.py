@@ -309,8 +309,9 @@ def main():
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=16384)
     ap.add_argument("--copy-probe", action="store_true")
-    ap.add_argument("--no-weight-side", action="store_true",
-                    help="skip the one-off λ search and GPTQ timings")
+    ap.add_argument("--weight-side", action="store_true",
+                    help="also time the one-off λ search and GPTQ (after the timed steps; their "
+                         "small GEMMs then share the kernel names of the step's)")
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer is "
@@ -408,7 +409,7 @@ def main():
     }
     if "core" in ms:
         out["core_gemm_tflops"] = round(st["core_flops"] / (ms["core"] * 1e-3) / 1e12, 2)
-    if not args.no_weight_side:
+    if args.weight_side:
         from w4a4_quantized_dit_amd import layer
         print("[bench] weight side: λ search and GPTQ", file=sys.stderr, flush=True)
         fmt = {"nvfp4": 0, "nvfp4-delta": 0, "int4": 1, "mxfp4": 2, "mxfp8": 3}[cfg["fmt"]]
