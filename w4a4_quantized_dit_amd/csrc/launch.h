@@ -88,6 +88,12 @@ hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, in
                                        uint8_t* codes, void* scales, float* tensor_scale,
                                        void* workspace, hipStream_t s);
 
+// Y_ref = bf16(X·Wᵀ) of the sampled rows (the scoring kernel's reference, fp32 accumulation)
+// into Yref [n_rows, N] (row stride ldr).
+hipError_t launch_reference_rows(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                                 int64_t M, int64_t N, int64_t K, const int32_t* rows,
+                                 int64_t n_rows, uint16_t* Yref, int64_t ldr, hipStream_t s);
+
 int64_t lambda_search_workspace_bytes(int fmt, int64_t N, int64_t K, int64_t ell, int64_t r,
                                       int64_t n_rows, int64_t n_alpha, int refit_iters);
 hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const uint16_t* W,

@@ -17,7 +17,9 @@ namespace {
 
 constexpr int kThreads = 256;
 
-__global__ __launch_bounds__(kThreads) void k_score(const uint16_t* __restrict__ Y, int64_t ldy,
+// WRITE: instead of the sums, Y_ref of sampled row i is stored at Y[i * ldy + n] (bf16).
+template <bool WRITE>
+__global__ __launch_bounds__(kThreads) void k_score(uint16_t* __restrict__ Y, int64_t ldy,
                                                     const uint16_t* __restrict__ X, int64_t ldx,
                                                     const uint16_t* __restrict__ W, int64_t ldw,
                                                     int64_t M, int64_t N, int64_t K,
@@ -74,6 +76,19 @@ __global__ __launch_bounds__(kThreads) void k_score(const uint16_t* __restrict__
   }
 
   // 32x32 accumulator layout: lane holds column r32 and rows (e/4)*8 + 4h + e%4
+  if (WRITE) {
+#pragma unroll
+    for (int i = 0; i < FM; ++i)
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int64_t idx = i_base + 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
+        if (idx < n_rows) {
+#pragma unroll
+          for (int j = 0; j < FN; ++j) Y[idx * ldy + n_base + 32 * j + r32] = f32_to_bf16(acc[i][j][e]);
+        }
+      }
+    return;
+  }
   double sd[4] = {0.0, 0.0, 0.0, 0.0}, sr[4] = {0.0, 0.0, 0.0, 0.0};
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
@@ -124,8 +139,17 @@ hipError_t launch_score(const uint16_t* Y, int64_t ldy, const uint16_t* X, int64
                         const int32_t* rows, const int8_t* grp, int64_t n_rows, double* sums,
                         hipStream_t s) {
   const dim3 grid((unsigned)(N / 128), (unsigned)((n_rows + 127) / 128));
-  k_score<<<grid, dim3(kThreads), 0, s>>>(Y, ldy, X, ldx, W, ldw, M, N, K, rows, grp, n_rows,
-                                           sums);
+  k_score<false><<<grid, dim3(kThreads), 0, s>>>(const_cast<uint16_t*>(Y), ldy, X, ldx, W, ldw, M,
+                                                  N, K, rows, grp, n_rows, sums);
+  return hipGetLastError();
+}
+
+hipError_t launch_reference_rows(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
+                                 int64_t M, int64_t N, int64_t K, const int32_t* rows,
+                                 int64_t n_rows, uint16_t* Yref, int64_t ldr, hipStream_t s) {
+  const dim3 grid((unsigned)(N / 128), (unsigned)((n_rows + 127) / 128));
+  k_score<true><<<grid, dim3(kThreads), 0, s>>>(Yref, ldr, X, ldx, W, ldw, M, N, K, rows,
+                                                 nullptr, n_rows, nullptr);
   return hipGetLastError();
 }
 

@@ -54,6 +54,28 @@ __global__ void k_zero_sums(double* __restrict__ sums) {
   if (threadIdx.x < 8) sums[threadIdx.x] = 0.0;
 }
 
+// sums[6] += Σ (Y − Y_ref)², sums[7] += Σ Y_ref² over n elements of bf16 Y and Y_ref (fp64,
+// one atomic pair per wave)
+__global__ __launch_bounds__(256) void k_diff_sums(const uint16_t* __restrict__ Y,
+                                                   const uint16_t* __restrict__ Yr, int64_t n,
+                                                   double* __restrict__ sums) {
+  double d2 = 0.0, r2 = 0.0;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n; t += (int64_t)gridDim.x * 256) {
+    const double y = (double)bf16_to_f32(Y[t]), r = (double)bf16_to_f32(Yr[t]);
+    const double d = y - r;
+    d2 += d * d;
+    r2 += r * r;
+  }
+  for (int off = 32; off > 0; off >>= 1) {
+    d2 += __shfl_xor(d2, off);
+    r2 += __shfl_xor(r2, off);
+  }
+  if ((threadIdx.x & 63) == 0) {
+    if (d2 != 0.0) atomicAdd(sums + 6, d2);
+    if (r2 != 0.0) atomicAdd(sums + 7, r2);
+  }
+}
+
 __global__ void k_set_inf(double* __restrict__ v) {
   if (threadIdx.x == 0) *v = __builtin_huge_val();
 }
@@ -165,7 +187,7 @@ int64_t scale_bytes(int fmt, int64_t rows, int64_t K) {
 struct SearchWs {
   float *lam_all, *amax, *g_w, *g_a, *D, *E;
   double *cur, *best;
-  uint16_t *down, *up, *xs, *ys;
+  uint16_t *down, *up, *xs, *ys, *yref;
   uint8_t *w_codes, *w_scales, *a_codes, *a_scales;
   int32_t* ids;
   int8_t* grp;
@@ -194,6 +216,7 @@ SearchWs carve(void* base, int fmt, int64_t N, int64_t K, int64_t ell, int64_t r
   w.up = static_cast<uint16_t*>(take(N * (r > 0 ? r : 1) * 2));
   w.xs = static_cast<uint16_t*>(take(S * K * 2));
   w.ys = static_cast<uint16_t*>(take(S * N * 2));
+  w.yref = static_cast<uint16_t*>(take(S * N * 2));
   w.w_codes = static_cast<uint8_t*>(take(code_bytes(fmt, N, K)));
   w.w_scales = static_cast<uint8_t*>(take(scale_bytes(fmt, N, K)));
   w.a_codes = static_cast<uint8_t*>(take(code_bytes(fmt, S, K)));
@@ -235,6 +258,9 @@ hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const
   SVDQ_TRY_HIP(hipGetLastError());
   k_rows_setup<<<dim3((unsigned)ceil_div(n_rows, 256)), dim3(256), 0, s>>>(n_rows, w.ids, w.grp);
   SVDQ_TRY_HIP(hipGetLastError());
+  // the reference rows do not depend on the candidate: once
+  SVDQ_TRY_HIP(launch_reference_rows(w.xs, K, W, ldw, n_rows, N, K, w.ids, n_rows, w.yref, N, s));
+  const unsigned diff_blocks = (unsigned)(ceil_div(n_rows * N, 256) < 1024 ? ceil_div(n_rows * N, 256) : 1024);
   const bool keep = r > 0 && best_down != nullptr;
   if (keep) {
     k_set_inf<<<dim3(1), dim3(64), 0, s>>>(w.best);
@@ -263,8 +289,8 @@ hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const
                                nullptr, nullptr, w.ys, N, s));
       k_zero_sums<<<dim3(1), dim3(64), 0, s>>>(w.sums);
       SVDQ_TRY_HIP(hipGetLastError());
-      SVDQ_TRY_HIP(launch_score(w.ys, N, w.xs, K, W, ldw, n_rows, N, K, w.ids, w.grp, n_rows,
-                                w.sums, s));
+      k_diff_sums<<<dim3(diff_blocks), dim3(256), 0, s>>>(w.ys, w.yref, n_rows * N, w.sums);
+      SVDQ_TRY_HIP(hipGetLastError());
       k_finish_iter<<<dim3(1), dim3(64), 0, s>>>(
           w.sums, t, scores + i,
           iter_scores ? iter_scores + i * (refit_iters + 1) + t : nullptr, w.cur);
