@@ -20,9 +20,9 @@
 //   damping H + 0.01 · mean(diag H) · I, copied index-reversed;  blocked lower Cholesky
 //   (64-column panels: a one-workgroup diagonal factor, a forward-substituted panel, a rank-64
 //   update of the trailing lower triangle);  C;  R32 (as the round-to-nearest path) and, for
-//   NVFP4, its tensor scale;  then per block of 64 columns: one thread per weight row
-//   quantises the block's columns in order, keeps w̃ of the block in LDS and updates it
-//   in-block, and writes the block's w − q;  a rank-64 product adds those to the running sums
+//   NVFP4, its tensor scale;  then per block of 64 columns: 16 lanes per weight row quantise
+//   the block's columns in order, keep w̃ of the block in registers and update it in-block,
+//   and write the block's w − q;  a rank-64 product adds those to the running sums
 //   T of all later columns.  A group's scale is fixed at its first column from the values the
 //   published sweep holds there; those differ from the partial sums above for every column but
 //   the first, and are recovered by a forward substitution inside the group (see the block
@@ -289,88 +289,101 @@ struct GroupQuant {
   }
 };
 
-// One block of 64 columns of the sweep; one thread per weight row.  The row's working values
-// w̃ of the block and its element codes live in LDS (lane-contiguous), the in-block
-// coefficients C[b0 + c][b0 + m] are shared by the workgroup.
+// One block of 64 columns of the sweep: 16 lanes per weight row, lane s of a row holding the
+// columns 4s .. 4s + 3 of the block in registers (the residual w and the running value w̃).
+// Column m is quantised by its owner lane and its w − q broadcast to the row's lanes, which fold
+// it into their later columns with the in-block coefficients C[b0 + m][b0 + c] (shared by the
+// workgroup in LDS).  At a group's first column the group's values as the published sweep holds
+// them are recovered by the forward substitution z_j = y_j − Σ_{m<=l<j} C_lj·z_l (y = w̃ − w),
+// one broadcast per column, and the group maximum by shuffles across the row's lanes.
 template <int FMT>
-__global__ __launch_bounds__(64) void k_gptq_block(const float* __restrict__ R32,
-                                                   const double* __restrict__ T,
-                                                   const double* __restrict__ C, int64_t N,
-                                                   int64_t K, int64_t b0,
-                                                   const float* __restrict__ tensor_g,
-                                                   uint8_t* __restrict__ codes,
-                                                   void* __restrict__ scales,
-                                                   double* __restrict__ D) {
+__global__ __launch_bounds__(256) void k_gptq_block(const float* __restrict__ R32,
+                                                    const double* __restrict__ T,
+                                                    const double* __restrict__ C, int64_t N,
+                                                    int64_t K, int64_t b0,
+                                                    const float* __restrict__ tensor_g,
+                                                    uint8_t* __restrict__ codes,
+                                                    void* __restrict__ scales,
+                                                    double* __restrict__ D) {
   constexpr int G = FMT == 0 ? 16 : (FMT == 1 ? 64 : 32);
+  constexpr int GL = G / 4;   // lanes of a group
   __shared__ double cb[kB][kB + 1];
-  __shared__ double vs[kB][64];
-  __shared__ double zs[G][64];
-  __shared__ uint8_t cs[kB][64];
   const int tid = threadIdx.x;
-  for (int t = tid; t < kB * kB; t += 64) cb[t / kB][t % kB] = C[(b0 + t / kB) * K + b0 + t % kB];
-  const int64_t n = (int64_t)blockIdx.x * 64 + tid;
+  for (int t = tid; t < kB * kB; t += 256) cb[t / kB][t % kB] = C[(b0 + t / kB) * K + b0 + t % kB];
+  __syncthreads();
+  const int lane = tid & 63;
+  const int sub = lane & 15, rbase = lane & 48;
+  const int64_t n = (int64_t)blockIdx.x * 16 + (tid >> 4);
   const bool live = n < N;
   const int64_t row = live ? n : N - 1;
-  for (int m = 0; m < kB; ++m) vs[m][tid] = (double)R32[row * K + b0 + m] + T[row * K + b0 + m];
-  __syncthreads();
+  const int64_t off = row * K + b0 + 4 * sub;
+  double w[4], v[4];
+#pragma unroll
+  for (int e = 0; e < 4; ++e) {
+    w[e] = (double)R32[off + e];
+    v[e] = w[e] + T[off + e];
+  }
   const float g = FMT == 0 ? *tensor_g : 1.0f;
   GroupQuant<FMT> gq;
-  for (int m = 0; m < kB; ++m) {
-    if (m % G == 0) {
-      // The group's current values as the published sweep has them at this column: the sums
-      // in vs are complete only for column m; for the later columns of the group the
-      // compensation of the columns already quantised is z = Ũ_FF⁻ᵀ·s (F the columns from m
-      // on), and with y = vs − w = diag(1/Ũ)·s the first G entries of z follow by forward
-      // substitution, z_j = y_j − Σ_{m<=l<j} C_lj·z_l.
-      float a = 0.0f;
-      for (int j = 0; j < G; ++j) {
-        const double wj = (double)R32[row * K + b0 + m + j];
-        double z = vs[m + j][tid] - wj;
-        for (int l = 0; l < j; ++l) z = __builtin_fma(-zs[l][tid], cb[m + l][m + j], z);
-        zs[j][tid] = z;
-        a = fmaxf(a, fabsf((float)(wj + z)));
+  uint32_t packed = 0u;
+  for (int q = 0; q < kB / 4; ++q) {
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int m = 4 * q + e;
+      if (e == 0 && q % GL == 0) {
+        // group entry at column m: z over the group's columns (lanes q .. q + GL - 1)
+        double y[4];
+#pragma unroll
+        for (int k = 0; k < 4; ++k) y[k] = v[k] - w[k];
+        for (int jq = 0; jq < GL; ++jq) {
+#pragma unroll
+          for (int ej = 0; ej < 4; ++ej) {
+            const int j = m + 4 * jq + ej;   // block column, final in its owner after this
+            const double zj = __shfl(y[ej], rbase + q + jq);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) {
+              const int c = 4 * sub + k;
+              if (c > j && c < m + G) y[k] = __builtin_fma(-cb[j][c], zj, y[k]);
+            }
+          }
+        }
+        float a = 0.0f;
+        if (sub >= q && sub < q + GL) {
+#pragma unroll
+          for (int k = 0; k < 4; ++k) a = fmaxf(a, fabsf((float)(w[k] + y[k])));
+        }
+#pragma unroll
+        for (int o = 1; o < 16; o <<= 1) a = fmaxf(a, __shfl_xor(a, o));
+        gq.set(a, g);
+        if (live && sub == q) {
+          const int64_t gi = (b0 + m) / G;
+          if (FMT == 1)
+            reinterpret_cast<uint16_t*>(scales)[n * (K / G) + gi] = (uint16_t)gq.stored;
+          else
+            reinterpret_cast<uint8_t*>(scales)[n * (K / G) + gi] = (uint8_t)gq.stored;
+        }
       }
-      gq.set(a, g);
-      if (live) {
-        const int64_t gi = (b0 + m) / G;
-        if (FMT == 1)
-          reinterpret_cast<uint16_t*>(scales)[n * (K / G) + gi] = (uint16_t)gq.stored;
-        else
-          reinterpret_cast<uint8_t*>(scales)[n * (K / G) + gi] = (uint8_t)gq.stored;
+      // column m: its owner's code; w − q to every lane of the row
+      double qv;
+      const uint32_t c = gq.code((float)v[e], &qv);
+      const double d_own = w[e] - qv;
+      if (sub == q) {
+        packed |= FMT == 3 ? c << (8 * e) : c << (4 * e);
+        if (live) D[n * kB + m] = d_own;
+      }
+      const double d = __shfl(d_own, rbase + q);
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const int col = 4 * sub + k;
+        if (col > m) v[k] = __builtin_fma(d, cb[m][col], v[k]);
       }
     }
-    double q;
-    cs[m][tid] = (uint8_t)gq.code((float)vs[m][tid], &q);
-    const double d = (double)R32[row * K + b0 + m] - q;
-    if (live) D[n * kB + m] = d;
-    for (int m2 = m + 1; m2 < kB; ++m2) vs[m2][tid] = __builtin_fma(d, cb[m][m2], vs[m2][tid]);
   }
   if (!live) return;
-  if (FMT == 3) {
-#pragma unroll
-    for (int w = 0; w < 4; ++w) {
-      u32x4_t o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p)
-        o[p] = (uint32_t)cs[16 * w + 4 * p][tid] | ((uint32_t)cs[16 * w + 4 * p + 1][tid] << 8) |
-               ((uint32_t)cs[16 * w + 4 * p + 2][tid] << 16) |
-               ((uint32_t)cs[16 * w + 4 * p + 3][tid] << 24);
-      reinterpret_cast<u32x4_t*>(codes + n * K + b0)[w] = o;
-    }
-  } else {
-#pragma unroll
-    for (int w = 0; w < 2; ++w) {
-      u32x4_t o;
-#pragma unroll
-      for (int p = 0; p < 4; ++p) {
-        uint32_t word = 0u;
-#pragma unroll
-        for (int e = 0; e < 8; ++e) word |= (uint32_t)cs[32 * w + 8 * p + e][tid] << (4 * e);
-        o[p] = word;
-      }
-      reinterpret_cast<u32x4_t*>(codes + n * (K / 2) + b0 / 2)[w] = o;
-    }
-  }
+  if (FMT == 3)
+    *reinterpret_cast<uint32_t*>(codes + n * K + b0 + 4 * sub) = packed;
+  else
+    *reinterpret_cast<uint16_t*>(codes + n * (K / 2) + (b0 + 4 * sub) / 2) = (uint16_t)packed;
 }
 
 struct GptqWs {
@@ -448,19 +461,19 @@ hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, in
   k_fill_f64<<<dim3((unsigned)ceil_div(N * K, 256)), dim3(256), 0, s>>>(w.T, N * K);
   SVDQ_TRY_HIP(hipGetLastError());
   // the sweep
-  const dim3 rows_grid((unsigned)ceil_div(N, 64));
+  const dim3 rows_grid((unsigned)ceil_div(N, 16));
   for (int64_t b0 = 0; b0 < K; b0 += kB) {
     if (fmt == 0)
-      k_gptq_block<0><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, tensor_scale,
+      k_gptq_block<0><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, tensor_scale,
                                                      codes, scales, w.D);
     else if (fmt == 1)
-      k_gptq_block<1><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
+      k_gptq_block<1><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
                                                      scales, w.D);
     else if (fmt == 2)
-      k_gptq_block<2><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
+      k_gptq_block<2><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
                                                      scales, w.D);
     else
-      k_gptq_block<3><<<rows_grid, dim3(64), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
+      k_gptq_block<3><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
                                                      scales, w.D);
     SVDQ_TRY_HIP(hipGetLastError());
     const int64_t rest = K - b0 - kB;
