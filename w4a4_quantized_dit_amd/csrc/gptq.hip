@@ -35,6 +35,7 @@ namespace svdq {
 namespace {
 
 constexpr int kB = 64;           // panel / sweep block width
+typedef __attribute__((ext_vector_type(2))) double f64x2_t;
 constexpr double kPercDamp = 0.01;
 
 int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
@@ -131,29 +132,40 @@ __global__ __launch_bounds__(256) void k_reverse_damped(const double* __restrict
   A[t] = v;
 }
 
-// Unblocked Cholesky of the 64 x 64 diagonal block at (j0, j0), in LDS; the upper part is zeroed.
-__global__ __launch_bounds__(256) void k_chol_diag(double* __restrict__ A, int64_t K, int64_t j0) {
-  __shared__ double a[kB][kB + 1];
-  const int tid = threadIdx.x;
-  for (int t = tid; t < kB * kB; t += 256) a[t / kB][t % kB] = A[(j0 + t / kB) * K + j0 + t % kB];
-  __syncthreads();
+// Lane l's value of x, as a wave-uniform value (l a compile-time constant after unrolling).
+__device__ __forceinline__ double lane_value(double x, int l) {
+  const int2 v = __builtin_bit_cast(int2, x);
+  return __builtin_bit_cast(double, int2{__builtin_amdgcn_readlane(v.x, l),
+                                         __builtin_amdgcn_readlane(v.y, l)});
+}
+
+// Unblocked Cholesky of the 64 x 64 diagonal block at (j0, j0) in one wave: lane i holds row i
+// in registers; each step takes the pivot and the scaled column from their lanes as uniform
+// values, so a step costs no barrier.  The upper part is written as zeros.
+__global__ __launch_bounds__(64) void k_chol_diag(double* __restrict__ A, int64_t K, int64_t j0) {
+  const int i = threadIdx.x;
+  double* rowp = A + (j0 + i) * K + j0;
+  double a[kB];
+#pragma unroll
+  for (int j = 0; j < kB; j += 2) {
+    const f64x2_t v = *reinterpret_cast<const f64x2_t*>(rowp + j);
+    a[j] = v[0];
+    a[j + 1] = v[1];
+  }
+#pragma unroll
   for (int c = 0; c < kB; ++c) {
-    if (tid == 0) a[c][c] = __builtin_sqrt(a[c][c]);
-    __syncthreads();
-    const double d = a[c][c];
-    for (int i = c + 1 + tid; i < kB; i += 256) a[i][c] /= d;
-    __syncthreads();
-    const int n = kB - 1 - c;   // trailing lower triangle of size n
-    for (int t = tid; t < n * n; t += 256) {
-      const int i = c + 1 + t / n, j = c + 1 + t % n;
-      if (j <= i) a[i][j] -= a[i][c] * a[j][c];
+    const double d = __builtin_sqrt(lane_value(a[c], c));
+    if (i == c) a[c] = d;
+    if (i > c) a[c] = a[c] / d;
+#pragma unroll
+    for (int j = c + 1; j < kB; ++j) {
+      const double ajc = lane_value(a[c], j);
+      if (i >= j) a[j] = a[j] - a[c] * ajc;
     }
-    __syncthreads();
   }
-  for (int t = tid; t < kB * kB; t += 256) {
-    const int i = t / kB, j = t % kB;
-    A[(j0 + i) * K + j0 + j] = j <= i ? a[i][j] : 0.0;
-  }
+#pragma unroll
+  for (int j = 0; j < kB; j += 2)
+    *reinterpret_cast<f64x2_t*>(rowp + j) = f64x2_t{j <= i ? a[j] : 0.0, j + 1 <= i ? a[j + 1] : 0.0};
 }
 
 // Panel rows i >= j0 + 64: L[i, j0 .. j0+64) by forward substitution against the factored
@@ -440,7 +452,7 @@ hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, in
   k_reverse_damped<<<dim3((unsigned)ceil_div(K * K, 256)), dim3(256), 0, s>>>(H, K, w.damp, w.A);
   SVDQ_TRY_HIP(hipGetLastError());
   for (int64_t j0 = 0; j0 < K; j0 += kB) {
-    k_chol_diag<<<dim3(1), dim3(256), 0, s>>>(w.A, K, j0);
+    k_chol_diag<<<dim3(1), dim3(64), 0, s>>>(w.A, K, j0);
     SVDQ_TRY_HIP(hipGetLastError());
     const int64_t rest = K - j0 - kB;
     if (rest > 0) {
