@@ -55,12 +55,26 @@ __global__ void k_zero_sums(double* __restrict__ sums) {
 }
 
 // sums[6] += Σ (Y − Y_ref)², sums[7] += Σ Y_ref² over n elements of bf16 Y and Y_ref (fp64,
-// one atomic pair per wave)
+// 8 elements per 16-byte load, one atomic pair per workgroup: atomics on one address serialise)
 __global__ __launch_bounds__(256) void k_diff_sums(const uint16_t* __restrict__ Y,
                                                    const uint16_t* __restrict__ Yr, int64_t n,
                                                    double* __restrict__ sums) {
+  __shared__ double red[2][4];
   double d2 = 0.0, r2 = 0.0;
-  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n; t += (int64_t)gridDim.x * 256) {
+  const int64_t n8 = n / 8;
+  for (int64_t t = (int64_t)blockIdx.x * 256 + threadIdx.x; t < n8; t += (int64_t)gridDim.x * 256) {
+    const u32x4_t a = reinterpret_cast<const u32x4_t*>(Y)[t];
+    const u32x4_t b = reinterpret_cast<const u32x4_t*>(Yr)[t];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const double r0 = (double)bf16_lo(b[e]), r1 = (double)bf16_hi(b[e]);
+      const double e0 = (double)bf16_lo(a[e]) - r0, e1 = (double)bf16_hi(a[e]) - r1;
+      d2 += e0 * e0 + e1 * e1;
+      r2 += r0 * r0 + r1 * r1;
+    }
+  }
+  for (int64_t t = n8 * 8 + (int64_t)blockIdx.x * 256 + threadIdx.x; t < n;
+       t += (int64_t)gridDim.x * 256) {
     const double y = (double)bf16_to_f32(Y[t]), r = (double)bf16_to_f32(Yr[t]);
     const double d = y - r;
     d2 += d * d;
@@ -71,8 +85,15 @@ __global__ __launch_bounds__(256) void k_diff_sums(const uint16_t* __restrict__ 
     r2 += __shfl_xor(r2, off);
   }
   if ((threadIdx.x & 63) == 0) {
-    if (d2 != 0.0) atomicAdd(sums + 6, d2);
-    if (r2 != 0.0) atomicAdd(sums + 7, r2);
+    red[0][threadIdx.x >> 6] = d2;
+    red[1][threadIdx.x >> 6] = r2;
+  }
+  __syncthreads();
+  if (threadIdx.x == 0) {
+    const double d = (red[0][0] + red[0][1]) + (red[0][2] + red[0][3]);
+    const double r = (red[1][0] + red[1][1]) + (red[1][2] + red[1][3]);
+    if (d != 0.0) atomicAdd(sums + 6, d);
+    if (r != 0.0) atomicAdd(sums + 7, r);
   }
 }
 
@@ -260,7 +281,8 @@ hipError_t launch_lambda_search(const uint16_t* X, int64_t M, int64_t ldx, const
   SVDQ_TRY_HIP(hipGetLastError());
   // the reference rows do not depend on the candidate: once
   SVDQ_TRY_HIP(launch_reference_rows(w.xs, K, W, ldw, n_rows, N, K, w.ids, n_rows, w.yref, N, s));
-  const unsigned diff_blocks = (unsigned)(ceil_div(n_rows * N, 256) < 1024 ? ceil_div(n_rows * N, 256) : 1024);
+  const unsigned diff_blocks =
+      (unsigned)(ceil_div(n_rows * N, 2048) < 256 ? ceil_div(n_rows * N, 2048) : 256);
   const bool keep = r > 0 && best_down != nullptr;
   if (keep) {
     k_set_inf<<<dim3(1), dim3(64), 0, s>>>(w.best);
