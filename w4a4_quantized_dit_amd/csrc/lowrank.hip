@@ -27,6 +27,7 @@ constexpr int kGramRows = 64;      // rows per partial Gram matrix
 constexpr int kJacobiThreads = 1024;
 constexpr int kMaxSweeps = 40;
 constexpr int kLdsEll = 80;        // the small factorisations run in LDS up to this ell
+constexpr int kCholThreads = 512;  // threads of the small Cholesky-inverse workgroup
 
 // The matrix is either the bf16 weight (scaled by λ per channel) or an fp32 matrix (the refit
 // target of the layer's low-rank branch).
@@ -260,7 +261,7 @@ __global__ __launch_bounds__(256) void k_gram_reduce(const double* __restrict__ 
 // end up at the bottom of the spectrum.  Both factorisations are right-looking: every step is a
 // pivot, a scaled row and a rank-1 update of the trailing part, each spread over the workgroup,
 // so a step costs a few barriers instead of a serial dot product.
-__global__ __launch_bounds__(256) void k_chol_inv(const double* __restrict__ G, int ell,
+__global__ __launch_bounds__(kCholThreads) void k_chol_inv(const double* __restrict__ G, int ell,
                                                   double* __restrict__ Rg,
                                                   double* __restrict__ Rinvg) {
   __shared__ double s_tiny;
@@ -276,7 +277,7 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* __restrict__ G, 
     s_tiny = (tr > 1e-300 ? tr : 1e-300) * 1e-28;
   }
   // R starts as the upper triangle of G, X as the identity
-  for (int t = tid; t < ell * ell; t += 256) {
+  for (int t = tid; t < ell * ell; t += kCholThreads) {
     const int i = t / ell, j = t % ell;
     R[t] = j >= i ? G[t] : 0.0;
     X[t] = i == j ? 1.0 : 0.0;
@@ -289,10 +290,10 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* __restrict__ G, 
     }
     __syncthreads();
     const double rjj = R[j * ell + j];
-    for (int i = j + 1 + tid; i < ell; i += 256) R[j * ell + i] /= rjj;
+    for (int i = j + 1 + tid; i < ell; i += kCholThreads) R[j * ell + i] /= rjj;
     __syncthreads();
     const int n = ell - 1 - j;   // trailing upper triangle: rows/columns j+1 .. ell-1
-    for (int t = tid; t < n * n; t += 256) {
+    for (int t = tid; t < n * n; t += kCholThreads) {
       const int k = j + 1 + t / n, i = j + 1 + t % n;
       if (i >= k) R[k * ell + i] -= R[j * ell + k] * R[j * ell + i];
     }
@@ -302,16 +303,16 @@ __global__ __launch_bounds__(256) void k_chol_inv(const double* __restrict__ G, 
   // above it in proportion to column k of R
   for (int k = ell - 1; k >= 0; --k) {
     const double rkk = R[k * ell + k];
-    for (int c = k + tid; c < ell; c += 256) X[k * ell + c] /= rkk;
+    for (int c = k + tid; c < ell; c += kCholThreads) X[k * ell + c] /= rkk;
     __syncthreads();
-    for (int t = tid; t < k * (ell - k); t += 256) {
+    for (int t = tid; t < k * (ell - k); t += kCholThreads) {
       const int i = t / (ell - k), c = k + t % (ell - k);
       X[i * ell + c] -= R[i * ell + k] * X[k * ell + c];
     }
     __syncthreads();
   }
   if (in_lds) {
-    for (int t = tid; t < ell * ell; t += 256) {
+    for (int t = tid; t < ell * ell; t += kCholThreads) {
       Rg[t] = s_r[t];
       Rinvg[t] = s_ri[t];
     }
@@ -585,7 +586,7 @@ hipError_t lowrank_impl(const T* W, int64_t N, int64_t K, int64_t ldw, const flo
   auto orth = [&](float*& M, float*& tmp, int64_t rows) -> hipError_t {
     for (int pass = 0; pass < 2; ++pass) {
       if ((err = gram(M, rows, w.g)) != hipSuccess) return err;
-      k_chol_inv<<<dim3(1), dim3(256), 0, s>>>(w.g, e, w.r, w.rinv);
+      k_chol_inv<<<dim3(1), dim3(kCholThreads), 0, s>>>(w.g, e, w.r, w.rinv);
       SVDQ_CHECK_LAUNCH();
       k_apply_rinv<<<dim3((unsigned)ceil_div(rows * ell, 256)), dim3(256), 0, s>>>(M, rows, e,
                                                                                   w.rinv, tmp);
