@@ -37,6 +37,7 @@ namespace {
 constexpr int kB = 64;           // panel / sweep block width
 typedef __attribute__((ext_vector_type(2))) double f64x2_t;
 constexpr double kPercDamp = 0.01;
+constexpr int kSuper = 4 * kB;   // columns whose w − q are carried to the later columns at once
 
 int64_t align256(int64_t b) { return (b + 255) & ~(int64_t)255; }
 int64_t ceil_div(int64_t a, int64_t b) { return (a + b - 1) / b; }
@@ -192,7 +193,7 @@ __global__ __launch_bounds__(64) void k_chol_panel(double* __restrict__ A, int64
   for (int c = 0; c < kB; ++c) row[c] = x[c];
 }
 
-// Out[i][j] += sign · Σ_{c<64} A[i][c] · B(c, j) on 64 x 64 output tiles, B(c, j) = B[c][j]
+// Out[i][j] += sign · Σ_{c < 64 nchunk} A[i][c] · B(c, j) on 64 x 64 output tiles, B(c, j) = B[c][j]
 // (row-major, ldb) or, TRANSB, Bt[j][c].  LOWER: tiles above the diagonal (tile row < tile
 // column) are skipped.  Thread (ty, tx) = 4 x 4 outputs; both operands staged in LDS with the
 // output index contiguous.
@@ -200,36 +201,41 @@ template <bool TRANSB, bool LOWER>
 __global__ __launch_bounds__(256) void k_rank64(const double* __restrict__ A, int64_t lda,
                                                 const double* __restrict__ B, int64_t ldb,
                                                 double* __restrict__ Out, int64_t ldo,
-                                                double sign) {
+                                                double sign, int nchunk) {
   if (LOWER && blockIdx.y < blockIdx.x) return;
   __shared__ double as[kB][kB + 2];   // as[c][i]
   __shared__ double bs[kB][kB + 2];   // bs[c][j]
   const int tid = threadIdx.x, ty = tid >> 4, tx = tid & 15;
   const int64_t i0 = (int64_t)blockIdx.y * kB, j0 = (int64_t)blockIdx.x * kB;
-  for (int t = tid; t < kB * kB; t += 256) {
-    const int r = t / kB, c = t % kB;
-    as[c][r] = A[(i0 + r) * lda + c];
-    if (TRANSB) bs[c][r] = B[(j0 + r) * ldb + c];
-    else bs[r][c] = B[(int64_t)r * ldb + j0 + c];
-  }
-  __syncthreads();
   double acc[4][4];
 #pragma unroll
   for (int p = 0; p < 4; ++p)
 #pragma unroll
     for (int q = 0; q < 4; ++q) acc[p][q] = 0.0;
-#pragma unroll 4
-  for (int c = 0; c < kB; ++c) {
-    double a[4], b[4];
-#pragma unroll
-    for (int p = 0; p < 4; ++p) {
-      a[p] = as[c][ty * 4 + p];
-      b[p] = bs[c][tx * 4 + p];
+  // the inner dimension is nchunk x 64, staged 64 at a time
+  for (int ch = 0; ch < nchunk; ++ch) {
+    const int64_t c0 = (int64_t)ch * kB;
+    __syncthreads();
+    for (int t = tid; t < kB * kB; t += 256) {
+      const int r = t / kB, c = t % kB;
+      as[c][r] = A[(i0 + r) * lda + c0 + c];
+      if (TRANSB) bs[c][r] = B[(j0 + r) * ldb + c0 + c];
+      else bs[r][c] = B[(c0 + r) * ldb + j0 + c];
     }
+    __syncthreads();
+#pragma unroll 4
+    for (int c = 0; c < kB; ++c) {
+      double a[4], b[4];
 #pragma unroll
-    for (int p = 0; p < 4; ++p)
+      for (int p = 0; p < 4; ++p) {
+        a[p] = as[c][ty * 4 + p];
+        b[p] = bs[c][tx * 4 + p];
+      }
 #pragma unroll
-      for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fma(a[p], b[q], acc[p][q]);
+      for (int p = 0; p < 4; ++p)
+#pragma unroll
+        for (int q = 0; q < 4; ++q) acc[p][q] = __builtin_fma(a[p], b[q], acc[p][q]);
+    }
   }
 #pragma unroll
   for (int p = 0; p < 4; ++p)
@@ -316,7 +322,7 @@ __global__ __launch_bounds__(256) void k_gptq_block(const float* __restrict__ R3
                                                     const float* __restrict__ tensor_g,
                                                     uint8_t* __restrict__ codes,
                                                     void* __restrict__ scales,
-                                                    double* __restrict__ D) {
+                                                    double* __restrict__ D, int64_t ldd) {
   constexpr int G = FMT == 0 ? 16 : (FMT == 1 ? 64 : 32);
   constexpr int GL = G / 4;   // lanes of a group
   __shared__ double cb[kB][kB + 1];
@@ -381,7 +387,7 @@ __global__ __launch_bounds__(256) void k_gptq_block(const float* __restrict__ R3
       const double d_own = w[e] - qv;
       if (sub == q) {
         packed |= FMT == 3 ? c << (8 * e) : c << (4 * e);
-        if (live) D[n * kB + m] = d_own;
+        if (live) D[n * ldd + m] = d_own;
       }
       const double d = __shfl(d_own, rbase + q);
 #pragma unroll
@@ -416,7 +422,7 @@ GptqWs carve(void* base, int64_t N, int64_t K) {
   w.A = static_cast<double*>(take(K * K * 8));
   w.C = static_cast<double*>(take(K * K * 8));
   w.T = static_cast<double*>(take(N * K * 8));
-  w.D = static_cast<double*>(take(N * kB * 8));
+  w.D = static_cast<double*>(take(N * kSuper * 8));
   w.R32 = static_cast<float*>(take(N * K * 4));
   w.damp = static_cast<double*>(take(8));
   w.bytes = off;
@@ -461,7 +467,7 @@ hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, in
       const unsigned tiles = (unsigned)(rest / kB);
       const int64_t p = (j0 + kB) * K + j0;   // the panel rows below the diagonal block
       k_rank64<true, true><<<dim3(tiles, tiles), dim3(256), 0, s>>>(
-          w.A + p, K, w.A + p, K, w.A + (j0 + kB) * K + j0 + kB, K, -1.0);
+          w.A + p, K, w.A + p, K, w.A + (j0 + kB) * K + j0 + kB, K, -1.0, 1);
       SVDQ_TRY_HIP(hipGetLastError());
     }
   }
@@ -472,26 +478,36 @@ hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, in
                                    fmt == 0 ? tensor_scale : nullptr, s));
   k_fill_f64<<<dim3((unsigned)ceil_div(N * K, 256)), dim3(256), 0, s>>>(w.T, N * K);
   SVDQ_TRY_HIP(hipGetLastError());
-  // the sweep
+  // the sweep.  Blocks are grouped in super-blocks of 256 columns: after a block, its w − q is
+  // carried only into the rest of its super-block; at the end of a super-block the w − q of all
+  // its columns is carried into every later column in one rank-256 update (the running sums T
+  // are rewritten once per super-block instead of once per block).
   const dim3 rows_grid((unsigned)ceil_div(N, 16));
   for (int64_t b0 = 0; b0 < K; b0 += kB) {
+    const int64_t sb0 = b0 - b0 % kSuper, sb1 = sb0 + kSuper < K ? sb0 + kSuper : K;
+    double* Db = w.D + (b0 - sb0);
     if (fmt == 0)
       k_gptq_block<0><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, tensor_scale,
-                                                     codes, scales, w.D);
+                                                      codes, scales, Db, kSuper);
     else if (fmt == 1)
       k_gptq_block<1><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
-                                                     scales, w.D);
+                                                      scales, Db, kSuper);
     else if (fmt == 2)
       k_gptq_block<2><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
-                                                     scales, w.D);
+                                                      scales, Db, kSuper);
     else
       k_gptq_block<3><<<rows_grid, dim3(256), 0, s>>>(w.R32, w.T, w.C, N, K, b0, nullptr, codes,
-                                                     scales, w.D);
+                                                      scales, Db, kSuper);
     SVDQ_TRY_HIP(hipGetLastError());
-    const int64_t rest = K - b0 - kB;
-    if (rest > 0) {
-      k_rank64<false, false><<<dim3((unsigned)(rest / kB), (unsigned)(N / kB)), dim3(256), 0, s>>>(
-          w.D, kB, w.C + b0 * K + b0 + kB, K, w.T + b0 + kB, K, 1.0);
+    const int64_t in_sb = sb1 - (b0 + kB);   // later columns of this super-block
+    if (in_sb > 0) {
+      k_rank64<false, false><<<dim3((unsigned)(in_sb / kB), (unsigned)(N / kB)), dim3(256), 0, s>>>(
+          Db, kSuper, w.C + b0 * K + b0 + kB, K, w.T + b0 + kB, K, 1.0, 1);
+      SVDQ_TRY_HIP(hipGetLastError());
+    } else if (K - sb1 > 0) {
+      k_rank64<false, false><<<dim3((unsigned)((K - sb1) / kB), (unsigned)(N / kB)), dim3(256), 0,
+                               s>>>(w.D, kSuper, w.C + sb0 * K + sb1, K, w.T + sb1, K, 1.0,
+                                    (int)((sb1 - sb0) / kB));
       SVDQ_TRY_HIP(hipGetLastError());
     }
   }
