@@ -248,11 +248,14 @@ __global__ __launch_bounds__(256) void k_gram_partial(const float* __restrict__ 
 // G = Σ_b Gp[b] (ascending b)
 __global__ __launch_bounds__(256) void k_gram_reduce(const double* __restrict__ Gp, int64_t nb,
                                                      int ell, double* __restrict__ G) {
-  const int i = blockIdx.x * 256 + threadIdx.x;
+  // one wave per element: lane l sums the partials l, l + 64, ... in order, then the wave adds
+  // its lanes in a fixed tree (deterministic)
+  const int i = blockIdx.x * 4 + (threadIdx.x >> 6), lane = threadIdx.x & 63;
   if (i >= ell * ell) return;
   double acc = 0.0;
-  for (int64_t b = 0; b < nb; ++b) acc += Gp[b * ell * ell + i];
-  G[i] = acc;
+  for (int64_t b = lane; b < nb; b += 64) acc += Gp[b * ell * ell + i];
+  for (int off = 32; off > 0; off >>= 1) acc += __shfl_xor(acc, off);
+  if (lane == 0) G[i] = acc;
 }
 
 // Cholesky G = RᵀR (R upper) and Rinv = R⁻¹ (upper), fp64, one workgroup.  A pivot that is not
@@ -578,7 +581,7 @@ hipError_t lowrank_impl(const T* W, int64_t N, int64_t K, int64_t ldw, const flo
     const int64_t nb = ceil_div(rows, kGramRows);
     k_gram_partial<<<dim3((unsigned)nb), dim3(256), 0, s>>>(M, rows, e, w.gp);
     SVDQ_CHECK_LAUNCH();
-    k_gram_reduce<<<dim3((unsigned)ceil_div(ell * ell, 256)), dim3(256), 0, s>>>(w.gp, nb, e, G);
+    k_gram_reduce<<<dim3((unsigned)ceil_div(ell * ell, 4)), dim3(256), 0, s>>>(w.gp, nb, e, G);
     SVDQ_CHECK_LAUNCH();
     return hipSuccess;
   };
