@@ -66,12 +66,16 @@ def test_exactly_low_rank_weight_is_recovered(L):
     assert _err(A, down, up) <= 1e-2 * np.linalg.norm(A)     # bf16 rounding of the factors
 
 
+# ell up to 64 keeps every small factorisation in LDS; 72 puts the eigensolver in global memory;
+# 136 and 160 (the largest ell) put both the Cholesky-inverse and the eigensolver there
 @pytest.mark.parametrize("N,K,r,ell,q", [(320, 512, 16, 24, 2), (333, 264, 8, 16, 0),
-                                         (256, 1024, 32, 40, 1)])
+                                         (256, 1024, 32, 40, 1), (384, 512, 64, 72, 2),
+                                         (512, 768, 128, 136, 1), (400, 640, 120, 160, 1)])
 def test_decaying_spectrum_against_oracle(L, N, K, r, ell, q):
     rng = np.random.default_rng(N + K)
     n = min(N, K)
-    s_true = np.concatenate([20.0 * 0.8 ** np.arange(r + 4), 0.05 * np.ones(n - r - 4)])
+    decay = 0.8 if r <= 32 else 0.97
+    s_true = np.concatenate([20.0 * decay ** np.arange(r + 4), 0.05 * np.ones(n - r - 4)])
     U = np.linalg.qr(rng.standard_normal((N, n)))[0]
     Vm = np.linalg.qr(rng.standard_normal((K, n)))[0]
     Wb = bf16_rne(U @ np.diag(s_true) @ Vm.T)

@@ -28,6 +28,7 @@ constexpr int kJacobiThreads = 1024;
 constexpr int kMaxSweeps = 40;
 constexpr int kLdsEll = 80;        // the small factorisations run in LDS up to this ell
 constexpr int kCholThreads = 512;  // threads of the small Cholesky-inverse workgroup
+constexpr int kJacLdsEll = 64;     // the Jacobi eigensolver keeps two H buffers and V in LDS up to this ell
 
 // The matrix is either the bf16 weight (scaled by λ per channel) or an fp32 matrix (the refit
 // target of the layer's low-rank branch).
@@ -342,17 +343,23 @@ __global__ __launch_bounds__(256) void k_apply_rinv(const float* __restrict__ M,
 __global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ Hg, int ell,
                                                            double* __restrict__ Vg,
                                                            double* __restrict__ U,
-                                                           double* __restrict__ eig) {
+                                                           double* __restrict__ eig,
+                                                           double* __restrict__ H2g) {
   __shared__ double s_c[kMaxEll / 2], s_s[kMaxEll / 2];
   __shared__ int s_p[kMaxEll / 2], s_q[kMaxEll / 2];
+  __shared__ double s_self[kMaxEll], s_cp[kMaxEll];   // per index: own and partner coefficient
+  __shared__ int s_partner[kMaxEll];
   __shared__ double s_red[kJacobiThreads], s_red2[kJacobiThreads];
   __shared__ int s_order[kMaxEll];
   __shared__ int s_done;
-  __shared__ double s_h[kLdsEll * kLdsEll], s_v[kLdsEll * kLdsEll];
+  __shared__ double s_h[kJacLdsEll * kJacLdsEll], s_h2[kJacLdsEll * kJacLdsEll];
+  __shared__ double s_v[kJacLdsEll * kJacLdsEll];
   const int tid = threadIdx.x;
-  // H and V live in LDS when they fit, in the caller's buffers otherwise (same arithmetic)
-  const bool in_lds = ell <= kLdsEll;
+  // H (two buffers: a round reads one and writes the other) and V live in LDS when they fit, in
+  // the caller's buffers otherwise (same arithmetic)
+  const bool in_lds = ell <= kJacLdsEll;
   double* H = in_lds ? s_h : Hg;
+  double* Hn = in_lds ? s_h2 : H2g;
   double* V = in_lds ? s_v : Vg;
   if (in_lds)
     for (int t = tid; t < ell * ell; t += kJacobiThreads) s_h[t] = Hg[t];
@@ -407,33 +414,41 @@ __global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ 
         s_q[tid] = q < ell ? q : -1;
         s_c[tid] = c;
         s_s[tid] = s;
+        // the rotation acts on index p as c·x_p − s·x_q and on q as c·x_q + s·x_p; an index
+        // without a partner this round keeps its value (coefficients 1 and 0, itself as partner)
+        if (q < ell) {
+          s_self[p] = c; s_cp[p] = -s; s_partner[p] = q;
+          s_self[q] = c; s_cp[q] = s; s_partner[q] = p;
+        } else if (p < ell) {
+          s_self[p] = 1.0; s_cp[p] = 0.0; s_partner[p] = p;
+        }
       }
       __syncthreads();
-      // rows: H <- Jᵀ H
-      for (int t = tid; t < half * ell; t += kJacobiThreads) {
-        const int pr = t / ell, j = t % ell;
-        const int p = s_p[pr], q = s_q[pr];
-        if (q < 0) continue;
-        const double c = s_c[pr], s = s_s[pr];
-        const double hp = H[p * ell + j], hq = H[q * ell + j];
-        H[p * ell + j] = c * hp - s * hq;
-        H[q * ell + j] = s * hp + c * hq;
+      // H <- Jᵀ H J in one pass from the old buffer into the new: for each element the rotated
+      // rows at columns b and partner(b), then the column rotation of those two values (the
+      // same operations, in the same order, as a row pass followed by a column pass)
+      for (int t = tid; t < ell * ell; t += kJacobiThreads) {
+        const int a = t / ell, b = t % ell;
+        const int pa = s_partner[a], pb = s_partner[b];
+        const double sa = s_self[a], ca = s_cp[a], sb = s_self[b], cb = s_cp[b];
+        const double rb = sa * H[a * ell + b] + ca * H[pa * ell + b];
+        const double rpb = sa * H[a * ell + pb] + ca * H[pa * ell + pb];
+        Hn[t] = sb * rb + cb * rpb;
       }
-      __syncthreads();
-      // columns: H <- H J, V <- V J
+      // V <- V J, one thread per (row, pair)
       for (int t = tid; t < half * ell; t += kJacobiThreads) {
         const int pr = t / ell, i = t % ell;
         const int p = s_p[pr], q = s_q[pr];
         if (q < 0) continue;
         const double c = s_c[pr], s = s_s[pr];
-        const double hp = H[i * ell + p], hq = H[i * ell + q];
-        H[i * ell + p] = c * hp - s * hq;
-        H[i * ell + q] = s * hp + c * hq;
         const double vp = V[i * ell + p], vq = V[i * ell + q];
         V[i * ell + p] = c * vp - s * vq;
         V[i * ell + q] = s * vp + c * vq;
       }
       __syncthreads();
+      double* tmp = H;
+      H = Hn;
+      Hn = tmp;
     }
   }
   // sort by decreasing eigenvalue (ties by index)
@@ -612,7 +627,7 @@ hipError_t lowrank_impl(const T* W, int64_t N, int64_t K, int64_t ldw, const flo
   }
   if ((err = at_times(y, z)) != hipSuccess) return err;       // Z = Aᵀ Q = Bᵀ
   if ((err = gram(z, N, w.g)) != hipSuccess) return err;      // B Bᵀ
-  k_jacobi<<<dim3(1), dim3(kJacobiThreads), 0, s>>>(w.g, e, w.v, w.u, w.eig);
+  k_jacobi<<<dim3(1), dim3(kJacobiThreads), 0, s>>>(w.g, e, w.v, w.u, w.eig, w.r);
   SVDQ_CHECK_LAUNCH();
   const int64_t nout = (r * K) + (N * r);
   k_factors<<<dim3((unsigned)ceil_div(nout, 256)), dim3(256), 0, s>>>(
