@@ -37,60 +37,86 @@ constexpr int kJacLdsEll = 64;     // the Jacobi eigensolver keeps two H buffers
 // into LDS as fp32 with 16-byte loads, all of a thread's loads in flight before the first
 // store.  COLS and c0 are multiples of the elements per 16 bytes and the rows are 16-byte
 // aligned (ldw a multiple of 8); a 16-byte piece that crosses c_end is read element by element.
-template <typename T, int ROWS, int COLS, int LDS_LD>
-__device__ __forceinline__ void stage_tile(const T* __restrict__ W, int64_t ldw, int64_t r0,
-                                           int64_t r_end, int64_t c0, int64_t c_end,
-                                           float* lds) {
-  constexpr int V = 16 / (int)sizeof(T);          // elements per 16 bytes
-  constexpr int PER = ROWS * COLS / V / 256;       // 16-byte loads per thread
+template <typename T, int ROWS, int COLS>
+struct TileBuf {
+  static constexpr int V = 16 / (int)sizeof(T);       // elements per 16 bytes
+  static constexpr int PER = ROWS * COLS / V / 256;    // 16-byte loads per thread
   static_assert(PER * 256 * V == ROWS * COLS, "tile must split evenly over 256 threads");
-  u32x4_t buf[PER];
+  u32x4_t v[PER];
+};
+
+// Load a ROWS x COLS tile of W (rows r0 .. r_end, columns c0 .. c_end; the rest reads as 0) into
+// registers with 16-byte loads.  COLS and c0 are multiples of the elements per 16 bytes and the
+// rows are 16-byte aligned (ldw a multiple of 8); a piece that crosses c_end is read element by
+// element.
+template <typename T, int ROWS, int COLS>
+__device__ __forceinline__ void load_tile(const T* __restrict__ W, int64_t ldw, int64_t r0,
+                                          int64_t r_end, int64_t c0, int64_t c_end,
+                                          TileBuf<T, ROWS, COLS>& b) {
+  constexpr int V = TileBuf<T, ROWS, COLS>::V;
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
+  for (int p = 0; p < TileBuf<T, ROWS, COLS>::PER; ++p) {
     const int idx = threadIdx.x + 256 * p;
     const int rr = idx / (COLS / V), cv = idx % (COLS / V);
     const int64_t c = c0 + cv * V;
-    buf[p] = u32x4_t{0u, 0u, 0u, 0u};
+    b.v[p] = u32x4_t{0u, 0u, 0u, 0u};
     if (r0 + rr < r_end) {
       const T* src = W + (r0 + rr) * ldw + c;
       if (c + V <= c_end) {
-        buf[p] = *reinterpret_cast<const u32x4_t*>(src);
+        b.v[p] = *reinterpret_cast<const u32x4_t*>(src);
       } else if (c < c_end) {
         T part[V];
 #pragma unroll
         for (int e = 0; e < V; ++e) part[e] = c + e < c_end ? src[e] : (T)0;
-        __builtin_memcpy(&buf[p], part, 16);
+        __builtin_memcpy(&b.v[p], part, 16);
       }
     }
   }
+}
+
+// ... and store it into LDS as fp32 (row pitch LDS_LD floats)
+template <typename T, int ROWS, int COLS, int LDS_LD>
+__device__ __forceinline__ void store_tile(const TileBuf<T, ROWS, COLS>& b, float* lds) {
+  constexpr int V = TileBuf<T, ROWS, COLS>::V;
 #pragma unroll
-  for (int p = 0; p < PER; ++p) {
+  for (int p = 0; p < TileBuf<T, ROWS, COLS>::PER; ++p) {
     const int idx = threadIdx.x + 256 * p;
     const int rr = idx / (COLS / V), cv = idx % (COLS / V);
     float* dst = lds + rr * LDS_LD + cv * V;
     if (sizeof(T) == 2) {
 #pragma unroll
       for (int e = 0; e < 4; ++e) {
-        dst[2 * e] = bf16_lo(buf[p][e]);
-        dst[2 * e + 1] = bf16_hi(buf[p][e]);
+        dst[2 * e] = bf16_lo(b.v[p][e]);
+        dst[2 * e + 1] = bf16_hi(b.v[p][e]);
       }
     } else {
 #pragma unroll
-      for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(buf[p][e]);
+      for (int e = 0; e < 4; ++e) dst[e] = __uint_as_float(b.v[p][e]);
     }
   }
 }
 
+template <typename T, int ROWS, int COLS, int LDS_LD>
+__device__ __forceinline__ void stage_tile(const T* __restrict__ W, int64_t ldw, int64_t r0,
+                                           int64_t r_end, int64_t c0, int64_t c_end,
+                                           float* lds) {
+  TileBuf<T, ROWS, COLS> b;
+  load_tile<T, ROWS, COLS>(W, ldw, r0, r_end, c0, c_end, b);
+  store_tile<T, ROWS, COLS, LDS_LD>(b, lds);
+}
+
 // Yp[s][k][j] = Σ_{n in split s} W[n, k] · X[n, j]: 256 columns k per workgroup (thread =
-// column), 40 columns of X per workgroup (blockIdx.z); W and X staged 32 rows at a time.
+// column), 40 columns of X per workgroup (blockIdx.z); W and X staged 64 rows at a time.  (Loading
+// the next chunk into registers while multiplying the current one timed slower.)
 template <typename T>
 __global__ __launch_bounds__(256) void k_sketch_wt(const T* __restrict__ W, int64_t N,
                                                    int64_t K, int64_t ldw,
                                                    const float* __restrict__ X, int ell,
                                                    float* __restrict__ Yp) {
-  constexpr int kR = 32;
+  constexpr int kR = 64;
   // the W chunk [kR][256] while accumulating, then the block of sums [256][kColTile]
-  __shared__ __attribute__((aligned(16))) float s_buf[256 * kColTile];
+  __shared__ __attribute__((aligned(16))) float s_buf[kR * 256];
+  static_assert(kR * 256 >= 256 * kColTile, "the sums fit the chunk buffer");
   float (*ws)[256] = reinterpret_cast<float (*)[256]>(s_buf);
   __shared__ float xs[kR][kColTile];
   const int64_t kb = (int64_t)blockIdx.x * 256;
