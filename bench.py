@@ -158,6 +158,39 @@ def cpu_baseline(cfg, X, W, down, up, rows):
                       f"float64 GEMM); {dt:.2f} s"}
 
 
+def cpu_weight_side(st, fmt_name, seed=0):
+    """The oracle, as it stands, on bounded samples of the weight-side work: one λ candidate
+    (randomized factors, residual quantisation, 1024 sampled rows, score) and GPTQ of 32 weight
+    rows under the Hessian of 2048 activation rows (Hessian and inverse factor included)."""
+    from oracle import search as OSe, gptq as OG, calib as OC, svd as OS
+    cfg = st["cfg"]
+    M, K, N, r = cfg["M"], cfg["K"], cfg["N"], cfg["r"]
+    X, W = st["X"], st["W"]
+    ax = st["ax"].cpu().numpy()
+    aw = st["aw"].cpu().numpy()
+    rng = np.random.default_rng([seed, 10])
+    rows = np.sort(rng.choice(M, 1024, replace=False))
+    omega = rng.standard_normal((N, r + 8)).astype(np.float32)
+    t0 = time.perf_counter()
+    OSe.candidate(X, W, ax, aw, 7, np.float32(0.5), fmt_name, rows, omega, r, 2)
+    t_cand = time.perf_counter() - t0
+    lam = OC.lambda_from_stats(ax, aw, 7, 0.5)
+    t0 = time.perf_counter()
+    H = OG.hessian(X[:min(2048, M)], lam)
+    R32 = OS.residual_f32(W[:32], lam, st["down"], st["up"][:32])
+    OG.gptq_quantize(R32, H, fmt_name if fmt_name != "nvfp4-delta" else "nvfp4")
+    t_gptq = time.perf_counter() - t0
+    try:
+        cores = len(os.sched_getaffinity(0))
+    except AttributeError:
+        cores = os.cpu_count()
+    return {"lambda_candidates_per_s": round(1.0 / t_cand, 4), "candidate_s": round(t_cand, 2),
+            "gptq_weight_rows_per_s": round(32.0 / t_gptq, 2), "gptq_32_rows_s": round(t_gptq, 2),
+            "cores": cores, "kind": "oracle",
+            "sample": "one λ candidate on 1024 rows; GPTQ of 32 weight rows (Hessian of 2048 rows "
+                      "and its inverse Cholesky factor included)"}
+
+
 def copy_probe(torch, nbytes=1 << 30, reps=3):
     """A plain elementwise device kernel that reads `nbytes` and writes `nbytes` per launch."""
     src = torch.ones(nbytes // 4, dtype=torch.int32, device="cuda")
@@ -413,7 +446,16 @@ def main():
         from w4a4_quantized_dit_amd import layer
         print("[bench] weight side: λ search and GPTQ", file=sys.stderr, flush=True)
         fmt = {"nvfp4": 0, "nvfp4-delta": 0, "int4": 1, "mxfp4": 2, "mxfp8": 3}[cfg["fmt"]]
-        out["weight_side_ms"] = weight_side_gpu(torch, layer, st, fmt)
+        ws = weight_side_gpu(torch, layer, st, fmt)
+        out["weight_side_ms"] = ws
+        out["weight_side_rates"] = {
+            "lambda_candidates_per_s": round(39.0 / (ws["lambda_search_39"] * 1e-3), 2),
+            "gptq_weight_rows_per_s": round(N / ((ws["gptq_hessian_2048_rows"] + ws["gptq"]) * 1e-3),
+                                            1)}
+        if not args.no_cpu_baseline:
+            print("[bench] weight side on the cpu (oracle)", file=sys.stderr, flush=True)
+            fmt_name = "nvfp4" if cfg["fmt"] == "nvfp4-delta" else cfg["fmt"]
+            out["weight_side_cpu_baseline"] = cpu_weight_side(st, fmt_name)
     if not args.no_cpu_baseline:
         print("[bench] cpu baseline (oracle)", file=sys.stderr, flush=True)
         if cfg["fmt"] == "nvfp4-delta":
