@@ -175,32 +175,66 @@ __global__ __launch_bounds__(kThreads) void k_delta_act(
 // core_out GEMM: workgroup tile 128 cubes x 128 columns, 4 waves of 64 x 64 (2 x 2 tiles of
 // 32x32).  K mapping: in a 64-element chunk, lane (row = lane % 32, h = lane / 32) holds elements
 // [32h, 32h + 32); MFMA step t takes [8t, 8t + 8), for the core and the weight alike.
+// Each chunk's operands are converted to fp16 once per workgroup (thread t: row t / 2, elements
+// [32 (t % 2), +32) of the core tile and of the weight tile) into a double-buffered LDS tile,
+// and the waves read ready fragments; the raw bytes of chunk c + 2 are loaded while chunk c is
+// multiplied.  Rows are 72 halves apart (144 B), which keeps both the 16-byte conversion stores
+// and the 16-byte fragment reads free of bank conflicts.
+constexpr int kCorePitch = 72;  // halves per LDS row
+
 __global__ __launch_bounds__(kThreads) void k_gemm_core(
     int64_t n_cubes, int64_t N, int64_t K, const uint8_t* __restrict__ cc,
     const float* __restrict__ cs, const uint8_t* __restrict__ B, const uint8_t* __restrict__ Bs,
     const float* __restrict__ g_w, float* __restrict__ out) {
   constexpr int FM = 2, FN = 2;
-  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  __shared__ __attribute__((aligned(16))) _Float16 s_a[2][128 * kCorePitch];
+  __shared__ __attribute__((aligned(16))) _Float16 s_b[2][128 * kCorePitch];
+  const int tid = threadIdx.x;
+  const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 1, wn = wave & 1;
   const int64_t c_base = (int64_t)blockIdx.y * 128 + wm * 64;
   const int64_t n_base = (int64_t)blockIdx.x * 128 + wn * 64;
   const int r32 = lane & 31, h = lane >> 5;
   const int64_t kb = K / 2, ks = K / 16;
-  const uint8_t* pa[FM];
+  const int64_t nchunk = K / 64;
+
+  // conversion role of this thread
+  const int crow = tid >> 1, chh = tid & 1;
+  int64_t ac = (int64_t)blockIdx.y * 128 + crow;
+  ac = ac < n_cubes ? ac : n_cubes - 1;
+  const uint8_t* pa = cc + ac * K + 32 * chh;
+  const int64_t bcol = (int64_t)blockIdx.x * 128 + crow;
+  const uint8_t* pb = B + bcol * kb + 16 * chh;
+  const uint8_t* psb = Bs + bcol * ks;
+
+  u32x4_t ra[2], rb;
+  uint32_t rs;
+  auto load_raw = [&](int64_t c0) {
+    ra[0] = reinterpret_cast<const u32x4_t*>(pa + c0 * 64)[0];
+    ra[1] = reinterpret_cast<const u32x4_t*>(pa + c0 * 64)[1];
+    rb = *reinterpret_cast<const u32x4_t*>(pb + c0 * 32);
+    rs = *reinterpret_cast<const uint32_t*>(psb + c0 * 4);
+  };
+  auto convert = [&](int buf) {
+    _Float16* da = &s_a[buf][crow * kCorePitch + 32 * chh];
 #pragma unroll
-  for (int i = 0; i < FM; ++i) {
-    int64_t c = c_base + 32 * i + r32;
-    c = c < n_cubes ? c : n_cubes - 1;
-    pa[i] = cc + c * K + 32 * h;
-  }
-  const uint8_t* pb[FN];
-  const uint8_t* psb[FN];
+    for (int q = 0; q < 4; ++q) {
+      const uint32_t w0 = ra[q >> 1][2 * (q & 1)], w1 = ra[q >> 1][2 * (q & 1) + 1];
+      const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
+      const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
+      const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
+      const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
+      *reinterpret_cast<f16x8_t*>(da + 8 * q) =
+          f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
+    }
+    const f16x2_t p = e4m3x2_to_f16x2((rs >> (16 * chh)) & 0xFFFFu);  // blocks 2hh, 2hh+1
+    _Float16* db = &s_b[buf][crow * kCorePitch + 32 * chh];
 #pragma unroll
-  for (int j = 0; j < FN; ++j) {
-    const int64_t col = n_base + 32 * j + r32;
-    pb[j] = B + col * kb + 16 * h;
-    psb[j] = Bs + col * ks;
-  }
+    for (int q = 0; q < 4; ++q)
+      *reinterpret_cast<f16x8_t*>(db + 8 * q) =
+          dequant8(rb[q], (q >> 1) ? f16x2_t{p[1], p[1]} : f16x2_t{p[0], p[0]});
+  };
+
   f32x16_t acc[FM][FN];
 #pragma unroll
   for (int i = 0; i < FM; ++i)
@@ -209,44 +243,36 @@ __global__ __launch_bounds__(kThreads) void k_gemm_core(
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  for (int64_t c0 = 0; c0 < K / 64; ++c0) {
-    u32x4_t ca[FM][2], cbv[FN];
-    uint32_t sbv[FN];
-#pragma unroll
-    for (int i = 0; i < FM; ++i) {
-      ca[i][0] = reinterpret_cast<const u32x4_t*>(pa[i] + c0 * 64)[0];
-      ca[i][1] = reinterpret_cast<const u32x4_t*>(pa[i] + c0 * 64)[1];
-    }
-#pragma unroll
-    for (int j = 0; j < FN; ++j) {
-      cbv[j] = *reinterpret_cast<const u32x4_t*>(pb[j] + c0 * 32);
-      sbv[j] = *reinterpret_cast<const uint32_t*>(psb[j] + c0 * 4);
-    }
+  load_raw(0);
+  convert(0);
+  if (nchunk > 1) load_raw(1);
+  __syncthreads();
+  for (int64_t c0 = 0; c0 < nchunk; ++c0) {
+    const int buf = (int)(c0 & 1);
+    const _Float16* fa = &s_a[buf][(wm * 64 + r32) * kCorePitch + 32 * h];
+    const _Float16* fb = &s_b[buf][(wn * 64 + r32) * kCorePitch + 32 * h];
 #pragma unroll
     for (int t = 0; t < 4; ++t) {
       f16x8_t a_op[FM], b_op[FN];
 #pragma unroll
-      for (int i = 0; i < FM; ++i) {
-        // elements 8t .. 8t+7 of the lane's 32 E4M3 bytes: dwords 2t, 2t+1
-        const uint32_t w0 = ca[i][t >> 1][2 * (t & 1)], w1 = ca[i][t >> 1][2 * (t & 1) + 1];
-        const f16x2_t p0 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, false);
-        const f16x2_t p1 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w0, 1.0f, true);
-        const f16x2_t p2 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, false);
-        const f16x2_t p3 = __builtin_amdgcn_cvt_scalef32_pk_f16_fp8(w1, 1.0f, true);
-        a_op[i] = f16x8_t{p0[0], p0[1], p1[0], p1[1], p2[0], p2[1], p3[0], p3[1]};
-      }
+      for (int i = 0; i < FM; ++i)
+        a_op[i] = *reinterpret_cast<const f16x8_t*>(fa + 32 * i * kCorePitch + 8 * t);
 #pragma unroll
-      for (int j = 0; j < FN; ++j) {
-        const uint32_t s2 = (sbv[j] >> (16 * h)) & 0xFFFFu;  // blocks 2h, 2h+1 of the chunk
-        const f16x2_t p = e4m3x2_to_f16x2(s2);
-        b_op[j] = dequant8(cbv[j][t], (t >> 1) ? f16x2_t{p[1], p[1]} : f16x2_t{p[0], p[0]});
-      }
+      for (int j = 0; j < FN; ++j)
+        b_op[j] = *reinterpret_cast<const f16x8_t*>(fb + 32 * j * kCorePitch + 8 * t);
 #pragma unroll
       for (int i = 0; i < FM; ++i)
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a_op[i], b_op[j], acc[i][j], 0, 0, 0);
     }
+    // chunk c0 + 1 into the other buffer (last read before the previous barrier), then the
+    // raw bytes of chunk c0 + 2
+    if (c0 + 1 < nchunk) {
+      convert(buf ^ 1);
+      if (c0 + 2 < nchunk) load_raw(c0 + 2);
+    }
+    __syncthreads();
   }
   const float gw = g_w[0];
 #pragma unroll
