@@ -252,7 +252,7 @@ svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t 
  * sat_count (nullable, device uint32[1]): the number of NVFP4 blocks whose absmax exceeds the
  * tensor amax is ADDED to it (the caller zeroes it).
  * Outputs: codes [M, K/2] (MXFP8: [M, K]), scales, tensor_scale, D.  Codes and scales
- * bit-exact.
+ * bit-exact.  ldx larger than 2^24 elements: SVDQ_UNSUPPORTED_SHAPE.
  */
 svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, int64_t K,
                                         int64_t ldx, const float* lambda, const float* act_amax,
@@ -310,7 +310,8 @@ svdq_status svdq_cube_geometry(int64_t T, int64_t H, int64_t W, int64_t ct, int6
  *   delta = X̂ − core[cube(m)] (fp32, unquantised core), NVFP4 with tensor amax 2·act_amax
  *   D = bf16(X̂)·lora_downᵀ  (fp32, as in svdq_quant_act_lowrank_down)
  * cube_ptr / cube_rows: device int32 CSR from svdq_cube_geometry (every cube has at most 16
- * rows; members beyond the 16th of a larger cube are not processed).  K <= 16384.  Outputs:
+ * rows; members beyond the 16th of a larger cube are not processed).  K <= 16384 and
+ * ldx <= 2^24 (otherwise SVDQ_UNSUPPORTED_SHAPE).  Outputs:
  * core_codes
  * [n_cubes, K] E4M3 bytes, core_scale fp32 [n_cubes], delta_codes [M, K/2], delta_scales
  * [M, K/16], g_delta float[1], D [M, r] fp32; sat_count (nullable) as in

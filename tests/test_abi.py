@@ -73,6 +73,8 @@ def test_quant_act_and_gemm_validation(lib):
     assert qa(0, P, 64, 256, 256, None, None, P, 32, P, P, None, P, None, None) == NULLP
     assert qa(0, P, 64, 256, 128, None, None, P, 32, P, P, P, P, None, None) == SHAPE
     assert qa(1, P, 64, 256, 256, None, None, P, 32, P, P, None, None, None, None) == NULLP
+    # row strides past 2^24 elements are refused (32-bit byte offsets inside a workgroup)
+    assert qa(0, P, 64, 256, (1 << 24) + 8, None, None, P, 32, P, P, P, P, None, None) == SHAPE
     g = lib.svdq_w4a4_gemm
     assert g(0, 64, 128, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
     assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
@@ -91,6 +93,8 @@ def test_other_validation(lib):
                                        None) == NULLP
     assert lib.svdq_delta_quant_act(P, 10, 256, 256, None, P, P, P, 11, P, 8, P, P, P, P, P, P,
                                     None, None) == INVALID
+    assert lib.svdq_delta_quant_act(P, 10, 256, (1 << 24) + 8, None, P, P, P, 8, P, 8, P, P, P,
+                                    P, P, P, None, None) == SHAPE
     assert lib.svdq_cube_geometry(2, 2, 2, 4, 4, 4, 0, 0, 4, None, None, None, None) == NULLP
 
 

@@ -65,6 +65,14 @@ svdq_status check_ld(const char* fn, const char* name, int64_t ld, int64_t K) {
   return SVDQ_OK;
 }
 
+// The activation kernels address the 64 rows of a workgroup with 32-bit byte offsets.
+svdq_status check_act_ld(const char* fn, int64_t ldx) {
+  if (ldx > ((int64_t)1 << 24))
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldx=%lld exceeds 2^24 elements", fn,
+                (long long)ldx);
+  return SVDQ_OK;
+}
+
 svdq_status check_rank(const char* fn, int64_t r) {
   if (r < 0 || r > 128 || r % 8 != 0)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: rank r=%lld must be a multiple of 8 in [0, 128]", fn,
@@ -338,6 +346,7 @@ svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, i
   if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
   TRY(check_k(fn, K));
   TRY(check_ld(fn, "ldx", ldx, K));
+  TRY(check_act_ld(fn, ldx));
   TRY(check_rank(fn, r));
   if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
   if ((size_t)K * sizeof(float) > 64 * 1024)
@@ -420,6 +429,7 @@ svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_
   if (n_cubes < 1 || n_cubes > M) return fail(SVDQ_INVALID_ARG, "%s: bad n_cubes", fn);
   TRY(check_k(fn, K));
   TRY(check_ld(fn, "ldx", ldx, K));
+  TRY(check_act_ld(fn, ldx));
   TRY(check_rank(fn, r));
   if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
   if ((size_t)K * sizeof(float) > 64 * 1024 || svdq::delta_act_lds_bytes(K) > 160 * 1024)

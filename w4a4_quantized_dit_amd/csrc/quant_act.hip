@@ -73,7 +73,8 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
 
   // coalesced X loads: instruction i covers rows 2i, 2i+1 of the wave, lane piece = lane % 32
   // (rows past M read row M-1; their results are never stored)
-  // (element offsets from the block's first row fit 32 bits: 64 rows of at most ldx each)
+  // (element offsets from the block's first row fit 32 bits: 64 rows of at most ldx each,
+  // and the entry points refuse ldx above 2^24)
   const uint16_t* xblk = X + (int64_t)blockIdx.x * kRowsPerBlock * ldx;
   uint32_t xo[8];
 #pragma unroll
