@@ -261,7 +261,10 @@ svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, i
                                         uint32_t* sat_count, svdq_stream_t stream);
 
 /*
- * W4A4 GEMM with the low-rank up-projection, bf16 output.
+ * W4A4 GEMM with the low-rank up-projection, bf16 output ("MiniMax-H3 · SVDQuant W4A4 (int4,
+ * rank 32, GPTQ)", opening paragraph: the 4-bit residual product of the quantised activations
+ * and weight, plus the 16-bit low-rank branch X̂·L1·L2, is the layer's output; section
+ * "Measured": this quantised GEMM is where the layer's time goes).
  *
  *   NVFP4:    Y = bf16( g_a·g_w · Σ_k (c_a·s_a)(c_w·s_w) + D·lora_upᵀ [+ core_out[cube(m)]] )
  *   INT4_G64: Y = bf16( Σ_groups s_a·s_w · Σ_k c_a·c_w + D·lora_upᵀ )

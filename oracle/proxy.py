@@ -2,11 +2,11 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-"MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", section "Why": NVFP4
-puts 16 consecutive input channels under one scale set by the group's absmax, so a channel
-whose own absmax lies below its group's loses log2(group absmax / channel absmax) bits; λ
-reshapes exactly that profile because the kernel sees X / λ; the page scores candidate λ per
-modality with this statistics-only proxy (no GPU, no layer output).
+Source: "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", section "Why".
+The rule, restated: a block scale is fixed by the largest magnitude in its block, so each
+channel's resolution shrinks by the ratio of the block maximum to its own maximum, measured in
+bits as log2(block max / channel max) after smoothing; changing λ changes those ratios.  The
+page ranks candidate λ per modality by this count alone, from calibration statistics.
 
 Readings where the page is silent:
   * the channel absmax of modality μ after smoothing is c_k = fl(ax_μ[k] · fl(1/λ_k)) in

@@ -2,9 +2,9 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-NVFP4 ("MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", section "Why":
-16 consecutive input channels share one FP8 scale set by that group's absmax; plus an fp32
-tensor scale).  The pages give the structure but not the arithmetic; the reading used here,
+NVFP4 (source: "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", section
+"Why"; the format: an E4M3 byte scales each block of 16 channels along K, derived from that
+block's maximum, under one fp32 scale for the whole tensor).  The pages give the structure but not the arithmetic; the reading used here,
 with its float32 operation order pinned so that codes are reproducible bit for bit:
 
     g   = amax_t / 2688            (2688 = 6 * 448; g = 1 when amax_t == 0)

@@ -2,10 +2,10 @@
 
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
-"MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph: activation outliers are
-absorbed into a 16-bit rank-32 low-rank branch and the residual is quantised to 4 bits.  With
-smoothing, the branch is the rank-r truncated SVD of the smoothed weight W' = diag(λ)·W (the
-weight seen by the smoothed activation X̂ = X/λ), so X·W = X̂·W' = X̂·L1·L2 + X̂·R.
+Source: "MiniMax-H3 · SVDQuant W4A4 (int4, rank 32, GPTQ)", opening paragraph.  The layer
+keeps a rank-32 branch in 16-bit precision beside a 4-bit residual weight.  Here the branch is
+the rank-r truncated SVD of the smoothed weight W' = diag(λ)·W, the weight that meets the
+smoothed activation X̂ = X/λ, so X·W = X̂·W' = X̂·L1·L2 + X̂·R.
 
 Storage here is [out, in] = [N, K]: W'[n, k] = λ_k · W[n, k].  With W'ᵀ (K x N) = U Σ Vᵀ:
     L1 = U_r Σ_r  (K x r),   L2 = V_rᵀ  (r x N)

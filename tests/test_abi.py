@@ -75,6 +75,9 @@ def test_quant_act_and_gemm_validation(lib):
     assert qa(1, P, 64, 256, 256, None, None, P, 32, P, P, None, None, None, None) == NULLP
     # row strides past 2^24 elements are refused (32-bit byte offsets inside a workgroup)
     assert qa(0, P, 64, 256, (1 << 24) + 8, None, None, P, 32, P, P, P, P, None, None) == SHAPE
+    # at rank 128 the L1 slice and 1/λ of K = 16384 channels do not fit one CU's 160 KB of LDS
+    assert qa(0, P, 64, 16384, 16384, None, None, P, 128, P, P, P, P, None, None) == SHAPE
+    assert "LDS" in _err(lib)
     g = lib.svdq_w4a4_gemm
     assert g(0, 64, 128, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
     assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
@@ -198,6 +201,9 @@ def test_lambda_search_validation(lib):
     assert call(bd=P) == NULLP                           # best factors go in pairs
     assert call(bd=P, bu=P, r=0, om=None) == INVALID
     assert call(bd=MIS, bu=P) == SHAPE
+    big = lib.svdq_lambda_search_workspace_bytes(0, 512, 16384, 136, 128, 1024, 39, 0)
+    assert call(K=16384, ldx=16384, ldw=16384, r=128, ell=136, wsb=big) == SHAPE
+    assert "LDS" in _err(lib)
 
 
 def test_gptq_validation(lib):

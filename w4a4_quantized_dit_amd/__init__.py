@@ -3,7 +3,7 @@
     from w4a4_quantized_dit_amd import layer
     cal = layer.calibrate(X, seg, W, mask=7)            # λ, act_amax (device tensors)
     pw = layer.prepare_weight(W, cal["lambda"], lora_down, lora_up, fmt=layer.NVFP4)
-    Y = layer.forward(X, pw, cal["act_amax"], lora_down)
+    Y = layer.forward(X, pw, cal["act_amax"], cal["lambda"], lora_down)
 
 The raw entry points (same names as include/svdq.h) live in w4a4_quantized_dit_amd._lib.
 """

@@ -112,8 +112,10 @@ def _torch():
     return torch
 
 
-def _ptr(t, dtype=None, name="tensor", numel=None):
-    """Device pointer of a contiguous cuda tensor (None -> NULL)."""
+def _ptr(t, dtype=None, name="tensor", numel=None, rows=False):
+    """Device pointer of a cuda tensor (None -> NULL).  The tensor must be contiguous, or with
+    rows=True a 2-D view whose rows are contiguous (stride(1) == 1): its row stride is then
+    passed as the matrix's leading dimension, which the library validates."""
     if t is None:
         return None
     torch = _torch()
@@ -123,11 +125,19 @@ def _ptr(t, dtype=None, name="tensor", numel=None):
         raise ValueError(f"{name} must be a device tensor")
     if dtype is not None and t.dtype not in (dtype if isinstance(dtype, tuple) else (dtype,)):
         raise TypeError(f"{name} has dtype {t.dtype}, expected {dtype}")
-    if not t.is_contiguous():
+    if rows:
+        if t.dim() != 2 or (t.shape[1] > 1 and t.stride(1) != 1):
+            raise ValueError(f"{name} must be a 2-D matrix with contiguous rows")
+    elif not t.is_contiguous():
         raise ValueError(f"{name} must be contiguous")
     if numel is not None and t.numel() < numel:
         raise ValueError(f"{name} has {t.numel()} elements, needs {numel}")
     return t.data_ptr()
+
+
+def _ld(t):
+    """Leading dimension (row stride, elements) of a matrix passed with rows=True."""
+    return t.stride(0) if t.shape[0] > 1 else max(t.stride(0), t.shape[1])
 
 
 def _stream(stream=None):
@@ -169,8 +179,8 @@ def svdq_calibrate_lambda(X, seg, W, modality_mask, alpha, accumulate, ax, aw, l
     seg_arr = (ctypes.c_int64 * 4)(*[int(v) for v in seg])
     f32 = torch.float32
     _check(load().svdq_calibrate_lambda(
-        _ptr(X, _bf16(), "X"), M, K, X.stride(0), ctypes.cast(seg_arr, _c_p),
-        _ptr(W, _bf16(), "W"), N, W.stride(0) if W is not None else K,
+        _ptr(X, _bf16(), "X", rows=True), M, K, _ld(X), ctypes.cast(seg_arr, _c_p),
+        _ptr(W, _bf16(), "W", rows=True), N, _ld(W) if W is not None else K,
         int(modality_mask), float(alpha), int(accumulate),
         _ptr(ax, f32, "ax", 3 * K), _ptr(aw, f32, "aw", K), _ptr(lam, f32, "lambda", K),
         _ptr(act_amax, f32, "act_amax", 1), _stream(stream)))
@@ -197,7 +207,7 @@ def svdq_lowrank_factors(W, lam, omega, r, power_iters, lora_down, lora_up, sigm
     N, K = W.shape
     ell = omega.shape[1]
     _check(load().svdq_lowrank_factors(
-        _ptr(W, _bf16(), "W"), N, K, W.stride(0), _ptr(lam, torch.float32, "lambda", K),
+        _ptr(W, _bf16(), "W", rows=True), N, K, _ld(W), _ptr(lam, torch.float32, "lambda", K),
         _ptr(omega, torch.float32, "omega", N * ell), ell, int(r), int(power_iters),
         _ptr(lora_down, _bf16(), "lora_down", r * K), _ptr(lora_up, _bf16(), "lora_up", N * r),
         _ptr(sigma, torch.float32, "sigma", r), _ptr(workspace, torch.uint8, "workspace"),
@@ -208,7 +218,7 @@ def svdq_gptq_hessian(X, lam, H, accumulate=False, stream=None):
     torch = _torch()
     M, K = X.shape
     _check(load().svdq_gptq_hessian(
-        _ptr(X, _bf16(), "X"), M, K, X.stride(0),
+        _ptr(X, _bf16(), "X", rows=True), M, K, _ld(X),
         _ptr(lam, torch.float32, "lambda", K) if lam is not None else None, int(bool(accumulate)),
         _ptr(H, torch.float64, "H", K * K), _stream(stream)))
 
@@ -222,7 +232,7 @@ def svdq_gptq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, H, codes, scal
     torch = _torch()
     N, K = W.shape
     _check(load().svdq_gptq_quantize_weight(
-        int(fmt), _ptr(W, _bf16(), "W"), N, K, W.stride(0),
+        int(fmt), _ptr(W, _bf16(), "W", rows=True), N, K, _ld(W),
         _ptr(lam, torch.float32, "lambda", K) if lam is not None else None,
         _ptr(lora_down, _bf16(), "lora_down", r * K) if r else None,
         _ptr(lora_up, _bf16(), "lora_up", N * r) if r else None, int(r),
@@ -250,7 +260,7 @@ def svdq_lambda_search(X, W, ax, aw, mask, alphas, fmt, omega, r, power_iters, r
     n = len(alphas)
     arr = (ctypes.c_float * n)(*[float(a) for a in alphas])
     _check(load().svdq_lambda_search(
-        _ptr(X, _bf16(), "X"), M, K, X.stride(0), _ptr(W, _bf16(), "W"), N, W.stride(0),
+        _ptr(X, _bf16(), "X", rows=True), M, K, _ld(X), _ptr(W, _bf16(), "W", rows=True), N, _ld(W),
         _ptr(ax, torch.float32, "ax", 3 * K), _ptr(aw, torch.float32, "aw", K), int(mask),
         ctypes.cast(arr, _c_p), n, int(fmt),
         _ptr(omega, torch.float32, "omega", N * ell) if omega is not None else None, ell, int(r),
@@ -272,7 +282,7 @@ def svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, tens
     N, K = W.shape
     blk = _block(fmt)
     _check(load().svdq_quantize_weight(
-        int(fmt), _ptr(W, _bf16(), "W"), N, K, W.stride(0), _ptr(lam, torch.float32, "lambda", K),
+        int(fmt), _ptr(W, _bf16(), "W", rows=True), N, K, _ld(W), _ptr(lam, torch.float32, "lambda", K),
         _ptr(lora_down if r else None, _bf16(), "lora_down", r * K),
         _ptr(lora_up if r else None, _bf16(), "lora_up", N * r), int(r),
         _ptr(codes, torch.uint8, "codes", _code_bytes(fmt, N, K)),
@@ -287,7 +297,7 @@ def svdq_quant_act_lowrank_down(fmt, X, lam, act_amax, lora_down, r, codes, scal
     M, K = X.shape
     blk = _block(fmt)
     _check(load().svdq_quant_act_lowrank_down(
-        int(fmt), _ptr(X, _bf16(), "X"), M, K, X.stride(0),
+        int(fmt), _ptr(X, _bf16(), "X", rows=True), M, K, _ld(X),
         _ptr(lam, torch.float32, "lambda", K), _ptr(act_amax, torch.float32, "act_amax", 1),
         _ptr(lora_down if r else None, _bf16(), "lora_down", r * K), int(r),
         _ptr(codes, torch.uint8, "codes", _code_bytes(fmt, M, K)),
@@ -310,7 +320,7 @@ def svdq_w4a4_gemm(fmt, M, N, K, a_codes, a_scales, g_a, w_codes, w_scales, g_w,
         _ptr(g_w, torch.float32, "g_w", 1), _ptr(D if r else None, torch.float32, "D", M * r),
         _ptr(lora_up if r else None, _bf16(), "lora_up", N * r), int(r),
         _ptr(core_out, torch.float32, "core_out"), _ptr(row_to_cube, torch.int32, "row_to_cube", M),
-        _ptr(Y, _bf16(), "Y", M * N), Y.stride(0), _stream(stream)))
+        _ptr(Y, _bf16(), "Y", M * N, rows=True), _ld(Y), _stream(stream)))
 
 
 def svdq_cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d):
@@ -337,7 +347,7 @@ def svdq_delta_quant_act(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, lora_do
     torch = _torch()
     M, K = X.shape
     _check(load().svdq_delta_quant_act(
-        _ptr(X, _bf16(), "X"), M, K, X.stride(0), _ptr(lam, torch.float32, "lambda", K),
+        _ptr(X, _bf16(), "X", rows=True), M, K, _ld(X), _ptr(lam, torch.float32, "lambda", K),
         _ptr(act_amax, torch.float32, "act_amax", 1), _ptr(cube_ptr, torch.int32, "cube_ptr"),
         _ptr(cube_rows, torch.int32, "cube_rows", M), int(n_cubes),
         _ptr(lora_down if r else None, _bf16(), "lora_down", r * K), int(r),
@@ -367,7 +377,7 @@ def svdq_score_modal_rel_l2(Y, X, W, rows, row_group, sums, stream=None):
     M, K = X.shape
     N = W.shape[0]
     _check(load().svdq_score_modal_rel_l2(
-        _ptr(Y, _bf16(), "Y", M * N), Y.stride(0), _ptr(X, _bf16(), "X"), X.stride(0),
-        _ptr(W, _bf16(), "W"), W.stride(0), M, N, K, _ptr(rows, torch.int32, "rows"),
+        _ptr(Y, _bf16(), "Y", M * N, rows=True), _ld(Y), _ptr(X, _bf16(), "X", rows=True), _ld(X),
+        _ptr(W, _bf16(), "W", rows=True), _ld(W), M, N, K, _ptr(rows, torch.int32, "rows"),
         _ptr(row_group, torch.int8, "row_group"), rows.numel(),
         _ptr(sums, torch.float64, "sums", 8), _stream(stream)))

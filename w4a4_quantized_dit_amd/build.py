@@ -1,11 +1,17 @@
 """Builds the gfx950 shared library libsvdq.so in-tree with hipcc.
 
+Every source is compiled to an object file in parallel (one hipcc per source), then the objects
+are linked into the shared library.
+
 Usage: python -m w4a4_quantized_dit_amd.build   (or build() from Python)
 """
 import os
+import shutil
 import subprocess
 import sys
+import tempfile
 import time
+from concurrent.futures import ThreadPoolExecutor
 
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
@@ -17,7 +23,7 @@ SOURCES = ["api.cpp", "geometry.cpp", "calib.hip", "quant_weight.hip", "quant_ac
            "lowrank.hip", "search.hip", "gptq.hip"]
 
 FLAGS = [
-    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-shared",
+    "--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC",
     # codes are defined by IEEE single operations in a fixed order: no contraction, exact
     # division and square root, denormals kept
     "-ffp-contract=off", "-fhip-fp32-correctly-rounded-divide-sqrt",
@@ -28,21 +34,44 @@ FLAGS = [
 ]
 
 
-def build(verbose=False, out=None, defines=()):
-    """Compile every source into libsvdq.so (always recompiles).  `out` / `defines` build a
-    differently named library with extra -D tuning definitions."""
-    srcs = [os.path.join(CSRC, s) for s in SOURCES]
-    target = out or LIB
-    tmp = target + ".tmp"
-    cmd = [HIPCC] + FLAGS + ["-D" + d for d in defines] + srcs + ["-o", tmp]
-    t0 = time.time()
+def _run(cmd):
     res = subprocess.run(cmd, stdout=subprocess.PIPE, stderr=subprocess.STDOUT, text=True)
     out = "\n".join(l for l in res.stdout.splitlines() if "packed-fp32-ops" not in l)
-    if res.returncode != 0:
-        raise RuntimeError("hipcc failed:\n" + out)
-    if verbose and out.strip():
-        print(out)
-    os.replace(tmp, target)
+    return res.returncode, out
+
+
+def build(verbose=False, out=None, defines=(), jobs=None):
+    """Compile every source into libsvdq.so (always recompiles).  `out` / `defines` build a
+    differently named library with extra -D definitions."""
+    target = out or LIB
+    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    t0 = time.time()
+    tmpdir = tempfile.mkdtemp(prefix="svdq_build_")
+    try:
+        dflags = ["-D" + d for d in defines]
+
+        def compile_one(src):
+            obj = os.path.join(tmpdir, os.path.splitext(src)[0] + ".o")
+            rc, text = _run([HIPCC] + FLAGS + dflags + ["-c", os.path.join(CSRC, src), "-o", obj])
+            return src, obj, rc, text
+
+        with ThreadPoolExecutor(max_workers=jobs) as ex:
+            results = list(ex.map(compile_one, SOURCES))
+        errors = [f"== {src} ==\n{text}" for src, _, rc, text in results if rc != 0]
+        if errors:
+            raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
+        tmp = target + ".tmp"
+        rc, text = _run([HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC"]
+                        + [obj for _, obj, _, _ in results] + ["-o", tmp])
+        if rc != 0:
+            raise RuntimeError("link failed:\n" + text)
+        if verbose:
+            for src, _, _, text in results:
+                if text.strip():
+                    print(f"== {src} ==\n{text}")
+        os.replace(tmp, target)
+    finally:
+        shutil.rmtree(tmpdir, ignore_errors=True)
     if verbose:
         print(f"built {target} in {time.time() - t0:.1f}s")
     return target

@@ -73,6 +73,16 @@ svdq_status check_act_ld(const char* fn, int64_t ldx) {
   return SVDQ_OK;
 }
 
+// The activation kernel keeps 1/λ for all K channels and the rank-r slice of L1 in LDS.
+svdq_status check_act_lds(const char* fn, int64_t K, int64_t r) {
+  const size_t need = svdq::quant_act_lds_bytes(K, r);
+  if (need > 160 * 1024)
+    return fail(SVDQ_UNSUPPORTED_SHAPE,
+                "%s: K=%lld at rank %lld needs %zu bytes of LDS, more than the 160 KB of a CU", fn,
+                (long long)K, (long long)r, need);
+  return SVDQ_OK;
+}
+
 svdq_status check_rank(const char* fn, int64_t r) {
   if (r < 0 || r > 128 || r % 8 != 0)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: rank r=%lld must be a multiple of 8 in [0, 128]", fn,
@@ -285,6 +295,7 @@ svdq_status svdq_lambda_search(const uint16_t* X, int64_t M, int64_t K, int64_t 
   REQUIRE_ALIGNED(best_down); REQUIRE_ALIGNED(best_up);
   if (n_rows < 1)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: n_rows=%lld must be >= 1", fn, (long long)n_rows);
+  TRY(check_act_lds(fn, K, r));
   const int64_t need =
       svdq::lambda_search_workspace_bytes(fmt, N, K, ell, r, n_rows, n_alpha, refit_iters);
   if (workspace_bytes < need)
@@ -349,8 +360,7 @@ svdq_status svdq_quant_act_lowrank_down(int fmt, const uint16_t* X, int64_t M, i
   TRY(check_act_ld(fn, ldx));
   TRY(check_rank(fn, r));
   if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
-  if ((size_t)K * sizeof(float) > 64 * 1024)
-    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: K=%lld exceeds 16384", fn, (long long)K);
+  TRY(check_act_lds(fn, K, r));
   return hip_result(svdq::launch_quant_act(fmt, X, M, K, ldx, lambda, act_amax, lora_down, r,
                                            codes, scales, tensor_scale, D, sat_count,
                                            reinterpret_cast<hipStream_t>(stream)),

@@ -47,6 +47,10 @@ hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, in
                             int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
                             float* D, uint32_t* sat, hipStream_t s);
 
+// LDS bytes (static + dynamic) of the activation kernel for K channels at rank r; a launch
+// needs at most 160 KB.
+size_t quant_act_lds_bytes(int64_t K, int64_t r);
+
 // D = bf16(X·1/λ)·lora_downᵀ alone (fp32 [M, r], r >= 1), with the activation kernel's tiling.
 hipError_t launch_lowrank_down(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                const float* lambda, const uint16_t* down, int64_t r, float* D,

@@ -396,6 +396,13 @@ hipError_t dispatch(int nt, dim3 grid, size_t lds, hipStream_t s, const uint16_t
 
 }  // namespace
 
+size_t quant_act_lds_bytes(int64_t K, int64_t r) {
+  const int nt = (int)((r + 15) / 16);
+  const size_t dyn = inv_lds_bytes(K);
+  const bool split = nt <= 2 && static_lds(nt, 2) + dyn <= 160 * 1024;
+  return static_lds(nt, split ? 2 : 1) + dyn;
+}
+
 hipError_t launch_lowrank_down(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                const float* lambda, const uint16_t* down, int64_t r, float* D,
                                hipStream_t s) {

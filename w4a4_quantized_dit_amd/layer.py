@@ -174,6 +174,29 @@ def quantize_activation(X, lam, act_amax, lora_down, fmt=NVFP4, sat_count=None):
     return codes, scales, g, D
 
 
+def delta_quantize_activation(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, lora_down,
+                              out=None, sat_count=None):
+    """DeltaQuant activations of X [M, K] for the device CSR cube_ptr / cube_rows: dict with
+    core codes cc [n_cubes, K], core scales cs [n_cubes], delta codes dc [M, K/2] and scales
+    dsc [M, K/16], g_delta gd [1] and D [M, r] (fp32).  Pass `out` to reuse its tensors."""
+    torch = _torch()
+    M, K = X.shape
+    r = 0 if lora_down is None else lora_down.shape[0]
+    dev = X.device
+    u8 = torch.uint8
+    if out is None:
+        out = dict(cc=torch.empty(n_cubes, K, dtype=u8, device=dev),
+                   cs=torch.empty(n_cubes, device=dev),
+                   dc=torch.empty(M, K // 2, dtype=u8, device=dev),
+                   dsc=torch.empty(M, K // 16, dtype=u8, device=dev),
+                   gd=torch.empty(1, device=dev),
+                   D=torch.empty(M, r, device=dev) if r else None)
+    _lib.svdq_delta_quant_act(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, lora_down, r,
+                              out["cc"], out["cs"], out["dc"], out["dsc"], out["gd"],
+                              out.get("D"), sat_count)
+    return out
+
+
 def gemm(codes, scales, g_a, D, pw, M, out=None, core_out=None, row_to_cube=None):
     torch = _torch()
     Y = out if out is not None else torch.empty(M, pw.N, dtype=torch.bfloat16, device=codes.device)
