@@ -419,16 +419,15 @@ def setup(torch, workload):
         st["gemm_peak"] = PEAK_I8_TOPS
     else:  # delta
         T, H, Wg = cfg["grid"]
-        r2c, ptr, crow = _lib.svdq_cube_geometry(T, H, Wg, *cfg["cube"], cfg["n_text"],
-                                                 cfg["n_audio"], cfg["cube1d"])
-        nc = len(ptr) - 1
-        r2c_d = torch.from_numpy(r2c).to(dev)
-        ptr_d, crow_d = torch.from_numpy(ptr).to(dev), torch.from_numpy(crow).to(dev)
-        dq = layer.delta_quantize_activation(Xd0, lam, amax, ptr_d, crow_d, nc, downd)
+        geo = layer.cube_geometry(T, H, Wg, *cfg["cube"], cfg["n_text"], cfg["n_audio"],
+                                  cfg["cube1d"])
+        nc = geo["n_cubes"]
+        r2c_d = geo["row_to_cube"]
+        dq = layer.delta_quantize_activation(Xd0, lam, amax, geo, downd)
         core_out = torch.empty(nc, N, device=dev)
 
         def qa(Xi):
-            layer.delta_quantize_activation(Xi, lam, amax, ptr_d, crow_d, nc, downd, out=dq)
+            layer.delta_quantize_activation(Xi, lam, amax, geo, downd, out=dq)
 
         def core(Xi):
             _lib.svdq_gemm_core(nc, N, K, dq["cc"], dq["cs"], w_codes, w_scales, g_w, core_out)

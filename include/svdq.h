@@ -288,13 +288,15 @@ svdq_status svdq_w4a4_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8
 
 /*
  * DeltaQuant cube geometry, HOST function ("DeltaQuant on MiniMax-H3", sections "The audio win
- * has a mechanism" (1-D cubes of consecutive rows for non-video rows) and "Standing
- * configuration" (geometry derived per request, identical across steps)).
+ * has a mechanism" (1-D cubes of consecutive rows for non-video rows), "Standing configuration"
+ * (geometry derived per request, identical across steps) and "Deviations from the paper, and one
+ * replication" (uniform cube-64)).
  *
  * Rows are [n_text | T·H·W video in raster (t, h, w) order | n_audio].  A video row belongs to
  * cube (t/ct, h/ch, w/cw) (ragged at the grid edges); text and audio rows form cubes of cube1d
  * consecutive rows of their segment.  Cubes are numbered in order of their first row; members
- * are listed ascending.  All pointers are HOST pointers: row_to_cube int32 [M],
+ * are listed ascending.  Cubes hold at most 64 rows: ct·ch·cw <= 64 and cube1d <= 64
+ * (otherwise SVDQ_UNSUPPORTED_SHAPE).  All pointers are HOST pointers: row_to_cube int32 [M],
  * cube_ptr int32 [n_cubes + 1], cube_rows int32 [M], n_cubes int64 [1].  Pass row_to_cube ==
  * NULL to only count: n_cubes is written and nothing else.
  */
@@ -304,29 +306,65 @@ svdq_status svdq_cube_geometry(int64_t T, int64_t H, int64_t W, int64_t ct, int6
                                int64_t* n_cubes);
 
 /*
+ * Divisor-aligned cube edges, HOST function ("DeltaQuant on MiniMax-H3", section "Deviations from
+ * the paper, and one replication": divisor-aligned cube shapes are an opt-in variant; the page
+ * gives no rule).  edges (host int64[3]) = for each of (T, ct), (H, ch), (W, cw) the largest
+ * divisor of the grid dimension not above the requested edge (an empty dimension keeps its
+ * edge), so that no video cube is ragged and none exceeds the requested shape.  Sizes >= 0,
+ * edges >= 1, else SVDQ_INVALID_ARG.
+ */
+svdq_status svdq_cube_divisor_aligned(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch,
+                                      int64_t cw, int64_t* edges);
+
+/*
+ * Per-step cube schedule lookup, HOST function ("DeltaQuant on MiniMax-H3", section "Deviations
+ * from the paper, and one replication": a timestep cube schedule, against uniform cube-64; the
+ * page does not print the schedule).  table (host int64 [n_entries][4]) holds rows
+ * (first_step, ct, ch, cw) with first_step strictly increasing from 0; edges (host int64[3])
+ * receives the (ct, ch, cw) of the last row whose first_step is <= step.  A malformed table or a
+ * negative step: SVDQ_INVALID_ARG.  The geometry of the step then comes from svdq_cube_geometry.
+ */
+svdq_status svdq_cube_schedule(const int64_t* table, int64_t n_entries, int64_t step,
+                               int64_t* edges);
+
+/*
+ * Work groups of the DeltaQuant activation kernel, HOST function.  Consecutive cubes of the CSR
+ * cube_ptr (host int32 [n_cubes + 1], cube_ptr[0] == 0) are packed greedily into groups of at
+ * most 64 rows and 16 cubes.  group_ptr (host int32, room for n_cubes + 1 entries; NULL to only
+ * count) receives the first cube of every group followed by n_cubes; *n_groups (host) the
+ * number of groups.  A cube with no rows or more than 64 rows: SVDQ_UNSUPPORTED_SHAPE.
+ */
+svdq_status svdq_cube_groups(const int32_t* cube_ptr, int64_t n_cubes, int32_t* group_ptr,
+                             int64_t* n_groups);
+
+/*
  * DeltaQuant activations ("DeltaQuant on MiniMax-H3", sections "Why DeltaQuant does not beat
- * SVDQuant here", "The activation scale bound held", "Deviations from the paper").
+ * SVDQuant here", "The activation scale bound held", "Deviations from the paper, and one
+ * replication").  One pass over X:
  *
  *   X̂ = fp32(X)·fp32(1/λ)
  *   core[c, k] = fp32(ascending fp32 sum of X̂ over the cube's rows) / |c|
  *   core codes: E4M3(core · 1/s_c) per core row, s_c = max_k|core[c, k]| / 448 (fp32)
  *   delta = X̂ − core[cube(m)] (fp32, unquantised core), NVFP4 with tensor amax 2·act_amax
  *   D = bf16(X̂)·lora_downᵀ  (fp32, as in svdq_quant_act_lowrank_down)
- * cube_ptr / cube_rows: device int32 CSR from svdq_cube_geometry (every cube has at most 16
- * rows; members beyond the 16th of a larger cube are not processed).  K <= 16384 and
- * ldx <= 2^24 (otherwise SVDQ_UNSUPPORTED_SHAPE).  Outputs:
- * core_codes
+ * cube_ptr / cube_rows: device int32 CSR from svdq_cube_geometry (or the caller's own, with
+ * members ascending); group_ptr: device int32 [n_groups + 1] from svdq_cube_groups over the same
+ * cube_ptr (a group the packer would not make gives its cubes a NaN core scale).
+ * workspace: at least svdq_delta_workspace_bytes(n_cubes, K) = 4·n_cubes·K bytes of device
+ * memory, 256-byte aligned, the caller's (the fp32 cores pass through it).  Outputs: core_codes
  * [n_cubes, K] E4M3 bytes, core_scale fp32 [n_cubes], delta_codes [M, K/2], delta_scales
  * [M, K/16], g_delta float[1], D [M, r] fp32; sat_count (nullable) as in
  * svdq_quant_act_lowrank_down.  Codes and scales bit-exact.
  */
+int64_t svdq_delta_workspace_bytes(int64_t n_cubes, int64_t K);
 svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                  const float* lambda, const float* act_amax,
                                  const int32_t* cube_ptr, const int32_t* cube_rows,
-                                 int64_t n_cubes, const uint16_t* lora_down, int64_t r,
-                                 uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
-                                 uint8_t* delta_scales, float* g_delta, float* D,
-                                 uint32_t* sat_count, svdq_stream_t stream);
+                                 int64_t n_cubes, const int32_t* group_ptr, int64_t n_groups,
+                                 const uint16_t* lora_down, int64_t r, uint8_t* core_codes,
+                                 float* core_scale, uint8_t* delta_codes, uint8_t* delta_scales,
+                                 float* g_delta, float* D, uint32_t* sat_count, void* workspace,
+                                 int64_t workspace_bytes, svdq_stream_t stream);
 
 /*
  * DeltaQuant core GEMM on a 16-bit path ("DeltaQuant on MiniMax-H3", section "Deviations from

@@ -67,6 +67,48 @@ def cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d):
     return row_to_cube, cube_ptr, cube_rows
 
 
+def divisor_aligned_edges(T, H, W, ct, ch, cw):
+    """Cube edges aligned to the grid ("DeltaQuant on MiniMax-H3", section "Deviations from the
+    paper, and one replication": divisor-aligned cube shapes as an opt-in variant).  The page
+    names the variant but not its rule; the reading here: along each axis the edge becomes the
+    largest divisor of that grid dimension not above the requested edge, so no cube is ragged
+    and none exceeds the requested shape.  An empty axis keeps the requested edge."""
+    def edge(n, e):
+        if n <= 0:
+            return e
+        return max(d for d in range(1, min(n, e) + 1) if n % d == 0)
+    return edge(T, ct), edge(H, ch), edge(W, cw)
+
+
+def padded_video_rows(T, H, W, ct, ch, cw):
+    """Rows that a cube-major layout padding every video cube to its full ct·ch·cw volume would
+    give the GEMMs (ragged edge cubes padded); equals T·H·W when the edges divide the grid."""
+    def up(n, e):
+        return -(-n // e) * e
+    return up(T, ct) * up(H, ch) * up(W, cw)
+
+
+def schedule_edges(schedule, step):
+    """Cube edges of a denoising step under a timestep cube schedule ("DeltaQuant on MiniMax-H3",
+    section "Deviations from the paper, and one replication": a per-timestep cube schedule
+    replicates against uniform cube-64).  The page does not print the schedule; the reading is a
+    table of (first_step, ct, ch, cw) rows with strictly increasing first_step starting at 0,
+    and a step takes the shape of the last row whose first_step is not above it."""
+    rows = [tuple(int(v) for v in r) for r in schedule]
+    if not rows or rows[0][0] != 0:
+        raise ValueError("a schedule starts at step 0")
+    for a, b in zip(rows, rows[1:]):
+        if b[0] <= a[0]:
+            raise ValueError("first steps must increase")
+    if step < 0:
+        raise ValueError("negative step")
+    cur = rows[0]
+    for r in rows:
+        if r[0] <= step:
+            cur = r
+    return cur[1], cur[2], cur[3]
+
+
 def cube_core(xhat32, cube_ptr, cube_rows):
     """core[c, k]: float32 ascending sum over the cube's rows, divided by the member count."""
     xhat32 = np.asarray(xhat32, dtype=F32)

@@ -94,10 +94,28 @@ def test_other_validation(lib):
     assert lib.svdq_gemm_core(0, 256, 256, P, P, P, P, P, P, None) == SHAPE
     assert lib.svdq_score_modal_rel_l2(P, 256, P, 256, P, 256, 10, 256, 256, P, P, 4, None,
                                        None) == NULLP
-    assert lib.svdq_delta_quant_act(P, 10, 256, 256, None, P, P, P, 11, P, 8, P, P, P, P, P, P,
-                                    None, None) == INVALID
-    assert lib.svdq_delta_quant_act(P, 10, 256, (1 << 24) + 8, None, P, P, P, 8, P, 8, P, P, P,
-                                    P, P, P, None, None) == SHAPE
+    d = lib.svdq_delta_quant_act
+    ws = 1 << 30
+    need = lib.svdq_delta_workspace_bytes(8, 256)
+    assert need == 8 * 256 * 4 and lib.svdq_delta_workspace_bytes(0, 256) == -1
+
+    def dcall(**kw):
+        a = dict(X=P, M=10, K=256, ldx=256, lam=None, amax=P, cp=P, cr=P, nc=8, gp=P, ng=2, down=P,
+                 r=8, cc=P, cs=P, dc=P, ds=P, gd=P, D=P, sat=None, ws=ws, wsb=need)
+        a.update(kw)
+        return d(a["X"], a["M"], a["K"], a["ldx"], a["lam"], a["amax"], a["cp"], a["cr"], a["nc"],
+                 a["gp"], a["ng"], a["down"], a["r"], a["cc"], a["cs"], a["dc"], a["ds"], a["gd"],
+                 a["D"], a["sat"], a["ws"], a["wsb"], None)
+    assert dcall(nc=11) == INVALID                        # more cubes than rows
+    assert dcall(ng=0) == INVALID and dcall(ng=9) == INVALID
+    assert dcall(gp=None) == NULLP
+    assert dcall(ws=None) == NULLP
+    assert dcall(ws=ws + 16) == SHAPE                     # not 256-byte aligned
+    assert dcall(wsb=need - 1) == SHAPE and "workspace" in _err(lib)
+    assert dcall(ldx=128) == SHAPE
+    assert dcall(K=200, ldx=200) == SHAPE
+    assert dcall(r=12) == SHAPE
+    assert dcall(D=None) == NULLP
     assert lib.svdq_cube_geometry(2, 2, 2, 4, 4, 4, 0, 0, 4, None, None, None, None) == NULLP
 
 
@@ -114,7 +132,10 @@ def test_cube_geometry_rejects_bad_sizes(lib):
     n = ctypes.c_int64(0)
     pn = ctypes.cast(ctypes.pointer(n), ctypes.c_void_p)
     assert lib.svdq_cube_geometry(2, 2, 2, 0, 2, 2, 0, 0, 4, None, None, None, pn) == INVALID
-    assert lib.svdq_cube_geometry(2, 2, 2, 4, 4, 2, 0, 0, 4, None, None, None, pn) == SHAPE
+    assert lib.svdq_cube_geometry(8, 8, 8, 4, 4, 8, 0, 0, 4, None, None, None, pn) == SHAPE
+    assert lib.svdq_cube_geometry(8, 8, 8, 2, 2, 2, 0, 0, 65, None, None, None, pn) == SHAPE
+    assert lib.svdq_cube_geometry(31, 24, 42, 4, 4, 4, 312, 128, 4, None, None, None, pn) == OK
+    assert n.value == 638                                 # uniform cube-64
     assert lib.svdq_cube_geometry(31, 24, 42, 2, 2, 2, 312, 128, 4, None, None, None, pn) == OK
     assert n.value == 4142
 
@@ -237,3 +258,56 @@ def test_gptq_validation(lib):
     assert call(ws=ws + 8) == SHAPE
     assert call(wsb=need - 1) == SHAPE and "workspace" in _err(lib)
     assert call(W=MIS) == SHAPE
+
+
+def test_cube64_and_aligned_geometry_match_oracle():
+    for args in ((31, 24, 42, 4, 4, 4, 312, 128, 4), (31, 24, 42, 4, 4, 4, 312, 128, 64),
+                 (31, 24, 42, 1, 4, 3, 312, 128, 4), (31, 24, 42, 1, 2, 2, 312, 128, 4),
+                 (5, 7, 9, 4, 4, 4, 3, 70, 64)):
+        got = _lib.svdq_cube_geometry(*args)
+        want = DQ.cube_geometry(*args)
+        for g, w in zip(got, want):
+            assert np.array_equal(g, w), args
+
+
+def test_divisor_aligned_and_schedule_match_oracle(lib):
+    for dims in ((31, 24, 42), (37, 15, 27), (32, 24, 42), (30, 20, 12), (1, 1, 1), (0, 5, 7),
+                 (64, 60, 49)):
+        for req in ((4, 4, 4), (2, 2, 2), (1, 1, 1), (8, 3, 5)):
+            assert _lib.svdq_cube_divisor_aligned(*dims, *req) == \
+                DQ.divisor_aligned_edges(*dims, *req), (dims, req)
+    sched = [(0, 4, 4, 4), (10, 2, 4, 4), (30, 2, 2, 2)]
+    for step in (0, 1, 9, 10, 11, 29, 30, 49, 10 ** 6):
+        assert _lib.svdq_cube_schedule(sched, step) == DQ.schedule_edges(sched, step)
+    for bad in ([(1, 2, 2, 2)], [(0, 2, 2, 2), (0, 4, 4, 4)], [(0, 2, 0, 2)]):
+        with pytest.raises(_lib.SvdqError):
+            _lib.svdq_cube_schedule(bad, 0)
+    with pytest.raises(_lib.SvdqError):
+        _lib.svdq_cube_schedule(sched, -1)
+    e = (ctypes.c_int64 * 3)()
+    assert lib.svdq_cube_divisor_aligned(4, 4, 4, 0, 1, 1, ctypes.cast(e, ctypes.c_void_p)) == INVALID
+
+
+def _check_groups(ptr, gp):
+    sizes = np.diff(ptr)
+    assert gp[0] == 0 and gp[-1] == len(sizes) and np.all(np.diff(gp) > 0)
+    for a, b in zip(gp[:-1], gp[1:]):
+        rows = sizes[a:b].sum()
+        assert rows <= 64 and b - a <= 16
+        if b < len(sizes):                         # greedy: the next cube would not fit
+            assert rows + sizes[b] > 64 or b - a == 16
+
+
+def test_cube_groups_pack_greedily():
+    for args in ((31, 24, 42, 2, 2, 2, 312, 128, 4), (31, 24, 42, 4, 4, 4, 312, 128, 64),
+                 (31, 24, 42, 1, 4, 3, 312, 128, 4), (5, 7, 9, 1, 1, 1, 3, 2, 1)):
+        _, ptr, _ = DQ.cube_geometry(*args)
+        _check_groups(ptr, _lib.svdq_cube_groups(ptr))
+    # a caller's CSR with a 64-row cube and a 65-row cube
+    ok = np.array([0, 3, 67, 70], np.int32)
+    _check_groups(ok, _lib.svdq_cube_groups(ok))
+    assert _lib.svdq_cube_groups(ok).tolist() == [0, 1, 2, 3]
+    with pytest.raises(_lib.SvdqError):
+        _lib.svdq_cube_groups(np.array([0, 3, 68, 70], np.int32))
+    with pytest.raises(_lib.SvdqError):
+        _lib.svdq_cube_groups(np.array([0, 3, 3, 7], np.int32))      # an empty cube

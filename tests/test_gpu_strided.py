@@ -101,14 +101,9 @@ def test_padded_leading_dimension_deltaquant(L):
     D_ref = OG.lowrank_down(xhat, down)
 
     Xd = _padded(X)
-    nc = len(ptr) - 1
-    u8 = torch.uint8
-    out = dict(cc=torch.empty(nc, K, dtype=u8, device="cuda"), cs=torch.empty(nc, device="cuda"),
-               dc=torch.empty(M, K // 2, dtype=u8, device="cuda"),
-               dsc=torch.empty(M, K // 16, dtype=u8, device="cuda"),
-               gd=torch.empty(1, device="cuda"), D=torch.empty(M, r, device="cuda"))
-    L.delta_quantize_activation(Xd, dev(lam), dev(np.array([amax], np.float32)), dev(ptr),
-                                dev(crow), nc, dev_bf16(down), out)
+    geo = L.cube_geometry(T, H, Wg, 2, 2, 2, nt, na, 4)
+    out = L.delta_quantize_activation(Xd, dev(lam), dev(np.array([amax], np.float32)), geo,
+                                      dev_bf16(down))
     torch.cuda.synchronize()
     assert np.array_equal(out["cc"].cpu().numpy(), cc)
     assert np.array_equal(out["cs"].cpu().numpy(), cs)

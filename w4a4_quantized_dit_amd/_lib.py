@@ -49,9 +49,13 @@ _SIGS = {
                                       _c_p, _c_p, _c_p, _c_p, _i64, _c_p, _c_p, _c_p, _i64,
                                       _c_p]),
     "svdq_cube_geometry": (ctypes.c_int, [_i64] * 9 + [_c_p, _c_p, _c_p, _c_p]),
+    "svdq_cube_divisor_aligned": (ctypes.c_int, [_i64] * 6 + [_c_p]),
+    "svdq_cube_schedule": (ctypes.c_int, [_c_p, _i64, _i64, _c_p]),
+    "svdq_cube_groups": (ctypes.c_int, [_c_p, _i64, _c_p, _c_p]),
+    "svdq_delta_workspace_bytes": (_i64, [_i64, _i64]),
     "svdq_delta_quant_act": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p,
-                                            _i64, _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _c_p,
-                                            _c_p, _c_p, _c_p]),
+                                            _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p,
+                                            _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
     "svdq_gemm_core": (ctypes.c_int, [_i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                       _c_p]),
     "svdq_score_modal_rel_l2": (ctypes.c_int, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _i64, _i64,
@@ -340,23 +344,60 @@ def svdq_cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d):
     return r2c, ptr, rows
 
 
-def svdq_delta_quant_act(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, lora_down, r,
-                         core_codes, core_scale, delta_codes, delta_scales, g_delta, D,
-                         sat_count=None, stream=None):
-    """DeltaQuant activations: FP8 cube-mean core + NVFP4 delta + D."""
+def svdq_cube_divisor_aligned(T, H, W, ct, ch, cw):
+    """Host: divisor-aligned cube edges (ct', ch', cw')."""
+    out = (ctypes.c_int64 * 3)()
+    _check(load().svdq_cube_divisor_aligned(T, H, W, ct, ch, cw, ctypes.cast(out, _c_p)))
+    return tuple(out)
+
+
+def svdq_cube_schedule(table, step):
+    """Host: cube edges of `step` under a schedule of (first_step, ct, ch, cw) rows."""
+    rows = [int(v) for row in table for v in row]
+    arr = (ctypes.c_int64 * max(1, len(rows)))(*rows)
+    out = (ctypes.c_int64 * 3)()
+    _check(load().svdq_cube_schedule(ctypes.cast(arr, _c_p), len(rows) // 4, int(step),
+                                     ctypes.cast(out, _c_p)))
+    return tuple(out)
+
+
+def svdq_cube_groups(cube_ptr):
+    """Host: work groups of the DeltaQuant activation kernel for a host CSR cube_ptr (numpy
+    int32 [n_cubes + 1]); returns group_ptr (numpy int32 [n_groups + 1])."""
+    import numpy as np
+    cp = np.ascontiguousarray(cube_ptr, dtype=np.int32)
+    nc = len(cp) - 1
+    n = ctypes.c_int64(0)
+    gp = np.zeros(nc + 1, np.int32)
+    _check(load().svdq_cube_groups(cp.ctypes.data, nc, gp.ctypes.data,
+                                   ctypes.cast(ctypes.pointer(n), _c_p)))
+    return gp[:n.value + 1].copy()
+
+
+def svdq_delta_workspace_bytes(n_cubes, K):
+    return int(load().svdq_delta_workspace_bytes(int(n_cubes), int(K)))
+
+
+def svdq_delta_quant_act(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, group_ptr, lora_down,
+                         r, core_codes, core_scale, delta_codes, delta_scales, g_delta, D,
+                         sat_count, workspace, stream=None):
+    """DeltaQuant activations: FP8 cube-mean core + NVFP4 delta + D; group_ptr from
+    svdq_cube_groups (device int32), workspace uint8 (svdq_delta_workspace_bytes)."""
     torch = _torch()
     M, K = X.shape
     _check(load().svdq_delta_quant_act(
         _ptr(X, _bf16(), "X", rows=True), M, K, _ld(X), _ptr(lam, torch.float32, "lambda", K),
         _ptr(act_amax, torch.float32, "act_amax", 1), _ptr(cube_ptr, torch.int32, "cube_ptr"),
         _ptr(cube_rows, torch.int32, "cube_rows", M), int(n_cubes),
+        _ptr(group_ptr, torch.int32, "group_ptr"), group_ptr.numel() - 1,
         _ptr(lora_down if r else None, _bf16(), "lora_down", r * K), int(r),
         _ptr(core_codes, torch.uint8, "core_codes", n_cubes * K),
         _ptr(core_scale, torch.float32, "core_scale", n_cubes),
         _ptr(delta_codes, torch.uint8, "delta_codes", M * K // 2),
         _ptr(delta_scales, torch.uint8, "delta_scales", M * K // 16),
         _ptr(g_delta, torch.float32, "g_delta", 1), _ptr(D if r else None, torch.float32, "D", M * r),
-        _ptr(sat_count, (torch.int32,), "sat_count", 1), _stream(stream)))
+        _ptr(sat_count, (torch.int32,), "sat_count", 1),
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 
 def svdq_gemm_core(n_cubes, N, K, core_codes, core_scale, w_codes, w_scales, g_w, core_out,

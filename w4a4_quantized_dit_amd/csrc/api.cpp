@@ -14,6 +14,9 @@ int64_t cube_count(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch, int6
 void cube_geometry_fill(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch, int64_t cw,
                         int64_t n_text, int64_t n_audio, int64_t c1, int32_t* row_to_cube,
                         int32_t* cube_ptr, int32_t* cube_rows);
+int64_t divisor_edge(int64_t n, int64_t e);
+int64_t cube_groups(const int32_t* cube_ptr, int64_t n_cubes, int64_t max_rows,
+                    int64_t max_cubes, int32_t* group_ptr);
 }  // namespace svdq
 
 namespace {
@@ -410,8 +413,8 @@ svdq_status svdq_cube_geometry(int64_t T, int64_t H, int64_t W, int64_t ct, int6
     return fail(SVDQ_INVALID_ARG, "%s: sizes must be non-negative", fn);
   if (ct < 1 || ch < 1 || cw < 1 || cube1d < 1)
     return fail(SVDQ_INVALID_ARG, "%s: cube sizes must be >= 1", fn);
-  if (ct * ch * cw > 16 || cube1d > 16)
-    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: cubes of more than 16 rows are not supported", fn);
+  if (ct > 64 || ch > 64 || cw > 64 || ct * ch * cw > 64 || cube1d > 64)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: cubes of more than 64 rows are not supported", fn);
   const int64_t M = n_text + T * H * W + n_audio;
   if (M < 1 || M > INT32_MAX) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: bad row count", fn);
   *n_cubes = svdq::cube_count(T, H, W, ct, ch, cw, n_text, n_audio, cube1d);
@@ -422,32 +425,99 @@ svdq_status svdq_cube_geometry(int64_t T, int64_t H, int64_t W, int64_t ct, int6
   return ok();
 }
 
+svdq_status svdq_cube_divisor_aligned(int64_t T, int64_t H, int64_t W, int64_t ct, int64_t ch,
+                                      int64_t cw, int64_t* edges) {
+  const char* fn = "svdq_cube_divisor_aligned";
+  REQUIRE_PTR(edges);
+  if (T < 0 || H < 0 || W < 0) return fail(SVDQ_INVALID_ARG, "%s: sizes must be non-negative", fn);
+  if (ct < 1 || ch < 1 || cw < 1) return fail(SVDQ_INVALID_ARG, "%s: edges must be >= 1", fn);
+  edges[0] = svdq::divisor_edge(T, ct);
+  edges[1] = svdq::divisor_edge(H, ch);
+  edges[2] = svdq::divisor_edge(W, cw);
+  return ok();
+}
+
+svdq_status svdq_cube_schedule(const int64_t* table, int64_t n_entries, int64_t step,
+                               int64_t* edges) {
+  const char* fn = "svdq_cube_schedule";
+  REQUIRE_PTR(table); REQUIRE_PTR(edges);
+  if (n_entries < 1 || table[0] != 0)
+    return fail(SVDQ_INVALID_ARG, "%s: the schedule must start at step 0", fn);
+  if (step < 0) return fail(SVDQ_INVALID_ARG, "%s: step=%lld is negative", fn, (long long)step);
+  int64_t pick = 0;
+  for (int64_t i = 0; i < n_entries; ++i) {
+    const int64_t* e = table + 4 * i;
+    if (i > 0 && e[0] <= table[4 * (i - 1)])
+      return fail(SVDQ_INVALID_ARG, "%s: first steps must increase (entry %lld)", fn,
+                  (long long)i);
+    if (e[1] < 1 || e[2] < 1 || e[3] < 1)
+      return fail(SVDQ_INVALID_ARG, "%s: edges of entry %lld must be >= 1", fn, (long long)i);
+    if (e[0] <= step) pick = i;
+  }
+  edges[0] = table[4 * pick + 1];
+  edges[1] = table[4 * pick + 2];
+  edges[2] = table[4 * pick + 3];
+  return ok();
+}
+
+svdq_status svdq_cube_groups(const int32_t* cube_ptr, int64_t n_cubes, int32_t* group_ptr,
+                             int64_t* n_groups) {
+  const char* fn = "svdq_cube_groups";
+  REQUIRE_PTR(cube_ptr); REQUIRE_PTR(n_groups);
+  if (n_cubes < 1) return fail(SVDQ_INVALID_ARG, "%s: n_cubes must be >= 1", fn);
+  if (cube_ptr[0] != 0) return fail(SVDQ_INVALID_ARG, "%s: cube_ptr[0] must be 0", fn);
+  const int64_t g = svdq::cube_groups(cube_ptr, n_cubes, svdq::kDeltaGroupRows,
+                                      svdq::kDeltaGroupCubes, nullptr);
+  if (g < 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE,
+                "%s: every cube must hold between 1 and %lld rows", fn,
+                (long long)svdq::kDeltaGroupRows);
+  *n_groups = g;
+  if (group_ptr) svdq::cube_groups(cube_ptr, n_cubes, svdq::kDeltaGroupRows,
+                                   svdq::kDeltaGroupCubes, group_ptr);
+  return ok();
+}
+
+int64_t svdq_delta_workspace_bytes(int64_t n_cubes, int64_t K) {
+  if (n_cubes < 1 || K < 1) return -1;
+  return svdq::delta_workspace_bytes(n_cubes, K);
+}
+
 svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                  const float* lambda, const float* act_amax,
                                  const int32_t* cube_ptr, const int32_t* cube_rows,
-                                 int64_t n_cubes, const uint16_t* lora_down, int64_t r,
-                                 uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
-                                 uint8_t* delta_scales, float* g_delta, float* D,
-                                 uint32_t* sat_count, svdq_stream_t stream) {
+                                 int64_t n_cubes, const int32_t* group_ptr, int64_t n_groups,
+                                 const uint16_t* lora_down, int64_t r, uint8_t* core_codes,
+                                 float* core_scale, uint8_t* delta_codes, uint8_t* delta_scales,
+                                 float* g_delta, float* D, uint32_t* sat_count, void* workspace,
+                                 int64_t workspace_bytes, svdq_stream_t stream) {
   const char* fn = "svdq_delta_quant_act";
   REQUIRE_PTR(X); REQUIRE_PTR(act_amax); REQUIRE_PTR(cube_ptr); REQUIRE_PTR(cube_rows);
-  REQUIRE_PTR(core_codes); REQUIRE_PTR(core_scale); REQUIRE_PTR(delta_codes);
-  REQUIRE_PTR(delta_scales); REQUIRE_PTR(g_delta);
+  REQUIRE_PTR(group_ptr); REQUIRE_PTR(core_codes); REQUIRE_PTR(core_scale);
+  REQUIRE_PTR(delta_codes); REQUIRE_PTR(delta_scales); REQUIRE_PTR(g_delta);
+  REQUIRE_PTR(workspace);
   REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(core_codes); REQUIRE_ALIGNED(delta_codes);
-  REQUIRE_ALIGNED(lora_down); REQUIRE_ALIGNED(D);
-  if (M < 1) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must be >= 1", fn, (long long)M);
+  REQUIRE_ALIGNED(delta_scales); REQUIRE_ALIGNED(lora_down); REQUIRE_ALIGNED(D);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+  if (M < 1 || M > INT32_MAX)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must lie in [1, 2^31)", fn, (long long)M);
   if (n_cubes < 1 || n_cubes > M) return fail(SVDQ_INVALID_ARG, "%s: bad n_cubes", fn);
+  if (n_groups < 1 || n_groups > n_cubes)
+    return fail(SVDQ_INVALID_ARG, "%s: n_groups=%lld must lie in [1, n_cubes]", fn,
+                (long long)n_groups);
   TRY(check_k(fn, K));
   TRY(check_ld(fn, "ldx", ldx, K));
-  TRY(check_act_ld(fn, ldx));
   TRY(check_rank(fn, r));
   if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
-  if ((size_t)K * sizeof(float) > 64 * 1024 || svdq::delta_act_lds_bytes(K) > 160 * 1024)
-    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: K=%lld exceeds 16384", fn, (long long)K);
+  const int64_t need = svdq::delta_workspace_bytes(n_cubes, K);
+  if (workspace_bytes < need)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace of %lld bytes, needs %lld", fn,
+                (long long)workspace_bytes, (long long)need);
   return hip_result(svdq::launch_delta_quant_act(X, M, K, ldx, lambda, act_amax, cube_ptr,
-                                                 cube_rows, n_cubes, lora_down, r, core_codes,
-                                                 core_scale, delta_codes, delta_scales, g_delta,
-                                                 D, sat_count,
+                                                 cube_rows, group_ptr, n_groups, lora_down, r,
+                                                 core_codes, core_scale, delta_codes,
+                                                 delta_scales, g_delta, D, sat_count, workspace,
                                                  reinterpret_cast<hipStream_t>(stream)),
                     fn);
 }

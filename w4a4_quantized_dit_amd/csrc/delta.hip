@@ -1,18 +1,25 @@
 // DeltaQuant variant ("DeltaQuant on MiniMax-H3": a cube of tokens is represented by one core
 // plus per-token deltas; the delta's NVFP4 tensor scale comes from the bound
 // |x − core| ≤ 2·max|x| ("The activation scale bound held"); the core branch stays on a 16-bit
-// path ("Deviations from the paper")).
+// path ("Deviations from the paper, and one replication")).
 //
-// k_delta_act: one workgroup per cube (at most 16 member rows), walking K in chunks of 256
-// channels.  Per chunk the members' smoothed rows X̂ = X · 1/λ are staged in LDS (fp32, read from
-// HBM once, coalesced, the next chunk's loads in flight while this one is processed); a thread
-// per channel sums the members in ascending row order in fp32 and divides by the member count
-// (the core row stays in LDS); a thread per member row and 16-channel block quantises the delta
-// X̂ − core (unquantised core) to NVFP4 with tensor amax 2·act_amax.  After the last chunk the
-// core row's amax gives its E4M3 scale amax/448 and the core codes are written from LDS.  The
-// workgroup needs about 4·K + 18 KB of LDS, so several cubes are resident per CU.
-// The members' low-rank activations D = bf16(X̂)·L1 come from the activation kernel's D-only
-// mode, whose 64-row tiles share each slice of L1 across many rows.
+// k_delta_act: one pass over X.  A workgroup (4 waves) owns a group of consecutive cubes of at
+// most 64 member rows and 16 cubes (packed on the host), gathers the members' rows through the
+// CSR and walks K in chunks of 128 channels:
+//   1. the rows' chunk (bf16) and the matching slice of L1 go from registers (loaded two chunks
+//      ahead) into LDS;
+//   2. a thread per (cube, channel pair) sums the cube's smoothed members X̂ = X · 1/λ in
+//      ascending row order in fp32 and divides by the member count; the core chunk stays in
+//      LDS for step 3 and goes to the caller's fp32 workspace for step 4, and the thread keeps
+//      the running |core| maximum of its channels;
+//   3. lane (row = lane % 16 of its wave, q = lane / 16) takes its row's 32 channels
+//      [32q, 32q + 32): the delta X̂ − core (unquantised core) is quantised to NVFP4 with the
+//      static tensor amax 2·act_amax (two whole blocks per lane, lane-local block maxima), and
+//      bf16(X̂) feeds v_mfma_f32_16x16x32_bf16 against the L1 slice for D = bf16(X̂)·L1 at rank r;
+//   4. after the last chunk every cube's amax gives its E4M3 scale amax/448, and each lane
+//      re-reads the fp32 core values it wrote in step 2 and encodes them.
+// The core's scale needs the whole row's maximum before any code can be written, which is why
+// the fp32 core makes one round trip through the workspace; X itself is read exactly once.
 // k_gemm_core: core_out[c, n] = s_c · g_w · Σ_k e4m3(core[c, k]) · (c_w·s_w)[n, k] on fp16 MFMA:
 // E4M3 values and the NVFP4 weight products are exact in fp16.
 #include "device.h"
@@ -22,149 +29,258 @@ namespace svdq {
 
 namespace {
 
-constexpr int kThreads = 256;       // k_gemm_core and k_delta_act: 4 waves
-constexpr int kMaxCube = 16;        // rows per cube (svdq_cube_geometry guarantees it)
-constexpr int kChunk = 256;         // channels per chunk
-constexpr int kStashPitch = kChunk + 4;  // floats per staged row (padded)
+constexpr int kThreads = 256;              // k_gemm_core and k_delta_act: 4 waves
+constexpr int kDRows = 64;                 // rows of a cube group (4 waves x 16)
+constexpr int kDCubes = 16;                // cubes of a cube group
+constexpr int kDChunk = 128;               // channels per chunk
+constexpr int kDPitch = kDChunk + 8;       // bf16 per staged row: 272 B, conflict-free 16-B reads
+constexpr int kDCorePitch = kDChunk + 4;   // fp32 per core row in LDS
 
-__global__ __launch_bounds__(kThreads) void k_delta_act(
+template <int NT>
+__global__ __launch_bounds__(kThreads, 2) void k_delta_act(
     const uint16_t* __restrict__ X, int64_t M, int64_t K, int64_t ldx,
     const float* __restrict__ lambda, const float* __restrict__ act_amax,
     const int32_t* __restrict__ cube_ptr, const int32_t* __restrict__ cube_rows,
+    const int32_t* __restrict__ group_ptr, const uint16_t* __restrict__ down, int r,
     uint8_t* __restrict__ core_codes, float* __restrict__ core_scale,
     uint8_t* __restrict__ dcodes, uint8_t* __restrict__ dscales, float* __restrict__ g_delta,
-    uint32_t* __restrict__ sat) {
-  extern __shared__ __attribute__((aligned(16))) float s_dyn[];
-  float* s_core = s_dyn;                          // [K] fp32 core row
-  float* s_x = s_dyn + K;                         // [kMaxCube][kStashPitch] staged X̂ chunk
-  float* s_inv = s_x + kMaxCube * kStashPitch;    // [2][kChunk] 1/λ of this and the next chunk
-  __shared__ int s_rows[kMaxCube];
-  __shared__ float s_red[kThreads / 64];
+    float* __restrict__ D, uint32_t* __restrict__ sat, float* __restrict__ core32) {
+  constexpr int NTc = NT > 0 ? NT : 1;
+  __shared__ __attribute__((aligned(16))) uint16_t s_x[kDRows * kDPitch];
+  __shared__ __attribute__((aligned(16))) uint16_t s_l[NTc * 16 * kDPitch];
+  __shared__ __attribute__((aligned(16))) float s_core[kDCubes * kDCorePitch];
+  __shared__ __attribute__((aligned(16))) float s_inv[2][kDChunk];
+  __shared__ int s_row[kDRows], s_slot[kDRows], s_first[kDCubes], s_cnt[kDCubes];
   const int tid = threadIdx.x, wave = tid >> 6, lane = tid & 63;
-  const int64_t c = blockIdx.x;
-  const int p0 = cube_ptr[c];
-  int n = cube_ptr[c + 1] - p0;
-  n = n < 0 ? 0 : (n > kMaxCube ? kMaxCube : n);
-  if (n == 0) return;  // uniform: nothing to do for an empty cube
-  if (tid < n) {
-    const int m = cube_rows[p0 + tid];
-    s_rows[tid] = m < 0 ? 0 : (m < M ? m : (int)M - 1);
+  const int c0 = group_ptr[blockIdx.x], ncub = group_ptr[blockIdx.x + 1] - c0;
+  const int p0 = cube_ptr[c0];
+  const int nrows = ncub > 0 ? cube_ptr[c0 + ncub] - p0 : 0;
+  if (ncub < 1 || ncub > kDCubes || nrows < 1 || nrows > kDRows) {
+    // not a group the host packer makes: its cubes get a NaN scale (uniform exit)
+    if (tid < ncub && tid < kDCubes) core_scale[c0 + tid] = __builtin_nanf("");
+    return;
   }
-  s_inv[tid] = lambda ? 1.0f / lambda[tid] : 1.0f;
+  if (tid < ncub) {
+    s_first[tid] = cube_ptr[c0 + tid] - p0;
+    s_cnt[tid] = cube_ptr[c0 + tid + 1] - cube_ptr[c0 + tid];
+  }
+  if (tid < kDRows) {
+    int m = cube_rows[p0 + (tid < nrows ? tid : nrows - 1)];
+    s_row[tid] = m < 0 ? 0 : (m < M ? m : (int)M - 1);  // rows past the group repeat its last
+  }
   const float amax_t = 2.0f * act_amax[0];
   const float g = amax_t == 0.0f ? 1.0f : amax_t / 2688.0f;
   const float d6 = 6.0f * g;
-  if (c == 0 && tid == 0) g_delta[0] = g;
+  if (blockIdx.x == 0 && tid == 0) g_delta[0] = g;
   __syncthreads();
-
-  // staging: rows tid/32 and tid/32 + 8, channels 8·(tid%32) .. +8 (rows past n repeat row n-1
-  // and are not stored)
-  const int g8 = tid & 31;
-  const uint16_t* xg[2];
-#pragma unroll
-  for (int t = 0; t < 2; ++t) {
-    const int row = (tid >> 5) + 8 * t;
-    xg[t] = X + (int64_t)s_rows[row < n ? row : n - 1] * ldx + 8 * g8;
+  if (tid < kDRows) {
+    int sl = -1;
+    if (tid < nrows)
+      for (int s = 0; s < ncub; ++s)
+        if (tid >= s_first[s]) sl = s;
+    s_slot[tid] = sl;
   }
-  u32x4_t xr[2];
+
+  // staging roles: X piece i of this thread is row (tid / 16) + 16 i, 16 bytes at 8·(tid % 16);
+  // L1 piece u is rank (tid + 256 u) / 16 at the same channels (ranks past r are zeroed)
+  const int seg = tid & 15;
+  const uint16_t* xp[4];
 #pragma unroll
-  for (int t = 0; t < 2; ++t) xr[t] = *reinterpret_cast<const u32x4_t*>(xg[t]);
-  const int dl_row = tid >> 4, dl_blk = tid & 15;  // delta: one 16-channel block of one row
-  float core_amax = 0.0f;
+  for (int i = 0; i < 4; ++i) xp[i] = X + (int64_t)s_row[(tid >> 4) + 16 * i] * ldx + 8 * seg;
+  const uint16_t* lp[NTc];
+#pragma unroll
+  for (int u = 0; u < NTc; ++u) {
+    const int n = (tid >> 4) + 16 * u;
+    lp[u] = down + (int64_t)(n < r ? n : (r > 0 ? r - 1 : 0)) * K + 8 * seg;
+  }
+  const int64_t nchunk = K / kDChunk;
+  auto load_x = [&](u32x4_t (&v)[4], int64_t c) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+      v[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xp[i] + c * kDChunk));
+  };
+  auto load_l = [&](u32x4_t (&v)[NTc], int64_t c) {
+#pragma unroll
+    for (int u = 0; u < NT; ++u) v[u] = *reinterpret_cast<const u32x4_t*>(lp[u] + c * kDChunk);
+  };
+  // 1/λ of chunk c into s_inv[c & 1]: threads 0..127, one channel each
+  auto stage_inv = [&](float lam_v, int64_t c) {
+    if (tid < kDChunk) s_inv[c & 1][tid] = lambda ? 1.0f / lam_v : 1.0f;
+  };
+  auto load_lam = [&](int64_t c) {
+    return (lambda && tid < kDChunk && c < nchunk) ? lambda[c * kDChunk + tid] : 1.0f;
+  };
+
+  // lane roles in steps 3 and 4
+  const int rl = lane & 15, q = lane >> 4;
+  const int srow = 16 * wave + rl;
+  const bool valid = srow < nrows;
+  const int64_t grow = s_row[srow];
+  f32x4_t acc[NTc];
+#pragma unroll
+  for (int j = 0; j < NTc; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
+  float camax[4] = {0.f, 0.f, 0.f, 0.f};
   uint32_t nsat = 0;
 
-  for (int64_t k0 = 0; k0 < K; k0 += kChunk) {
-    const int buf = (int)((k0 / kChunk) & 1);
-    const float* inv = s_inv + buf * kChunk;
-    // 1. stage X̂ (fp32) and issue the next chunk's loads
+  auto chunk = [&](int64_t c, u32x4_t (&xcur)[4], u32x4_t (&lr)[NTc], float& lam_next) {
+    const int64_t k0 = c * kDChunk;
+    // 1. registers -> LDS
 #pragma unroll
-    for (int t = 0; t < 2; ++t) {
-      const int row = (tid >> 5) + 8 * t;
-      if (row < n) {
-        const f32x4_t i0 = *reinterpret_cast<const f32x4_t*>(inv + 8 * g8);
-        const f32x4_t i1 = *reinterpret_cast<const f32x4_t*>(inv + 8 * g8 + 4);
-        const u32x4_t v = xr[t];
-        f32x4_t x0, x1;
-        x0[0] = bf16_lo(v[0]) * i0[0]; x0[1] = bf16_hi(v[0]) * i0[1];
-        x0[2] = bf16_lo(v[1]) * i0[2]; x0[3] = bf16_hi(v[1]) * i0[3];
-        x1[0] = bf16_lo(v[2]) * i1[0]; x1[1] = bf16_hi(v[2]) * i1[1];
-        x1[2] = bf16_lo(v[3]) * i1[2]; x1[3] = bf16_hi(v[3]) * i1[3];
-        float* dst = s_x + row * kStashPitch + 8 * g8;
-        *reinterpret_cast<f32x4_t*>(dst) = x0;
-        *reinterpret_cast<f32x4_t*>(dst + 4) = x1;
+    for (int i = 0; i < 4; ++i)
+      *reinterpret_cast<u32x4_t*>(&s_x[((tid >> 4) + 16 * i) * kDPitch + 8 * seg]) = xcur[i];
+#pragma unroll
+    for (int u = 0; u < NT; ++u) {
+      const int n = (tid >> 4) + 16 * u;
+      *reinterpret_cast<u32x4_t*>(&s_l[n * kDPitch + 8 * seg]) =
+          n < r ? lr[u] : u32x4_t{0u, 0u, 0u, 0u};
+    }
+    __syncthreads();
+    // the next chunks' loads: X two chunks ahead (into the registers just stored), L1 and λ one
+    if (c + 2 < nchunk) load_x(xcur, c + 2);
+    if (c + 1 < nchunk) load_l(lr, c + 1);
+    const float lam_c1 = lam_next;
+    lam_next = load_lam(c + 2);
+    // 2. core chunk: (cube slot, channel pair) items, ascending fp32 sum over the members
+    const float* inv = s_inv[c & 1];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      const int item = tid + kThreads * i;
+      const int sl = item >> 6, pr = item & 63;
+      if (sl < ncub) {
+        const int f = s_first[sl], n = s_cnt[sl];
+        const float i0 = inv[2 * pr], i1 = inv[2 * pr + 1];
+        float a0 = 0.0f, a1 = 0.0f;
+        for (int j = 0; j < n; ++j) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(&s_x[(f + j) * kDPitch + 2 * pr]);
+          a0 += bf16_lo(w) * i0;
+          a1 += bf16_hi(w) * i1;
+        }
+        const float v0 = a0 / (float)n, v1 = a1 / (float)n;
+        *reinterpret_cast<float2*>(&s_core[sl * kDCorePitch + 2 * pr]) = float2{v0, v1};
+        *reinterpret_cast<float2*>(core32 + (int64_t)(c0 + sl) * K + k0 + 2 * pr) =
+            float2{v0, v1};
+        camax[i] = fmaxf(camax[i], fmaxf(fabsf(v0), fabsf(v1)));
       }
     }
-    if (k0 + kChunk < K) {
-#pragma unroll
-      for (int t = 0; t < 2; ++t)
-        xr[t] = *reinterpret_cast<const u32x4_t*>(xg[t] + k0 + kChunk);
-      s_inv[(buf ^ 1) * kChunk + tid] = lambda ? 1.0f / lambda[k0 + kChunk + tid] : 1.0f;
-    }
+    stage_inv(lam_c1, c + 1);   // s_inv[(c + 1) & 1] was last read before the previous barrier
     __syncthreads();
-
-    // 2. core channel: ascending fp32 sum over the members, divided by the count
+    // 3. delta NVFP4 blocks and the low-rank MFMA of the lane's row and 32 channels
     {
-      float acc = 0.0f;
-      for (int j = 0; j < n; ++j) acc += s_x[j * kStashPitch + tid];
-      const float cv = acc / (float)n;
-      s_core[k0 + tid] = cv;
-      core_amax = fmaxf(core_amax, fabsf(cv));
-    }
-    __syncthreads();
-
-    // 3. delta block: X̂ − core, NVFP4 with the static tensor amax
-    if (dl_row < n) {
-      const float* xrow = s_x + dl_row * kStashPitch + 16 * dl_blk;
-      const float* crow = s_core + k0 + 16 * dl_blk;
-      float d[16];
-      float a = 0.0f;
+      const int sl = s_slot[srow] < 0 ? 0 : s_slot[srow];
+      float x[32];
 #pragma unroll
-      for (int e4 = 0; e4 < 4; ++e4) {
-        const f32x4_t xq = *reinterpret_cast<const f32x4_t*>(xrow + 4 * e4);
-        const f32x4_t cq = *reinterpret_cast<const f32x4_t*>(crow + 4 * e4);
+      for (int i = 0; i < 4; ++i) {
+        const u32x4_t v = *reinterpret_cast<const u32x4_t*>(&s_x[srow * kDPitch + 32 * q + 8 * i]);
+        const f32x4_t ia = *reinterpret_cast<const f32x4_t*>(inv + 32 * q + 8 * i);
+        const f32x4_t ib = *reinterpret_cast<const f32x4_t*>(inv + 32 * q + 8 * i + 4);
+        x[8 * i + 0] = bf16_lo(v[0]) * ia[0]; x[8 * i + 1] = bf16_hi(v[0]) * ia[1];
+        x[8 * i + 2] = bf16_lo(v[1]) * ia[2]; x[8 * i + 3] = bf16_hi(v[1]) * ia[3];
+        x[8 * i + 4] = bf16_lo(v[2]) * ib[0]; x[8 * i + 5] = bf16_hi(v[2]) * ib[1];
+        x[8 * i + 6] = bf16_lo(v[3]) * ib[2]; x[8 * i + 7] = bf16_hi(v[3]) * ib[3];
+      }
+      const float* cr = s_core + sl * kDCorePitch + 32 * q;
+      uint32_t cw[4];
+      uint32_t sb = 0;
 #pragma unroll
-        for (int e = 0; e < 4; ++e) {
-          d[4 * e4 + e] = xq[e] - cq[e];
-          a = fmaxf(a, fabsf(d[4 * e4 + e]));
+      for (int b = 0; b < 2; ++b) {
+        float d[16];
+        float a = 0.0f;
+#pragma unroll
+        for (int e4 = 0; e4 < 4; ++e4) {
+          const f32x4_t cq = *reinterpret_cast<const f32x4_t*>(cr + 16 * b + 4 * e4);
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            d[4 * e4 + e] = x[16 * b + 4 * e4 + e] - cq[e];
+            a = fmaxf(a, fabsf(d[4 * e4 + e]));
+          }
+        }
+        nsat += (valid && a > amax_t) ? 1u : 0u;
+        float sinv;
+        sb |= nvfp4_block_scale(a, g, d6, &sinv) << (8 * b);
+        float y[16];
+#pragma unroll
+        for (int e = 0; e < 16; ++e) y[e] = d[e] * sinv;
+        cw[2 * b] = e2m1_pack8(y);
+        cw[2 * b + 1] = e2m1_pack8(y + 8);
+      }
+      if (valid) {
+        const int64_t kq = k0 + 32 * q;
+        *reinterpret_cast<u32x4_t*>(dcodes + grow * (K / 2) + kq / 2) =
+            u32x4_t{cw[0], cw[1], cw[2], cw[3]};
+        *reinterpret_cast<uint16_t*>(dscales + grow * (K / 16) + kq / 16) = (uint16_t)sb;
+      }
+      if (NT > 0) {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+          u32x4_t av;
+          av[0] = pack_bf16x2(x[8 * t + 0], x[8 * t + 1]);
+          av[1] = pack_bf16x2(x[8 * t + 2], x[8 * t + 3]);
+          av[2] = pack_bf16x2(x[8 * t + 4], x[8 * t + 5]);
+          av[3] = pack_bf16x2(x[8 * t + 6], x[8 * t + 7]);
+          const bf16x8_t a_op = __builtin_bit_cast(bf16x8_t, av);
+#pragma unroll
+          for (int j = 0; j < NT; ++j) {
+            const u32x4_t bv = *reinterpret_cast<const u32x4_t*>(
+                &s_l[(16 * j + rl) * kDPitch + 32 * q + 8 * t]);
+            acc[j] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                a_op, __builtin_bit_cast(bf16x8_t, bv), acc[j], 0, 0, 0);
+          }
         }
       }
-      nsat += a > amax_t ? 1u : 0u;
-      float sinv;
-      const uint32_t scode = nvfp4_block_scale(a, g, d6, &sinv);
-      float y[16];
-#pragma unroll
-      for (int e = 0; e < 16; ++e) y[e] = d[e] * sinv;
-      const int64_t m = s_rows[dl_row];
-      const int64_t kq = k0 + 16 * dl_blk;
-      *reinterpret_cast<uint2*>(dcodes + m * (K / 2) + kq / 2) =
-          uint2{e2m1_pack8(y), e2m1_pack8(y + 8)};
-      dscales[m * (K / 16) + kq / 16] = (uint8_t)scode;
     }
-    __syncthreads();  // the staged rows are rewritten by the next chunk
+    __syncthreads();  // the staging buffers are rewritten by the next chunk
+  };
+
+  // prologue: chunks 0 and 1 of X, chunk 0 of L1, 1/λ of chunk 0; λ of chunk 1 in flight
+  u32x4_t xa[4], xb[4], lr[NTc];
+  load_x(xa, 0);
+  if (nchunk > 1) load_x(xb, 1);
+  load_l(lr, 0);
+  stage_inv(load_lam(0), 0);
+  float lam_next = load_lam(1);
+  __syncthreads();
+  for (int64_t c = 0; c < nchunk; c += 2) {
+    chunk(c, xa, lr, lam_next);
+    if (c + 1 < nchunk) chunk(c + 1, xb, lr, lam_next);
   }
 
-  // core scale and FP8 codes: sign | E4M3(|core| · 1/s_c), 8 channels per thread per step
-  for (int off = 32; off > 0; off >>= 1) core_amax = fmaxf(core_amax, __shfl_xor(core_amax, off));
-  if (lane == 0) s_red[wave] = core_amax;
-  __syncthreads();
-  const float am = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-  const float sc = am / 448.0f;
-  const float inv_c = sc != 0.0f ? 1.0f / sc : 0.0f;
-  if (tid == 0) core_scale[c] = sc;
-  for (int64_t k = 8 * tid; k < K; k += 8 * kThreads) {
-    uint32_t lo = 0, hi = 0;
+  // D rows (16x16 output: lane holds rank column 16j + rl and staged rows 4q .. 4q + 3)
+  if (NT > 0) {
 #pragma unroll
-    for (int e = 0; e < 8; ++e) {
-      const float v = s_core[k + e];
-      float val;
-      const uint32_t code =
-          e4m3_encode_pos(fabsf(v) * inv_c, &val) | (__builtin_signbit(v) ? 0x80u : 0u);
-      if (e < 4)
-        lo |= code << (8 * e);
-      else
-        hi |= code << (8 * (e - 4));
+    for (int j = 0; j < NT; ++j) {
+      const int n = 16 * j + rl;
+      if (n < r) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+          const int sr = 16 * wave + 4 * q + i;
+          if (sr < nrows) D[(int64_t)s_row[sr] * r + n] = acc[j][i];
+        }
+      }
     }
-    *reinterpret_cast<uint2*>(core_codes + c * K + k) = uint2{lo, hi};
+  }
+  // 4. core scales and FP8 codes: wave w owns cube slots w, w + 4, ...; lane l re-reads the
+  // channel pair 2l, 2l + 1 of every chunk that it wrote in step 2 (its own stores, visible
+  // to it after the barrier's fence)
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const int sl = wave + 4 * i;
+    if (sl < ncub) {
+      float am = camax[i];
+      for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+      const float sc = am / 448.0f;
+      const float inv_c = sc != 0.0f ? 1.0f / sc : 0.0f;
+      const int64_t c = c0 + sl;
+      if (lane == 0) core_scale[c] = sc;
+      for (int64_t k = 2 * lane; k < K; k += kDChunk) {
+        const float2 v = *reinterpret_cast<const float2*>(core32 + c * K + k);
+        float val;
+        const uint32_t e0 =
+            e4m3_encode_pos(fabsf(v.x) * inv_c, &val) | (__builtin_signbit(v.x) ? 0x80u : 0u);
+        const uint32_t e1 =
+            e4m3_encode_pos(fabsf(v.y) * inv_c, &val) | (__builtin_signbit(v.y) ? 0x80u : 0u);
+        *reinterpret_cast<uint16_t*>(core_codes + c * K + k) = (uint16_t)(e0 | (e1 << 8));
+      }
+    }
   }
   if (sat) {
     for (int off = 32; off > 0; off >>= 1) nsat += __shfl_xor(nsat, off);
@@ -291,27 +407,39 @@ __global__ __launch_bounds__(kThreads) void k_gemm_core(
 
 }  // namespace
 
-size_t delta_act_lds_bytes(int64_t K) {
-  return ((size_t)K + kMaxCube * kStashPitch + 2 * kChunk) * sizeof(float);
-}
+int64_t delta_workspace_bytes(int64_t n_cubes, int64_t K) { return n_cubes * K * 4; }
 
 hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* lambda, const float* act_amax,
                                   const int32_t* cube_ptr, const int32_t* cube_rows,
-                                  int64_t n_cubes, const uint16_t* down, int64_t r,
-                                  uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
-                                  uint8_t* delta_scales, float* g_delta, float* D, uint32_t* sat,
+                                  const int32_t* group_ptr, int64_t n_groups,
+                                  const uint16_t* down, int64_t r, uint8_t* core_codes,
+                                  float* core_scale, uint8_t* delta_codes, uint8_t* delta_scales,
+                                  float* g_delta, float* D, uint32_t* sat, void* workspace,
                                   hipStream_t s) {
-  const size_t lds = delta_act_lds_bytes(K);
-  hipError_t e = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_delta_act),
-                                     hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds);
-  if (e != hipSuccess) return e;
-  k_delta_act<<<dim3((unsigned)n_cubes), dim3(kThreads), lds, s>>>(
-      X, M, K, ldx, lambda, act_amax, cube_ptr, cube_rows, core_codes, core_scale, delta_codes,
-      delta_scales, g_delta, sat);
-  e = hipGetLastError();
-  if (e != hipSuccess || r == 0) return e;
-  return launch_lowrank_down(X, M, K, ldx, lambda, down, r, D, s);
+  const int nt = (int)((r + 15) / 16);
+  float* core32 = reinterpret_cast<float*>(workspace);
+#define SVDQ_DELTA_CASE(NTV)                                                                 \
+  case NTV:                                                                                  \
+    k_delta_act<NTV><<<dim3((unsigned)n_groups), dim3(kThreads), 0, s>>>(                    \
+        X, M, K, ldx, lambda, act_amax, cube_ptr, cube_rows, group_ptr, down, (int)r,        \
+        core_codes, core_scale, delta_codes, delta_scales, g_delta, D, sat, core32);         \
+    break;
+  switch (nt) {
+    SVDQ_DELTA_CASE(0)
+    SVDQ_DELTA_CASE(1)
+    SVDQ_DELTA_CASE(2)
+    SVDQ_DELTA_CASE(3)
+    SVDQ_DELTA_CASE(4)
+    SVDQ_DELTA_CASE(5)
+    SVDQ_DELTA_CASE(6)
+    SVDQ_DELTA_CASE(7)
+    SVDQ_DELTA_CASE(8)
+    default:
+      return hipErrorInvalidValue;
+  }
+#undef SVDQ_DELTA_CASE
+  return hipGetLastError();
 }
 
 hipError_t launch_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,

@@ -51,10 +51,6 @@ hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, in
 // needs at most 160 KB.
 size_t quant_act_lds_bytes(int64_t K, int64_t r);
 
-// D = bf16(X·1/λ)·lora_downᵀ alone (fp32 [M, r], r >= 1), with the activation kernel's tiling.
-hipError_t launch_lowrank_down(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
-                               const float* lambda, const uint16_t* down, int64_t r, float* D,
-                               hipStream_t s);
 
 hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const void* a_scales, const float* g_a, const uint8_t* w_codes,
@@ -62,16 +58,20 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
                        const uint16_t* up, int64_t r, const float* core_out,
                        const int32_t* row_to_cube, uint16_t* Y, int64_t ldy, hipStream_t s);
 
+// DeltaQuant activations over host-packed cube groups (group_ptr: cube index of each group's first
+// cube, n_groups + 1 entries; at most 64 rows and 16 cubes per group); workspace: fp32
+// [n_cubes, K] (delta_workspace_bytes).
+int64_t delta_workspace_bytes(int64_t n_cubes, int64_t K);
+constexpr int64_t kDeltaGroupRows = 64;
+constexpr int64_t kDeltaGroupCubes = 16;
 hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* lambda, const float* act_amax,
                                   const int32_t* cube_ptr, const int32_t* cube_rows,
-                                  int64_t n_cubes, const uint16_t* down, int64_t r,
-                                  uint8_t* core_codes, float* core_scale, uint8_t* delta_codes,
-                                  uint8_t* delta_scales, float* g_delta, float* D,
-                                  uint32_t* sat, hipStream_t s);
-
-// Dynamic LDS bytes of the DeltaQuant activation kernel for K channels.
-size_t delta_act_lds_bytes(int64_t K);
+                                  const int32_t* group_ptr, int64_t n_groups,
+                                  const uint16_t* down, int64_t r, uint8_t* core_codes,
+                                  float* core_scale, uint8_t* delta_codes, uint8_t* delta_scales,
+                                  float* g_delta, float* D, uint32_t* sat, void* workspace,
+                                  hipStream_t s);
 
 hipError_t launch_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,
                             const float* core_scale, const uint8_t* w_codes,

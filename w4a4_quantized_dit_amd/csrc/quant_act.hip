@@ -12,8 +12,8 @@
 // v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry channels
 // k0 + 64q + 8t .. +8, and the block stages the matching slice of L1 (lora_down[:, k0:k0+256])
 // in LDS once for its waves.  The next chunk's global loads are issued before the current
-// chunk is processed, and two K groups of waves walk alternate chunks of the same rows.  FMT 2 computes D alone (the DeltaQuant path quantises its deltas in its
-// own kernel and takes D from here); FMT 3 / 4 are the MX formats (E8M0 scale per 32 with E2M1
+// chunk is processed, and two K groups of waves walk alternate chunks of the same rows.
+// FMT 0 is NVFP4, FMT 1 int4-g64; FMT 3 / 4 are the MX formats (E8M0 scale per 32 with E2M1
 // / E4M3 elements: "MiniMax-H3 — MXFP8 (weight-quantized, vLLM-Omni native layout)", section
 // "Quant format"), each lane's 64 channels being two whole blocks.
 #include "device.h"
@@ -401,15 +401,6 @@ size_t quant_act_lds_bytes(int64_t K, int64_t r) {
   const size_t dyn = inv_lds_bytes(K);
   const bool split = nt <= 2 && static_lds(nt, 2) + dyn <= 160 * 1024;
   return static_lds(nt, split ? 2 : 1) + dyn;
-}
-
-hipError_t launch_lowrank_down(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
-                               const float* lambda, const uint16_t* down, int64_t r, float* D,
-                               hipStream_t s) {
-  const int nt = (int)((r + 15) / 16);
-  const dim3 grid((unsigned)((M + kRowsPerBlock - 1) / kRowsPerBlock));
-  return dispatch<2>(nt, grid, inv_lds_bytes(K), s, X, M, K, ldx, lambda, nullptr, down,
-                     (int)r, nullptr, nullptr, nullptr, 0, D, nullptr);
 }
 
 hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, int64_t ldx,

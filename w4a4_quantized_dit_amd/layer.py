@@ -174,26 +174,45 @@ def quantize_activation(X, lam, act_amax, lora_down, fmt=NVFP4, sat_count=None):
     return codes, scales, g, D
 
 
-def delta_quantize_activation(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, lora_down,
-                              out=None, sat_count=None):
-    """DeltaQuant activations of X [M, K] for the device CSR cube_ptr / cube_rows: dict with
-    core codes cc [n_cubes, K], core scales cs [n_cubes], delta codes dc [M, K/2] and scales
-    dsc [M, K/16], g_delta gd [1] and D [M, r] (fp32).  Pass `out` to reuse its tensors."""
+def cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d, device="cuda"):
+    """DeltaQuant geometry on the host, uploaded: dict(row_to_cube, cube_ptr, cube_rows,
+    group_ptr (device int32), n_cubes, host (the numpy arrays))."""
+    import numpy as np
+    torch = _torch()
+    r2c, ptr, rows = _lib.svdq_cube_geometry(T, H, W, ct, ch, cw, n_text, n_audio, cube1d)
+    gp = _lib.svdq_cube_groups(ptr)
+    up = lambda a: torch.from_numpy(np.ascontiguousarray(a)).to(device)  # noqa: E731
+    return dict(row_to_cube=up(r2c), cube_ptr=up(ptr), cube_rows=up(rows), group_ptr=up(gp),
+                n_cubes=len(ptr) - 1, host=dict(row_to_cube=r2c, cube_ptr=ptr, cube_rows=rows,
+                                                group_ptr=gp))
+
+
+def delta_quantize_activation(X, lam, act_amax, geo, lora_down, out=None, sat_count=None):
+    """DeltaQuant activations of X [M, K] for the cube geometry `geo` (cube_geometry, or a dict
+    with device cube_ptr / cube_rows / group_ptr and n_cubes): dict with core codes cc
+    [n_cubes, K], core scales cs [n_cubes], delta codes dc [M, K/2] and scales dsc [M, K/16],
+    g_delta gd [1], D [M, r] (fp32) and the fp32 core workspace ws.  Pass `out` to reuse its
+    tensors."""
     torch = _torch()
     M, K = X.shape
     r = 0 if lora_down is None else lora_down.shape[0]
     dev = X.device
     u8 = torch.uint8
+    nc = geo["n_cubes"]
     if out is None:
-        out = dict(cc=torch.empty(n_cubes, K, dtype=u8, device=dev),
-                   cs=torch.empty(n_cubes, device=dev),
+        nbytes = _lib.svdq_delta_workspace_bytes(nc, K)
+        ws = torch.empty(nbytes + 256, dtype=u8, device=dev)
+        off = (-ws.data_ptr()) % 256
+        out = dict(cc=torch.empty(nc, K, dtype=u8, device=dev),
+                   cs=torch.empty(nc, device=dev),
                    dc=torch.empty(M, K // 2, dtype=u8, device=dev),
                    dsc=torch.empty(M, K // 16, dtype=u8, device=dev),
                    gd=torch.empty(1, device=dev),
-                   D=torch.empty(M, r, device=dev) if r else None)
-    _lib.svdq_delta_quant_act(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, lora_down, r,
-                              out["cc"], out["cs"], out["dc"], out["dsc"], out["gd"],
-                              out.get("D"), sat_count)
+                   D=torch.empty(M, r, device=dev) if r else None,
+                   ws=ws[off:off + nbytes])
+    _lib.svdq_delta_quant_act(X, lam, act_amax, geo["cube_ptr"], geo["cube_rows"], nc,
+                              geo["group_ptr"], lora_down, r, out["cc"], out["cs"], out["dc"],
+                              out["dsc"], out["gd"], out.get("D"), sat_count, out["ws"])
     return out
 
 
