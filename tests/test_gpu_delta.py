@@ -52,7 +52,8 @@ def _delta_case(cfg, geo, seed=0, csr=None):
     down, up = OS.lowrank_factors(W, lam, r) if r else (np.zeros((0, cfg["K"]), np.uint16),
                                                         np.zeros((cfg["N"], 0), np.uint16))
     if csr is None:
-        r2c, ptr, crow = DQ.cube_geometry(T, H, Wd, *geo, cfg["n_text"], cfg["n_audio"])
+        ct, ch, cw, c1 = geo
+        r2c, ptr, crow = DQ.cube_geometry(T, H, Wd, ct, ch, cw, cfg["n_text"], cfg["n_audio"], c1)
     else:
         r2c, ptr, crow = csr
     xhat = OC.smooth(X, lam)
@@ -70,7 +71,8 @@ def _gpu_delta(L, o, cfg, geo, csr=None):
     from w4a4_quantized_dit_amd import _lib
     T, H, Wg = cfg["grid"]
     if csr is None:
-        g = L.cube_geometry(T, H, Wg, *geo, cfg["n_text"], cfg["n_audio"])
+        ct, ch, cw, c1 = geo
+        g = L.cube_geometry(T, H, Wg, ct, ch, cw, cfg["n_text"], cfg["n_audio"], c1)
         host = (g["host"]["row_to_cube"], g["host"]["cube_ptr"], g["host"]["cube_rows"])
     else:
         r2c, ptr, crow = csr
@@ -191,3 +193,32 @@ def test_deltaquant_full_size(L, geo):
     rows = _full_rows(cfg)
     print(f"[delta] {geo}: {len(rows)} sampled rows rel-L2 {_compare_delta(o, g, rows):.2e}",
           flush=True)
+
+
+def test_exact_deltaquant_layer_is_bit_exact(L):
+    """The exactly quantisable DeltaQuant layer (every scale a power of two or E4M3-exact, every
+    value on its grid, every fp32 partial sum exact): the GPU's core GEMM plus delta GEMM must
+    give bf16(X·Wᵀ) bit for bit."""
+    torch = torch_mod()
+    from w4a4_quantized_dit_amd import _lib
+    from tests.test_oracle_delta_score import _exact_deltaquant_case
+    from oracle.formats import bf16_bits_to_f32, bf16_rne
+    Xb, Wb, seg, geo = _exact_deltaquant_case(P=128, K=256, N=256, seed=4)
+    M, K, N = Xb.shape[0], 256, 256
+    want = bf16_rne(bf16_bits_to_f32(Xb).astype(np.float64)
+                    @ bf16_bits_to_f32(Wb).astype(np.float64).T)
+    Xd, Wd = dev_bf16(Xb), dev_bf16(Wb)
+    cal = L.calibrate(Xd, seg, Wd, 0)
+    pw = L.prepare_weight(Wd, cal["lambda"], None, None, 0)
+    g = L.cube_geometry(*geo)
+    assert g["n_cubes"] == 129
+    dq = L.delta_quantize_activation(Xd, cal["lambda"], cal["act_amax"], g, None)
+    co = torch.empty(g["n_cubes"], N, device="cuda")
+    _lib.svdq_gemm_core(g["n_cubes"], N, K, dq["cc"], dq["cs"], pw.codes, pw.scales, pw.g, co)
+    Y = torch.empty(M, N, dtype=torch.bfloat16, device="cuda")
+    _lib.svdq_w4a4_gemm(0, M, N, K, dq["dc"], dq["dsc"], dq["gd"], pw.codes, pw.scales, pw.g,
+                        None, None, 0, Y, core_out=co, row_to_cube=g["row_to_cube"])
+    torch.cuda.synchronize()
+    assert cal["act_amax"].cpu().numpy()[0] == 1344.0
+    assert dq["gd"].cpu().numpy()[0] == 1.0
+    assert np.array_equal(host_bits(Y), want)

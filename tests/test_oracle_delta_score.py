@@ -186,3 +186,69 @@ def test_synthetic_recipe_counts_correlation_and_chunks():
     n = np.bincount(grp, minlength=4)
     assert n.tolist() == [655, 4096, 262, 4096]
     assert len(np.unique(rows[grp == 1])) == 4096
+
+
+def _exact_deltaquant_case(P=6, K=64, N=32, seed=0):
+    """A DeltaQuant layer whose every quantisation step is exact (power-of-two and E4M3-exact
+    scales, values on their grids): pair cubes x = c ± d with core c on the E4M3 grid (row amax
+    448, so s_c = 1) and delta d on the E2M1 grid (every non-zero block holds a ±6; with
+    act_amax = 1344 the delta tensor scale is 2·1344/2688 = 1); one 1-row cube [1344, 0, ...]
+    sets act_amax; the weight has tensor scale 2^-10 (amax 6·448·2^-10) and E4M3-exact block
+    scales (a ±6 code in every block).  Returns (X bits, W bits, seg, geometry args)."""
+    rng = np.random.default_rng(seed)
+    e2m1 = np.array([0, 0.5, 1, 1.5, 2, 3, 4, 6])
+    rows = []
+    for _ in range(P):
+        c = rng.choice([0.0, 1, 2, 4, 8, 16], K) * rng.choice([-1.0, 1.0], K)
+        d = rng.choice(e2m1, K) * rng.choice([-1.0, 1.0], K)
+        j = rng.integers(K)                       # the channel of the core's 448
+        c[j], d[j] = 448.0 * rng.choice([-1.0, 1.0]), 0.0
+        for b in range(K // 16):                  # a ±6 in every delta block, away from j
+            i = 16 * b + rng.integers(16)
+            i = i if i != j else 16 * b + (i - 16 * b + 1) % 16
+            d[i] = 6.0 * rng.choice([-1.0, 1.0])
+        rows += [c + d, c - d]
+    big = np.zeros(K)
+    big[0] = 1344.0
+    rows.append(big)
+    X = np.array(rows)
+    W = np.zeros((N, K))
+    for n in range(N):
+        for b in range(K // 16):
+            s = 448.0 if (n == 0 and b == 0) else 256.0
+            codes = rng.choice(e2m1, 16) * rng.choice([-1.0, 1.0], 16)
+            codes[rng.integers(16)] = 6.0
+            W[n, 16 * b:16 * b + 16] = codes * s * 2.0 ** -10
+    Xb, Wb = synth.gen.to_bf16_bits(X), synth.gen.to_bf16_bits(W)
+    assert np.array_equal(F.bf16_bits_to_f32(Xb), X) and np.array_equal(F.bf16_bits_to_f32(Wb), W)
+    M = 2 * P + 1
+    # video grid 1 x 1 x 2P with 1x1x2 cubes (the pairs), then one audio row in a 1-D cube
+    return Xb, Wb, (0, 0, 2 * P, M), (1, 1, 2 * P, 1, 1, 2, 0, 1, 1)
+
+
+def test_exact_deltaquant_layer_reproduces_x_w_transpose():
+    """With every step exact, core term + delta term = X̂·W'ᵀ exactly: a dropped core term, a
+    wrong cube index, a sign error in the delta or a mis-scaled core would all break it."""
+    from oracle import layer as OL
+    Xb, Wb, seg, geo = _exact_deltaquant_case()
+    ax, aw, lam, amax = C.calibrate(Xb, seg, Wb, 0)
+    assert np.all(lam == 1) and amax == F32(1344)
+    r2c, ptr, crow = DQ.cube_geometry(*geo)
+    assert np.array_equal(np.diff(ptr), [2] * 6 + [1])
+    xhat = C.smooth(Xb, lam)
+    core = DQ.cube_core(xhat, ptr, crow)
+    cc, cs = DQ.core_fp8(core)
+    assert np.all(cs[:-1] == 1) and cs[-1] == 3
+    d = DQ.delta_rows(xhat, core, r2c)
+    dc, dsc, gd, sat = DQ.delta_quantize(d, amax)
+    assert gd == 1 and sat == 0
+    assert np.array_equal(Q.nvfp4_dequantize(dc, dsc, gd), d.astype(np.float64))
+    wt = OL.prepare_weight(Wb, lam, np.zeros((0, 64), np.uint16), np.zeros((32, 0), np.uint16),
+                           "nvfp4")
+    assert wt["g"] == F32(2.0 ** -10)
+    co = DQ.core_out_f64(cc, cs, wt["codes"], wt["scales"], wt["g"])
+    y64, y = DQ.delta_linear(co, r2c, dc, dsc, gd, wt["codes"], wt["scales"], wt["g"],
+                             np.zeros((13, 0)), np.zeros((32, 0), np.uint16))
+    want = F.bf16_bits_to_f32(Xb).astype(np.float64) @ F.bf16_bits_to_f32(Wb).astype(np.float64).T
+    assert np.array_equal(y64, want)
+    assert np.array_equal(y, F.bf16_rne(want))
