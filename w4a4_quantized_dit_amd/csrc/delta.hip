@@ -150,8 +150,22 @@ __global__ __launch_bounds__(kThreads, 2) void k_delta_act(
         const int f = s_first[sl], n = s_cnt[sl];
         const float i0 = inv[2 * pr], i1 = inv[2 * pr + 1];
         float a0 = 0.0f, a1 = 0.0f;
-        for (int j = 0; j < n; ++j) {
-          const uint32_t w = *reinterpret_cast<const uint32_t*>(&s_x[(f + j) * kDPitch + 2 * pr]);
+        const uint16_t* xc = &s_x[f * kDPitch + 2 * pr];
+        int j = 0;
+        // four members' reads issued together, then added in ascending order
+        for (; j + 4 <= n; j += 4) {
+          uint32_t w[4];
+#pragma unroll
+          for (int u = 0; u < 4; ++u)
+            w[u] = *reinterpret_cast<const uint32_t*>(xc + (j + u) * kDPitch);
+#pragma unroll
+          for (int u = 0; u < 4; ++u) {
+            a0 += bf16_lo(w[u]) * i0;
+            a1 += bf16_hi(w[u]) * i1;
+          }
+        }
+        for (; j < n; ++j) {
+          const uint32_t w = *reinterpret_cast<const uint32_t*>(xc + j * kDPitch);
           a0 += bf16_lo(w) * i0;
           a1 += bf16_hi(w) * i1;
         }
@@ -271,14 +285,26 @@ __global__ __launch_bounds__(kThreads, 2) void k_delta_act(
       const float inv_c = sc != 0.0f ? 1.0f / sc : 0.0f;
       const int64_t c = c0 + sl;
       if (lane == 0) core_scale[c] = sc;
-      for (int64_t k = 2 * lane; k < K; k += kDChunk) {
-        const float2 v = *reinterpret_cast<const float2*>(core32 + c * K + k);
-        float val;
-        const uint32_t e0 =
-            e4m3_encode_pos(fabsf(v.x) * inv_c, &val) | (__builtin_signbit(v.x) ? 0x80u : 0u);
-        const uint32_t e1 =
-            e4m3_encode_pos(fabsf(v.y) * inv_c, &val) | (__builtin_signbit(v.y) ? 0x80u : 0u);
-        *reinterpret_cast<uint16_t*>(core_codes + c * K + k) = (uint16_t)(e0 | (e1 << 8));
+      // kBatch chunks' values in flight per lane (K is a multiple of 256: whole batches of 2)
+      constexpr int kBatch = 8;
+      for (int64_t kb = 0; kb < K; kb += kBatch * kDChunk) {
+        float2 v[kBatch];
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int64_t k = kb + b * kDChunk + 2 * lane;
+          v[b] = k < K ? *reinterpret_cast<const float2*>(core32 + c * K + k) : float2{0.f, 0.f};
+        }
+#pragma unroll
+        for (int b = 0; b < kBatch; ++b) {
+          const int64_t k = kb + b * kDChunk + 2 * lane;
+          float val;
+          const uint32_t e0 = e4m3_encode_pos(fabsf(v[b].x) * inv_c, &val) |
+                              (__builtin_signbit(v[b].x) ? 0x80u : 0u);
+          const uint32_t e1 = e4m3_encode_pos(fabsf(v[b].y) * inv_c, &val) |
+                              (__builtin_signbit(v[b].y) ? 0x80u : 0u);
+          if (k < K)
+            *reinterpret_cast<uint16_t*>(core_codes + c * K + k) = (uint16_t)(e0 | (e1 << 8));
+        }
       }
     }
   }

@@ -95,24 +95,40 @@ __device__ __forceinline__ void gemm_store(const f32x16_t (&acc)[FM][FN], float 
                                            const int32_t* __restrict__ row_to_cube,
                                            uint16_t* __restrict__ Y, int64_t ldy) {
   static_assert(FN >= 2, "the piece swizzle needs at least 8 pieces per staged row");
+  static_assert(FM == 4, "the cube-id lookup covers 128 rows per wave");
   constexpr int kRowB = FN * 64;
   const int r32 = lane & 31, h = lane >> 5;
+  // DeltaQuant core term: the cube ids of the wave's 128 rows are fetched once (lane l holds
+  // rows l and 64 + l) and handed out with lane permutes; each row tile's 16·FN core values
+  // are then requested together, so the gather costs a few memory round trips per tile
+  // instead of one dependent pair of loads per row.
+  int cube_lo = 0, cube_hi = 0;
+  if (core_out) {
+    int64_t r0 = m_base + lane, r1 = m_base + 64 + lane;
+    cube_lo = row_to_cube[r0 < M ? r0 : M - 1];
+    cube_hi = row_to_cube[r1 < M ? r1 : M - 1];
+  }
 #pragma unroll
   for (int i = 0; i < FM; ++i) {
+    float cv[16][FN];
+    if (core_out) {
+#pragma unroll
+      for (int e = 0; e < 16; ++e) {
+        const int row = 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
+        const int cube = __shfl(i < 2 ? cube_lo : cube_hi, row & 63);
+        const float* co = core_out + (int64_t)cube * N + n_base;
+#pragma unroll
+        for (int j = 0; j < FN; ++j) cv[e][j] = co[32 * j + r32];
+      }
+    }
 #pragma unroll
     for (int e = 0; e < 16; ++e) {
       const int row = 32 * i + (e >> 2) * 8 + 4 * h + (e & 3);
-      const float* co = nullptr;
-      if (core_out) {
-        int64_t grow = m_base + row;
-        grow = grow < M ? grow : M - 1;
-        co = core_out + (int64_t)row_to_cube[grow] * N + n_base;
-      }
 #pragma unroll
       for (int j = 0; j < FN; ++j) {
         const int col = 32 * j + r32;
         float v = acc[i][j][e] * gsc;
-        if (co) v += co[col];
+        if (core_out) v += cv[e][j];
         const int piece = (col >> 3) ^ (((row >> 2) & 1) << 2);
         *reinterpret_cast<uint16_t*>(region + row * kRowB + piece * 16 + (col & 7) * 2) =
             f32_to_bf16(v);
