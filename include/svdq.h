@@ -367,6 +367,27 @@ svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_
                                  int64_t workspace_bytes, svdq_stream_t stream);
 
 /*
+ * svdq_delta_quant_act without a workspace, for callers that cannot allocate device memory
+ * (code under HIP graph capture, tight serving loops, harnesses that forbid hipMalloc).  Same
+ * arguments, results and validation as svdq_delta_quant_act; the fp32 cores go through a
+ * static device buffer of 128 MiB inside the library instead of a caller workspace (each GPU
+ * the library runs on holds one until the process ends).  n_cubes·K·4 above 128 MiB:
+ * SVDQ_UNSUPPORTED_SHAPE.  The buffer needs no clearing (every element the kernel reads it
+ * wrote earlier in the same call), but all calls on one GPU share it: calls that overlap on a
+ * GPU (on different streams, or from several threads without ordering) race and give
+ * undefined results.  Allocates nothing.
+ */
+svdq_status svdq_delta_quant_act_noalloc(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                         const float* lambda, const float* act_amax,
+                                         const int32_t* cube_ptr, const int32_t* cube_rows,
+                                         int64_t n_cubes, const int32_t* group_ptr,
+                                         int64_t n_groups, const uint16_t* lora_down, int64_t r,
+                                         uint8_t* core_codes, float* core_scale,
+                                         uint8_t* delta_codes, uint8_t* delta_scales,
+                                         float* g_delta, float* D, uint32_t* sat_count,
+                                         svdq_stream_t stream);
+
+/*
  * DeltaQuant core GEMM on a 16-bit path ("DeltaQuant on MiniMax-H3", section "Deviations from
  * the paper": the core branch does not take the FP4 scaled dot):
  *   core_out[c, n] = s_c · g_w · Σ_k e4m3(core_codes[c, k]) · (c_w·s_w)[n, k]     fp32 [n_cubes, N]

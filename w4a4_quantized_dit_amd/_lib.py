@@ -56,6 +56,9 @@ _SIGS = {
     "svdq_delta_quant_act": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p,
                                             _i64, _c_p, _i64, _c_p, _i64, _c_p, _c_p, _c_p,
                                             _c_p, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
+    "svdq_delta_quant_act_noalloc": (ctypes.c_int, [_c_p, _i64, _i64, _i64, _c_p, _c_p, _c_p,
+                                                    _c_p, _i64, _c_p, _i64, _c_p, _i64, _c_p,
+                                                    _c_p, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p]),
     "svdq_gemm_core": (ctypes.c_int, [_i64, _i64, _i64, _c_p, _c_p, _c_p, _c_p, _c_p, _c_p,
                                       _c_p]),
     "svdq_score_modal_rel_l2": (ctypes.c_int, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _i64, _i64,
@@ -398,6 +401,26 @@ def svdq_delta_quant_act(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, group_p
         _ptr(g_delta, torch.float32, "g_delta", 1), _ptr(D if r else None, torch.float32, "D", M * r),
         _ptr(sat_count, (torch.int32,), "sat_count", 1),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def svdq_delta_quant_act_noalloc(X, lam, act_amax, cube_ptr, cube_rows, n_cubes, group_ptr,
+                                 lora_down, r, core_codes, core_scale, delta_codes, delta_scales,
+                                 g_delta, D, sat_count=None, stream=None):
+    """svdq_delta_quant_act through the library's static scratch (no workspace argument)."""
+    torch = _torch()
+    M, K = X.shape
+    _check(load().svdq_delta_quant_act_noalloc(
+        _ptr(X, _bf16(), "X", rows=True), M, K, _ld(X), _ptr(lam, torch.float32, "lambda", K),
+        _ptr(act_amax, torch.float32, "act_amax", 1), _ptr(cube_ptr, torch.int32, "cube_ptr"),
+        _ptr(cube_rows, torch.int32, "cube_rows", M), int(n_cubes),
+        _ptr(group_ptr, torch.int32, "group_ptr"), group_ptr.numel() - 1,
+        _ptr(lora_down if r else None, _bf16(), "lora_down", r * K), int(r),
+        _ptr(core_codes, torch.uint8, "core_codes", n_cubes * K),
+        _ptr(core_scale, torch.float32, "core_scale", n_cubes),
+        _ptr(delta_codes, torch.uint8, "delta_codes", M * K // 2),
+        _ptr(delta_scales, torch.uint8, "delta_scales", M * K // 16),
+        _ptr(g_delta, torch.float32, "g_delta", 1), _ptr(D if r else None, torch.float32, "D", M * r),
+        _ptr(sat_count, (torch.int32,), "sat_count", 1), _stream(stream)))
 
 
 def svdq_gemm_core(n_cubes, N, K, core_codes, core_scale, w_codes, w_scales, g_w, core_out,

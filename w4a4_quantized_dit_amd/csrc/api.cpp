@@ -483,23 +483,22 @@ int64_t svdq_delta_workspace_bytes(int64_t n_cubes, int64_t K) {
   return svdq::delta_workspace_bytes(n_cubes, K);
 }
 
-svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
-                                 const float* lambda, const float* act_amax,
-                                 const int32_t* cube_ptr, const int32_t* cube_rows,
-                                 int64_t n_cubes, const int32_t* group_ptr, int64_t n_groups,
-                                 const uint16_t* lora_down, int64_t r, uint8_t* core_codes,
-                                 float* core_scale, uint8_t* delta_codes, uint8_t* delta_scales,
-                                 float* g_delta, float* D, uint32_t* sat_count, void* workspace,
-                                 int64_t workspace_bytes, svdq_stream_t stream) {
-  const char* fn = "svdq_delta_quant_act";
+}  // extern "C"
+
+namespace {
+
+// Validation shared by the DeltaQuant activation entry points (workspace checked by the caller).
+svdq_status check_delta(const char* fn, const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                        const float* act_amax, const int32_t* cube_ptr, const int32_t* cube_rows,
+                        int64_t n_cubes, const int32_t* group_ptr, int64_t n_groups,
+                        const uint16_t* lora_down, int64_t r, const uint8_t* core_codes,
+                        const float* core_scale, const uint8_t* delta_codes,
+                        const uint8_t* delta_scales, const float* g_delta, const float* D) {
   REQUIRE_PTR(X); REQUIRE_PTR(act_amax); REQUIRE_PTR(cube_ptr); REQUIRE_PTR(cube_rows);
   REQUIRE_PTR(group_ptr); REQUIRE_PTR(core_codes); REQUIRE_PTR(core_scale);
   REQUIRE_PTR(delta_codes); REQUIRE_PTR(delta_scales); REQUIRE_PTR(g_delta);
-  REQUIRE_PTR(workspace);
   REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(core_codes); REQUIRE_ALIGNED(delta_codes);
   REQUIRE_ALIGNED(delta_scales); REQUIRE_ALIGNED(lora_down); REQUIRE_ALIGNED(D);
-  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
-    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace must be 256-byte aligned", fn);
   if (M < 1 || M > INT32_MAX)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: M=%lld must lie in [1, 2^31)", fn, (long long)M);
   if (n_cubes < 1 || n_cubes > M) return fail(SVDQ_INVALID_ARG, "%s: bad n_cubes", fn);
@@ -510,6 +509,27 @@ svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_
   TRY(check_ld(fn, "ldx", ldx, K));
   TRY(check_rank(fn, r));
   if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(D); }
+  return SVDQ_OK;
+}
+
+}  // namespace
+
+extern "C" {
+
+svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                 const float* lambda, const float* act_amax,
+                                 const int32_t* cube_ptr, const int32_t* cube_rows,
+                                 int64_t n_cubes, const int32_t* group_ptr, int64_t n_groups,
+                                 const uint16_t* lora_down, int64_t r, uint8_t* core_codes,
+                                 float* core_scale, uint8_t* delta_codes, uint8_t* delta_scales,
+                                 float* g_delta, float* D, uint32_t* sat_count, void* workspace,
+                                 int64_t workspace_bytes, svdq_stream_t stream) {
+  const char* fn = "svdq_delta_quant_act";
+  TRY(check_delta(fn, X, M, K, ldx, act_amax, cube_ptr, cube_rows, n_cubes, group_ptr, n_groups,
+                  lora_down, r, core_codes, core_scale, delta_codes, delta_scales, g_delta, D));
+  REQUIRE_PTR(workspace);
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace must be 256-byte aligned", fn);
   const int64_t need = svdq::delta_workspace_bytes(n_cubes, K);
   if (workspace_bytes < need)
     return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace of %lld bytes, needs %lld", fn,
@@ -518,6 +538,36 @@ svdq_status svdq_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_
                                                  cube_rows, group_ptr, n_groups, lora_down, r,
                                                  core_codes, core_scale, delta_codes,
                                                  delta_scales, g_delta, D, sat_count, workspace,
+                                                 reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_delta_quant_act_noalloc(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
+                                         const float* lambda, const float* act_amax,
+                                         const int32_t* cube_ptr, const int32_t* cube_rows,
+                                         int64_t n_cubes, const int32_t* group_ptr,
+                                         int64_t n_groups, const uint16_t* lora_down, int64_t r,
+                                         uint8_t* core_codes, float* core_scale,
+                                         uint8_t* delta_codes, uint8_t* delta_scales,
+                                         float* g_delta, float* D, uint32_t* sat_count,
+                                         svdq_stream_t stream) {
+  const char* fn = "svdq_delta_quant_act_noalloc";
+  TRY(check_delta(fn, X, M, K, ldx, act_amax, cube_ptr, cube_rows, n_cubes, group_ptr, n_groups,
+                  lora_down, r, core_codes, core_scale, delta_codes, delta_scales, g_delta, D));
+  const int64_t need = svdq::delta_workspace_bytes(n_cubes, K);
+  if ((uint64_t)need > svdq::kDeltaScratchBytes)
+    return fail(SVDQ_UNSUPPORTED_SHAPE,
+                "%s: n_cubes=%lld x K=%lld needs %lld bytes of scratch, more than the %zu of the "
+                "static buffer (use svdq_delta_quant_act with a workspace)",
+                fn, (long long)n_cubes, (long long)K, (long long)need, svdq::kDeltaScratchBytes);
+  void* scratch_ptr = nullptr;
+  const hipError_t e = svdq::delta_scratch(&scratch_ptr);
+  if (e != hipSuccess)
+    return fail(SVDQ_HIP_ERROR, "%s: scratch address: %s", fn, hipGetErrorString(e));
+  return hip_result(svdq::launch_delta_quant_act(X, M, K, ldx, lambda, act_amax, cube_ptr,
+                                                 cube_rows, group_ptr, n_groups, lora_down, r,
+                                                 core_codes, core_scale, delta_codes,
+                                                 delta_scales, g_delta, D, sat_count, scratch_ptr,
                                                  reinterpret_cast<hipStream_t>(stream)),
                     fn);
 }

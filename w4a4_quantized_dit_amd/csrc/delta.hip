@@ -22,10 +22,17 @@
 // the fp32 core makes one round trip through the workspace; X itself is read exactly once.
 // k_gemm_core: core_out[c, n] = s_c · g_w · Σ_k e4m3(core[c, k]) · (c_w·s_w)[n, k] on fp16 MFMA:
 // E4M3 values and the NVFP4 weight products are exact in fp16.
+#include <mutex>
+
 #include "device.h"
 #include "launch.h"
 
 namespace svdq {
+
+// Scratch of the allocation-free DeltaQuant entry point: the fp32 cores of one call.  Each GPU
+// the library runs on holds its own copy until the process ends.  Host code never uses this
+// name as an address: the per-device address comes from hipGetSymbolAddress.
+static __device__ __align__(256) uint8_t scratch[kDeltaScratchBytes];
 
 namespace {
 
@@ -466,6 +473,29 @@ hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64
   }
 #undef SVDQ_DELTA_CASE
   return hipGetLastError();
+}
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
+}  // namespace
+
+hipError_t delta_scratch(void** ptr) {
+  int dev = 0;
+  hipError_t e = hipGetDevice(&dev);
+  if (e != hipSuccess) return e;
+  if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+  // once per device, with that device current
+  std::call_once(g_scratch_once[dev], [dev] {
+    void* p = nullptr;
+    g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    g_scratch_ptr[dev] = p;
+  });
+  if (g_scratch_err[dev] != hipSuccess) return g_scratch_err[dev];
+  *ptr = g_scratch_ptr[dev];
+  return hipSuccess;
 }
 
 hipError_t launch_gemm_core(int64_t n_cubes, int64_t N, int64_t K, const uint8_t* core_codes,

@@ -63,6 +63,10 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
 // [n_cubes, K] (delta_workspace_bytes).
 int64_t delta_workspace_bytes(int64_t n_cubes, int64_t K);
 constexpr int64_t kDeltaGroupRows = 64;
+// The allocation-free variant's static scratch (fp32 cores, bytes) and its device address on the
+// current device (looked up once per device).
+constexpr size_t kDeltaScratchBytes = (size_t)128 << 20;
+hipError_t delta_scratch(void** ptr);
 constexpr int64_t kDeltaGroupCubes = 16;
 hipError_t launch_delta_quant_act(const uint16_t* X, int64_t M, int64_t K, int64_t ldx,
                                   const float* lambda, const float* act_amax,
