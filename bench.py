@@ -16,11 +16,13 @@ per-modality scoring for each of λ = 1, all rows, video rows, text rows), the D
 cube-field layer (31x24x42 grid, K = N = 5120, rank 128) and the MX formats (MXFP4 W4A4, MXFP8
 W8A8) on the attention-projection shape.
 
-Timing: W warm-up steps, then exactly K timed steps between two synchronisations (the step
-time, and per-kernel means from HIP events on the launch stream); then a separate pass of
-`--stat-reps` steps gives each kernel's p10 / p50 / p90.  A plain dtype-narrowing copy that
-reads X (2 bytes per element) and writes half a byte per element — the activation kernel's byte
-mix — is timed the same way, as the measured bandwidth that kernel is compared against.
+Timing: untimed steps for `--settle-ms` of wall time (the GPU's clock ramps up over tens of
+milliseconds of load; without this the first timed steps run several per cent slower than
+the steady state), W warm-up steps, then exactly K timed steps between two synchronisations
+(the step time, and per-kernel means from HIP events on the launch stream); then a separate
+pass of `--stat-reps` steps gives each kernel's p10 / p50 / p90.  A plain streaming kernel
+(libsvdq_probe.so) that reads X and writes as many bytes as the activation kernel writes is
+timed the same way, as the measured bandwidth that kernel is compared against.
 `--copy-probe` runs a plain 1 GiB device copy whose hardware byte counters calibrate the
 per-kernel traffic figures.
 
@@ -254,25 +256,38 @@ def copy_probe(torch, nbytes=1 << 30, reps=3):
     print(json.dumps({"copy_probe_bytes_per_launch": nbytes, "launches": reps}), flush=True)
 
 
-def copy_mix_rate(torch, Xs, reps):
-    """Measured bandwidth of a plain device copy with the activation kernel's byte mix: X read
-    as int32 words (2 bytes per bf16 element) and narrowed to int8 (half a byte per element
-    written), rotating over the same copies of X.  Returns (GB/s, dict of ms percentiles)."""
+def copy_mix_rate(torch, Xs, write_bytes, reps):
+    """Measured bandwidth of a plain streaming copy with the activation kernel's byte mix: the
+    library's memory probe reads all of X (16-byte nontemporal loads) and writes `write_bytes`
+    (the kernel's codes, scales and D) in the same pass, rotating over the same copies of X.
+    Returns (GB/s of the median launch, dict of ms percentiles)."""
+    import ctypes
+    from w4a4_quantized_dit_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    fn = lib.svdq_probe_stream
+    fn.restype = ctypes.c_int
+    fn.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                   ctypes.c_void_p]
     M, K = Xs[0].shape
-    out = torch.empty(M, K // 2, dtype=torch.int8, device="cuda")
-    src = [x.view(torch.int32) for x in Xs]
+    rd = M * K * 2
+    wr = (write_bytes + 15) // 16 * 16
+    dst = torch.empty(max(wr, 16), dtype=torch.uint8, device="cuda")
+    s = torch.cuda.current_stream().cuda_stream
+
+    def launch(i):
+        if fn(Xs[i % len(Xs)].data_ptr(), rd, dst.data_ptr(), wr, s) != 0:
+            raise RuntimeError("memory probe launch failed")
     for i in range(3):
-        out.copy_(src[i % len(src)])
+        launch(i)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(reps + 1)]
     torch.cuda.synchronize()
     ev[0].record()
     for i in range(reps):
-        out.copy_(src[i % len(src)])
+        launch(i)
         ev[i + 1].record()
     torch.cuda.synchronize()
     ms = [ev[i].elapsed_time(ev[i + 1]) for i in range(reps)]
-    nbytes = M * K * 2 + M * K // 2
-    return nbytes / (np.median(ms) * 1e-3) / 1e9, percentiles(ms)
+    return (rd + wr) / (np.median(ms) * 1e-3) / 1e9, percentiles(ms)
 
 
 def to_dev(torch, bits):
@@ -446,9 +461,15 @@ def setup(torch, workload):
     return st
 
 
-def run_steps(torch, st, n, warm, record):
-    """Warm-up, then n steps; with `record`, HIP events around every launch.  Returns
-    (wall seconds of the n steps, {kernel name: [ms of every launch]})."""
+def run_steps(torch, st, n, warm, record, settle_s=0.0):
+    """Clock settling (untimed steps until `settle_s` seconds of them have run), `warm` warm-up
+    steps, then n steps; with `record`, HIP events around every launch.  Returns (wall seconds
+    of the n steps, {kernel name: [ms of every launch]}).
+
+    The GPU's power management slows the first milliseconds of work that follow an idle gap,
+    so all host-side preparation (event creation, garbage collection) happens while earlier
+    work is still queued, and the only idle moment before the measured steps is the
+    synchronisation that opens them."""
     names = [nm for nm, _ in st["steps"]]
     n_rot = len(st["Xs"])
     evs = None
@@ -460,13 +481,21 @@ def run_steps(torch, st, n, warm, record):
         for e in evs:
             for x in e:
                 x.record()
-        torch.cuda.synchronize()
-    for i in range(warm):
+
+    def one(i):
         for _, fn in st["steps"]:
             fn(st["Xs"][i % n_rot])
-    torch.cuda.synchronize()
+
+    t_settle = time.perf_counter()
+    i = 0
+    while time.perf_counter() - t_settle < settle_s:
+        one(i)         # no synchronisation: once the launch queue is full the host waits in it
+        i += 1
     gc.collect()
     gc.disable()           # no collector pause inside the measured region
+    for j in range(warm):
+        one(i + j)
+    torch.cuda.synchronize()
     t0 = time.perf_counter()
     for i in range(n):
         Xi = st["Xs"][i % n_rot]
@@ -499,6 +528,9 @@ def main():
                     help="steps of the separate pass that gives per-kernel p10/p50/p90 "
                          "(0: skip)")
     ap.add_argument("--workload", choices=sorted(WORKLOADS), default="attn")
+    ap.add_argument("--settle-ms", type=float, default=300.0,
+                    help="untimed steps run before the warm-up until this much wall time has "
+                         "passed, so that the timed steps run at the GPU's settled clock")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-rows", type=int, default=None)
     ap.add_argument("--copy-probe", action="store_true")
@@ -525,17 +557,20 @@ def main():
     names = list(dict.fromkeys(nm for nm, _ in st["steps"]))
 
     print("[bench] warmup + timed steps", file=sys.stderr, flush=True)
-    wall, per = run_steps(torch, st, args.steps, args.warmup, record=True)
+    wall, per = run_steps(torch, st, args.steps, args.warmup, record=True,
+                          settle_s=args.settle_ms * 1e-3)
     ms = {k: float(np.mean(v)) for k, v in per.items()}
     ms_step = wall * 1e3 / args.steps
     stats = None
     if args.stat_reps > 0:
         print(f"[bench] {args.stat_reps} steps for the per-kernel distribution", file=sys.stderr,
               flush=True)
-        _, per2 = run_steps(torch, st, args.stat_reps, 1, record=True)
+        _, per2 = run_steps(torch, st, args.stat_reps, 1, record=True,
+                            settle_s=min(0.1, args.settle_ms * 1e-3))
         stats = {k: percentiles(v) for k, v in per2.items()}
     print("[bench] copy probe with the activation kernel's byte mix", file=sys.stderr, flush=True)
-    copy_gbs, copy_ms = copy_mix_rate(torch, st["Xs"], max(args.stat_reps, 20))
+    copy_gbs, copy_ms = copy_mix_rate(torch, st["Xs"], st["qa_bytes"] - M * K * 2,
+                                      max(args.stat_reps, 20))
 
     gemm_flops = st["gemm_flops"]
     layer_flops = st["layer_flops"]

@@ -311,3 +311,18 @@ def test_cube_groups_pack_greedily():
         _lib.svdq_cube_groups(np.array([0, 3, 68, 70], np.int32))
     with pytest.raises(_lib.SvdqError):
         _lib.svdq_cube_groups(np.array([0, 3, 3, 7], np.int32))      # an empty cube
+
+
+def test_probe_library_loads_and_validates():
+    """The benchmark's memory probe is its own library and refuses bad arguments on the host."""
+    from w4a4_quantized_dit_amd import build as B
+    lib = ctypes.CDLL(B.PROBE_LIB)
+    f = lib.svdq_probe_stream
+    f.restype = ctypes.c_int
+    f.argtypes = [ctypes.c_void_p, ctypes.c_int64, ctypes.c_void_p, ctypes.c_int64,
+                  ctypes.c_void_p]
+    assert f(None, 16, P, 16, None) == 1
+    assert f(P, 17, P, 16, None) == 1              # not whole 16-byte pieces
+    assert f(P, -16, P, 16, None) == 1
+    assert f(P, 0, P, 0, None) == 0                # nothing to do: nothing launched
+    assert not hasattr(_lib.load(), "svdq_probe_stream")

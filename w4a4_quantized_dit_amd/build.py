@@ -16,6 +16,8 @@ from concurrent.futures import ThreadPoolExecutor
 HERE = os.path.dirname(os.path.abspath(__file__))
 CSRC = os.path.join(HERE, "csrc")
 LIB = os.path.join(HERE, "libsvdq.so")
+PROBE_LIB = os.path.join(HERE, "libsvdq_probe.so")   # the benchmark's memory probe
+PROBE_SOURCES = ["probe.hip"]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 
 SOURCES = ["api.cpp", "geometry.cpp", "calib.hip", "quant_weight.hip", "quant_act.hip",
@@ -41,10 +43,16 @@ def _run(cmd):
 
 
 def build(verbose=False, out=None, defines=(), jobs=None):
-    """Compile every source into libsvdq.so (always recompiles).  `out` / `defines` build a
-    differently named library with extra -D definitions."""
-    target = out or LIB
-    jobs = jobs or min(len(SOURCES), max(1, (os.cpu_count() or 4)))
+    """Compile every source into libsvdq.so and the benchmark's probe into libsvdq_probe.so
+    (always recompiles).  `out` / `defines` build a differently named layer library with extra
+    -D definitions (and no probe)."""
+    if out is None:
+        _link(PROBE_SOURCES, PROBE_LIB, (), jobs, verbose)
+    return _link(SOURCES, out or LIB, defines, jobs, verbose)
+
+
+def _link(sources, target, defines, jobs, verbose):
+    jobs = jobs or min(len(sources), max(1, (os.cpu_count() or 4)))
     t0 = time.time()
     tmpdir = tempfile.mkdtemp(prefix="svdq_build_")
     try:
@@ -56,7 +64,7 @@ def build(verbose=False, out=None, defines=(), jobs=None):
             return src, obj, rc, text
 
         with ThreadPoolExecutor(max_workers=jobs) as ex:
-            results = list(ex.map(compile_one, SOURCES))
+            results = list(ex.map(compile_one, sources))
         errors = [f"== {src} ==\n{text}" for src, _, rc, text in results if rc != 0]
         if errors:
             raise RuntimeError("hipcc failed:\n" + "\n".join(errors))
