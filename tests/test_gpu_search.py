@@ -123,31 +123,43 @@ def test_refit_iterations(L, small, fmt, r):
     assert g["lora_down"].shape == (r, X.shape[1]) and g["lora_up"].shape == (W.shape[0], r)
 
 
-def test_best_factors_reproduce_the_best_score(L, small):
-    """The factors the search returns, run through the layer's own entry points with the
-    winner's λ, give the winner's score again."""
+@pytest.mark.parametrize("fmt,r", [("nvfp4", 8), ("int4", 8), ("mxfp4", 16), ("mxfp8", 8)])
+def test_best_factors_reproduce_the_best_score(L, small, fmt, r):
+    """The factors the search returns (possibly from a refit iterate) are scored twice: through
+    the layer's own entry points with the winner's λ, and through the oracle's layer with the
+    same λ and factors.  Both must give the GPU's winning score to the layer tolerance
+    1e-3 · (1 + score): with the factors fixed, the only differences left are the GPU GEMM's
+    fp32 accumulation, which the layer parity bar covers."""
     torch = torch_mod()
     X, W, ax, aw = small
     rows = np.sort(np.random.default_rng(9).choice(X.shape[0], 192, replace=False))
-    omega = np.random.default_rng(10).standard_normal((W.shape[0], 16)).astype(F32)
-    g = _run(L, X, W, ax, aw, OSe.alpha_grid()[::6], "nvfp4", rows, omega, 8, 2, refit=5)
+    omega = np.random.default_rng(10).standard_normal((W.shape[0], r + 8)).astype(F32)
+    g = _run(L, X, W, ax, aw, OSe.alpha_grid()[::6], fmt, rows, omega, r, 2, refit=5)
     i = int(g["index"][0])
     Xd, Wd = dev_bf16(X), dev_bf16(W)
     lam = g["lam"].cuda()
-    amax = torch.tensor([OC.act_amax_from_stats(ax, g["lam"].numpy())], device="cuda")
+    lam_h = g["lam"].numpy()
+    amax_h = OC.act_amax_from_stats(ax, lam_h)
+    amax = torch.tensor([amax_h], device="cuda")
     down, up = g["lora_down"].cuda(), g["lora_up"].cuda()
-    pw = L.prepare_weight(Wd, lam, down, up, 0)
+    pw = L.prepare_weight(Wd, lam, down, up, FMT[fmt])
     Xs = Xd[torch.from_numpy(rows).long().cuda()].contiguous()
-    codes, scales, ga, D = L.quantize_activation(Xs, lam, amax, down, 0)
+    codes, scales, ga, D = L.quantize_activation(Xs, lam, amax, down, FMT[fmt])
     Y = L.gemm(codes, scales, ga, D, pw, len(rows))
     torch.cuda.synchronize()
     from oracle import score as OSc
     from tests.gpu_common import host_bits
-    sums = OSc.modal_sums(host_bits(Y), OSc.reference_rows(X, W, rows), np.full(len(rows), 3))
+    Yref = OSc.reference_rows(X, W, rows)
+    sums = OSc.modal_sums(host_bits(Y), Yref, np.full(len(rows), 3))
     again = np.sqrt(sums[3, 0]) / np.sqrt(sums[3, 1])
+    down_h = g["lora_down"].view(torch.int16).numpy().view(np.uint16)
+    up_h = g["lora_up"].view(torch.int16).numpy().view(np.uint16)
+    oracle_score, _ = OSe._score(X, W, lam_h, amax_h, down_h, up_h, fmt, rows, Yref)
     best = float(g["scores"][i])
-    print(f"[search] best factors: search score {best:.6f}, layer again {again:.6f}", flush=True)
+    print(f"[search] {fmt} r={r} best factors: search score {best:.6f}, layer again "
+          f"{again:.6f}, oracle with the same factors {oracle_score:.6f}", flush=True)
     assert abs(again - best) <= 1e-3 * (1 + best)
+    assert abs(oracle_score - best) <= 1e-3 * (1 + best)
 
 
 def test_full_size_attention_projection(L):
