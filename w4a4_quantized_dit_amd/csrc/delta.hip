@@ -142,11 +142,13 @@ __global__ __launch_bounds__(kThreads, 2) void k_delta_act(
           n < r ? lr[u] : u32x4_t{0u, 0u, 0u, 0u};
     }
     __syncthreads();
-    // the next chunks' loads: X two chunks ahead (into the registers just stored), L1 and λ one
-    if (c + 2 < nchunk) load_x(xcur, c + 2);
-    if (c + 1 < nchunk) load_l(lr, c + 1);
+    // the next chunks' loads: λ two chunks ahead, L1 one, X two (into the registers just
+    // stored).  Loads complete in issue order for the wait counter, so X goes last: waiting for
+    // the L1 slice at the next chunk then leaves the X prefetch in flight.
     const float lam_c1 = lam_next;
     lam_next = load_lam(c + 2);
+    if (c + 1 < nchunk) load_l(lr, c + 1);
+    if (c + 2 < nchunk) load_x(xcur, c + 2);
     // 2. core chunk: (cube slot, channel pair) items, ascending fp32 sum over the members
     const float* inv = s_inv[c & 1];
 #pragma unroll
@@ -254,11 +256,12 @@ __global__ __launch_bounds__(kThreads, 2) void k_delta_act(
 
   // prologue: chunks 0 and 1 of X, chunk 0 of L1, 1/λ of chunk 0; λ of chunk 1 in flight
   u32x4_t xa[4], xb[4], lr[NTc];
+  const float lam0 = load_lam(0);
+  float lam_next = load_lam(1);
+  load_l(lr, 0);
   load_x(xa, 0);
   if (nchunk > 1) load_x(xb, 1);
-  load_l(lr, 0);
-  stage_inv(load_lam(0), 0);
-  float lam_next = load_lam(1);
+  stage_inv(lam0, 0);
   __syncthreads();
   for (int64_t c = 0; c < nchunk; c += 2) {
     chunk(c, xa, lr, lam_next);
@@ -281,39 +284,59 @@ __global__ __launch_bounds__(kThreads, 2) void k_delta_act(
   }
   // 4. core scales and FP8 codes: wave w owns cube slots w, w + 4, ...; lane l re-reads the
   // channel pair 2l, 2l + 1 of every chunk that it wrote in step 2 (its own stores, visible
-  // to it after the barrier's fence)
+  // to it after the barrier's fence).  The values of all the wave's slots are requested
+  // together, 32 per lane, so a wave waits for memory a few times per group rather than once
+  // per slot and batch.
+  float inv_c[4];
 #pragma unroll
   for (int i = 0; i < 4; ++i) {
     const int sl = wave + 4 * i;
-    if (sl < ncub) {
-      float am = camax[i];
-      for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
-      const float sc = am / 448.0f;
-      const float inv_c = sc != 0.0f ? 1.0f / sc : 0.0f;
-      const int64_t c = c0 + sl;
-      if (lane == 0) core_scale[c] = sc;
-      // kBatch chunks' values in flight per lane (K is a multiple of 256: whole batches of 2)
-      constexpr int kBatch = 8;
-      for (int64_t kb = 0; kb < K; kb += kBatch * kDChunk) {
-        float2 v[kBatch];
+    float am = camax[i];
+    for (int off = 32; off > 0; off >>= 1) am = fmaxf(am, __shfl_xor(am, off));
+    const float sc = am / 448.0f;
+    inv_c[i] = sc != 0.0f ? 1.0f / sc : 0.0f;
+    if (lane == 0 && sl < ncub) core_scale[c0 + sl] = sc;
+  }
+  {
+    // a batch covers 2^LCB chunks of each of the wave's (up to four) slots: 32 values per lane
+    const int own = ncub > wave ? (ncub - wave + 3) / 4 : 0;  // slots of this wave
+    auto encode = [&](auto lcb_c) {
+      constexpr int LCB = decltype(lcb_c)::value, CB = 1 << LCB, NS = 32 >> LCB;
+      const float* src[NS];
+      uint8_t* dst[NS];
 #pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          const int64_t k = kb + b * kDChunk + 2 * lane;
-          v[b] = k < K ? *reinterpret_cast<const float2*>(core32 + c * K + k) : float2{0.f, 0.f};
-        }
-#pragma unroll
-        for (int b = 0; b < kBatch; ++b) {
-          const int64_t k = kb + b * kDChunk + 2 * lane;
-          float val;
-          const uint32_t e0 = e4m3_encode_pos(fabsf(v[b].x) * inv_c, &val) |
-                              (__builtin_signbit(v[b].x) ? 0x80u : 0u);
-          const uint32_t e1 = e4m3_encode_pos(fabsf(v[b].y) * inv_c, &val) |
-                              (__builtin_signbit(v[b].y) ? 0x80u : 0u);
-          if (k < K)
-            *reinterpret_cast<uint16_t*>(core_codes + c * K + k) = (uint16_t)(e0 | (e1 << 8));
-        }
+      for (int i = 0; i < NS; ++i) {
+        const int64_t c = c0 + wave + 4 * (i < own ? i : 0);
+        src[i] = core32 + c * K + 2 * lane;
+        dst[i] = core_codes + c * K + 2 * lane;
       }
-    }
+      for (int64_t cc0 = 0; cc0 < nchunk; cc0 += CB) {
+        float2 v[NS][CB];
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+#pragma unroll
+          for (int b = 0; b < CB; ++b)
+            v[i][b] = (i < own && cc0 + b < nchunk)
+                          ? *reinterpret_cast<const float2*>(src[i] + (cc0 + b) * kDChunk)
+                          : float2{0.f, 0.f};
+#pragma unroll
+        for (int i = 0; i < NS; ++i)
+#pragma unroll
+          for (int b = 0; b < CB; ++b)
+            if (i < own && cc0 + b < nchunk) {
+              float val;
+              const uint32_t e0 = e4m3_encode_pos(fabsf(v[i][b].x) * inv_c[i], &val) |
+                                  (__builtin_signbit(v[i][b].x) ? 0x80u : 0u);
+              const uint32_t e1 = e4m3_encode_pos(fabsf(v[i][b].y) * inv_c[i], &val) |
+                                  (__builtin_signbit(v[i][b].y) ? 0x80u : 0u);
+              *reinterpret_cast<uint16_t*>(dst[i] + (cc0 + b) * kDChunk) =
+                  (uint16_t)(e0 | (e1 << 8));
+            }
+      }
+    };
+    if (own > 2) encode(std::integral_constant<int, 3>{});
+    else if (own == 2) encode(std::integral_constant<int, 4>{});
+    else if (own == 1) encode(std::integral_constant<int, 5>{});
   }
   if (sat) {
     for (int off = 32; off > 0; off >>= 1) nsat += __shfl_xor(nsat, off);

@@ -11,8 +11,8 @@
 // group, so every block absmax is lane-local (no cross-lane reduction).  The same registers feed
 // v_mfma_f32_16x16x32_bf16: in MFMA step t the lane's k-slots 8q..8q+7 carry channels
 // k0 + 64q + 8t .. +8, and the block stages the matching slice of L1 (lora_down[:, k0:k0+256])
-// in LDS once for its waves.  The next chunk's global loads are issued before the current
-// chunk is processed, and two K groups of waves walk alternate chunks of the same rows.
+// in LDS once for its waves.  X is prefetched one or two chunks ahead of the one processed,
+// and two K groups of waves walk alternate chunks of the same rows.
 // FMT 0 is NVFP4, FMT 1 int4-g64; FMT 3 / 4 are the MX formats (E8M0 scale per 32 with E2M1
 // / E4M3 elements: "MiniMax-H3 — MXFP8 (weight-quantized, vLLM-Omni native layout)", section
 // "Quant format"), each lane's 64 channels being two whole blocks.
@@ -98,18 +98,34 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
   for (int j = 0; j < NTc; ++j) acc[j] = f32x4_t{0.f, 0.f, 0.f, 0.f};
   uint32_t nsat = 0;
 
-  u32x4_t xr[8], lr[kLPieces > 0 ? kLPieces : 1];
-  if (ks < nchunk) {
-    const int64_t k0 = (int64_t)ks * kChunk;
+  // X of the group's next kAhead chunks is in flight while a chunk is processed (E2M1 formats:
+  // two register sets used alternately; int4 and MXFP8, whose quantisers need more registers,
+  // measured no faster with the second set); the L1 slice one chunk ahead.  The L1 loads are
+  // issued before the X loads they are consumed with, because loads complete in issue order for
+  // the wait counter: waiting for the L1 slice then leaves the younger X prefetch in flight.
+  constexpr int kAhead = (FMT == 0 || FMT == 3) ? 2 : 1;
+  u32x4_t xa[8], xb[8], lr[kLPieces > 0 ? kLPieces : 1];
+  auto load_x = [&](u32x4_t (&xr)[8], int64_t kc) {
+    if (kc < nchunk) {
 #pragma unroll
-    for (int i = 0; i < 8; ++i)
-      xr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xblk + k0 + xo[i]));
+      for (int i = 0; i < 8; ++i)
+        xr[i] = __builtin_nontemporal_load(
+            reinterpret_cast<const u32x4_t*>(xblk + kc * kChunk + xo[i]));
+    }
+  };
+  auto load_l = [&](int64_t kc) {
+    if (kc < nchunk) {
 #pragma unroll
-    for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(down + k0 + lo[u]);
-  }
+      for (int u = 0; u < kLPieces; ++u)
+        lr[u] = *reinterpret_cast<const u32x4_t*>(down + kc * kChunk + lo[u]);
+    }
+  };
+  load_l(ks);
+  load_x(xa, ks);
+  if (kAhead == 2) load_x(xb, ks + kSplit);
   __syncthreads();  // s_inv complete
 
-  for (int64_t it = 0; it < nloop; ++it) {
+  auto body = [&](int64_t it, u32x4_t (&xr)[8]) {
     const int64_t kc = it * kSplit + ks;  // this group's chunk
     const bool has = kc < nchunk;
     // registers -> LDS (the previous chunk's readers finished at the loop-end barrier)
@@ -126,14 +142,8 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
       }
     }
     __syncthreads();
-    if (kc + kSplit < nchunk) {
-      const int64_t kn = (kc + kSplit) * kChunk;
-#pragma unroll
-      for (int i = 0; i < 8; ++i)
-        xr[i] = __builtin_nontemporal_load(reinterpret_cast<const u32x4_t*>(xblk + kn + xo[i]));
-#pragma unroll
-      for (int u = 0; u < kLPieces; ++u) lr[u] = *reinterpret_cast<const u32x4_t*>(down + kn + lo[u]);
-    }
+    load_l(kc + kSplit);
+    load_x(xr, kc + kAhead * kSplit);
     if (has) {
       const int64_t kb = kc * kChunk + 64 * q;  // first channel of this lane
       const int64_t kbp = kb + 4 * (kb >> 6);   // its padded index in s_inv
@@ -265,6 +275,14 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
       }
     }
     __syncthreads();  // the LDS chunk buffers are rewritten next iteration
+  };
+  if (kAhead == 2) {
+    for (int64_t it = 0; it < nloop; it += 2) {
+      body(it, xa);
+      if (it + 1 < nloop) body(it + 1, xb);
+    }
+  } else {
+    for (int64_t it = 0; it < nloop; ++it) body(it, xa);
   }
 
   if (NT > 0) {
