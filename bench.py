@@ -360,7 +360,13 @@ def setup(torch, workload):
             lam_m = torch.empty(K, device=dev)
             _lib.svdq_calibrate_lambda(Xd0, seg, Wd, m, 0.5, 0, ax, aw, lam_m, amax)
             factors[m] = lowrank_factors_gpu(torch, layer, Wd, lam_m, r, reps=1)[:2]
-        steps = []
+        # the bf16 reference rows of the batch's sampled rows do not depend on λ: computed once
+        # per step, and every λ is scored against them
+        Yref = torch.empty(len(rows), N, dtype=torch.bfloat16, device=dev)
+
+        def ref_rows(Xi):
+            _lib.svdq_score_reference_rows(Xi, Wd, rows_d, Yref)
+        steps = [("ref", ref_rows)]
         for m in SWEEP_MASKS:
             fd, fu = factors[m]
 
@@ -380,7 +386,7 @@ def setup(torch, workload):
 
             def score_m(Xi, m=m):
                 sums[m].zero_()
-                _lib.svdq_score_modal_rel_l2(Y, Xi, Wd, rows_d, grp_d, sums[m])
+                _lib.svdq_score_modal_rel_l2_ref(Y, Yref, rows_d, grp_d, sums[m])
             steps += [("cal", cal_m), ("wq", wq_m), ("qa", qa_m), ("gemm", gemm_m),
                       ("score", score_m)]
         st["steps"] = steps

@@ -413,6 +413,29 @@ svdq_status svdq_score_modal_rel_l2(const uint16_t* Y, int64_t ldy, const uint16
                                     const int8_t* row_group, int64_t n_rows, double* sums,
                                     svdq_stream_t stream);
 
+/*
+ * The scoring above in two parts, for a caller that scores several candidates (λ, formats) of
+ * the same batch: the reference rows do not depend on the candidate (same passage as
+ * svdq_score_modal_rel_l2).
+ *
+ * svdq_score_reference_rows: Yref[i, :] = bf16(X[rows[i], :] · Wᵀ) for i < n_rows, fp32
+ * accumulation, bf16 Yref [n_rows, N] with row stride ldr (caller-allocated, written).  Bit for
+ * bit the reference rows svdq_score_modal_rel_l2 forms internally.  Shape rules as there.
+ *
+ * svdq_score_modal_rel_l2_ref: for each sampled row i with group μ = row_group[i] in 0..3,
+ *   sums[μ][0] += Σ_n (Y[rows[i], n] − Yref[i, n])²,   sums[μ][1] += Σ_n Yref[i, n]²   (fp64)
+ * sums (device double[8]) is ADDED to (the caller zeroes it).  N a positive multiple of 8;
+ * ldy, ldr >= N and multiples of 8; rows outside [0, M) read row 0 or M - 1.
+ */
+svdq_status svdq_score_reference_rows(const uint16_t* X, int64_t ldx, const uint16_t* W,
+                                      int64_t ldw, int64_t M, int64_t N, int64_t K,
+                                      const int32_t* rows, int64_t n_rows, uint16_t* Yref,
+                                      int64_t ldr, svdq_stream_t stream);
+svdq_status svdq_score_modal_rel_l2_ref(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
+                                        int64_t ldr, int64_t M, int64_t N, const int32_t* rows,
+                                        const int8_t* row_group, int64_t n_rows, double* sums,
+                                        svdq_stream_t stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -94,6 +94,21 @@ def test_other_validation(lib):
     assert lib.svdq_gemm_core(0, 256, 256, P, P, P, P, P, P, None) == SHAPE
     assert lib.svdq_score_modal_rel_l2(P, 256, P, 256, P, 256, 10, 256, 256, P, P, 4, None,
                                        None) == NULLP
+    # the two-part scoring: reference rows, then sums against them
+    ref = lib.svdq_score_reference_rows
+    assert ref(P, 256, P, 256, 10, 256, 256, P, 4, None, 256, None) == NULLP
+    assert ref(P, 256, P, 256, 10, 128, 256, P, 4, P, 128, None) == SHAPE    # N % 256
+    assert ref(P, 256, P, 256, 10, 256, 256, P, 4, P, 200, None) == SHAPE    # ldr < N
+    assert ref(P, 256, P, 256, 10, 256, 200, P, 4, P, 256, None) == SHAPE    # K % 256
+    assert ref(P, 256, MIS, 256, 10, 256, 256, P, 4, P, 256, None) == SHAPE    # misaligned W
+    assert ref(P, 256, P, 256, 10, 256, 256, P, 0, P, 256, None) == OK       # nothing to do
+    sr = lib.svdq_score_modal_rel_l2_ref
+    assert sr(P, 256, P, 256, 10, 256, P, P, 4, None, None) == NULLP
+    assert sr(P, 256, P, 256, 10, 12, P, P, 4, P, None) == SHAPE              # N % 8
+    assert sr(P, 256, P, 248, 10, 256, P, P, 4, P, None) == SHAPE             # ldr < N
+    assert sr(P, 260, P, 256, 10, 256, P, P, 4, P, None) == SHAPE             # ldy % 8
+    assert sr(P, 256, P, 256, 0, 256, P, P, 4, P, None) == SHAPE              # M < 1
+    assert sr(P, 256, P, 256, 10, 256, P, P, 0, P, None) == OK
     d = lib.svdq_delta_quant_act
     ws = 1 << 30
     need = lib.svdq_delta_workspace_bytes(8, 256)

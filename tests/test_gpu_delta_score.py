@@ -61,6 +61,48 @@ def test_score_kernel_on_oracle_output(L):
     assert np.all(np.abs(SC.rel_l2(got) - SC.rel_l2(want)) <= SCORE_ABS)
 
 
+def test_two_part_scoring_matches_fused_and_oracle(L):
+    """Reference rows stored once, then sums against them (what a multi-λ sweep runs): the
+    stored rows are the oracle's bf16(X·Wᵀ) rows to within one bf16 rounding, the sums equal the
+    fused kernel's (same per-element terms, fp64 in another order), and the rel-L2 scores equal
+    the oracle's.  Y, X, W and the reference rows are row-strided views."""
+    torch = torch_mod()
+    from w4a4_quantized_dit_amd import _lib
+    M, K, N = 700, 768, 512
+    cfg = dict(M=M, K=K, N=N, seg=synth.segments(M, 40, 30), gen="outlier")
+    X, W = synth.x_bits(cfg, 13), synth.weight_bits(N, K, 13)
+    ax, aw, lam, amax = OC.calibrate(X, cfg["seg"], W, 7)
+    down, up = OS.lowrank_factors(W, lam, 16)
+    act = OL.prepare_activation(X, lam, amax, down, "nvfp4")
+    wt = OL.prepare_weight(W, lam, down, up, "nvfp4")
+    _, y = OL.forward(act, wt, up, "nvfp4")
+    rows, grp = synth.sample_rows(cfg["seg"], n_per=100, seed=5)
+    ref_want = SC.reference_rows(X, W, rows)
+
+    def padded(bits, pad=64):
+        buf = np.zeros((bits.shape[0], bits.shape[1] + pad), np.uint16)
+        buf[:, :bits.shape[1]] = bits
+        return dev_bf16(buf)[:, :bits.shape[1]]
+
+    Xd, Wd, Yd = padded(X), padded(W), padded(y)
+    Yref = torch.zeros(len(rows), N + 128, dtype=torch.bfloat16, device="cuda")[:, :N]
+    _lib.svdq_score_reference_rows(Xd, Wd, dev(rows), Yref)
+    got_ref = bf16_bits_to_f32(host_bits(Yref)).astype(np.float64)
+    want_ref = bf16_bits_to_f32(ref_want).astype(np.float64)
+    rms = np.sqrt(np.mean(want_ref ** 2))
+    assert np.all(np.abs(got_ref - want_ref) <= 2.0 ** -7 * np.abs(want_ref) + 1e-6 * rms)
+    assert np.mean(got_ref == want_ref) > 0.99
+
+    sums = torch.zeros(8, dtype=torch.float64, device="cuda")
+    _lib.svdq_score_modal_rel_l2_ref(Yd, Yref, dev(rows), dev(grp), sums)
+    two_part = sums.cpu().numpy().reshape(4, 2)
+    fused = _gpu_scores(Yd, Xd, Wd, rows, grp)
+    assert np.allclose(two_part, fused, rtol=1e-9, atol=0)
+    want = SC.modal_sums(y[rows], ref_want, grp)
+    assert np.allclose(two_part, want, rtol=2e-3, atol=0)
+    assert np.all(np.abs(SC.rel_l2(two_part) - SC.rel_l2(want)) <= SCORE_ABS)
+
+
 def test_score_end_to_end_small(L):
     M, K, N = 900, 768, 512
     cfg = dict(M=M, K=K, N=N, seg=synth.segments(M, 30, 20), gen="outlier")

@@ -63,6 +63,10 @@ _SIGS = {
                                       _c_p]),
     "svdq_score_modal_rel_l2": (ctypes.c_int, [_c_p, _i64, _c_p, _i64, _c_p, _i64, _i64, _i64,
                                                _i64, _c_p, _c_p, _i64, _c_p, _c_p]),
+    "svdq_score_reference_rows": (ctypes.c_int, [_c_p, _i64, _c_p, _i64, _i64, _i64, _i64, _c_p,
+                                                 _i64, _c_p, _i64, _c_p]),
+    "svdq_score_modal_rel_l2_ref": (ctypes.c_int, [_c_p, _i64, _c_p, _i64, _i64, _i64, _c_p, _c_p,
+                                                   _i64, _c_p, _c_p]),
 }
 
 _lib = None
@@ -433,6 +437,30 @@ def svdq_gemm_core(n_cubes, N, K, core_codes, core_scale, w_codes, w_scales, g_w
         _ptr(w_codes, torch.uint8, "w_codes", N * K // 2),
         _ptr(w_scales, torch.uint8, "w_scales", N * K // 16), _ptr(g_w, torch.float32, "g_w", 1),
         _ptr(core_out, torch.float32, "core_out", n_cubes * N), _stream(stream)))
+
+
+def svdq_score_reference_rows(X, W, rows, Yref, stream=None):
+    """Yref [n_rows, N] bf16 = bf16(X[rows] · Wᵀ) (written)."""
+    torch = _torch()
+    M, K = X.shape
+    N = W.shape[0]
+    n = rows.numel()
+    _check(load().svdq_score_reference_rows(
+        _ptr(X, _bf16(), "X", rows=True), _ld(X), _ptr(W, _bf16(), "W", rows=True), _ld(W), M, N,
+        K, _ptr(rows, torch.int32, "rows"), n, _ptr(Yref, _bf16(), "Yref", n * N, rows=True),
+        _ld(Yref), _stream(stream)))
+
+
+def svdq_score_modal_rel_l2_ref(Y, Yref, rows, row_group, sums, stream=None):
+    """Adds per-group (Σ(Y[rows]−Yref)², ΣYref²) into sums (fp64 [4, 2])."""
+    torch = _torch()
+    M, N = Y.shape
+    n = rows.numel()
+    _check(load().svdq_score_modal_rel_l2_ref(
+        _ptr(Y, _bf16(), "Y", M * N, rows=True), _ld(Y),
+        _ptr(Yref, _bf16(), "Yref", n * N, rows=True), _ld(Yref), M, N,
+        _ptr(rows, torch.int32, "rows"), _ptr(row_group, torch.int8, "row_group"), n,
+        _ptr(sums, torch.float64, "sums", 8), _stream(stream)))
 
 
 def svdq_score_modal_rel_l2(Y, X, W, rows, row_group, sums, stream=None):

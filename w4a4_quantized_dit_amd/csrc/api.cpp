@@ -615,4 +615,48 @@ svdq_status svdq_score_modal_rel_l2(const uint16_t* Y, int64_t ldy, const uint16
                     fn);
 }
 
+svdq_status svdq_score_reference_rows(const uint16_t* X, int64_t ldx, const uint16_t* W,
+                                      int64_t ldw, int64_t M, int64_t N, int64_t K,
+                                      const int32_t* rows, int64_t n_rows, uint16_t* Yref,
+                                      int64_t ldr, svdq_stream_t stream) {
+  const char* fn = "svdq_score_reference_rows";
+  REQUIRE_PTR(X); REQUIRE_PTR(W); REQUIRE_PTR(rows); REQUIRE_PTR(Yref);
+  REQUIRE_ALIGNED(X); REQUIRE_ALIGNED(W); REQUIRE_ALIGNED(Yref);
+  if (M < 1 || n_rows < 0) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: bad M or n_rows", fn);
+  if (N < 1 || N % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 256", fn,
+                (long long)N);
+  TRY(check_k(fn, K));
+  TRY(check_ld(fn, "ldx", ldx, K));
+  TRY(check_ld(fn, "ldw", ldw, K));
+  if (ldr < N || ldr % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldr must be >= N and a multiple of 8", fn);
+  if (n_rows == 0) return ok();
+  return hip_result(svdq::launch_reference_rows(X, ldx, W, ldw, M, N, K, rows, n_rows, Yref, ldr,
+                                                reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
+svdq_status svdq_score_modal_rel_l2_ref(const uint16_t* Y, int64_t ldy, const uint16_t* Yref,
+                                        int64_t ldr, int64_t M, int64_t N, const int32_t* rows,
+                                        const int8_t* row_group, int64_t n_rows, double* sums,
+                                        svdq_stream_t stream) {
+  const char* fn = "svdq_score_modal_rel_l2_ref";
+  REQUIRE_PTR(Y); REQUIRE_PTR(Yref); REQUIRE_PTR(rows); REQUIRE_PTR(row_group);
+  REQUIRE_PTR(sums);
+  REQUIRE_ALIGNED(Y); REQUIRE_ALIGNED(Yref);
+  if (M < 1 || n_rows < 0) return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: bad M or n_rows", fn);
+  if (N < 1 || N % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: N=%lld must be a positive multiple of 8", fn,
+                (long long)N);
+  if (ldy < N || ldy % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldy must be >= N and a multiple of 8", fn);
+  if (ldr < N || ldr % 8 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: ldr must be >= N and a multiple of 8", fn);
+  if (n_rows == 0) return ok();
+  return hip_result(svdq::launch_score_ref(Y, ldy, Yref, ldr, M, N, rows, row_group, n_rows, sums,
+                                           reinterpret_cast<hipStream_t>(stream)),
+                    fn);
+}
+
 }  // extern "C"

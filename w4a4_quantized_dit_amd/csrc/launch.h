@@ -98,6 +98,9 @@ hipError_t launch_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, in
 
 // Y_ref = bf16(X·Wᵀ) of the sampled rows (the scoring kernel's reference, fp32 accumulation)
 // into Yref [n_rows, N] (row stride ldr).
+hipError_t launch_score_ref(const uint16_t* Y, int64_t ldy, const uint16_t* Yref, int64_t ldr,
+                            int64_t M, int64_t N, const int32_t* rows, const int8_t* grp,
+                            int64_t n_rows, double* sums, hipStream_t s);
 hipError_t launch_reference_rows(const uint16_t* X, int64_t ldx, const uint16_t* W, int64_t ldw,
                                  int64_t M, int64_t N, int64_t K, const int32_t* rows,
                                  int64_t n_rows, uint16_t* Yref, int64_t ldr, hipStream_t s);

@@ -6,6 +6,8 @@
 // the X rows gathered by index; the epilogue forms (Y − Y_ref)² and Y_ref² per element and
 // accumulates them per row group in fp64, then adds each wave's eight sums to `sums`.
 // Workgroup tile 128 sampled rows x 128 columns, 4 waves of 64 x 64 (2 x 2 MFMA 32x32 tiles).
+// The same kernel can instead store Y_ref of the sampled rows (a sweep over several λ computes
+// them once per batch: they do not depend on λ), and k_score_ref then scores against them.
 // K mapping: in a 64-element chunk, lane (row = lane % 32, h = lane / 32) holds elements
 // [32h, 32h + 32) of its row; MFMA step t takes [8t, 8t + 8) of them, for X and W alike.
 #include "device.h"
@@ -132,7 +134,67 @@ __global__ __launch_bounds__(kThreads) void k_score(uint16_t* __restrict__ Y, in
   }
 }
 
+// Sums against stored reference rows: sampled row i compares Y[rows[i], :] with Yref[i, :].  A
+// wave takes one sampled row at a time (grid-stride over rows), its lanes 16-byte pieces of the
+// two rows; each lane keeps fp64 sums per row group, the workgroup combines them in LDS and adds
+// one value per (group, quantity) to `sums`.
+__global__ __launch_bounds__(256) void k_score_ref(const uint16_t* __restrict__ Y, int64_t ldy,
+                                                   const uint16_t* __restrict__ Yr, int64_t ldr,
+                                                   int64_t M, int64_t N,
+                                                   const int32_t* __restrict__ rows,
+                                                   const int8_t* __restrict__ grp, int64_t n_rows,
+                                                   double* __restrict__ sums) {
+  __shared__ double red[4][8];
+  const int wave = threadIdx.x >> 6, lane = threadIdx.x & 63;
+  double acc[8] = {0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0, 0.0};  // [group][d2, r2]
+  const int64_t n8 = N / 8;
+  for (int64_t i = (int64_t)blockIdx.x * 4 + wave; i < n_rows; i += (int64_t)gridDim.x * 4) {
+    int64_t m = rows[i];
+    m = m < 0 ? 0 : (m < M ? m : M - 1);  // an out-of-range index reads a valid row
+    const int g = grp[i];
+    const u32x4_t* py = reinterpret_cast<const u32x4_t*>(Y + m * ldy);
+    const u32x4_t* pr = reinterpret_cast<const u32x4_t*>(Yr + i * ldr);
+    double d2 = 0.0, r2 = 0.0;
+    for (int64_t p = lane; p < n8; p += 64) {
+      const u32x4_t a = py[p], b = pr[p];
+#pragma unroll
+      for (int e = 0; e < 4; ++e) {
+        const double r0 = (double)bf16_lo(b[e]), r1 = (double)bf16_hi(b[e]);
+        const double e0 = (double)bf16_lo(a[e]) - r0, e1 = (double)bf16_hi(a[e]) - r1;
+        d2 += e0 * e0 + e1 * e1;
+        r2 += r0 * r0 + r1 * r1;
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < 4; ++q) {
+      acc[2 * q] += q == g ? d2 : 0.0;
+      acc[2 * q + 1] += q == g ? r2 : 0.0;
+    }
+  }
+#pragma unroll
+  for (int q = 0; q < 8; ++q) {
+    for (int off = 32; off > 0; off >>= 1) acc[q] += __shfl_xor(acc[q], off);
+    if (lane == 0) red[wave][q] = acc[q];
+  }
+  __syncthreads();
+  if (threadIdx.x < 8) {
+    const int q = threadIdx.x;
+    const double v = (red[0][q] + red[1][q]) + (red[2][q] + red[3][q]);
+    if (v != 0.0) atomicAdd(sums + q, v);
+  }
+}
+
 }  // namespace
+
+hipError_t launch_score_ref(const uint16_t* Y, int64_t ldy, const uint16_t* Yref, int64_t ldr,
+                            int64_t M, int64_t N, const int32_t* rows, const int8_t* grp,
+                            int64_t n_rows, double* sums, hipStream_t s) {
+  int64_t blocks = (n_rows + 3) / 4;
+  blocks = blocks < 2048 ? blocks : 2048;
+  k_score_ref<<<dim3((unsigned)blocks), dim3(256), 0, s>>>(Y, ldy, Yref, ldr, M, N, rows, grp,
+                                                           n_rows, sums);
+  return hipGetLastError();
+}
 
 hipError_t launch_score(const uint16_t* Y, int64_t ldy, const uint16_t* X, int64_t ldx,
                         const uint16_t* W, int64_t ldw, int64_t M, int64_t N, int64_t K,
