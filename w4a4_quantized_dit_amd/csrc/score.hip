@@ -56,16 +56,19 @@ __global__ __launch_bounds__(kThreads) void k_score(uint16_t* __restrict__ Y, in
 #pragma unroll
       for (int e = 0; e < 16; ++e) acc[i][j][e] = 0.0f;
 
-  for (int64_t k0 = 0; k0 < K; k0 += 64) {
-    u32x4_t a[FM][4], b[FN][4];
+  // the operands of chunk k0 + 64 are loaded while chunk k0 is multiplied (two register sets)
+  u32x4_t a[2][FM][4], b[2][FN][4];
+  auto load = [&](int buf, int64_t k0) {
 #pragma unroll
     for (int i = 0; i < FM; ++i)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) a[i][t] = reinterpret_cast<const u32x4_t*>(pa[i] + k0)[t];
+      for (int t = 0; t < 4; ++t) a[buf][i][t] = reinterpret_cast<const u32x4_t*>(pa[i] + k0)[t];
 #pragma unroll
     for (int j = 0; j < FN; ++j)
 #pragma unroll
-      for (int t = 0; t < 4; ++t) b[j][t] = reinterpret_cast<const u32x4_t*>(pb[j] + k0)[t];
+      for (int t = 0; t < 4; ++t) b[buf][j][t] = reinterpret_cast<const u32x4_t*>(pb[j] + k0)[t];
+  };
+  auto mul = [&](int buf) {
 #pragma unroll
     for (int t = 0; t < 4; ++t)
 #pragma unroll
@@ -73,8 +76,17 @@ __global__ __launch_bounds__(kThreads) void k_score(uint16_t* __restrict__ Y, in
 #pragma unroll
         for (int j = 0; j < FN; ++j)
           acc[i][j] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-              __builtin_bit_cast(bf16x8_t, a[i][t]), __builtin_bit_cast(bf16x8_t, b[j][t]),
+              __builtin_bit_cast(bf16x8_t, a[buf][i][t]), __builtin_bit_cast(bf16x8_t, b[buf][j][t]),
               acc[i][j], 0, 0, 0);
+  };
+  load(0, 0);
+  for (int64_t k0 = 0; k0 < K; k0 += 128) {
+    if (k0 + 64 < K) load(1, k0 + 64);
+    mul(0);
+    if (k0 + 64 < K) {
+      if (k0 + 128 < K) load(0, k0 + 128);
+      mul(1);
+    }
   }
 
   // 32x32 accumulator layout: lane holds column r32 and rows (e/4)*8 + 4h + e%4
