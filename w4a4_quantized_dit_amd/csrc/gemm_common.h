@@ -13,6 +13,16 @@ namespace svdq {
 // compact block of tiles and share their A rows and W columns in that XCD's L2.  Returns false
 // for the few padding workgroups of the last run.
 constexpr int kGroupM = 8;
+__device__ __forceinline__ void tile_of_seq32(int seq, int tiles_m, int tiles_n, int& tm,
+                                              int& tn) {
+  const int span = kGroupM * tiles_n;
+  const int first = (seq / span) * kGroupM;
+  const int rows = tiles_m - first < kGroupM ? tiles_m - first : kGroupM;
+  const int w = seq % span;
+  tm = first + w % rows;
+  tn = w / rows;
+}
+
 __device__ __forceinline__ bool tile_of_block(int64_t tiles_m, int64_t tiles_n, int64_t& tm,
                                               int64_t& tn) {
   const int64_t total = tiles_m * tiles_n;

@@ -14,6 +14,8 @@
 // K mapping: MFMA step t of a 64-element stage covers elements [16t, 16t + 16); lane (row =
 // lane % 32, h = lane / 32) supplies elements [16t + 8h, 16t + 8h + 8) of its row, for A and W
 // alike, so every product pairs equal K indices.
+#include <atomic>
+
 #include "device.h"
 #include "gemm_common.h"
 #include "launch.h"
@@ -86,32 +88,54 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
     const int32_t* __restrict__ row_to_cube, uint16_t* __restrict__ Y, int64_t ldy) {
   constexpr int FM = 4, FN = 2;
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
-  int64_t tm, tn;
-  if (!tile_of_block((M + kBM - 1) / kBM, N / kBN, tm, tn)) return;
-  const int64_t m0 = tm * kBM, n0 = tn * kBN;
+  // Tile walk: workgroup `slot` of an XCD takes positions slot, slot + P, slot + 2P, ... of that
+  // XCD's run of the tile sequence (P workgroups per XCD; P = the run's length gives one tile per
+  // workgroup).  The next tile's first loads are issued before the current tile's store, so its
+  // load latency and the store's write burst overlap instead of following one another.
+  // (Tile counts fit 32 bits: M < 2^31 rows and N < 2^31 columns in tiles of 256.)
+  const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)(N / kBN);
+  const int total = tiles_m * tiles_n, per_xcd = (total + 7) / 8;
+  const int P = (int)gridDim.x / 8, xcd = (int)blockIdx.x % 8, slot = (int)blockIdx.x / 8;
+  auto seq_of = [&](int k) -> int {
+    const int w = slot + P * k, sq = xcd * per_xcd + w;
+    return (w < per_xcd && sq < total) ? sq : -1;
+  };
+  const int seq0 = seq_of(0);
+  if (seq0 < 0) return;
   const int tid = threadIdx.x;
   const int wave = tid >> 6, lane = tid & 63;
   const int wm = wave >> 2, wn = wave & 3;
-  const int64_t m_base = m0 + wm * 128, n_base = n0 + wn * 64;
   const int r32 = lane & 31, h = lane >> 5;
   const int64_t kb = K / 2, ks = K / 16;
   const int64_t nstage = K / kBK;    // a multiple of 4 (K % 256 == 0)
   const int64_t nround = nstage / 2;  // code rounds of two stages
   const int64_t nchunk = nstage / 4;  // scale chunks of four stages
 
-  // Conversion share: operand co (0 A, 1 W), row crow.  Rows of A past M read row M-1 (never
-  // stored).
+  // Conversion share: operand co (0 A, 1 W), row crow of the tile.  Rows of A past M read row
+  // M-1 (never stored).
   const int co = tid & 1, crow = tid >> 1;
-  int64_t ar = m0 + crow;
-  ar = ar < M ? ar : M - 1;
-  const uint8_t* pcode = co ? B + (n0 + crow) * kb : A + ar * kb;
   const int w_base = co * kWOffset + crow * kRowBytes;
   const int w_swz = swz(crow) ^ (co << 2);
+  const uint8_t* pcode;
+  const uint8_t* pscale;
+  int64_t m_base, n_base;
+  // the conversion rows of tile `sq` (and its wave-tile origin: m0 + 128 wm, n0 + 64 wn)
+  auto tile_rows = [&](int sq, int64_t& mb, int64_t& nb) {
+    int tm, tn;
+    tile_of_seq32(sq, tiles_m, tiles_n, tm, tn);
+    const int64_t m0 = (int64_t)tm * kBM, n0 = (int64_t)tn * kBN;
+    int64_t ar = m0 + crow;
+    ar = ar < M ? ar : M - 1;
+    pcode = co ? B + (n0 + crow) * kb : A + ar * kb;
+    pscale = co ? Bs + (n0 + crow) * ks : As + ar * ks;
+    mb = m0 + wm * 128;
+    nb = n0 + wn * 64;
+  };
+  tile_rows(seq0, m_base, n_base);
 
   // Scale chunks: the thread fetches the 16 scale bytes (four stages) of its own row and operand
   // into LDS slot tid (global_load_lds puts lane l of wave w at w * 1024 + 16 l) and reads them
   // back from there.
-  const uint8_t* pscale = co ? Bs + (n0 + crow) * ks : As + ar * ks;
   auto load_scales = [&](int buf, int64_t c) {
     __builtin_amdgcn_global_load_lds((gvoid_t*)(pscale + c * 16),
                                      (lvoid_t*)(lds + kScaleOffset + buf * kScaleChunk +
@@ -158,29 +182,41 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
       fb[j] = *reinterpret_cast<const f16x8_t*>(lds + buf * kOpBytes + rb[t] + j * 32 * kRowBytes);
   };
 
-  // prologue: scale chunks 0, 1 and code rounds 0, 1 in flight, low-rank term into the
-  // accumulators, stage 0 converted into buffer 0
-  const float gsc = g_a[0] * g_w[0];
-  load_scales(0, 0);
-  load_scales(1, nchunk > 1 ? 1 : 0);
+  // a tile's first loads: scale chunks 0, 1 and code rounds 0, 1
   u32x4_t g0[4], g1[4];
-  load_round(g0, 0);
-  load_round(g1, nround > 1 ? 1 : 0);
+  auto first_loads = [&]() {
+    load_scales(0, 0);
+    load_scales(1, nchunk > 1 ? 1 : 0);
+    load_round(g0, 0);
+    load_round(g1, nround > 1 ? 1 : 0);
+  };
+  const float gsc = g_a[0] * g_w[0];
+  first_loads();
   f32x16_t acc[FM][FN];
-  gemm_lowrank_init<FM, FN>(acc, 1.0f / gsc, M, m_base, n_base, r32, h, D, up, r);
-  wait_vmcnt<0>();
-  barrier_lds();
-  u32x4_t sq = read_chunk(0);  // scales of stages 4c .. 4c + 3 (chunk c of the stage converted)
-  {
-    f16x2_t s01, s23;
-    stage_scales(sq[0], s01, s23);
-    const uint32_t* w = reinterpret_cast<const uint32_t*>(g0);
-#pragma unroll
-    for (int d = 0; d < 8; ++d) convert(w, s01, s23, 0, d);
-  }
-  barrier_lds();
+  u32x4_t sq;  // scales of stages 4c .. 4c + 3 (chunk c of the stage converted)
   f16x8_t a_op[FM], b_op[FN];
-  read_frags(0, 0, a_op, b_op);
+  // prologue of a tile (its first loads in flight): low-rank term into the accumulators, stage 0
+  // converted into buffer 0
+  auto prologue = [&]() {
+    // (lane behind an opaque copy per tile: the compiler would otherwise compute the store's and
+    // the low-rank term's lane-dependent addresses once, before the tile loop, and keep them
+    // live through the main loop)
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    gemm_lowrank_init<FM, FN>(acc, 1.0f / gsc, M, m_base, n_base, lo & 31, lo >> 5, D, up, r);
+    wait_vmcnt<0>();
+    barrier_lds();
+    sq = read_chunk(0);
+    {
+      f16x2_t s01, s23;
+      stage_scales(sq[0], s01, s23);
+      const uint32_t* w = reinterpret_cast<const uint32_t*>(g0);
+#pragma unroll
+      for (int d = 0; d < 8; ++d) convert(w, s01, s23, 0, d);
+    }
+    barrier_lds();
+    read_frags(0, 0, a_op, b_op);
+  };
 
   // Iteration s computes stage s from buffer s % 2 while converting stage s+1 (words w of a
   // register round) into the other buffer.  Extra work of the four-stage pattern, by s % 4:
@@ -237,19 +273,35 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
     barrier_lds();
     read_frags(p ^ 1, 0, a_op, b_op);
   };
-  for (int64_t s = 0; s < nstage; s += 4) {
-    // stage s+1: second half of round s/2 (g0); s+2, s+3: round s/2 + 1 (g1); s+4: g0 again
-    iteration(std::integral_constant<int, 0>{}, s, reinterpret_cast<const uint32_t*>(g0) + 8, g0);
-    iteration(std::integral_constant<int, 1>{}, s + 1, reinterpret_cast<const uint32_t*>(g1), g1);
-    iteration(std::integral_constant<int, 2>{}, s + 2, reinterpret_cast<const uint32_t*>(g1) + 8, g1);
-    iteration(std::integral_constant<int, 3>{}, s + 3, reinterpret_cast<const uint32_t*>(g0), g0);
+  for (int k = 0;; ++k) {
+    prologue();
+    for (int64_t s = 0; s < nstage; s += 4) {
+      // stage s+1: second half of round s/2 (g0); s+2, s+3: round s/2 + 1 (g1); s+4: g0 again
+      iteration(std::integral_constant<int, 0>{}, s, reinterpret_cast<const uint32_t*>(g0) + 8, g0);
+      iteration(std::integral_constant<int, 1>{}, s + 1, reinterpret_cast<const uint32_t*>(g1), g1);
+      iteration(std::integral_constant<int, 2>{}, s + 2, reinterpret_cast<const uint32_t*>(g1) + 8, g1);
+      iteration(std::integral_constant<int, 3>{}, s + 3, reinterpret_cast<const uint32_t*>(g0), g0);
+    }
+    // The next tile's first loads go out before this tile's store: the loads the last
+    // iterations repeated past the end have landed first (the scale buffers are rewritten),
+    // and g0, g1 are free.
+    // Every wave passed the last barrier after its final fragment reads: the fp16 buffers are
+    // free for the output staging (each wave its own 16 KB; the scale chunks lie above them).
+    static_assert(8 * gemm_store_bytes<FM, FN>() <= kScaleOffset, "output staging fits the LDS");
+    int lo = lane;
+    asm volatile("" : "+v"(lo));
+    gemm_store<FM, FN>(acc, gsc, lds + wave * gemm_store_bytes<FM, FN>(), lo, M, N, m_base,
+                       n_base, core_out, row_to_cube, Y, ldy);
+    const int seq_n = seq_of(k + 1);
+    if (seq_n < 0) break;
+    // the next tile: the loads the last iterations repeated past the end have landed (the scale
+    // buffers are rewritten), the store's writes drain while the tile starts
+    wait_vmcnt<0>();
+    tile_rows(seq_n, m_base, n_base);
+    first_loads();
+    // every wave's staging reads are done before stage 0 is converted into buffer 0
+    barrier_lds();
   }
-
-  // Every wave passed the last barrier after its final fragment reads: the fp16 buffers are
-  // free for the output staging (each wave its own 16 KB).
-  static_assert(8 * gemm_store_bytes<FM, FN>() <= kScaleOffset, "output staging fits the LDS");
-  gemm_store<FM, FN>(acc, gsc, lds + wave * gemm_store_bytes<FM, FN>(), lane, M, N, m_base, n_base,
-                     core_out, row_to_cube, Y, ldy);
 }
 
 }  // namespace
@@ -264,6 +316,21 @@ hipError_t launch_gemm_mx(int fp8, int64_t M, int64_t N, int64_t K, const uint8_
                           const uint8_t* w_scales, const float* D, const uint16_t* up, int64_t r,
                           uint16_t* Y, int64_t ldy, hipStream_t s);
 
+int device_cus() {
+  static std::atomic<int> cache[64];
+  int dev = 0;
+  if (hipGetDevice(&dev) != hipSuccess || dev < 0) return 0;
+  if (dev < 64) {
+    const int v = cache[dev].load(std::memory_order_relaxed);
+    if (v > 0) return v;
+  }
+  int n = 0;
+  if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess)
+    return 0;
+  if (dev < 64) cache[dev].store(n, std::memory_order_relaxed);
+  return n;
+}
+
 hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const void* a_scales, const float* g_a, const uint8_t* w_codes,
                        const void* w_scales, const float* g_w, const float* D,
@@ -275,7 +342,11 @@ hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* 
     return launch_gemm_mx(fmt == 3, M, N, K, a_codes, reinterpret_cast<const uint8_t*>(a_scales),
                           w_codes, reinterpret_cast<const uint8_t*>(w_scales), D, up, r, Y, ldy,
                           s);
-  const dim3 grid(grid_of_tiles((M + kBM - 1) / kBM, N / kBN));
+  // one workgroup per CU walking its XCD's share of the tile sequence
+  const int64_t total = ((M + kBM - 1) / kBM) * (N / kBN), per_xcd = (total + 7) / 8;
+  int64_t per = device_cus() / 8;
+  if (per < 1 || per > per_xcd) per = per_xcd;
+  const dim3 grid((unsigned)(8 * per));
   k_gemm_nvfp4<<<grid, dim3(kThreads), 0, s>>>(
       M, N, K, a_codes, reinterpret_cast<const uint8_t*>(a_scales), g_a, w_codes,
       reinterpret_cast<const uint8_t*>(w_scales), g_w, D, up, (int)r, core_out, row_to_cube, Y,

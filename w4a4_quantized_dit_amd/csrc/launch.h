@@ -52,6 +52,9 @@ hipError_t launch_quant_act(int fmt, const uint16_t* X, int64_t M, int64_t K, in
 size_t quant_act_lds_bytes(int64_t K, int64_t r);
 
 
+// Compute units of the current device (cached per device; 0 if the query fails).
+int device_cus();
+
 hipError_t launch_gemm(int fmt, int64_t M, int64_t N, int64_t K, const uint8_t* a_codes,
                        const void* a_scales, const float* g_a, const uint8_t* w_codes,
                        const void* w_scales, const float* g_w, const float* D,
