@@ -23,6 +23,26 @@ typedef __attribute__((ext_vector_type(2))) uint16_t u16x2_t;
 constexpr int NVFP4_BLOCK = 16;
 constexpr int INT4_GROUP = 64;
 
+// Raw (unstrided) buffer resource over `bytes` bytes from `base`.  A buffer load whose offset is
+// at or past `bytes` returns zeros without touching memory, so a look-ahead load that has run
+// past the data can still be issued, with kNoLoad as its offset: every path through a loop then
+// issues the same loads, which keeps the compiler's wait counts exact instead of draining the
+// loads in flight at the loop head.
+constexpr uint32_t kNoLoad = 0x80000000u;
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t raw_rsrc(const void* base, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), (short)0, (int)bytes,
+                                           0x00020000);
+}
+// Cache-policy operand of a streaming (nontemporal) buffer load.
+constexpr int kNt = 2;
+
+// s_waitcnt vmcnt(n) (other counters untouched), gfx9 encoding
+template <int N>
+__device__ __forceinline__ void wait_vmcnt() {
+  static_assert(N >= 0 && N < 64, "vmcnt range");
+  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
+}
+
 __device__ __forceinline__ float bf16_lo(uint32_t w) { return __uint_as_float(w << 16); }
 __device__ __forceinline__ float bf16_hi(uint32_t w) { return __uint_as_float(w & 0xFFFF0000u); }
 __device__ __forceinline__ float bf16_to_f32(uint16_t b) { return __uint_as_float((uint32_t)b << 16); }

@@ -305,12 +305,6 @@ __device__ __forceinline__ int dma_chunk_swz(int row) {
   return FP8 ? (row >> 1) & 7 : (row >> 2) & 3;
 }
 
-// s_waitcnt vmcnt(n) (other counters untouched), gfx9 encoding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 // This wave's share of one stage: code chunks (chunk id c of an operand: row c / kChunks, stored
 // part c % kChunks holding logical part (c % kChunks) ^ f(row)); then the scale dwords of 64 rows

@@ -72,12 +72,6 @@ __device__ __forceinline__ void barrier_lds() {
   asm volatile("s_waitcnt lgkmcnt(0)\n\ts_barrier" ::: "memory");
 }
 
-// s_waitcnt vmcnt(n) (other counters untouched), gfx9 encoding
-template <int N>
-__device__ __forceinline__ void wait_vmcnt() {
-  static_assert(N >= 0 && N < 64, "vmcnt range");
-  __builtin_amdgcn_s_waitcnt((N & 15) | ((N >> 4) << 14) | (7 << 4) | (15 << 8));
-}
 
 __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
     int64_t M, int64_t N, int64_t K, const uint8_t* __restrict__ A,

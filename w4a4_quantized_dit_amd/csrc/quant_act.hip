@@ -51,8 +51,6 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
   extern __shared__ float s_inv[];
   __shared__ __attribute__((aligned(16))) uint16_t s_x[kWaves * kSplit][16 * kPitch];
   __shared__ __attribute__((aligned(16))) uint16_t s_l[kSplit][NTc * 16 * kPitch];
-  for (int64_t k = threadIdx.x; k < K; k += kThreads)
-    s_inv[k + 4 * (k >> 6)] = lambda ? 1.0f / lambda[k] : 1.0f;
 
   float amax = 0.0f, g = 1.0f, d6 = 6.0f;
   if (FMT == 0) {
@@ -72,25 +70,29 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
   const int64_t nloop = (nchunk + kSplit - 1) / kSplit;
 
   // coalesced X loads: instruction i covers rows 2i, 2i+1 of the wave, lane piece = lane % 32
-  // (rows past M read row M-1; their results are never stored)
-  // (element offsets from the block's first row fit 32 bits: 64 rows of at most ldx each,
-  // and the entry points refuse ldx above 2^24)
-  const uint16_t* xblk = X + (int64_t)blockIdx.x * kRowsPerBlock * ldx;
+  // (rows past M read row M-1; their results are never stored).  Byte offsets from the block's
+  // first row stay below 2^31: 64 rows of at most ldx elements each, and the entry points refuse
+  // ldx above 2^24.
+  const int64_t blk_row = (int64_t)blockIdx.x * kRowsPerBlock;
+  const int64_t blk_rows = M - blk_row < kRowsPerBlock ? M - blk_row : kRowsPerBlock;
+  const __amdgpu_buffer_rsrc_t x_rsrc =
+      raw_rsrc(X + blk_row * ldx, (uint32_t)(((blk_rows - 1) * ldx + K) * 2));
   uint32_t xo[8];
 #pragma unroll
   for (int i = 0; i < 8; ++i) {
     int64_t xrow = row0 + 2 * i + (lane >> 5);
     xrow = xrow < M ? xrow : M - 1;
-    xo[i] = (uint32_t)((xrow - (int64_t)blockIdx.x * kRowsPerBlock) * ldx + 8 * (lane & 31));
+    xo[i] = (uint32_t)(((xrow - blk_row) * ldx + 8 * (lane & 31)) * 2);
   }
   // L1 staging within the K group: piece p = rank p / 32, channels 8 * (p % 32) .. +8 (ranks
   // past r read rank r-1 and are zeroed)
+  const __amdgpu_buffer_rsrc_t l_rsrc = raw_rsrc(down, (uint32_t)(r > 0 ? r * K * 2 : 0));
   uint32_t lo[kLPieces > 0 ? kLPieces : 1];
 #pragma unroll
   for (int u = 0; u < kLPieces; ++u) {
     const int p = gtid + kGroupThreads * u;
     const int n = p >> 5;
-    lo[u] = (uint32_t)((n < r ? n : r - 1) * K + 8 * (p & 31));
+    lo[u] = (uint32_t)(((n < r ? n : r - 1) * K + 8 * (p & 31)) * 2);
   }
 
   f32x4_t acc[NTc];
@@ -103,26 +105,57 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
   // measured no faster with the second set); the L1 slice one chunk ahead.  The L1 loads are
   // issued before the X loads they are consumed with, because loads complete in issue order for
   // the wait counter: waiting for the L1 slice then leaves the younger X prefetch in flight.
+  // Look-ahead loads past the last chunk are still issued, out of the buffers' range (zeros, no
+  // memory access), so that every iteration issues the same loads and the compiler can count
+  // them across the loop instead of draining the look-ahead at the loop head.
   constexpr int kAhead = (FMT == 0 || FMT == 3) ? 2 : 1;
   u32x4_t xa[8], xb[8], lr[kLPieces > 0 ? kLPieces : 1];
   auto load_x = [&](u32x4_t (&xr)[8], int64_t kc) {
-    if (kc < nchunk) {
+    const uint32_t at = kc < nchunk ? (uint32_t)(kc * kChunk * 2) : kNoLoad;
 #pragma unroll
-      for (int i = 0; i < 8; ++i)
-        xr[i] = __builtin_nontemporal_load(
-            reinterpret_cast<const u32x4_t*>(xblk + kc * kChunk + xo[i]));
-    }
+    for (int i = 0; i < 8; ++i)
+      xr[i] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(x_rsrc, (int)(xo[i] + at), 0, kNt));
   };
   auto load_l = [&](int64_t kc) {
-    if (kc < nchunk) {
+    const uint32_t at = kc < nchunk ? (uint32_t)(kc * kChunk * 2) : kNoLoad;
 #pragma unroll
-      for (int u = 0; u < kLPieces; ++u)
-        lr[u] = *reinterpret_cast<const u32x4_t*>(down + kc * kChunk + lo[u]);
-    }
+    for (int u = 0; u < kLPieces; ++u)
+      lr[u] = __builtin_bit_cast(
+          u32x4_t, __builtin_amdgcn_raw_buffer_load_b128(l_rsrc, (int)(lo[u] + at), 0, 0));
   };
   load_l(ks);
   load_x(xa, ks);
   if (kAhead == 2) load_x(xb, ks + kSplit);
+  // 1/λ of every channel, its loads issued after the first chunks' so that the two latencies
+  // overlap
+  if (lambda) {
+    // 16 channels per thread at a time; the first batch outside any loop, so that the wait for
+    // its loads does not also wait for the X look-ahead issued before it
+    const __amdgpu_buffer_rsrc_t lam_rsrc = raw_rsrc(lambda, (uint32_t)(K * 4));
+    auto inv_batch = [&](int64_t k0) {
+      float v[16];
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t k = k0 + threadIdx.x + kThreads * j;
+        v[j] = __builtin_bit_cast(
+            float, __builtin_amdgcn_raw_buffer_load_b32(
+                       lam_rsrc, (int)(k < K ? (uint32_t)(k * 4) : kNoLoad), 0, 0));
+      }
+#pragma unroll
+      for (int j = 0; j < 16; ++j) {
+        const int64_t k = k0 + threadIdx.x + kThreads * j;
+        if (k < K) s_inv[k + 4 * (k >> 6)] = 1.0f / v[j];
+      }
+      // nothing of the batch is left in flight (the X look-ahead, older, has completed too);
+      // stated explicitly so that the compiler's wait counting at the main loop starts clean
+      wait_vmcnt<0>();
+    };
+    inv_batch(0);
+    for (int64_t k0 = 16 * kThreads; k0 < K; k0 += 16 * kThreads) inv_batch(k0);
+  } else {
+    for (int64_t k = threadIdx.x; k < K; k += kThreads) s_inv[k + 4 * (k >> 6)] = 1.0f;
+  }
   __syncthreads();  // s_inv complete
 
   auto body = [&](int64_t it, u32x4_t (&xr)[8]) {
@@ -277,10 +310,13 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
     __syncthreads();  // the LDS chunk buffers are rewritten next iteration
   };
   if (kAhead == 2) {
-    for (int64_t it = 0; it < nloop; it += 2) {
+    // both bodies on every path through the loop (see the look-ahead loads above)
+    int64_t it = 0;
+    for (; it + 1 < nloop; it += 2) {
       body(it, xa);
-      if (it + 1 < nloop) body(it + 1, xb);
+      body(it + 1, xb);
     }
+    if (it < nloop) body(it, xa);
   } else {
     for (int64_t it = 0; it < nloop; ++it) body(it, xa);
   }
