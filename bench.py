@@ -50,6 +50,9 @@ PEAK_I8_TOPS = 5000.0         # MI355X dense int8 MFMA
 PEAK_FP8_TFLOPS = 5000.0      # MI355X dense fp8 MFMA
 PEAK_FP4_TFLOPS = 10100.0     # MI355X dense fp4 / fp6 MFMA
 PEAK_HBM_GBS = 8000.0         # MI355X HBM3E
+# Vector ALU, one fp32 lane operation per lane and clock without packed instructions: 256 CUs x
+# 4 SIMDs x 16 lanes x 2.4 GHz, in tera-operations per second.
+PEAK_VALU_TOPS = 256 * 4 * 16 * 2.4e9 / 1e12
 WORKLOADS = {"attn": 1, "attn-mxfp4": 1, "attn-mxfp8": 1, "mlp-up-int4": 2,
              "mlp-down-sweep": 3, "delta": 4}
 MX_FORMATS = {"attn-mxfp4": (2, "mxfp4"), "attn-mxfp8": (3, "mxfp8")}
@@ -626,6 +629,15 @@ def main():
                      "unit": "TFLOP/s", "frac": round(gemm_tflops / peak, 4),
                      "traffic": measured_traffic(args.workload)},
     }
+    if args.workload == "mlp-up-int4":
+        # The exact int4 route rescales every 64-group partial sum of every output element on
+        # the vector ALU (convert, scale product, fused multiply-add): that, not the MFMA, bounds
+        # the kernel, so its roofline is the vector ALU's lane-operation rate.
+        valu_tops = 3.0 * M * N * (K // 64) / (ms["gemm"] * 1e-3) / 1e12
+        out["roofline"] = {"bound": "alu", "achieved": round(valu_tops, 2),
+                           "peak": round(PEAK_VALU_TOPS, 2), "unit": "TOP/s",
+                           "frac": round(valu_tops / PEAK_VALU_TOPS, 4),
+                           "traffic": measured_traffic(args.workload)}
     if "core" in ms:
         out["core_gemm_tflops"] = round(st["core_flops"] / (ms["core"] * 1e-3) / 1e12, 2)
     if args.workload == "mlp-down-sweep":
