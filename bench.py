@@ -495,13 +495,16 @@ def run_steps(torch, st, n, warm, record, settle_s=0.0):
         for _, fn in st["steps"]:
             fn(st["Xs"][i % n_rot])
 
+    # the collector runs before the settling steps, not after them: a collection takes tens of
+    # milliseconds, long enough for the GPU to drain its queue and idle, and the launches that
+    # follow such an idle gap run slower for a while
+    gc.collect()
+    gc.disable()           # no collector pause from here to the end of the measured region
     t_settle = time.perf_counter()
     i = 0
     while time.perf_counter() - t_settle < settle_s:
         one(i)         # no synchronisation: once the launch queue is full the host waits in it
         i += 1
-    gc.collect()
-    gc.disable()           # no collector pause inside the measured region
     for j in range(warm):
         one(i + j)
     torch.cuda.synchronize()
