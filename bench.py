@@ -104,6 +104,28 @@ def measured_traffic(workload):
     return float(val.group(1))
 
 
+def gpu_cotenants():
+    """Other processes holding a GPU context on this machine (the driver lists one directory per
+    process under /sys/class/kfd/kfd/proc), read just before the timed steps; None where that
+    listing does not exist."""
+    root = "/sys/class/kfd/kfd/proc"
+    try:
+        pids = sorted(int(p) for p in os.listdir(root) if p.isdigit())
+    except OSError:
+        return None
+    others = []
+    for pid in pids:
+        if pid == os.getpid():
+            continue
+        try:
+            with open(f"/proc/{pid}/comm") as f:
+                name = f.read().strip()
+        except OSError:
+            name = "?"
+        others.append({"pid": pid, "name": name})
+    return {"source": root, "count": len(others), "processes": others[:16]}
+
+
 def percentiles(v):
     v = np.asarray(v, dtype=np.float64)
     return {"mean": round(float(v.mean()), 4), "p10": round(float(np.percentile(v, 10)), 4),
@@ -568,6 +590,7 @@ def main():
     seg = cfg["seg"]
     names = list(dict.fromkeys(nm for nm, _ in st["steps"]))
 
+    cotenants = gpu_cotenants()
     print("[bench] warmup + timed steps", file=sys.stderr, flush=True)
     wall, per = run_steps(torch, st, args.steps, args.warmup, record=True,
                           settle_s=args.settle_ms * 1e-3)
@@ -613,6 +636,7 @@ def main():
                                                                  seg[3] - seg[2]],
                    "lambda": lam_desc, "step": " + ".join(nm for nm, _ in st["steps"]),
                    "x_copies_rotated": st["n_rot"]},
+        "gpu_cotenants": cotenants,
         "kernels_ms": {k: round(v, 4) for k, v in ms.items()},
         "kernel_stats_ms": stats,
         "lowrank_factors_ms": round(st["lowrank_ms"], 3),

@@ -28,7 +28,11 @@ constexpr int kJacobiThreads = 1024;
 constexpr int kMaxSweeps = 40;
 constexpr int kLdsEll = 80;        // the small factorisations run in LDS up to this ell
 constexpr int kCholThreads = 512;  // threads of the small Cholesky-inverse workgroup
-constexpr int kJacLdsEll = 64;     // the Jacobi eigensolver keeps two H buffers and V in LDS up to this ell
+constexpr int kJacHLdsEll = 138;   // the Jacobi eigensolver keeps H in LDS up to this ell
+constexpr int kJacVLdsEll = 64;    // and V as well up to this ell
+constexpr int kJacItems = (kMaxEll / 2 * kMaxEll + kJacobiThreads - 1) / kJacobiThreads;  // per thread and pass
+// odd row pitch of the Jacobi H in LDS: a column of H then spreads over the banks
+__host__ __device__ constexpr int jacobi_pitch(int ell) { return ell | 1; }
 
 // The matrix is either the bf16 weight (scaled by λ per channel) or an fp32 matrix (the refit
 // target of the layer's low-rank branch).
@@ -362,57 +366,94 @@ __global__ __launch_bounds__(256) void k_apply_rinv(const float* __restrict__ M,
   Mo[t] = (float)acc;
 }
 
-// Parallel cyclic Jacobi on the symmetric H (ell x ell, fp64, in place; both in global memory,
-// one workgroup), eigenvectors accumulated in V; then the eigenpairs sorted by decreasing
-// eigenvalue: eig[i], U[:, i].  Rounds pair the indices by the circle method (index 0 fixed,
-// the others rotating); an odd ell gets a dummy index that sits out its pairs.
+// Parallel cyclic Jacobi on the symmetric H (ell x ell, fp64), eigenvectors accumulated as the
+// rows of Vt (Vt = Vᵀ); then the eigenpairs sorted by decreasing eigenvalue: eig[i], U[:, i].
+// Rounds pair the indices by the circle method (index 0 fixed, the others rotating); an odd ell
+// gets a dummy index that sits out its pairs.  A round applies its rotations in place: rows p
+// and q of H and of Vt, a barrier, then columns p and q of H.  H lives in LDS up to kJacHLdsEll
+// with an odd row pitch (the column pass then reads and writes across the banks instead of
+// one bank in sixteen), Vt too up to kJacVLdsEll; larger ones stay in the caller's buffers
+// (same arithmetic).
 __global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ Hg, int ell,
                                                            double* __restrict__ Vg,
                                                            double* __restrict__ U,
-                                                           double* __restrict__ eig,
-                                                           double* __restrict__ H2g) {
+                                                           double* __restrict__ eig) {
+  extern __shared__ double s_dyn[];  // H (ell x jacobi_pitch, when in LDS), then Vt (ell²)
   __shared__ double s_c[kMaxEll / 2], s_s[kMaxEll / 2];
   __shared__ int s_p[kMaxEll / 2], s_q[kMaxEll / 2];
-  __shared__ double s_self[kMaxEll], s_cp[kMaxEll];   // per index: own and partner coefficient
-  __shared__ int s_partner[kMaxEll];
-  __shared__ double s_red[kJacobiThreads], s_red2[kJacobiThreads];
+  __shared__ double s_red[2][kJacobiThreads / 64];
   __shared__ int s_order[kMaxEll];
   __shared__ int s_done;
-  __shared__ double s_h[kJacLdsEll * kJacLdsEll], s_h2[kJacLdsEll * kJacLdsEll];
-  __shared__ double s_v[kJacLdsEll * kJacLdsEll];
-  const int tid = threadIdx.x;
-  // H (two buffers: a round reads one and writes the other) and V live in LDS when they fit, in
-  // the caller's buffers otherwise (same arithmetic)
-  const bool in_lds = ell <= kJacLdsEll;
-  double* H = in_lds ? s_h : Hg;
-  double* Hn = in_lds ? s_h2 : H2g;
-  double* V = in_lds ? s_v : Vg;
-  if (in_lds)
-    for (int t = tid; t < ell * ell; t += kJacobiThreads) s_h[t] = Hg[t];
+  __shared__ double s_prev;
+  const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+  if (tid == 0) s_prev = 0.0;
+  const bool h_lds = ell <= kJacHLdsEll, v_lds = ell <= kJacVLdsEll;
+  const int ldh = h_lds ? jacobi_pitch(ell) : ell;
+  double* H = h_lds ? s_dyn : Hg;
+  double* Vt = v_lds ? s_dyn + (h_lds ? ell * ldh : 0) : Vg;
+  if (h_lds)
+    for (int t = tid; t < ell * ell; t += kJacobiThreads) H[(t / ell) * ldh + t % ell] = Hg[t];
   const int m = (ell + 1) & ~1;  // even player count
   const int half = m / 2;
-  for (int t = tid; t < ell * ell; t += kJacobiThreads) V[t] = (t / ell == t % ell) ? 1.0 : 0.0;
-  if (tid == 0) s_done = 0;
+  for (int t = tid; t < ell * ell; t += kJacobiThreads) Vt[t] = (t / ell == t % ell) ? 1.0 : 0.0;
+  // One rotation pass of a round over A (row pitch ld): rows p, q (by_row) or columns p, q of
+  // every pair of the round, for every position along them.  Item t of the pass is (pair
+  // t / ell, position t % ell); a thread's items are fixed for the whole solve, so their
+  // coordinates are computed once.
+  int item_pr[kJacItems], item_x[kJacItems];
+#pragma unroll
+  for (int k = 0; k < kJacItems; ++k) {
+    const int t = tid + k * kJacobiThreads;
+    item_pr[k] = t < half * ell ? t / ell : -1;
+    item_x[k] = t < half * ell ? t % ell : 0;
+  }
+  auto rotate = [&](double* A, int ld, bool by_row) {
+#pragma unroll
+    for (int k = 0; k < kJacItems; ++k) {
+      const int pr = item_pr[k];
+      if (pr < 0) break;
+      const int p = s_p[pr], q = s_q[pr];
+      if (q < 0) continue;
+      const int x = item_x[k];
+      const int ip = by_row ? p * ld + x : x * ld + p;
+      const int iq = by_row ? q * ld + x : x * ld + q;
+      const double ap = A[ip], aq = A[iq];
+      const double c = s_c[pr], sn = s_s[pr];
+      A[ip] = c * ap - sn * aq;
+      A[iq] = sn * ap + c * aq;
+    }
+  };
   __syncthreads();
   for (int sweep = 0; sweep < kMaxSweeps; ++sweep) {
     // convergence: off-diagonal mass against the whole matrix
     double off = 0.0, all = 0.0;
     for (int t = tid; t < ell * ell; t += kJacobiThreads) {
-      const double h = H[t];
+      const int a = t / ell, b = t % ell;
+      const double h = H[a * ldh + b];
       all += h * h;
-      if (t / ell != t % ell) off += h * h;
+      if (a != b) off += h * h;
     }
-    s_red[tid] = off;
-    s_red2[tid] = all;
+    for (int o = 32; o > 0; o >>= 1) {
+      off += __shfl_xor(off, o);
+      all += __shfl_xor(all, o);
+    }
+    if (lane == 0) {
+      s_red[0][wave] = off;
+      s_red[1][wave] = all;
+    }
     __syncthreads();
-    for (int w = kJacobiThreads / 2; w > 0; w >>= 1) {
-      if (tid < w) {
-        s_red[tid] += s_red[tid + w];
-        s_red2[tid] += s_red2[tid + w];
+    if (tid == 0) {
+      double so = 0.0, sa = 0.0;
+      for (int w = 0; w < kJacobiThreads / 64; ++w) {
+        so += s_red[0][w];
+        sa += s_red[1][w];
       }
-      __syncthreads();
+      // done at 1e-15 of the norm, or once the off-diagonal mass, already below 1e-10 of the
+      // norm (the quadratic phase), no longer falls 4x per sweep: it has reached the rounding
+      // floor of the rotations, which for larger ell lies above 1e-15
+      s_done = (so <= 1e-30 * sa || (so <= 1e-20 * sa && so >= 0.25 * s_prev)) ? 1 : 0;
+      s_prev = so;
     }
-    if (tid == 0) s_done = (s_red[0] <= 1e-30 * s_red2[0]) ? 1 : 0;
     __syncthreads();
     if (s_done) break;
     for (int round = 0; round < m - 1; ++round) {
@@ -426,55 +467,29 @@ __global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ 
           b = 1 + (round - tid + (m - 1)) % (m - 1);
         }
         const int p = a < b ? a : b, q = a < b ? b : a;
-        double c = 1.0, s = 0.0;
+        double c = 1.0, sn = 0.0;
         if (q < ell) {
-          const double hpq = H[p * ell + q];
+          const double hpq = H[p * ldh + q];
           if (hpq != 0.0) {
-            const double tau = (H[q * ell + q] - H[p * ell + p]) / (2.0 * hpq);
+            const double tau = (H[q * ldh + q] - H[p * ldh + p]) / (2.0 * hpq);
             const double tt = (tau >= 0.0 ? 1.0 : -1.0) / (fabs(tau) + sqrt(1.0 + tau * tau));
             c = 1.0 / sqrt(1.0 + tt * tt);
-            s = tt * c;
+            sn = tt * c;
           }
         }
         s_p[tid] = p;
         s_q[tid] = q < ell ? q : -1;
         s_c[tid] = c;
-        s_s[tid] = s;
-        // the rotation acts on index p as c·x_p − s·x_q and on q as c·x_q + s·x_p; an index
-        // without a partner this round keeps its value (coefficients 1 and 0, itself as partner)
-        if (q < ell) {
-          s_self[p] = c; s_cp[p] = -s; s_partner[p] = q;
-          s_self[q] = c; s_cp[q] = s; s_partner[q] = p;
-        } else if (p < ell) {
-          s_self[p] = 1.0; s_cp[p] = 0.0; s_partner[p] = p;
-        }
+        s_s[tid] = sn;
       }
       __syncthreads();
-      // H <- Jᵀ H J in one pass from the old buffer into the new: for each element the rotated
-      // rows at columns b and partner(b), then the column rotation of those two values (the
-      // same operations, in the same order, as a row pass followed by a column pass)
-      for (int t = tid; t < ell * ell; t += kJacobiThreads) {
-        const int a = t / ell, b = t % ell;
-        const int pa = s_partner[a], pb = s_partner[b];
-        const double sa = s_self[a], ca = s_cp[a], sb = s_self[b], cb = s_cp[b];
-        const double rb = sa * H[a * ell + b] + ca * H[pa * ell + b];
-        const double rpb = sa * H[a * ell + pb] + ca * H[pa * ell + pb];
-        Hn[t] = sb * rb + cb * rpb;
-      }
-      // V <- V J, one thread per (row, pair)
-      for (int t = tid; t < half * ell; t += kJacobiThreads) {
-        const int pr = t / ell, i = t % ell;
-        const int p = s_p[pr], q = s_q[pr];
-        if (q < 0) continue;
-        const double c = s_c[pr], s = s_s[pr];
-        const double vp = V[i * ell + p], vq = V[i * ell + q];
-        V[i * ell + p] = c * vp - s * vq;
-        V[i * ell + q] = s * vp + c * vq;
-      }
+      // rows p, q of H and of Vt: p <- c·p − s·q, q <- s·p + c·q
+      rotate(H, ldh, true);
+      rotate(Vt, ell, true);
       __syncthreads();
-      double* tmp = H;
-      H = Hn;
-      Hn = tmp;
+      // columns p, q of H
+      rotate(H, ldh, false);
+      __syncthreads();
     }
   }
   // sort by decreasing eigenvalue (ties by index)
@@ -483,7 +498,7 @@ __global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ 
     for (int i = 0; i < ell; ++i) {
       int best = i;
       for (int j = i + 1; j < ell; ++j)
-        if (H[s_order[j] * ell + s_order[j]] > H[s_order[best] * ell + s_order[best]]) best = j;
+        if (H[s_order[j] * ldh + s_order[j]] > H[s_order[best] * ldh + s_order[best]]) best = j;
       const int tmp = s_order[i];
       s_order[i] = s_order[best];
       s_order[best] = tmp;
@@ -492,9 +507,16 @@ __global__ __launch_bounds__(kJacobiThreads) void k_jacobi(double* __restrict__ 
   __syncthreads();
   for (int t = tid; t < ell * ell; t += kJacobiThreads) {
     const int i = t / ell, c = t % ell;
-    U[i * ell + c] = V[i * ell + s_order[c]];
+    U[i * ell + c] = Vt[s_order[c] * ell + i];
   }
-  for (int c = tid; c < ell; c += kJacobiThreads) eig[c] = H[s_order[c] * ell + s_order[c]];
+  for (int c = tid; c < ell; c += kJacobiThreads) eig[c] = H[s_order[c] * ldh + s_order[c]];
+}
+
+size_t jacobi_lds_bytes(int ell) {
+  size_t n = 0;
+  if (ell <= kJacHLdsEll) n += (size_t)ell * jacobi_pitch(ell) * 8;
+  if (ell <= kJacVLdsEll) n += (size_t)ell * ell * 8;
+  return n;
 }
 
 // lora_down[i][k] = bf16(σ_i Σ_j Q[k][j] U[j][i]);  lora_up[n][i] = bf16(Σ_j Z[n][j] U[j][i] / σ_i)
@@ -653,7 +675,14 @@ hipError_t lowrank_impl(const T* W, int64_t N, int64_t K, int64_t ldw, const flo
   }
   if ((err = at_times(y, z)) != hipSuccess) return err;       // Z = Aᵀ Q = Bᵀ
   if ((err = gram(z, N, w.g)) != hipSuccess) return err;      // B Bᵀ
-  k_jacobi<<<dim3(1), dim3(kJacobiThreads), 0, s>>>(w.g, e, w.v, w.u, w.eig, w.r);
+  {
+    const size_t lds = jacobi_lds_bytes(e);
+    if ((err = hipFuncSetAttribute(reinterpret_cast<const void*>(&k_jacobi),
+                                   hipFuncAttributeMaxDynamicSharedMemorySize, (int)lds)) !=
+        hipSuccess)
+      return err;
+    k_jacobi<<<dim3(1), dim3(kJacobiThreads), lds, s>>>(w.g, e, w.v, w.u, w.eig);
+  }
   SVDQ_CHECK_LAUNCH();
   const int64_t nout = (r * K) + (N * r);
   k_factors<<<dim3((unsigned)ceil_div(nout, 256)), dim3(256), 0, s>>>(
