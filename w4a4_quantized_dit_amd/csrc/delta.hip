@@ -324,13 +324,8 @@ __global__ __launch_bounds__(kThreads, 2) void k_delta_act(
 #pragma unroll
           for (int b = 0; b < CB; ++b)
             if (i < own && cc0 + b < nchunk) {
-              float val;
-              const uint32_t e0 = e4m3_encode_pos(fabsf(v[i][b].x) * inv_c[i], &val) |
-                                  (__builtin_signbit(v[i][b].x) ? 0x80u : 0u);
-              const uint32_t e1 = e4m3_encode_pos(fabsf(v[i][b].y) * inv_c[i], &val) |
-                                  (__builtin_signbit(v[i][b].y) ? 0x80u : 0u);
               *reinterpret_cast<uint16_t*>(dst[i] + (cc0 + b) * kDChunk) =
-                  (uint16_t)(e0 | (e1 << 8));
+                  (uint16_t)e4m3_pack2(v[i][b].x * inv_c[i], v[i][b].y * inv_c[i]);
             }
       }
     };

@@ -85,6 +85,27 @@ __device__ __forceinline__ uint32_t e4m3_encode_signed(float q) {
   return e4m3_encode_pos(fabsf(q), &v) | ((__float_as_uint(q) >> 31) << 7);
 }
 
+// Four fp32 values -> four E4M3 codes (value i in byte i), round to nearest even, saturating at
+// ±448: the same codes as e4m3_encode_signed, from the hardware conversion after a clamp to
+// ±448 (the conversion turns values beyond the format's range into NaN).  An in-bounds
+// comparison over every code midpoint (and its fp32 neighbours), a 2^-12 grid over ±600 and a
+// million random finite values found no difference.
+__device__ __forceinline__ uint32_t e4m3_pack4(float a, float b, float c, float d) {
+  const float lo = -448.0f, hi = 448.0f;
+  int w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi),
+                                          __builtin_amdgcn_fmed3f(b, lo, hi), 0, false);
+  w = __builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(c, lo, hi),
+                                      __builtin_amdgcn_fmed3f(d, lo, hi), w, true);
+  return (uint32_t)w;
+}
+// Two values -> two E4M3 codes in the low 16 bits (as e4m3_pack4).
+__device__ __forceinline__ uint32_t e4m3_pack2(float a, float b) {
+  const float lo = -448.0f, hi = 448.0f;
+  return (uint32_t)__builtin_amdgcn_cvt_pk_fp8_f32(__builtin_amdgcn_fmed3f(a, lo, hi),
+                                                   __builtin_amdgcn_fmed3f(b, lo, hi), 0, false) &
+         0xFFFFu;
+}
+
 // MX block exponent ("MiniMax-H3 — MXFP8 (weight-quantized, vLLM-Omni native layout)", section
 // "Quant format": E8M0 scale per 32; block exponent by the OCP microscaling rule):
 // floor(log2 a) − emax for a block maximum a > 0, −127 for a == 0, clamped to [−127, 127].

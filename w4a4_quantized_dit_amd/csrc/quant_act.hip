@@ -269,12 +269,9 @@ __global__ __launch_bounds__(kGroupThreads * SPLIT) void k_quant_act(
               uint32_t cw[4];
 #pragma unroll
               for (int d = 0; d < 4; ++d) {
-                uint32_t w = 0;
-#pragma unroll
-                for (int t = 0; t < 4; ++t)
-                  w |= e4m3_encode_signed(__builtin_ldexpf(x[32 * b + 16 * v + 4 * d + t], -e))
-                       << (8 * t);
-                cw[d] = w;
+                const float* xs = x + 32 * b + 16 * v + 4 * d;
+                cw[d] = e4m3_pack4(__builtin_ldexpf(xs[0], -e), __builtin_ldexpf(xs[1], -e),
+                                   __builtin_ldexpf(xs[2], -e), __builtin_ldexpf(xs[3], -e));
               }
               if (valid)
                 reinterpret_cast<u32x4_t*>(codes + row * K + kb)[2 * b + v] =

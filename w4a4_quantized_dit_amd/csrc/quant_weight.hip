@@ -228,12 +228,8 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
         if (MODE == 3) {
           *reinterpret_cast<uint32_t*>(codes + n * (K / 2) + kc / 2) = e2m1_pack8(y);
         } else {
-          uint32_t w0 = 0, w1 = 0;
-#pragma unroll
-          for (int t = 0; t < 4; ++t) {
-            w0 |= e4m3_encode_signed(y[t]) << (8 * t);
-            w1 |= e4m3_encode_signed(y[4 + t]) << (8 * t);
-          }
+          const uint32_t w0 = e4m3_pack4(y[0], y[1], y[2], y[3]);
+          const uint32_t w1 = e4m3_pack4(y[4], y[5], y[6], y[7]);
           *reinterpret_cast<uint2*>(codes + n * K + kc) = uint2{w0, w1};
         }
         if ((cb & 3) == 0) reinterpret_cast<uint8_t*>(scales)[n * (K / 32) + kc / 32] = (uint8_t)(ex + 127);
