@@ -116,10 +116,12 @@ __device__ __forceinline__ int mx_exponent(float a, int emax) {
   return e < -127 ? -127 : (e > 127 ? 127 : e);
 }
 
-// NVFP4 block scale: q = a / d6, s = E4M3(q), S = s·g, inv = 1/S (0 when S == 0).
+// NVFP4 block scale: q = a / d6, s = E4M3(q), S = s·g, inv = 1/S (0 when S == 0).  The code
+// comes from the hardware conversion (as e4m3_pack2) and its value from the exact hardware
+// decode.
 __device__ __forceinline__ uint32_t nvfp4_block_scale(float a, float g, float d6, float* inv) {
-  float sval;
-  uint32_t code = e4m3_encode_pos(a / d6, &sval);
+  const uint32_t code = e4m3_pack2(a / d6, 0.0f) & 0xFFu;
+  const float sval = __builtin_amdgcn_cvt_f32_fp8((int)code, 0);
   float S = sval * g;
   *inv = (S != 0.0f) ? 1.0f / S : 0.0f;
   return code;
