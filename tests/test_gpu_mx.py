@@ -84,3 +84,41 @@ def test_mx_full_attention_projection(L, f):
     _, y = OL.forward(act, wt, up, FMTS[f])
     rel = check_y(host_bits(Y)[rows], y)
     print(f"[mx-full] {FMTS[f]}: {len(rows)} sampled rows, rel-L2 {rel:.2e}", flush=True)
+
+
+def test_mxfp8_codes_at_every_e4m3_midpoint(L):
+    """MXFP8 activation codes at the inputs where an E4M3 encoder can go wrong: every midpoint
+    between neighbouring E4M3 values (a tie, to even), the bf16 values on either side of it, the
+    subnormal range, and values past 448 that must saturate (the kernels' conversion turns those
+    into NaN unless clamped first).  Each 32-block holds 448 (block exponent 0, so the elements
+    are converted unscaled) and 31 such values; codes and scales bit-exact against the oracle."""
+    torch = torch_mod()
+    from oracle import mx as OM
+    from oracle.formats import bf16_bits_to_f32
+    vals = []
+    def dec(c):
+        e, m = (c >> 3) & 15, c & 7
+        return m / 512.0 if e == 0 else (1.0 + m / 8.0) * 2.0 ** (e - 7)
+    for c in range(0x7E):
+        mid = np.float32(0.5 * (dec(c) + dec(c + 1)))
+        b = int(np.array([mid], np.float32).view(np.uint32)[0] >> 16)
+        vals += [b, b - 1, b + 1]                 # the midpoint (exact in bf16) and its neighbours
+    over = np.array([448.5, 456, 463.9, 464, 464.1, 472, 480, 496, 504, 511], np.float32)
+    vals += list((over.view(np.uint32) >> 16).astype(int))
+    vals = np.array(vals, np.uint16)
+    vals = np.concatenate([vals, vals | 0x8000])  # both signs
+    n_blocks = -(-len(vals) // 31)
+    blocks = np.zeros((n_blocks, 32), np.uint16)
+    blocks[:, 0] = 0x43E0                          # 448
+    fill = np.resize(vals, n_blocks * 31).reshape(n_blocks, 31)
+    blocks[:, 1:] = fill
+    K = 1024
+    rows = -(-n_blocks * 32 // K)
+    X = np.zeros(rows * K, np.uint16)
+    X[:blocks.size] = blocks.reshape(-1)
+    X = X.reshape(rows, K)
+    codes, scales, g, D = L.quantize_activation(dev_bf16(X), None, None, None, 3)
+    torch.cuda.synchronize()
+    ref_codes, ref_scales = OM.mx_quantize(bf16_bits_to_f32(X), "e4m3")
+    assert np.array_equal(scales.cpu().numpy(), ref_scales)
+    assert np.array_equal(codes.cpu().numpy(), ref_codes)
