@@ -125,7 +125,8 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
     const int next = i0 + kRankChunk;
     const int rn = r - next < kRankChunk ? r - next : kRankChunk;
     if (next < r) load_chunk(next, rn, pd, pu);
-    for (int i = 0; i < rc; ++i) {
+#pragma unroll 4
+    for (int i = 0; i < rc; ++i) {  // unrolled: the next ranks' LDS reads overlap these FMAs
       const double* dp = s_down + i * kTileCols + cb * 8;
       const double* upp = s_up + i * kTileRows + rg * 8;
       double d[8], u[8];
