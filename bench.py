@@ -105,7 +105,7 @@ def measured_traffic(workload):
 
 
 def gpu_cotenants():
-    """Other processes holding a GPU context on this machine (the driver lists one directory per
+    """Other processes holding a GPU context on this machine (the kernel module lists one directory per
     process under /sys/class/kfd/kfd/proc), read just before the timed steps; None where that
     listing does not exist."""
     root = "/sys/class/kfd/kfd/proc"
@@ -574,7 +574,7 @@ def main():
     args = ap.parse_args()
     if args.gpus != 1:
         print(f"bench.py measures one GPU only (asked for --gpus {args.gpus}); the layer is "
-              "data-parallel over rows and this build has no multi-GPU path.", file=sys.stderr)
+              "data-parallel over rows and the library has no multi-GPU path.", file=sys.stderr)
         sys.exit(2)
 
     import torch
