@@ -353,9 +353,14 @@ def setup(torch, workload):
         w_codes = torch.empty(N, K // 2, dtype=u8, device=dev)
         w_scales = torch.empty(N, K // 16, dtype=u8, device=dev)
         g_w = torch.empty(1, device=dev)
+        # the residual formed once and kept in a workspace between the amax and the codes
+        nb = _lib.svdq_quantize_weight_workspace_bytes(0, N, K)
+        wbuf = torch.empty(nb + 256, dtype=u8, device=dev)
+        woff = (-wbuf.data_ptr()) % 256
+        wq_ws = wbuf[woff:woff + nb]
 
         def wq(Xi):
-            _lib.svdq_quantize_weight(0, Wd, lam, downd, upd, r, w_codes, w_scales, g_w)
+            _lib.svdq_quantize_weight_ws(0, Wd, lam, downd, upd, r, w_codes, w_scales, g_w, wq_ws)
     if workload in ("attn", "mlp-down-sweep"):
         a_codes = torch.empty(M, K // 2, dtype=u8, device=dev)
         a_scales = torch.empty(M, K // 16, dtype=u8, device=dev)
@@ -399,7 +404,7 @@ def setup(torch, workload):
                 _lib.svdq_calibrate_lambda(Xi, seg, Wd, m, 0.5, 0, ax, aw, lam, amax)
 
             def wq_m(Xi, fd=fd, fu=fu):
-                _lib.svdq_quantize_weight(0, Wd, lam, fd, fu, r, w_codes, w_scales, g_w)
+                _lib.svdq_quantize_weight_ws(0, Wd, lam, fd, fu, r, w_codes, w_scales, g_w, wq_ws)
 
             def qa_m(Xi, fd=fd):
                 _lib.svdq_quant_act_lowrank_down(0, Xi, lam, amax, fd, r, a_codes, a_scales,

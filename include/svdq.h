@@ -237,6 +237,23 @@ svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t 
                                  void* scales, float* tensor_scale, svdq_stream_t stream);
 
 /*
+ * svdq_quantize_weight with a caller workspace (same passage, arguments, results and
+ * validation).  NVFP4 needs max|R32| before any code, so without a workspace the residual is
+ * formed twice (once for the maximum, once to quantise); here it is formed once, R32 is kept
+ * in the workspace (fp32 [N, K]) and the quantising pass reads it back.  Codes, scales and the
+ * tensor scale are identical to svdq_quantize_weight's.  workspace: at least
+ * svdq_quantize_weight_workspace_bytes(fmt, N, K) bytes (4·N·K for NVFP4, 0 for the
+ * single-pass formats, for which the call is svdq_quantize_weight), 256-byte aligned, device
+ * memory, the caller's; its contents after the call are unspecified.
+ */
+int64_t svdq_quantize_weight_workspace_bytes(int fmt, int64_t N, int64_t K);
+svdq_status svdq_quantize_weight_ws(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                    const float* lambda, const uint16_t* lora_down,
+                                    const uint16_t* lora_up, int64_t r, uint8_t* codes,
+                                    void* scales, float* tensor_scale, void* workspace,
+                                    int64_t workspace_bytes, svdq_stream_t stream);
+
+/*
  * Activation quantisation fused with the low-rank down-projection (the kernel sees X / λ:
  * "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", section "Why").
  *

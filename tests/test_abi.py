@@ -68,6 +68,23 @@ def test_quantize_weight_validation(lib):
     assert f(0, P, 64, 320, 320, None, P, P, 32, P, P, P, None) == SHAPE
 
 
+def test_quantize_weight_workspace_validation(lib):
+    f = lib.svdq_quantize_weight_ws
+    need = lib.svdq_quantize_weight_workspace_bytes(0, 64, 256)
+    assert need == 4 * 64 * 256
+    assert lib.svdq_quantize_weight_workspace_bytes(1, 64, 256) == 0      # single-pass formats
+    assert lib.svdq_quantize_weight_workspace_bytes(2, 64, 256) == 0
+    # the workspace variant validates like svdq_quantize_weight, then the workspace (NVFP4);
+    # every case here fails before any launch
+    assert f(7, P, 64, 256, 256, None, P, P, 32, P, P, P, P, need, None) == INVALID
+    assert f(0, P, 64, 256, 256, None, P, P, 12, P, P, P, P, need, None) == SHAPE
+    assert f(0, P, 64, 256, 256, None, P, P, 32, P, P, P, None, need, None) == NULLP
+    assert f(0, P, 64, 256, 256, None, P, P, 32, P, P, P, P + 16, need, None) == SHAPE
+    assert "aligned" in _err(lib)
+    assert f(0, P, 64, 256, 256, None, P, P, 32, P, P, P, P, need - 1, None) == SHAPE
+    assert "workspace" in _err(lib)
+
+
 def test_quant_act_and_gemm_validation(lib):
     qa = lib.svdq_quant_act_lowrank_down
     assert qa(0, P, 64, 256, 256, None, None, P, 32, P, P, None, P, None, None) == NULLP

@@ -195,3 +195,31 @@ def test_mispermuted_lambda_fails_parity(L):
     c, s, g, D = L.quantize_activation(dev_bf16(X), dev(lam_bad), dev(np.array([o["amax"]])),
                                        dev_bf16(o["down"]), 0)
     assert not np.array_equal(c.cpu().numpy(), o["act"]["codes"])
+
+
+@pytest.mark.parametrize("fmt,N,K,r", [(0, 768, 1024, 32), (0, 300, 512, 0), (0, 256, 256, 8),
+                                       (1, 300, 512, 16), (3, 256, 512, 8)])
+def test_quantize_weight_with_workspace_matches(L, fmt, N, K, r):
+    """svdq_quantize_weight_ws (the NVFP4 residual formed once, kept in the workspace and read
+    back by the quantising pass) gives the codes, scales and tensor scale of
+    svdq_quantize_weight bit for bit, and the oracle's; twice in a row, the second on a smaller
+    weight through the same workspace."""
+    from oracle import layer as OL
+    names = {0: "nvfp4", 1: "int4", 2: "mxfp4", 3: "mxfp8"}
+    ws = L.quantize_weight_workspace(N, K, fmt)
+    for n in (N, N // 2):
+        rng = np.random.default_rng(n)
+        W = synth.weight_bits(n, K, 11)
+        lam = (rng.random(K).astype(np.float32) + 0.5)
+        down = synth.weight_bits(r, K, 12) if r else np.zeros((0, K), np.uint16)
+        up = synth.weight_bits(n, r, 13) if r else np.zeros((n, 0), np.uint16)
+        args = (dev_bf16(W), dev(lam), dev_bf16(down) if r else None, dev_bf16(up) if r else None)
+        a = L.prepare_weight(*args, fmt)
+        b = L.prepare_weight(*args, fmt, workspace=ws)
+        ref = OL.prepare_weight(W, lam, down, up, names[fmt])
+        for pw in (a, b):
+            assert np.array_equal(pw.codes.cpu().numpy(), ref["codes"])
+            assert np.array_equal(pw.scales.cpu().numpy().view(np.uint8),
+                                  np.asarray(ref["scales"]).view(np.uint8))
+            if fmt == 0:
+                assert pw.g.cpu().numpy()[0] == ref["g"]

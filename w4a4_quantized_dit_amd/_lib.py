@@ -42,6 +42,9 @@ _SIGS = {
                                             ctypes.c_int, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
     "svdq_quantize_weight": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p, _c_p,
                                             _c_p, _i64, _c_p, _c_p, _c_p, _c_p]),
+    "svdq_quantize_weight_workspace_bytes": (_i64, [ctypes.c_int, _i64, _i64]),
+    "svdq_quantize_weight_ws": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p, _c_p,
+                                               _c_p, _i64, _c_p, _c_p, _c_p, _c_p, _i64, _c_p]),
     "svdq_quant_act_lowrank_down": (ctypes.c_int, [ctypes.c_int, _c_p, _i64, _i64, _i64, _c_p,
                                                    _c_p, _c_p, _i64, _c_p, _c_p, _c_p, _c_p,
                                                    _c_p, _c_p]),
@@ -283,6 +286,27 @@ def svdq_lambda_search(X, W, ax, aw, mask, alphas, fmt, omega, r, power_iters, r
         _ptr(best_index, torch.int32, "best_index", 1),
         _ptr(best_down, _bf16(), "best_down", r * K) if best_down is not None else None,
         _ptr(best_up, _bf16(), "best_up", N * r) if best_up is not None else None,
+        _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
+
+
+def svdq_quantize_weight_workspace_bytes(fmt, N, K):
+    return int(load().svdq_quantize_weight_workspace_bytes(int(fmt), int(N), int(K)))
+
+
+def svdq_quantize_weight_ws(fmt, W, lam, lora_down, lora_up, r, codes, scales, tensor_scale,
+                            workspace, stream=None):
+    """svdq_quantize_weight with the caller's workspace (uint8, 256-byte aligned; the NVFP4
+    residual is formed once and kept there)."""
+    torch = _torch()
+    N, K = W.shape
+    blk = _block(fmt)
+    _check(load().svdq_quantize_weight_ws(
+        int(fmt), _ptr(W, _bf16(), "W", rows=True), N, K, _ld(W), _ptr(lam, torch.float32, "lambda", K),
+        _ptr(lora_down if r else None, _bf16(), "lora_down", r * K),
+        _ptr(lora_up if r else None, _bf16(), "lora_up", N * r), int(r),
+        _ptr(codes, torch.uint8, "codes", _code_bytes(fmt, N, K)),
+        _ptr(scales, _scale_dtype(fmt), "scales", N * K // blk),
+        _ptr(tensor_scale, torch.float32, "tensor_scale", 1),
         _ptr(workspace, torch.uint8, "workspace"), workspace.numel(), _stream(stream)))
 
 

@@ -326,11 +326,12 @@ svdq_status svdq_bits_lost(const float* ax, const float* lambda, int64_t K, int6
                     fn);
 }
 
-svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
-                                 const float* lambda, const uint16_t* lora_down,
-                                 const uint16_t* lora_up, int64_t r, uint8_t* codes,
-                                 void* scales, float* tensor_scale, svdq_stream_t stream) {
-  const char* fn = "svdq_quantize_weight";
+namespace {
+// (static: inside the extern "C" block an unnamed namespace alone does not make it internal)
+static svdq_status check_quantize_weight(const char* fn, int fmt, const uint16_t* W, int64_t N,
+                                  int64_t K, int64_t ldw, const uint16_t* lora_down,
+                                  const uint16_t* lora_up, int64_t r, uint8_t* codes,
+                                  void* scales, float* tensor_scale) {
   TRY(check_fmt(fn, fmt));
   REQUIRE_PTR(W); REQUIRE_PTR(codes); REQUIRE_PTR(scales);
   if (fmt == SVDQ_NVFP4) REQUIRE_PTR(tensor_scale);
@@ -340,6 +341,48 @@ svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t 
   TRY(check_ld(fn, "ldw", ldw, K));
   TRY(check_rank(fn, r));
   if (r > 0) { REQUIRE_PTR(lora_down); REQUIRE_PTR(lora_up); }
+  return ok();
+}
+}  // namespace
+
+int64_t svdq_quantize_weight_workspace_bytes(int fmt, int64_t N, int64_t K) {
+  if (fmt != SVDQ_NVFP4 || N < 1 || K < 1) return 0;
+  return 4 * N * K;
+}
+
+svdq_status svdq_quantize_weight_ws(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                    const float* lambda, const uint16_t* lora_down,
+                                    const uint16_t* lora_up, int64_t r, uint8_t* codes,
+                                    void* scales, float* tensor_scale, void* workspace,
+                                    int64_t workspace_bytes, svdq_stream_t stream) {
+  const char* fn = "svdq_quantize_weight_ws";
+  TRY(check_quantize_weight(fn, fmt, W, N, K, ldw, lora_down, lora_up, r, codes, scales,
+                            tensor_scale));
+  const hipStream_t s = reinterpret_cast<hipStream_t>(stream);
+  if (fmt != SVDQ_NVFP4)  // single-pass formats: the workspace is not needed
+    return hip_result(svdq::launch_quantize_weight(fmt, W, N, K, ldw, lambda, lora_down, lora_up,
+                                                   r, codes, scales, tensor_scale, s),
+                      fn);
+  REQUIRE_PTR(workspace);
+  if (reinterpret_cast<uintptr_t>(workspace) % 256 != 0)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace must be 256-byte aligned", fn);
+  const int64_t need = svdq_quantize_weight_workspace_bytes(fmt, N, K);
+  if (workspace_bytes < need)
+    return fail(SVDQ_UNSUPPORTED_SHAPE, "%s: workspace of %lld bytes, needs %lld", fn,
+                (long long)workspace_bytes, (long long)need);
+  return hip_result(svdq::launch_quantize_weight_r32(W, N, K, ldw, lambda, lora_down, lora_up, r,
+                                                     codes, scales, tensor_scale,
+                                                     static_cast<float*>(workspace), s),
+                    fn);
+}
+
+svdq_status svdq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                 const float* lambda, const uint16_t* lora_down,
+                                 const uint16_t* lora_up, int64_t r, uint8_t* codes,
+                                 void* scales, float* tensor_scale, svdq_stream_t stream) {
+  const char* fn = "svdq_quantize_weight";
+  TRY(check_quantize_weight(fn, fmt, W, N, K, ldw, lora_down, lora_up, r, codes, scales,
+                            tensor_scale));
   return hip_result(svdq::launch_quantize_weight(fmt, W, N, K, ldw, lambda, lora_down, lora_up, r,
                                                  codes, scales, tensor_scale,
                                                  reinterpret_cast<hipStream_t>(stream)),

@@ -36,6 +36,13 @@ hipError_t launch_quantize_weight(int fmt, const uint16_t* W, int64_t N, int64_t
                                   int64_t r, uint8_t* codes, void* scales, float* tensor_scale,
                                   hipStream_t s);
 
+// NVFP4 launch_quantize_weight through R32 [N, K] fp32 scratch (the residual is formed once
+// and stored, and the quantising pass reads it back): same codes, scales and tensor scale.
+hipError_t launch_quantize_weight_r32(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                      const float* lambda, const uint16_t* down,
+                                      const uint16_t* up, int64_t r, uint8_t* codes, void* scales,
+                                      float* tensor_scale, float* R32, hipStream_t s);
+
 // R32 = fl32(λ·W − up·down) exactly as launch_quantize_weight forms it, into R32 [N, K]; with
 // tensor_scale, also the NVFP4 tensor scale max|R32| / 2688 (1 when the residual is zero).
 hipError_t launch_residual_f32(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,

@@ -265,6 +265,39 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
   }
 }
 
+// NVFP4 codes and scales of R32 [N, K] (fp32, from the residual pass) with the tensor amax in
+// amax_p: one thread per 16-block (64 contiguous bytes), the arithmetic of the quantising
+// residual pass (MODE 1) on the same fp32 values.
+__global__ __launch_bounds__(256) void k_quant_r32(const float* __restrict__ R32, int64_t nblk,
+                                                   const float* __restrict__ amax_p,
+                                                   uint8_t* __restrict__ codes,
+                                                   uint8_t* __restrict__ scales) {
+  const float amax = amax_p[0];
+  const float g = amax == 0.0f ? 1.0f : amax / 2688.0f;
+  const float d6 = 6.0f * g;
+  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk;
+       b += (int64_t)gridDim.x * 256) {
+    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(R32 + b * 16);
+    float x[16];
+#pragma unroll
+    for (int v = 0; v < 4; ++v) {
+      const f32x4_t t = __builtin_nontemporal_load(src + v);
+#pragma unroll
+      for (int e = 0; e < 4; ++e) x[4 * v + e] = t[e];
+    }
+    float a = 0.0f;
+#pragma unroll
+    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(x[e]));
+    float inv;
+    const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
+    float y[16];
+#pragma unroll
+    for (int e = 0; e < 16; ++e) y[e] = x[e] * inv;
+    *reinterpret_cast<uint2*>(codes + b * 8) = uint2{e2m1_pack8(y), e2m1_pack8(y + 8)};
+    scales[b] = (uint8_t)sc;
+  }
+}
+
 __global__ void k_amax_to_g(float* t) {
   const float a = t[0];
   t[0] = a == 0.0f ? 1.0f : a / 2688.0f;
@@ -295,6 +328,27 @@ hipError_t launch_residual_f32(const uint16_t* W, int64_t N, int64_t K, int64_t 
       W, N, K, ldw, lambda, down, up, (int)r, tensor_scale, reinterpret_cast<uint8_t*>(R32),
       nullptr);
   if (tensor_scale) k_amax_to_g<<<1, 1, 0, s>>>(tensor_scale);
+  return hipGetLastError();
+}
+
+hipError_t launch_quantize_weight_r32(const uint16_t* W, int64_t N, int64_t K, int64_t ldw,
+                                      const float* lambda, const uint16_t* down,
+                                      const uint16_t* up, int64_t r, uint8_t* codes, void* scales,
+                                      float* tensor_scale, float* R32, hipStream_t s) {
+  const int64_t tiles = ((N + kTileRows - 1) / kTileRows) * (K / kTileCols);
+  const size_t lds = lds_bytes(r);
+  hipError_t e = allow_lds<5>(lds);
+  if (e != hipSuccess) return e;
+  // R32 and its max|R32| in one residual pass; the codes from R32; then g = amax / 2688
+  k_zero1<<<1, 1, 0, s>>>(tensor_scale);
+  k_resid<5><<<dim3((unsigned)tiles), dim3(kThreads), lds, s>>>(
+      W, N, K, ldw, lambda, down, up, (int)r, tensor_scale, reinterpret_cast<uint8_t*>(R32),
+      nullptr);
+  const int64_t nblk = N * (K / 16);
+  const int64_t grid = (nblk + 255) / 256 < 4096 ? (nblk + 255) / 256 : 4096;
+  k_quant_r32<<<dim3((unsigned)grid), dim3(256), 0, s>>>(R32, nblk, tensor_scale, codes,
+                                                         reinterpret_cast<uint8_t*>(scales));
+  k_amax_to_g<<<1, 1, 0, s>>>(tensor_scale);
   return hipGetLastError();
 }
 

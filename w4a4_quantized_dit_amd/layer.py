@@ -125,14 +125,28 @@ def lambda_search(X, W, state, alphas, rows, fmt=NVFP4, omega=None, r=32, power_
     return out
 
 
-def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4):
-    """Quantised residual of diag(λ)·W − L1·L2 (W [N, K] bf16)."""
+def prepare_weight(W, lam, lora_down, lora_up, fmt=NVFP4, workspace=None):
+    """Quantised residual of diag(λ)·W − L1·L2 (W [N, K] bf16).  With `workspace` (uint8, at
+    least quantize_weight_workspace_bytes, 256-byte aligned) the NVFP4 residual is formed once."""
     torch = _torch()
     N, K = W.shape
     r = 0 if lora_down is None else lora_down.shape[0]
     codes, scales, g = _alloc_codes_scales(fmt, N, K, W.device)
-    _lib.svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, g)
+    if workspace is None:
+        _lib.svdq_quantize_weight(fmt, W, lam, lora_down, lora_up, r, codes, scales, g)
+    else:
+        _lib.svdq_quantize_weight_ws(fmt, W, lam, lora_down, lora_up, r, codes, scales, g,
+                                     workspace)
     return PreparedWeight(fmt, N, K, r, codes, scales, g, lora_up)
+
+
+def quantize_weight_workspace(N, K, fmt=NVFP4, device="cuda"):
+    """A 256-byte aligned workspace for prepare_weight(..., workspace=...)."""
+    torch = _torch()
+    nb = _lib.svdq_quantize_weight_workspace_bytes(fmt, N, K)
+    buf = torch.empty(nb + 256, dtype=torch.uint8, device=device)
+    off = (-buf.data_ptr()) % 256
+    return buf[off:off + nb]
 
 
 def gptq_hessian(X, lam, H=None):
