@@ -44,6 +44,7 @@ def _run(L, X, seg, W, mask, f, down, up):
     (1, 256, 256, 8, 2),         # a single row
     (517, 768, 256, 0, 0),       # no low-rank branch, λ = 1
     (260, 256, 768, 128, 1),     # rank 128
+    (100, 1280, 256, 8, 7),      # K stages not a multiple of the scale fetch (5 of MXFP4, 10 of MXFP8)
 ])
 def test_mx_shapes(L, f, M, K, N, r, mask):
     cfg = dict(M=M, K=K, N=N, seg=synth.segments(M), gen="outlier")
