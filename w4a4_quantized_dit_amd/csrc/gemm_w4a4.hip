@@ -84,8 +84,8 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
   __shared__ __attribute__((aligned(16))) uint8_t lds[kLdsBytes];
   // Tile walk: workgroup `slot` of an XCD takes positions slot, slot + P, slot + 2P, ... of that
   // XCD's run of the tile sequence (P workgroups per XCD; P = the run's length gives one tile per
-  // workgroup).  The next tile's first loads are issued before the current tile's store, so its
-  // load latency and the store's write burst overlap instead of following one another.
+  // workgroup).  After a tile's store the next tile's first loads are issued at once, ahead of
+  // its low-rank prologue, so their latency overlaps the prologue's own loads.
   // (Tile counts fit 32 bits: M < 2^31 rows and N < 2^31 columns in tiles of 256.)
   const int tiles_m = (int)((M + kBM - 1) / kBM), tiles_n = (int)(N / kBN);
   const int total = tiles_m * tiles_n, per_xcd = (total + 7) / 8;
@@ -276,9 +276,6 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
       iteration(std::integral_constant<int, 2>{}, s + 2, reinterpret_cast<const uint32_t*>(g1) + 8, g1);
       iteration(std::integral_constant<int, 3>{}, s + 3, reinterpret_cast<const uint32_t*>(g0), g0);
     }
-    // The next tile's first loads go out before this tile's store: the loads the last
-    // iterations repeated past the end have landed first (the scale buffers are rewritten),
-    // and g0, g1 are free.
     // Every wave passed the last barrier after its final fragment reads: the fp16 buffers are
     // free for the output staging (each wave its own 16 KB; the scale chunks lie above them).
     static_assert(8 * gemm_store_bytes<FM, FN>() <= kScaleOffset, "output staging fits the LDS");
@@ -288,8 +285,10 @@ __global__ __launch_bounds__(kThreads) void k_gemm_nvfp4(
                        n_base, core_out, row_to_cube, Y, ldy);
     const int seq_n = seq_of(k + 1);
     if (seq_n < 0) break;
-    // the next tile: the loads the last iterations repeated past the end have landed (the scale
-    // buffers are rewritten), the store's writes drain while the tile starts
+    // the next tile: the loads the last iterations repeated past the end have landed before its
+    // first loads rewrite the same scale buffers and registers.  (The wait also covers the
+    // store's writes; leaving it out, with the prologue's full wait covering both, measured the
+    // same.)
     wait_vmcnt<0>();
     tile_rows(seq_n, m_base, n_base);
     first_loads();
