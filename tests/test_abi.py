@@ -95,6 +95,12 @@ def test_quant_act_and_gemm_validation(lib):
     # at rank 128 the L1 slice and 1/λ of K = 16384 channels do not fit one CU's 160 KB of LDS
     assert qa(0, P, 64, 16384, 16384, None, None, P, 128, P, P, P, P, None, None) == SHAPE
     assert "LDS" in _err(lib)
+    # one step of 256 past the largest K at each rank (28416 at r = 0, 26624 at r = 32, 14592 at
+    # r = 128, which the GPU suite runs) is refused
+    for K, r in ((28672, 0), (26880, 32), (14848, 128)):
+        assert qa(0, P, 64, K, K, None, None, P if r else None, r, P, P, P, P if r else None,
+                  None, None) == SHAPE, (K, r)
+        assert "LDS" in _err(lib)
     g = lib.svdq_w4a4_gemm
     assert g(0, 64, 128, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
     assert g(0, 64, 256, 256, P, P, P, P, P, P, P, P, 32, None, None, P, 128, None) == SHAPE
