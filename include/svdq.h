@@ -109,9 +109,10 @@ svdq_status svdq_calibrate_lambda(const uint16_t* X, int64_t M, int64_t K, int64
 
 /*
  * Statistics-only "bits lost" proxy of a smoothing scale, per modality ("MiniMax-H3 NVFP4 —
- * what the smoothing scale should be calibrated on", section "Why": a channel whose absmax lies
- * below its quantisation group's loses log2(group absmax / channel absmax) bits, and λ reshapes
- * that profile because the kernel sees X / λ).
+ * what the smoothing scale should be calibrated on", section "Why": one block scale serves a
+ * whole group of channels, so each channel's resolution falls short by the log2 ratio of the
+ * group's largest smoothed magnitude to its own, and λ changes these ratios since smoothing comes
+ * before quantisation).
  *
  *   c[μ, k] = fp32(ax[μ, k] · fp32(1/λ[k]))                  (lambda may be NULL: λ = 1)
  *   out[μ]  = mean over k with c[μ, k] > 0 of log2(max_{j in k's group} c[μ, j] / c[μ, k])
@@ -180,8 +181,8 @@ svdq_status svdq_gptq_quantize_weight(int fmt, const uint16_t* W, int64_t N, int
  * λ grid search against the layer's output error ("MiniMax-H3 NVFP4 — what the smoothing scale
  * should be calibrated on", sections "Calibration": candidate λ scored against the OutputsError
  * objective with a number of low-rank refit iterations each, and "The metric that picks the
- * winner also hides the cost": that objective is the relative L2 against bf16 on rows drawn
- * uniformly from the packed sequence).  For each alphas[i] (host array, each in (0, 1)), in
+ * winner also hides the cost": that objective is the relative L2 against the bf16 layer over a
+ * uniform sample of all rows).  For each alphas[i] (host array, each in (0, 1)), in
  * stream order on the device:
  *   λ_i, act_amax_i from the statistics ax [3, K] and aw [K] (as svdq_calibrate_lambda, same
  *   modality_mask); when r > 0 the factors of svdq_lowrank_factors (omega [N, ell], ell,

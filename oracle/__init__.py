@@ -8,7 +8,7 @@ benchmark may import it.  It shares no code with the HIP library and imports not
 
 Sources (cited by page title and section):
   * "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", sections
-    "Why" (NVFP4: 16 consecutive channels under one FP8 scale set by the group absmax; the
+    "Why" (NVFP4: one E4M3 scale, from the block maximum, per 16 consecutive channels; the
     kernel sees X / λ; the statistics-only bits-lost proxy), "Calibration" (activation
     statistics accumulated under a modality mask feed λ), "The metric that picks the winner also hides the cost" (uniform-row and
     per-modality relative L2).

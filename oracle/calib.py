@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on":
   * section "Calibration": the per-channel activation statistics are accumulated under a
     modality mask, and the selected absmax feeds λ;
-  * opening section: one λ per input channel is shared by every modality because a linear
-    layer has one weight (W·λ);
+  * opening section: one λ per input channel is shared by every modality, since the layer's
+    single weight (W·λ) serves all of them;
   * section "Why": the kernel sees X / λ.
 
 Readings where the pages are silent:

@@ -3,7 +3,7 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 "DeltaQuant on MiniMax-H3":
-  * "Why DeltaQuant does not beat SVDQuant here": tokens inside a spatiotemporal cube are
+  * "Why DeltaQuant does not beat SVDQuant here": the tokens of one spatiotemporal cube are
     represented by one core plus small deltas;
   * "The audio win has a mechanism": non-video rows are covered by 1-D cubes of consecutive
     rows ("cover_remaining");

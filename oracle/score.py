@@ -3,8 +3,8 @@
 TEST INFRASTRUCTURE ONLY (see the package docstring).
 
 "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", section "The metric that
-picks the winner also hides the cost": relative L2 against bf16, once on rows drawn uniformly
-from the packed sequence (the calibration's own column) and once on rows sampled per modality.
+picks the winner also hides the cost": relative L2 against bf16, once over a uniform sample of
+all rows of the packed sequence (the column the calibration itself reports) and once per modality.
 
     rel_μ = sqrt(Σ (Y − Y_ref)²) / sqrt(Σ Y_ref²)   over the sampled rows of group μ,
     Y_ref = bf16(X @ Wᵀ) from the unsmoothed bf16 X and W (product in float64).

@@ -5,8 +5,8 @@ TEST INFRASTRUCTURE ONLY (see the package docstring).
 "MiniMax-H3 NVFP4 — what the smoothing scale should be calibrated on", sections "Calibration"
 (a grid of 39 candidate λ, built from the activation statistics accumulated under a modality
 mask, each scored with the OutputsError objective) and "The metric that picks the winner also
-hides the cost" (that objective is the relative L2 of the layer output against bf16, on rows
-drawn uniformly from the packed sequence, the rank-32 branch included).
+hides the cost" (the objective: relative L2 of the layer's output against the bf16 layer over a
+uniform sample of all rows, with the rank-32 branch in the output).
 
 Readings where the pages are silent:
   * the grid is the migration strength α of λ_k = a_k^α / w_k^(1−α) (a_k the masked

@@ -50,7 +50,7 @@ def test_lambda_equal_to_a_profile_flattens_that_modality():
 
 
 def test_uncorrelated_lambda_sharpens_the_other_modalities():
-    # page 1 "Why": dividing by a vector uncorrelated with a modality's own channel profile
+    # page 1 "Why": smoothing by a λ unrelated to a modality's own channel profile
     # sharpens it, while λ built from a modality's own statistics flattens that modality
     rng = np.random.default_rng(2)
     K = 4096

@@ -1,6 +1,6 @@
 // Per-modality relative-L2 scoring against the unquantised bf16 layer ("MiniMax-H3 NVFP4 — what
 // the smoothing scale should be calibrated on", section "The metric that picks the winner also
-// hides the cost": relative L2 on rows drawn uniformly and on rows sampled per modality).
+// hides the cost": relative L2 over a uniform sample of all rows and over each modality's rows).
 //
 // For the sampled rows, Y_ref = bf16(X·Wᵀ) is computed on bf16 MFMA (fp32 accumulation) with the
 // X rows gathered by index (k_ref_rows).  Either the rows are stored (a sweep over several λ

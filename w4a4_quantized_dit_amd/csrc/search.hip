@@ -1,8 +1,8 @@
 // λ grid search against the layer's output error ("MiniMax-H3 NVFP4 — what the smoothing scale
 // should be calibrated on", sections "Calibration" — a grid of candidate λ scored against the
 // OutputsError objective — and "The metric that picks the winner also hides the cost" — that
-// objective is the relative L2 of the layer output against bf16 on rows drawn uniformly from the
-// packed sequence).  For each α of the grid, entirely on the device and in stream order:
+// objective is the relative L2 of the layer's output against the bf16 layer over a uniform sample
+// of all rows).  For each α of the grid, entirely on the device and in stream order:
 //   λ_α from the calibration statistics; rank-r factors of diag(λ_α)·Wᵀ (randomized SVD);
 //   residual weight quantisation; activation quantisation of the sampled rows (static amax of
 //   λ_α) with the low-rank down-projection; the W4A4 GEMM; relative L2 against bf16(X·Wᵀ)
