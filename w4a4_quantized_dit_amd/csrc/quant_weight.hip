@@ -266,35 +266,43 @@ __global__ __launch_bounds__(kThreads) void k_resid(const uint16_t* __restrict__
 }
 
 // NVFP4 codes and scales of R32 [N, K] (fp32, from the residual pass) with the tensor amax in
-// amax_p: one thread per 16-block (64 contiguous bytes), the arithmetic of the quantising
-// residual pass (MODE 1) on the same fp32 values.
-__global__ __launch_bounds__(256) void k_quant_r32(const float* __restrict__ R32, int64_t nblk,
+// amax_p, the arithmetic of the quantising residual pass (MODE 1) on the same fp32 values.  R32
+// is read in 1 KB pieces, lane l of a wave holding bytes [16 l, 16 l + 16) of a piece, so every
+// load instruction covers 8 whole cache lines (one thread per 64-byte block made each
+// instruction touch 32 lines, every line four times).  Four lanes hold one 16-block: their
+// maxima combine with two lane exchanges, each computes the block scale, and lane l writes the
+// two code bytes of its four values (128 contiguous bytes per piece) and lane 4b the scale byte
+// of block b.  A wave takes kPieces consecutive pieces per round.
+constexpr int kPieces = 4;
+__global__ __launch_bounds__(256) void k_quant_r32(const float* __restrict__ R32, int64_t npiece,
                                                    const float* __restrict__ amax_p,
                                                    uint8_t* __restrict__ codes,
                                                    uint8_t* __restrict__ scales) {
   const float amax = amax_p[0];
   const float g = amax == 0.0f ? 1.0f : amax / 2688.0f;
   const float d6 = 6.0f * g;
-  for (int64_t b = (int64_t)blockIdx.x * 256 + threadIdx.x; b < nblk;
-       b += (int64_t)gridDim.x * 256) {
-    const f32x4_t* src = reinterpret_cast<const f32x4_t*>(R32 + b * 16);
-    float x[16];
+  const int lane = threadIdx.x & 63;
+  const int64_t nwave = (int64_t)gridDim.x * 4;
+  for (int64_t p0 = ((int64_t)blockIdx.x * 4 + (threadIdx.x >> 6)) * kPieces; p0 < npiece;
+       p0 += nwave * kPieces) {
+    f32x4_t x[kPieces];
 #pragma unroll
-    for (int v = 0; v < 4; ++v) {
-      const f32x4_t t = __builtin_nontemporal_load(src + v);
+    for (int u = 0; u < kPieces; ++u)
+      if (p0 + u < npiece)
+        x[u] = __builtin_nontemporal_load(reinterpret_cast<const f32x4_t*>(R32 + (p0 + u) * 256) + lane);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) x[4 * v + e] = t[e];
+    for (int u = 0; u < kPieces; ++u) {
+      if (p0 + u >= npiece) break;
+      float a = fmaxf(fmaxf(fabsf(x[u][0]), fabsf(x[u][1])), fmaxf(fabsf(x[u][2]), fabsf(x[u][3])));
+      a = fmaxf(a, __shfl_xor(a, 1));
+      a = fmaxf(a, __shfl_xor(a, 2));
+      float inv;
+      const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
+      uint32_t w = e2m1_pack2<0>(0u, x[u][0] * inv, x[u][1] * inv);
+      w = e2m1_pack2<1>(w, x[u][2] * inv, x[u][3] * inv);
+      *reinterpret_cast<uint16_t*>(codes + (p0 + u) * 128 + 2 * lane) = (uint16_t)w;
+      if ((lane & 3) == 0) scales[(p0 + u) * 16 + (lane >> 2)] = (uint8_t)sc;
     }
-    float a = 0.0f;
-#pragma unroll
-    for (int e = 0; e < 16; ++e) a = fmaxf(a, fabsf(x[e]));
-    float inv;
-    const uint32_t sc = nvfp4_block_scale(a, g, d6, &inv);
-    float y[16];
-#pragma unroll
-    for (int e = 0; e < 16; ++e) y[e] = x[e] * inv;
-    *reinterpret_cast<uint2*>(codes + b * 8) = uint2{e2m1_pack8(y), e2m1_pack8(y + 8)};
-    scales[b] = (uint8_t)sc;
   }
 }
 
@@ -344,9 +352,10 @@ hipError_t launch_quantize_weight_r32(const uint16_t* W, int64_t N, int64_t K, i
   k_resid<5><<<dim3((unsigned)tiles), dim3(kThreads), lds, s>>>(
       W, N, K, ldw, lambda, down, up, (int)r, tensor_scale, reinterpret_cast<uint8_t*>(R32),
       nullptr);
-  const int64_t nblk = N * (K / 16);
-  const int64_t grid = (nblk + 255) / 256 < 4096 ? (nblk + 255) / 256 : 4096;
-  k_quant_r32<<<dim3((unsigned)grid), dim3(256), 0, s>>>(R32, nblk, tensor_scale, codes,
+  const int64_t npiece = N * (K / 256);  // 1 KB pieces of R32 (K % 256 == 0)
+  const int64_t waves = (npiece + kPieces - 1) / kPieces;
+  const int64_t grid = (waves + 3) / 4 < 2048 ? (waves + 3) / 4 : 2048;
+  k_quant_r32<<<dim3((unsigned)grid), dim3(256), 0, s>>>(R32, npiece, tensor_scale, codes,
                                                          reinterpret_cast<uint8_t*>(scales));
   k_amax_to_g<<<1, 1, 0, s>>>(tensor_scale);
   return hipGetLastError();
