@@ -11,7 +11,8 @@
 // subtract after the multiply.  NVFP4 blocks are quantised from registers; an int4 group of 64
 // spans four lanes, which combine their absmax with two shuffles.  NVFP4 needs the tensor amax
 // first: a pass computes max|R32| (one atomic per block), then the quantising pass recomputes
-// the residual instead of storing it.
+// the residual instead of storing it; with a caller workspace the residual pass stores R32 with
+// its maximum and k_quant_r32 quantises the stored values instead.
 #include "device.h"
 #include "launch.h"
 
